@@ -1,0 +1,160 @@
+"""fp64 CPU oracle for block-quantized weight GEMV (ctypes wrapper over oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product package.  It shares no
+code with the HIP library and imports nothing from it.
+
+Functions follow oracle.c; see the header there for the definitions and the
+passages of the pages each format rests on.  The verdict metric is
+``max_rel_err``: max over outputs of |yhat - y| / L1, where L1 is the sum of
+|w * x| over the row (zero L1 requires yhat == 0 exactly).
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+Q8_0, Q4_0, MXFP4 = 0, 1, 2
+X_F32, X_BF16 = 0, 1
+MOE_GATE_UP, MOE_DOWN = 0, 1
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17}
+
+
+def build(force=False):
+    """Compile oracle.c with gcc (-O2, OpenMP, no fast-math) into liboracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+        for name, rt, args in [
+            ("orc_fp16", ctypes.c_double, [ctypes.c_uint16]),
+            ("orc_bf16", ctypes.c_double, [ctypes.c_uint16]),
+            ("orc_e8m0", ctypes.c_double, [ctypes.c_uint8]),
+            ("orc_e2m1", ctypes.c_double, [ctypes.c_uint8]),
+            ("orc_decode", ctypes.c_int, [ctypes.c_int, vp, i64, i64, dp]),
+            ("orc_gemv", ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, ctypes.c_int, i64,
+                                        vp, i64, dp, dp]),
+            ("orc_moe", ctypes.c_int, [ctypes.c_int, vp, i64, i64, i64, vp, vp, i64, i64,
+                                       vp, ctypes.c_int, ctypes.c_int, vp, i64, dp, dp]),
+        ]:
+            f = getattr(L, name)
+            f.restype, f.argtypes = rt, args
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def fp16(h):
+    return lib().orc_fp16(int(h))
+
+
+def bf16(b):
+    return lib().orc_bf16(int(b))
+
+
+def e8m0(e):
+    return lib().orc_e8m0(int(e))
+
+
+def e2m1(c):
+    return lib().orc_e2m1(int(c))
+
+
+def _blocks(fmt, blocks, n, k):
+    b = np.ascontiguousarray(blocks, dtype=np.uint8)
+    if b.size != n * (k // 32) * BLOCK_BYTES[fmt]:
+        raise ValueError("block array size does not match n, k")
+    return b
+
+
+def _x(x, xt):
+    if xt == X_F32:
+        return np.ascontiguousarray(x, dtype=np.float32)
+    return np.ascontiguousarray(x, dtype=np.uint16)
+
+
+def decode(fmt, blocks, n, k):
+    """All weights as float64 [n, k]."""
+    b = _blocks(fmt, blocks, n, k)
+    w = np.empty((n, k), dtype=np.float64)
+    if lib().orc_decode(fmt, _ptr(b), n, k, _ptr(w)) != 0:
+        raise ValueError("orc_decode rejected its arguments")
+    return w
+
+
+def gemv(fmt, blocks, n, k, x, xt, rows=None):
+    """y, l1 as float64 [m, nrows]; x is [m, k] (float32 or bf16 bit patterns)."""
+    b = _blocks(fmt, blocks, n, k)
+    xa = _x(x, xt).reshape(-1, k)
+    m = xa.shape[0]
+    if rows is None:
+        nrows, rp = n, None
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows, rp = r.size, _ptr(r)
+    y = np.empty((m, nrows), dtype=np.float64)
+    l1 = np.empty((m, nrows), dtype=np.float64)
+    if lib().orc_gemv(fmt, _ptr(b), n, k, _ptr(xa), xt, m, rp, nrows, _ptr(y), _ptr(l1)) != 0:
+        raise ValueError("orc_gemv rejected its arguments")
+    return y, l1
+
+
+def moe(fmt, experts, n_experts, n, k, ids, g, x, xt, mode, rows=None):
+    """GATE_UP: y, l1 [m, top_k, nrows]; DOWN: y, l1 [m, nrows]."""
+    e = np.ascontiguousarray(experts, dtype=np.uint8)
+    if e.size != n_experts * n * (k // 32) * BLOCK_BYTES[fmt]:
+        raise ValueError("expert array size does not match")
+    ida = np.ascontiguousarray(ids, dtype=np.int32)
+    m, top_k = ida.shape
+    ga = None if g is None else np.ascontiguousarray(g, dtype=np.float32).reshape(m, top_k)
+    xa = _x(x, xt)
+    if rows is None:
+        nrows, rp = n, None
+    else:
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows, rp = r.size, _ptr(r)
+    shape = (m, top_k, nrows) if mode == MOE_GATE_UP else (m, nrows)
+    y = np.empty(shape, dtype=np.float64)
+    l1 = np.empty(shape, dtype=np.float64)
+    rc = lib().orc_moe(fmt, _ptr(e), n_experts, n, k, _ptr(ida),
+                       None if ga is None else _ptr(ga), m, top_k, _ptr(xa), xt, mode,
+                       rp, nrows, _ptr(y), _ptr(l1))
+    if rc != 0:
+        raise ValueError("orc_moe rejected its arguments")
+    return y, l1
+
+
+def max_rel_err(yhat, y, l1):
+    """max |yhat - y| / l1; where l1 == 0 the output must be exactly 0 (else inf)."""
+    yhat = np.asarray(yhat, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    l1 = np.asarray(l1, dtype=np.float64)
+    diff = np.abs(yhat - y)
+    zero = l1 == 0
+    err = np.zeros_like(diff)
+    nz = ~zero
+    err[nz] = diff[nz] / l1[nz]
+    err[zero & (yhat != 0)] = np.inf
+    err[~np.isfinite(yhat)] = np.inf
+    return float(err.max()) if err.size else 0.0

@@ -1,0 +1,302 @@
+"""Pins for the fp64 oracle: each check reaches the expected value by a route
+other than the oracle's own code (library routines, literal values, exact
+rational arithmetic, closed forms, page facts)."""
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _page_facts():
+    facts = {}
+    with open(os.path.join(GOLD, "page_facts.txt")) as f:
+        for line in f:
+            line = line.split("|")[0].strip()
+            if line and not line.startswith("#"):
+                k, v = [s.strip() for s in line.split("=")]
+                facts[k] = v
+    return facts
+
+
+def _e2m1_table():
+    t = {}
+    with open(os.path.join(GOLD, "e2m1_values.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                c, v = line.split()
+                t[int(c)] = float(v)
+    return t
+
+
+# ------------------------------------------------------------- scalar decoders
+def test_fp16_all_patterns_match_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.fp16(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signs of zeros as well
+    assert math.copysign(1.0, oracle.fp16(0x8000)) == -1.0
+
+
+def test_bf16_all_patterns_match_ieee_single_top_half():
+    for b in range(0, 65536, 1):
+        ref = struct.unpack("<f", struct.pack("<I", b << 16))[0]
+        got = oracle.bf16(b)
+        if math.isnan(ref):
+            assert math.isnan(got)
+        else:
+            assert got == ref, hex(b)
+
+
+def test_bf16_literals():
+    assert oracle.bf16(0x3F80) == 1.0
+    assert oracle.bf16(0xC000) == -2.0
+    assert oracle.bf16(0x4049) == 3.140625
+    assert oracle.bf16(0x0001) == 2.0 ** -133
+
+
+def test_e8m0_literals():
+    assert oracle.e8m0(127) == 1.0
+    assert oracle.e8m0(128) == 2.0
+    assert oracle.e8m0(126) == 0.5
+    assert oracle.e8m0(119) == 0.00390625        # 2^-8, lower end of the MoE workload draw
+    assert oracle.e8m0(125) == 0.25              # 2^-2, upper end
+    assert oracle.e8m0(0) == 5.877471754111438e-39
+    assert oracle.e8m0(254) == 1.7014118346046923e38
+    assert math.isnan(oracle.e8m0(255))
+
+
+def test_e2m1_table_and_structure():
+    table = _e2m1_table()
+    for c in range(16):
+        assert oracle.e2m1(c) == table[c]
+    # sign bit is bit 3; magnitudes are increasing in the 3 low bits
+    mags = [oracle.e2m1(c) for c in range(8)]
+    assert mags == sorted(mags) and len(set(mags)) == 8
+    for c in range(8):
+        assert oracle.e2m1(c | 8) == -oracle.e2m1(c)
+
+
+def test_mxfp4_block_size_matches_pages():
+    facts = _page_facts()
+    bits = 8 * oracle.BLOCK_BYTES[oracle.MXFP4] / 32.0
+    assert bits == float(facts["mxfp4_bits_per_weight"])
+    assert 2 * 32 == int(facts["gpt_oss_20b_experts"]) * 2
+    assert wl.CONFIGS[4]["n_experts"] == int(facts["gpt_oss_20b_experts"])
+    assert wl.CONFIGS[4]["top_k"] == int(facts["gpt_oss_20b_top_k"])
+
+
+# ------------------------------------------------------------ hand-built blocks
+def _hand_q8_block():
+    codes = [0, 1, -1, 2, -2, 127, -127, -128] + list(range(-4, 20))
+    blk = bytes([0x00, 0x38]) + bytes([(c + 256) % 256 for c in codes])   # d = 0x3800 = 0.5
+    return np.frombuffer(blk, dtype=np.uint8), [0.5 * c for c in codes]
+
+
+def _hand_q4_block():
+    body = bytes([(j & 15) | (((15 - j) & 15) << 4) for j in range(16)])
+    blk = bytes([0x00, 0x40]) + body                                       # d = 0x4000 = 2.0
+    want = [2.0 * (j - 8) for j in range(16)] + [2.0 * ((15 - j) - 8) for j in range(16)]
+    return np.frombuffer(blk, dtype=np.uint8), want
+
+
+def _hand_mxfp4_block():
+    table = _e2m1_table()
+    body = bytes([(j & 15) | (((15 - j) & 15) << 4) for j in range(16)])
+    blk = bytes([126]) + body                                              # scale 2^-1
+    want = [0.5 * table[j] for j in range(16)] + [0.5 * table[15 - j] for j in range(16)]
+    return np.frombuffer(blk, dtype=np.uint8), want
+
+
+@pytest.mark.parametrize("fmt,maker", [(oracle.Q8_0, _hand_q8_block), (oracle.Q4_0, _hand_q4_block),
+                                       (oracle.MXFP4, _hand_mxfp4_block)])
+def test_hand_built_block_decodes(fmt, maker):
+    blk, want = maker()
+    w = oracle.decode(fmt, blk, 1, 32)
+    assert w.shape == (1, 32)
+    assert list(w[0]) == want
+
+
+def test_q8_subnormal_and_negative_scale():
+    blk = np.frombuffer(bytes([0x01, 0x80]) + bytes([3] * 32), dtype=np.uint8)   # d = -2^-24
+    w = oracle.decode(oracle.Q8_0, blk, 1, 32)
+    assert np.all(w == -3.0 * 2.0 ** -24)
+
+
+def test_rows_and_blocks_are_row_major():
+    # two rows x two blocks, each block all-equal with a distinct scale
+    blks = []
+    for d in (0x3C00, 0x4000, 0x4200, 0x4400):        # 1, 2, 3, 4
+        blks.append(bytes([d & 0xFF, d >> 8]) + bytes([1] * 32))
+    arr = np.frombuffer(b"".join(blks), dtype=np.uint8)
+    w = oracle.decode(oracle.Q8_0, arr, 2, 64)
+    assert np.all(w[0, :32] == 1) and np.all(w[0, 32:] == 2)
+    assert np.all(w[1, :32] == 3) and np.all(w[1, 32:] == 4)
+
+
+# --------------------------------------------------------- exact rational sums
+def _frac_weights(fmt, blocks, n, k):
+    """Exact weights as Fractions, decoded by numpy / struct / the E2M1 table."""
+    table = _e2m1_table()
+    bb = oracle.BLOCK_BYTES[fmt]
+    b = blocks.reshape(n, k // 32, bb)
+    W = [[None] * k for _ in range(n)]
+    for r in range(n):
+        for blk in range(k // 32):
+            row = b[r, blk]
+            if fmt == oracle.MXFP4:
+                sc = Fraction(2) ** (int(row[0]) - 127)
+                body = row[1:]
+            else:
+                sc = Fraction(float(np.array([int(row[0]) | (int(row[1]) << 8)], dtype=np.uint16).view(np.float16)[0]))
+                body = row[2:]
+            for i in range(32):
+                if fmt == oracle.Q8_0:
+                    v = int(np.int8(body[i]))
+                elif fmt == oracle.Q4_0:
+                    v = (int(body[i]) & 15) - 8 if i < 16 else (int(body[i - 16]) >> 4) - 8
+                else:
+                    c = (int(body[i]) & 15) if i < 16 else (int(body[i - 16]) >> 4)
+                    v = Fraction(table[c])
+                W[r][32 * blk + i] = sc * v
+    return W
+
+
+def _frac_x(x, xt):
+    if xt == oracle.X_F32:
+        return [Fraction(float(v)) for v in x.reshape(-1)]
+    return [Fraction(struct.unpack("<f", struct.pack("<I", int(v) << 16))[0]) for v in x.reshape(-1)]
+
+
+@pytest.mark.parametrize("fmt", [oracle.Q8_0, oracle.Q4_0, oracle.MXFP4])
+@pytest.mark.parametrize("xt", [oracle.X_F32, oracle.X_BF16])
+def test_brute_force_4x64_exact(fmt, xt):
+    n, k, m = 4, 64, 2
+    blocks = wl.blocks_for(fmt, n, k, config=90 + fmt, matrix=xt)
+    rng = wl.rng_for(91, fmt, "x")
+    x = wl.x_f32((m, k), rng) if xt == oracle.X_F32 else wl.x_bf16_bits((m, k), rng)
+    y, l1 = oracle.gemv(fmt, blocks, n, k, x, xt)
+    W = _frac_weights(fmt, blocks, n, k)
+    X = _frac_x(x, xt)
+    for t in range(m):
+        for r in range(n):
+            prods = [W[r][c] * X[t * k + c] for c in range(k)]
+            exact = sum(prods, Fraction(0))
+            a = sum((abs(p) for p in prods), Fraction(0))
+            assert abs(Fraction(y[t, r]) - exact) <= Fraction(1, 2 ** 50) * a
+            assert abs(Fraction(l1[t, r]) - a) <= Fraction(1, 2 ** 50) * a
+
+
+def test_numpy_blas_cross_check_c0_size():
+    n = k = 2048
+    blocks = wl.blocks_for(oracle.Q8_0, n, k, config=0, matrix=0)
+    x = wl.x_f32((1, k), wl.rng_for(0, 0, "x"))
+    W = oracle.decode(oracle.Q8_0, blocks, n, k)
+    y, l1 = oracle.gemv(oracle.Q8_0, blocks, n, k, x, oracle.X_F32)
+    ref = W @ x.astype(np.float64)[0]
+    assert np.max(np.abs(ref - y[0]) / l1[0]) < 1e-13
+    assert np.allclose(l1[0], np.abs(W) @ np.abs(x.astype(np.float64)[0]), rtol=1e-13)
+
+
+def test_row_subset_matches_full():
+    n, k = 64, 256
+    blocks = wl.blocks_for(oracle.Q4_0, n, k, config=92, matrix=0)
+    x = wl.x_bf16_bits((3, k), wl.rng_for(92, 0, "x"))
+    y, l1 = oracle.gemv(oracle.Q4_0, blocks, n, k, x, oracle.X_BF16)
+    rows = np.array([63, 0, 17, 17])
+    ys, l1s = oracle.gemv(oracle.Q4_0, blocks, n, k, x, oracle.X_BF16, rows=rows)
+    assert np.array_equal(ys, y[:, rows]) and np.array_equal(l1s, l1[:, rows])
+
+
+# --------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("fmt", [oracle.Q8_0, oracle.Q4_0, oracle.MXFP4])
+def test_all_equal_blocks_closed_form(fmt):
+    n, k = 3, 96
+    x = wl.x_f32((1, k), wl.rng_for(93, fmt, "x"))
+    sx = float(np.sum(x.astype(np.float64)))
+    if fmt == oracle.Q8_0:
+        blk, val = bytes([0x00, 0x3A]) + bytes([256 - 5] * 32), 0.75 * -5          # d = 0.75
+    elif fmt == oracle.Q4_0:
+        blk, val = bytes([0x00, 0x3A]) + bytes([0x33] * 16), 0.75 * (3 - 8)
+    else:
+        blk, val = bytes([125]) + bytes([0xDD] * 16), 0.25 * -3.0                  # code 13 = -3
+    blocks = np.frombuffer(blk * (n * k // 32), dtype=np.uint8)
+    y, _ = oracle.gemv(fmt, blocks, n, k, x, oracle.X_F32)
+    assert np.allclose(y[0], val * sx, rtol=0, atol=1e-12 * abs(val) * np.sum(np.abs(x)))
+
+
+@pytest.mark.parametrize("fmt", [oracle.Q8_0, oracle.Q4_0, oracle.MXFP4])
+def test_one_hot_x_selects_a_column(fmt):
+    n, k = 5, 128
+    blocks = wl.blocks_for(fmt, n, k, config=94, matrix=fmt)
+    W = oracle.decode(fmt, blocks, n, k)
+    for col in (0, 31, 32, 77, 127):
+        x = np.zeros((1, k), dtype=np.float32)
+        x[0, col] = 1.0
+        y, l1 = oracle.gemv(fmt, blocks, n, k, x, oracle.X_F32)
+        assert np.array_equal(y[0], W[:, col])
+        assert np.array_equal(l1[0], np.abs(W[:, col]))
+
+
+def test_error_metric():
+    y = np.array([1.0, 0.0, 2.0])
+    l1 = np.array([10.0, 0.0, 4.0])
+    assert oracle.max_rel_err(np.array([1.1, 0.0, 2.0]), y, l1) == pytest.approx(0.01)
+    assert oracle.max_rel_err(np.array([1.0, 1e-30, 2.0]), y, l1) == math.inf
+    assert oracle.max_rel_err(np.array([1.0, 0.0, np.nan]), y, l1) == math.inf
+
+
+# ----------------------------------------------------------------------- MoE
+def test_moe_hand_example_exact():
+    # 3 experts of a 1 x 32 Q8_0 matrix; expert e has all codes e+1, d = 1.0
+    experts = b"".join(bytes([0x00, 0x3C]) + bytes([e + 1] * 32) for e in range(3))
+    experts = np.frombuffer(experts, dtype=np.uint8)
+    ids = np.array([[2, 0]], dtype=np.int32)
+    g = np.array([[0.75, 0.25]], dtype=np.float32)
+    x = np.ones((1, 32), dtype=np.float32)
+    y, _ = oracle.moe(oracle.Q8_0, experts, 3, 1, 32, ids, g, x, oracle.X_F32, oracle.MOE_GATE_UP)
+    assert y[0, 0, 0] == 3 * 32 and y[0, 1, 0] == 1 * 32
+    h = np.stack([np.full(32, 2.0), np.full(32, -1.0)]).astype(np.float32).reshape(1, 2, 32)
+    y, l1 = oracle.moe(oracle.Q8_0, experts, 3, 1, 32, ids, g, h, oracle.X_F32, oracle.MOE_DOWN)
+    # 0.75 * (3*2*32) + 0.25 * (1*-1*32) = 144 - 8
+    assert y[0, 0] == 136.0
+    assert l1[0, 0] == 0.75 * 192 + 0.25 * 32
+
+
+def test_moe_matches_dense_per_slot():
+    fmt, E, n, k, m, top_k = oracle.MXFP4, 6, 16, 64, 3, 2
+    experts = np.concatenate([wl.blocks_for(fmt, n, k, config=95, matrix=e).reshape(-1) for e in range(E)])
+    _, ids, g = wl.router_topk(m, E, top_k, wl.rng_for(95, 0, "router"))
+    x = wl.x_bf16_bits((m, k), wl.rng_for(95, 0, "x"))
+    h = wl.x_bf16_bits((m, top_k, k), wl.rng_for(95, 0, "h"))
+    yg, _ = oracle.moe(fmt, experts, E, n, k, ids, g, x, oracle.X_BF16, oracle.MOE_GATE_UP)
+    yd, _ = oracle.moe(fmt, experts, E, n, k, ids, g, h, oracle.X_BF16, oracle.MOE_DOWN)
+    mat = n * (k // 32) * 17
+    for t in range(m):
+        acc = np.zeros(n)
+        for j in range(top_k):
+            e = ids[t, j]
+            Wb = experts[e * mat:(e + 1) * mat]
+            yj, _ = oracle.gemv(fmt, Wb, n, k, x[t:t + 1], oracle.X_BF16)
+            assert np.array_equal(yg[t, j], yj[0])
+            hj, _ = oracle.gemv(fmt, Wb, n, k, h[t, j:j + 1], oracle.X_BF16)
+            acc += float(g[t, j]) * hj[0]
+        assert np.allclose(yd[t], acc, rtol=1e-14, atol=1e-14)
+
+
+def test_oracle_rejects_bad_arguments():
+    blk, _ = _hand_q8_block()
+    with pytest.raises(ValueError):
+        oracle.gemv(oracle.Q8_0, blk, 1, 32, np.ones((1, 32), np.float32), 7)
+    with pytest.raises(ValueError):
+        oracle.gemv(oracle.Q8_0, blk, 1, 32, np.ones((1, 32), np.float32), oracle.X_F32, rows=[1])

@@ -1,0 +1,14 @@
+"""Seeded synthetic inputs for the block-quantized GEMV workloads.
+
+This module is shared by the tests, the benchmark and the oracle harness.  It
+only *draws* inputs and encodes them in the canonical block byte layout; it
+holds none of the method's arithmetic (no decoding, no dot products), so the
+oracle and the HIP path cannot agree with each other through it.
+"""
+from .gen import (  # noqa: F401
+    FMT_Q8_0, FMT_Q4_0, FMT_MXFP4, FMT_NAMES, BLOCK_BYTES, QK,
+    rng_for, q8_0_blocks, q4_0_blocks, mxfp4_blocks, blocks_for,
+    x_f32, x_bf16_bits, f32_to_bf16_bits_rne, router_topk,
+    encode_q8_0, encode_q4_0, encode_mxfp4,
+)
+from .configs import CONFIGS, c2_sweep_shapes  # noqa: F401
