@@ -1,0 +1,226 @@
+"""Python binding of libqgemv.so, the block-quantized weight GEMV library for MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/qgemv.h.  PyTorch supplies device
+memory and the current stream.  There is no fallback path: if the library is
+missing or a call fails, an exception is raised.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqgemv.so")
+
+# enums of include/qgemv.h
+QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_EALIGN, QG_EHIP = 0, 1, 2, 3, 4
+Q8_0, Q4_0, MXFP4 = 0, 1, 2
+X_F32, X_BF16 = 0, 1
+MOE_GATE_UP, MOE_DOWN_COMBINE = 0, 1
+MAX_M = 8
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17}
+
+# exported functions: name -> (restype, argtypes)
+_i, _i64, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+SIGNATURES = {
+    "qg_status_str": (ctypes.c_char_p, [_i]),
+    "qg_packed_bytes": (_i64, [_i, _i64, _i64]),
+    "qg_layout": (_i, [_i, _i64, _i64, _vp]),
+    "qg_pack_host": (_i, [_i, _vp, _i64, _i64, _vp]),
+    "qg_unpack_host": (_i, [_i, _vp, _i64, _i64, _vp]),
+    "qg_pack": (_i, [_i, _vp, _i64, _i64, _vp, _vp]),
+    "qg_unpack": (_i, [_i, _vp, _i64, _i64, _vp, _vp]),
+    "qg_dequant_f32": (_i, [_i, _vp, _i64, _i64, _vp, _vp]),
+    "qgemv_q8_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
+    "qgemv_q4_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
+    "qgemv_mxfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
+    "moe_qgemv_topk": (_i, [_i, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i, _i, _vp, _vp]),
+}
+
+
+class QGError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("lanes_per_row", ctypes.c_int32),
+                ("rows_per_tile", ctypes.c_int32), ("parts_per_step", ctypes.c_int32),
+                ("scale_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("steps", ctypes.c_int64),
+                ("tiles", ctypes.c_int64), ("code_tile_bytes", ctypes.c_int64),
+                ("scale_tile_bytes", ctypes.c_int64), ("scale_offset", ctypes.c_int64),
+                ("packed_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with block_quantized_weight_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (rt, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = rt, args
+        _lib = L
+    return _lib
+
+
+def status_str(status):
+    return lib().qg_status_str(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != QG_OK:
+        raise QGError(fn, status)
+
+
+# ------------------------------------------------------------------ layout
+def packed_bytes(fmt, n, k):
+    v = lib().qg_packed_bytes(fmt, n, k)
+    if v < 0:
+        raise QGError("qg_packed_bytes", QG_EINVAL)
+    return v
+
+
+def layout(fmt, n, k):
+    out = Layout()
+    _check("qg_layout", lib().qg_layout(fmt, n, k, ctypes.byref(out)))
+    return out.as_dict()
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def pack_host(fmt, canon, n, k):
+    """Canonical blocks (numpy uint8) -> packed bytes (numpy uint8), on the CPU."""
+    c = np.ascontiguousarray(canon, dtype=np.uint8).reshape(-1)
+    if c.size != n * (k // 32) * BLOCK_BYTES.get(fmt, 0):
+        raise ValueError("canonical array size does not match (fmt, n, k)")
+    out = np.empty(packed_bytes(fmt, n, k), dtype=np.uint8)
+    _check("qg_pack_host", lib().qg_pack_host(fmt, _np_ptr(c), n, k, _np_ptr(out)))
+    return out
+
+
+def unpack_host(fmt, packed, n, k):
+    p = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1)
+    if p.size != packed_bytes(fmt, n, k):
+        raise ValueError("packed array size does not match (fmt, n, k)")
+    out = np.zeros(n * (k // 32) * BLOCK_BYTES[fmt], dtype=np.uint8)
+    _check("qg_unpack_host", lib().qg_unpack_host(fmt, _np_ptr(p), n, k, _np_ptr(out)))
+    return out
+
+
+# ------------------------------------------------------------ device calls
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_ptr(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _xt(x):
+    torch = _torch()
+    if x.dtype == torch.float32:
+        return X_F32
+    if x.dtype == torch.bfloat16:
+        return X_BF16
+    raise ValueError("activations must be float32 or bfloat16")
+
+
+def pack(fmt, canon, n, k, out=None, stream=None):
+    """Canonical blocks (device uint8 tensor) -> packed weights (device uint8 tensor)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(packed_bytes(fmt, n, k), dtype=torch.uint8, device=canon.device)
+    _check("qg_pack", lib().qg_pack(fmt, _dev_ptr(canon, "canon"), n, k, _dev_ptr(out, "out"), _stream(stream)))
+    return out
+
+
+def unpack(fmt, packed, n, k, out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.zeros(n * (k // 32) * BLOCK_BYTES[fmt], dtype=torch.uint8, device=packed.device)
+    _check("qg_unpack", lib().qg_unpack(fmt, _dev_ptr(packed, "packed"), n, k, _dev_ptr(out, "out"),
+                                        _stream(stream)))
+    return out
+
+
+def dequant_f32(fmt, packed, n, k, out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=packed.device)
+    _check("qg_dequant_f32", lib().qg_dequant_f32(fmt, _dev_ptr(packed, "packed"), n, k, _dev_ptr(out, "out"),
+                                                  _stream(stream)))
+    return out
+
+
+_GEMV = {Q8_0: "qgemv_q8_0", Q4_0: "qgemv_q4_0", MXFP4: "qgemv_mxfp4"}
+
+
+def qgemv(fmt, w_packed, n, k, x, y=None, stream=None):
+    """y[m, n] = W x[m, k]^T for packed W; x float32 or bfloat16 [m, k] (or [k])."""
+    torch = _torch()
+    x2 = x.reshape(-1, k)
+    m = x2.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    fn = _GEMV[fmt]
+    st = getattr(lib(), fn)(_dev_ptr(w_packed, "w_packed"), n, k, _dev_ptr(x2, "x"), _xt(x2), m,
+                            _dev_ptr(y, "y"), _stream(stream))
+    _check(fn, st)
+    return y
+
+
+def qgemv_q8_0(w_packed, n, k, x, y=None, stream=None):
+    return qgemv(Q8_0, w_packed, n, k, x, y, stream)
+
+
+def qgemv_q4_0(w_packed, n, k, x, y=None, stream=None):
+    return qgemv(Q4_0, w_packed, n, k, x, y, stream)
+
+
+def qgemv_mxfp4(w_packed, n, k, x, y=None, stream=None):
+    return qgemv(MXFP4, w_packed, n, k, x, y, stream)
+
+
+def moe_qgemv_topk(fmt, w_experts, n_experts, n, k, topk_ids, topk_w, x, mode, y=None, stream=None):
+    """Top-k expert GEMV.  GATE_UP: x [m, k] -> y [m, top_k, n];
+    DOWN_COMBINE: x [m, top_k, k] -> y [m, n] (router weights combine, slot order)."""
+    torch = _torch()
+    m, top_k = topk_ids.shape
+    if topk_ids.dtype != torch.int32:
+        raise ValueError("topk_ids must be int32")
+    if topk_w is not None and topk_w.dtype != torch.float32:
+        raise ValueError("topk_w must be float32")
+    if y is None:
+        shape = (m, top_k, n) if mode == MOE_GATE_UP else (m, n)
+        y = torch.empty(shape, dtype=torch.float32, device=x.device)
+    wp = None if topk_w is None else _dev_ptr(topk_w, "topk_w")
+    st = lib().moe_qgemv_topk(fmt, _dev_ptr(w_experts, "w_experts"), n_experts, n, k,
+                              _dev_ptr(topk_ids, "topk_ids"), wp, m, top_k, _dev_ptr(x, "x"), _xt(x), mode,
+                              _dev_ptr(y, "y"), _stream(stream))
+    _check("moe_qgemv_topk", st)
+    return y

@@ -1,0 +1,336 @@
+// qg_api.hip -- C ABI of libqgemv.so: argument validation, layout, launch
+// plans, the packer kernels and the dequantization test aid.
+#include "qg_common.h"
+
+namespace qg {
+namespace {
+
+// ---------------------------------------------------------------- dequant
+// Test aid: one thread per (tile, step, lane) record writes its 32 weights.
+__global__ void k_dequant(LayoutArgs a, const uint8_t *__restrict__ packed, float *__restrict__ w, int64_t k, int64_t nrec)
+{
+    for (int64_t rec = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; rec < nrec; rec += (int64_t)gridDim.x * blockDim.x) {
+        int64_t row, blk, co, so;
+        record_geom(a, rec, &row, &blk, &co, &so);
+        if (row >= a.n || blk >= a.nb) continue;
+        const uint4 c0 = *(const uint4 *)(packed + co);
+        float *out = w + row * k + blk * QK;
+        if (a.fmt == QG_Q8_0) {
+            const uint4 c1 = *(const uint4 *)(packed + co + 1024);
+            uint32_t s = packed[so] | (packed[so + 1] << 8);
+            float d = f16_bits_to_f32(s);
+            uint32_t c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) out[4 * i + p] = d * i8_at(c[i], p);
+        } else if (a.fmt == QG_Q4_0) {
+            uint32_t s = packed[so] | (packed[so + 1] << 8);
+            float d = f16_bits_to_f32(s);
+            uint32_t c[4] = {c0.x, c0.y, c0.z, c0.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    uint32_t v = __builtin_bit_cast(uint32_t, q4_pair(c[i], kk));
+                    float lo = __builtin_bit_cast(float, v << 16) - 136.0f;
+                    float hi = __builtin_bit_cast(float, v & 0xFFFF0000u) - 136.0f;
+                    out[8 * i + 2 * kk] = d * lo;
+                    out[8 * i + 2 * kk + 1] = d * hi;
+                }
+        } else {
+            float sc = e8m0_to_f32(packed[so]);
+            uint32_t c[4] = {c0.x, c0.y, c0.z, c0.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bf16x2_t pr[4] = {fp4_pair_bf16<0>(c[i]), fp4_pair_bf16<1>(c[i]), fp4_pair_bf16<2>(c[i]),
+                                  fp4_pair_bf16<3>(c[i])};
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    uint32_t v = __builtin_bit_cast(uint32_t, pr[p]);
+                    out[8 * i + 2 * p] = sc * __builtin_bit_cast(float, v << 16);
+                    out[8 * i + 2 * p + 1] = sc * __builtin_bit_cast(float, v & 0xFFFF0000u);
+                }
+            }
+        }
+    }
+}
+
+
+__global__ void k_pack(LayoutArgs a, const uint8_t *__restrict__ canon, uint8_t *__restrict__ packed, int64_t nrec)
+{
+    const int64_t tid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (tid < a.total - a.end) packed[a.end + tid] = 0;
+    for (int64_t r = tid; r < nrec; r += (int64_t)gridDim.x * blockDim.x)
+        pack_record(a, canon, packed, r);
+}
+
+__global__ void k_unpack(LayoutArgs a, const uint8_t *__restrict__ packed, uint8_t *__restrict__ canon, int64_t nrec)
+{
+    for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < nrec; r += (int64_t)gridDim.x * blockDim.x)
+        unpack_record(a, packed, canon, r);
+}
+
+// ------------------------------------------------------------ host side
+hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_shape(int fmt, int64_t n, int64_t k)
+{
+    if (!valid_fmt(fmt) || n <= 0 || k <= 0 || (k % QK) != 0) return QG_EINVAL;
+    if (n > 0x7FFFFFFF || k > 0x7FFFFFFF) return QG_EUNSUPPORTED;
+    return QG_OK;
+}
+
+// Launch plan: split-K factor KS (waves per tile) and the activation window.
+Plan make_plan(const Layout &lo, int M, bool dot, int maxslots_lds)
+{
+    Plan p{};
+    Geom &g = p.g;
+    g.n = (int32_t)lo.n;
+    g.k = (int32_t)lo.k;
+    g.nb = (int32_t)lo.nb;
+    g.L = lo.L;
+    g.lsh = lo.lsh;
+    g.R = lo.R;
+    g.S = (int32_t)lo.S;
+    g.tiles = (int32_t)lo.tiles;
+    g.ctb = lo.ctb;
+    g.stb = lo.stb;
+    g.soff = lo.soff;
+    // activation window: as many steps as fit XBUDGET (at least one)
+    const int QPB = dot ? 4 : 8;
+    const size_t per_block = (size_t)maxslots_lds * QPB * 16 + (lo.fmt == QG_Q4_0 ? (size_t)maxslots_lds * 4 : 0);
+    int64_t sw_max = (int64_t)(XBUDGET / per_block) / lo.L;
+    if (sw_max < 1) sw_max = 1;
+    // split-K factor: more waves per tile when tiles are few; never more than
+    // the steps of a tile or of a window
+    int KS = 1;
+    if (lo.tiles < 4096) KS = 2;
+    if (lo.tiles < 2048) KS = 4;
+    while (KS > 1 && (lo.S < KS || sw_max < KS)) KS >>= 1;
+    g.KS = KS;
+    g.ksh = ilog2(KS);
+    g.tpi = WAVES / KS;
+    g.ngroups = (int32_t)((lo.tiles + g.tpi - 1) / g.tpi);
+    int64_t sw = sw_max / KS * KS;                         // a multiple of KS
+    if (sw >= lo.S) sw = ((lo.S + KS - 1) / KS) * KS;
+    g.SW = (int32_t)sw;
+    g.nwin = (int32_t)((lo.S + sw - 1) / sw);
+    g.wblk = (int32_t)(sw * lo.L);
+    p.lds = lds_bytes(maxslots_lds, dot, lo.fmt, g.wblk);
+    int grid = g.ngroups;
+    if (grid > 65535) grid = 65535;
+    p.grid = grid;
+    return p;
+}
+
+inline bool uses_dot(int fmt, int xt) { return fmt != QG_Q8_0 && xt == QG_BF16; }
+
+int launch_status()
+{
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+int dense(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return st;
+    if (!w || !x || !y) return QG_EINVAL;
+    if (xt != QG_F32 && xt != QG_BF16) return QG_EINVAL;
+    if (m < 1 || m > QG_MAX_M) return QG_EINVAL;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
+    const Layout lo = make_layout(fmt, n, k);
+    const bool dot = uses_dot(fmt, xt);
+    Plan p = make_plan(lo, (int)m, dot, (int)m);
+    p.g.w = (const uint8_t *)w;
+    dense_fn f = fmt == QG_Q8_0 ? dense_kernel_q8_0(xt, (int)m)
+                 : fmt == QG_Q4_0 ? dense_kernel_q4_0(xt, (int)m) : dense_kernel_mxfp4(xt, (int)m);
+    void *args[] = {(void *)&p.g, (void *)&x, (void *)&y};
+    if (allow_lds((const void *)f, p.lds) != hipSuccess) return QG_EHIP;
+    hipError_t e = hipLaunchKernel((const void *)f, dim3(p.grid), dim3(TPB), args, p.lds, as_stream(stream));
+    return e == hipSuccess ? launch_status() : QG_EHIP;
+}
+
+int64_t nrecords(const Layout &lo) { return lo.tiles * lo.S * 64; }
+
+int grid_for(int64_t items, int block)
+{
+    int64_t g = (items + block - 1) / block;
+    if (g > 65535 * 8) g = 65535 * 8;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
+} // namespace
+} // namespace qg
+
+using namespace qg;
+
+
+// ================================================================ C ABI
+extern "C" {
+
+const char *qg_status_str(int status)
+{
+    switch (status) {
+    case QG_OK: return "ok";
+    case QG_EINVAL: return "invalid argument";
+    case QG_EUNSUPPORTED: return "unsupported shape or size";
+    case QG_EALIGN: return "misaligned device pointer";
+    case QG_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int64_t qg_packed_bytes(int fmt, int64_t n, int64_t k)
+{
+    if (check_shape(fmt, n, k)) return -1;
+    return make_layout(fmt, n, k).total;
+}
+
+int qg_layout(int fmt, int64_t n, int64_t k, qg_layout_t *out)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return st;
+    if (!out) return QG_EINVAL;
+    const Layout lo = make_layout(fmt, n, k);
+    memset(out, 0, sizeof(*out));
+    out->fmt = fmt;
+    out->lanes_per_row = lo.L;
+    out->rows_per_tile = lo.R;
+    out->parts_per_step = lo.P;
+    out->scale_bytes = lo.sb;
+    out->n = n;
+    out->k = k;
+    out->steps = lo.S;
+    out->tiles = lo.tiles;
+    out->code_tile_bytes = lo.ctb;
+    out->scale_tile_bytes = lo.stb;
+    out->scale_offset = lo.soff;
+    out->packed_bytes = lo.total;
+    return QG_OK;
+}
+
+int qg_pack_host(int fmt, const void *canon, int64_t n, int64_t k, void *packed)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return st;
+    if (!canon || !packed) return QG_EINVAL;
+    const Layout lo = make_layout(fmt, n, k);
+    const LayoutArgs a = layout_args(lo);
+    const int64_t nrec = nrecords(lo);
+    memset((uint8_t *)packed + a.end, 0, (size_t)(a.total - a.end));
+    for (int64_t r = 0; r < nrec; ++r) pack_record(a, (const uint8_t *)canon, (uint8_t *)packed, r);
+    return QG_OK;
+}
+
+int qg_unpack_host(int fmt, const void *packed, int64_t n, int64_t k, void *canon)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return st;
+    if (!canon || !packed) return QG_EINVAL;
+    const Layout lo = make_layout(fmt, n, k);
+    const LayoutArgs a = layout_args(lo);
+    const int64_t nrec = nrecords(lo);
+    for (int64_t r = 0; r < nrec; ++r) unpack_record(a, (const uint8_t *)packed, (uint8_t *)canon, r);
+    return QG_OK;
+}
+
+int qg_pack(int fmt, const void *canon, int64_t n, int64_t k, void *packed, void *stream)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return st;
+    if (!canon || !packed) return QG_EINVAL;
+    if (!aligned(packed, 16)) return QG_EALIGN;
+    const Layout lo = make_layout(fmt, n, k);
+    const int64_t nrec = nrecords(lo);
+    hipLaunchKernelGGL(k_pack, dim3(grid_for(nrec, 256)), dim3(256), 0, as_stream(stream), layout_args(lo),
+                       (const uint8_t *)canon, (uint8_t *)packed, nrec);
+    return launch_status();
+}
+
+int qg_unpack(int fmt, const void *packed, int64_t n, int64_t k, void *canon, void *stream)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return st;
+    if (!canon || !packed) return QG_EINVAL;
+    if (!aligned(packed, 16)) return QG_EALIGN;
+    const Layout lo = make_layout(fmt, n, k);
+    const int64_t nrec = nrecords(lo);
+    hipLaunchKernelGGL(k_unpack, dim3(grid_for(nrec, 256)), dim3(256), 0, as_stream(stream), layout_args(lo),
+                       (const uint8_t *)packed, (uint8_t *)canon, nrec);
+    return launch_status();
+}
+
+int qg_dequant_f32(int fmt, const void *w_packed, int64_t n, int64_t k, float *w, void *stream)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return st;
+    if (!w_packed || !w) return QG_EINVAL;
+    if (!aligned(w_packed, 16) || !aligned(w, 4)) return QG_EALIGN;
+    const Layout lo = make_layout(fmt, n, k);
+    const int64_t nrec = nrecords(lo);
+    hipLaunchKernelGGL(k_dequant, dim3(grid_for(nrec, 256)), dim3(256), 0, as_stream(stream), layout_args(lo),
+                       (const uint8_t *)w_packed, w, k, nrec);
+    return launch_status();
+}
+
+int qgemv_q8_0(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
+{
+    return dense(QG_Q8_0, w, n, k, x, xt, m, y, stream);
+}
+
+int qgemv_q4_0(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
+{
+    return dense(QG_Q4_0, w, n, k, x, xt, m, y, stream);
+}
+
+int qgemv_mxfp4(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
+{
+    return dense(QG_MXFP4, w, n, k, x, xt, m, y, stream);
+}
+
+int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n, int64_t k,
+                   const int32_t *topk_ids, const float *topk_w, int64_t m, int64_t top_k,
+                   const void *x, int xt, int mode, float *y, void *stream)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return st;
+    if (!w_experts || !topk_ids || !x || !y) return QG_EINVAL;
+    if (xt != QG_F32 && xt != QG_BF16) return QG_EINVAL;
+    if (mode != QG_MOE_GATE_UP && mode != QG_MOE_DOWN_COMBINE) return QG_EINVAL;
+    if (mode == QG_MOE_DOWN_COMBINE && !topk_w) return QG_EINVAL;
+    if (m < 1 || m > QG_MAX_M || n_experts < 1 || top_k < 1 || top_k > n_experts) return QG_EINVAL;
+    if (m * top_k > 64 || n_experts > 65536) return QG_EUNSUPPORTED;
+    if (!aligned(w_experts, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(topk_ids, 4) ||
+        (topk_w && !aligned(topk_w, 4)))
+        return QG_EALIGN;
+    const Layout lo = make_layout(fmt, n, k);
+    const bool dot = uses_dot(fmt, xt);
+    Plan p = make_plan(lo, QG_MAX_M, dot, QG_MAX_M);
+    MoeArgs a;
+    a.experts = (const uint8_t *)w_experts;
+    a.expert_bytes = lo.total;
+    a.ids = topk_ids;
+    a.gw = topk_w;
+    a.n_experts = (int32_t)n_experts;
+    a.m = (int32_t)m;
+    a.top_k = (int32_t)top_k;
+    const int maxdistinct = (int)((m * top_k < n_experts) ? m * top_k : n_experts);
+    size_t lds = p.lds;
+    if (mode == QG_MOE_DOWN_COMBINE) {
+        const size_t rows_pg = (size_t)p.g.tpi * p.g.R;
+        lds += (size_t)(m * top_k + QG_MAX_M) * rows_pg * 4;
+    }
+    hipStream_t s = as_stream(stream);
+    hipError_t e = fmt == QG_Q8_0 ? launch_moe_q8_0(xt, mode, p, a, maxdistinct, lds, x, y, s)
+                   : fmt == QG_Q4_0 ? launch_moe_q4_0(xt, mode, p, a, maxdistinct, lds, x, y, s)
+                                    : launch_moe_mxfp4(xt, mode, p, a, maxdistinct, lds, x, y, s);
+    if (e != hipSuccess) return QG_EHIP;
+    return launch_status();
+}
+
+} // extern "C"

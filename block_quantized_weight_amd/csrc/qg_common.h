@@ -1,0 +1,916 @@
+#pragma once
+// qg_common.h -- shared device code of the block-quantized weight GEMV library
+// for MI355X (gfx950, CDNA4).
+//
+// The decode step of an LLM streams each weight matrix once per token through
+// a matrix-vector product, so the product is bound by HBM bandwidth (imp
+// README, "Known limitations": lower bandwidth "decodes roughly 25% slower,
+// since decode is bandwidth-bound").  Everything here is shaped for that:
+//
+//  * Packed layout (built once at load time).  A tile holds R = 64/L rows.
+//    Lane l of a wavefront owns row l/L of the tile and, at step j, block
+//    j*L + l%L of that row.  The codes of one step are stored lane-major, so
+//    each wavefront load instruction (64 lanes x 16 B) reads 1 KiB that is
+//    contiguous in memory.  Scales are a separate stream in the same
+//    (tile, step, lane) order.  Nibbles are permuted inside a block so that
+//    the unpack below needs one or two ALU operations per pair of weights.
+//  * Activations are staged once per workgroup into LDS in the type the
+//    inner product uses (fp32 for int8 codes, bf16 pairs for 4-bit codes),
+//    in a quad-major order that makes every ds_read_b128 conflict-free.
+//  * Inner products: int8 codes go through one sign-extending byte convert
+//    and one fp32 FMA per weight; Q4_0 nibbles are turned into bf16 (128+q)
+//    with one and-or per pair and fed to v_dot2c_f32_bf16, the 136*sum(x)
+//    offset being removed per block; E2M1 nibbles are converted two at a time
+//    by the gfx950 scaled FP4->bf16 convert and also fed to the bf16 dot.
+//    Accumulation is fp32; the block scale is applied once per block.
+//  * Split-K inside a workgroup (KS waves per tile) is reduced through LDS in
+//    a fixed order, then across the L lanes of a row by a xor butterfly.  No
+//    atomics: results are bitwise reproducible.
+//
+// Prior art on the pages: imp's NVFP4 block-scaled GEMV with packed E2M1
+// dequant in registers (imp README, "Features" table, sm_120a kernels row),
+// its dp4a Q8_0 decode route (imp release notes, v0.4.1), and Imparo's
+// private GateUp weight layout kept beside the canonical GGUF one (Imparo
+// README, opening release notes).  Those were built for NVIDIA GPUs; the
+// design here is for 64-wide wavefronts, LDS and HBM3E.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+
+#include "../../include/qgemv.h"
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+namespace qg {
+
+
+constexpr int QK = 32;          // weights per block
+constexpr int WAVES = 4;        // wavefronts per workgroup
+constexpr int TPB = 64 * WAVES; // threads per workgroup
+constexpr int XBUDGET = 64 * 1024;  // LDS bytes for one window of staged activations
+
+// ------------------------------------------------------------------ layout
+struct Layout {
+    int fmt, L, lsh, R, P, sb;
+    int64_t n, k, nb, S, tiles;
+    int64_t ctb, stb, soff, total;
+};
+
+inline int block_bytes(int fmt) { return fmt == QG_Q8_0 ? 34 : fmt == QG_Q4_0 ? 18 : 17; }
+
+inline bool valid_fmt(int fmt) { return fmt == QG_Q8_0 || fmt == QG_Q4_0 || fmt == QG_MXFP4; }
+
+inline int ilog2(int v) { int s = 0; while ((1 << s) < v) ++s; return s; }
+
+// Lanes per row.  Padding (blocks beyond k/32 and rows beyond n) is avoided
+// first; among the low-padding choices the fewest lanes per row that still give
+// >= 512 tiles is taken (long per-lane streams, short reductions), else the
+// choice with the most tiles.
+inline Layout make_layout(int fmt, int64_t n, int64_t k)
+{
+    Layout lo{};
+    lo.fmt = fmt;
+    lo.n = n;
+    lo.k = k;
+    lo.nb = k / QK;
+    lo.P = fmt == QG_Q8_0 ? 2 : 1;
+    lo.sb = fmt == QG_MXFP4 ? 1 : 2;
+    const int cand[7] = {1, 2, 4, 8, 16, 32, 64};
+    double waste[7];
+    double best_w = 1e30;
+    for (int i = 0; i < 7; ++i) {
+        int L = cand[i], R = 64 / L;
+        int64_t S = (lo.nb + L - 1) / L, tiles = (n + R - 1) / R;
+        double padded = (double)tiles * R * S * L;
+        waste[i] = padded / ((double)n * (double)lo.nb) - 1.0;
+        if (waste[i] < best_w) best_w = waste[i];
+    }
+    int pick = -1;
+    int64_t target = n < 512 ? n : 512;
+    for (int i = 0; i < 7; ++i) {
+        if (waste[i] > best_w + 0.005) continue;
+        int64_t tiles = (n + 64 / cand[i] - 1) / (64 / cand[i]);
+        if (tiles >= target) { pick = i; break; }
+    }
+    if (pick < 0) {
+        for (int i = 6; i >= 0; --i)
+            if (waste[i] <= best_w + 0.005) { pick = i; break; }
+    }
+    lo.L = cand[pick];
+    lo.lsh = ilog2(lo.L);
+    lo.R = 64 / lo.L;
+    lo.S = (lo.nb + lo.L - 1) / lo.L;
+    lo.tiles = (n + lo.R - 1) / lo.R;
+    lo.ctb = lo.S * lo.P * 1024;
+    lo.stb = lo.S * 64 * lo.sb;
+    lo.soff = lo.tiles * lo.ctb;
+    lo.total = (lo.soff + lo.tiles * lo.stb + 255) / 256 * 256;   // experts stay 256-byte aligned
+    return lo;
+}
+
+// ------------------------------------------------- per-block code permutation
+// Canonical block -> packed codes (P*16 bytes) and scale; and back.
+//  Q8_0 : part 0 = codes 0..15, part 1 = codes 16..31 (no permutation).
+//  Q4_0 : packed dword i, bits [4k,4k+4) = q[8i+2k], bits [16+4k,..) = q[8i+2k+1],
+//         so (dword >> 4k) & 0x000F000F holds the pair (8i+2k, 8i+2k+1).
+//  MXFP4: packed byte B = q[2B] | q[2B+1] << 4 (one byte = one adjacent pair).
+__host__ __device__ inline void nibbles_from_canon(const uint8_t *body, uint8_t q[32])
+{
+    for (int j = 0; j < 16; ++j) {
+        q[j] = body[j] & 15;
+        q[j + 16] = body[j] >> 4;
+    }
+}
+
+__host__ __device__ inline void nibbles_to_canon(const uint8_t q[32], uint8_t *body)
+{
+    for (int j = 0; j < 16; ++j)
+        body[j] = (uint8_t)(q[j] | (q[j + 16] << 4));
+}
+
+__host__ __device__ inline void canon_to_packed(int fmt, const uint8_t *blk, uint8_t *codes, uint16_t *scale)
+{
+    if (fmt == QG_Q8_0) {
+        *scale = (uint16_t)(blk[0] | (blk[1] << 8));
+        for (int i = 0; i < 32; ++i) codes[i] = blk[2 + i];
+        return;
+    }
+    uint8_t q[32];
+    if (fmt == QG_Q4_0) {
+        *scale = (uint16_t)(blk[0] | (blk[1] << 8));
+        nibbles_from_canon(blk + 2, q);
+        for (int i = 0; i < 4; ++i) {
+            const uint8_t *e = q + 8 * i;
+            codes[4 * i + 0] = (uint8_t)(e[0] | (e[2] << 4));
+            codes[4 * i + 1] = (uint8_t)(e[4] | (e[6] << 4));
+            codes[4 * i + 2] = (uint8_t)(e[1] | (e[3] << 4));
+            codes[4 * i + 3] = (uint8_t)(e[5] | (e[7] << 4));
+        }
+        return;
+    }
+    *scale = blk[0];
+    nibbles_from_canon(blk + 1, q);
+    for (int b = 0; b < 16; ++b) codes[b] = (uint8_t)(q[2 * b] | (q[2 * b + 1] << 4));
+}
+
+__host__ __device__ inline void packed_to_canon(int fmt, const uint8_t *codes, uint16_t scale, uint8_t *blk)
+{
+    if (fmt == QG_Q8_0) {
+        blk[0] = (uint8_t)(scale & 0xFF);
+        blk[1] = (uint8_t)(scale >> 8);
+        for (int i = 0; i < 32; ++i) blk[2 + i] = codes[i];
+        return;
+    }
+    uint8_t q[32];
+    if (fmt == QG_Q4_0) {
+        blk[0] = (uint8_t)(scale & 0xFF);
+        blk[1] = (uint8_t)(scale >> 8);
+        for (int i = 0; i < 4; ++i) {
+            uint8_t *e = q + 8 * i;
+            e[0] = codes[4 * i + 0] & 15; e[2] = codes[4 * i + 0] >> 4;
+            e[4] = codes[4 * i + 1] & 15; e[6] = codes[4 * i + 1] >> 4;
+            e[1] = codes[4 * i + 2] & 15; e[3] = codes[4 * i + 2] >> 4;
+            e[5] = codes[4 * i + 3] & 15; e[7] = codes[4 * i + 3] >> 4;
+        }
+        nibbles_to_canon(q, blk + 2);
+        return;
+    }
+    blk[0] = (uint8_t)scale;
+    for (int b = 0; b < 16; ++b) {
+        q[2 * b] = codes[b] & 15;
+        q[2 * b + 1] = codes[b] >> 4;
+    }
+    nibbles_to_canon(q, blk + 1);
+}
+
+// Geometry passed to the layout kernels.
+struct LayoutArgs {
+    int fmt, L, lsh, R, P, sb, bb;
+    int64_t n, nb, S, tiles, ctb, stb, soff, end, total;   // [end, total) is tail padding
+};
+
+inline LayoutArgs layout_args(const Layout &lo)
+{
+    LayoutArgs a;
+    a.fmt = lo.fmt; a.L = lo.L; a.lsh = lo.lsh; a.R = lo.R; a.P = lo.P; a.sb = lo.sb;
+    a.bb = block_bytes(lo.fmt);
+    a.n = lo.n; a.nb = lo.nb; a.S = lo.S; a.tiles = lo.tiles;
+    a.ctb = lo.ctb; a.stb = lo.stb; a.soff = lo.soff;
+    a.end = lo.soff + lo.tiles * lo.stb;
+    a.total = lo.total;
+    return a;
+}
+
+// One record = (tile, step, lane): its row/block and its byte offsets.
+__host__ __device__ inline void record_geom(const LayoutArgs &a, int64_t rec, int64_t *row, int64_t *blk,
+                                            int64_t *code_off, int64_t *scale_off)
+{
+    int64_t lane = rec & 63, rest = rec >> 6;
+    int64_t j = rest % a.S, tile = rest / a.S;
+    *row = tile * a.R + (lane >> a.lsh);
+    *blk = j * a.L + (lane & (a.L - 1));
+    *code_off = tile * a.ctb + j * a.P * 1024 + lane * 16;
+    *scale_off = a.soff + tile * a.stb + j * 64 * a.sb + lane * a.sb;
+}
+
+__host__ __device__ inline void pack_record(const LayoutArgs &a, const uint8_t *canon, uint8_t *packed, int64_t rec)
+{
+    int64_t row, blk, co, so;
+    record_geom(a, rec, &row, &blk, &co, &so);
+    uint8_t codes[32];
+    uint16_t scale = 0;
+    for (int i = 0; i < 32; ++i) codes[i] = 0;
+    if (row < a.n && blk < a.nb) {
+        uint8_t b[34];
+        const uint8_t *src = canon + (row * a.nb + blk) * a.bb;
+        for (int i = 0; i < a.bb; ++i) b[i] = src[i];
+        canon_to_packed(a.fmt, b, codes, &scale);
+    }
+    for (int h = 0; h < a.P; ++h)
+        for (int i = 0; i < 16; ++i) packed[co + h * 1024 + i] = codes[16 * h + i];
+    packed[so] = (uint8_t)(scale & 0xFF);
+    if (a.sb == 2) packed[so + 1] = (uint8_t)(scale >> 8);
+}
+
+__host__ __device__ inline void unpack_record(const LayoutArgs &a, const uint8_t *packed, uint8_t *canon, int64_t rec)
+{
+    int64_t row, blk, co, so;
+    record_geom(a, rec, &row, &blk, &co, &so);
+    if (row >= a.n || blk >= a.nb) return;
+    uint8_t codes[32];
+    for (int h = 0; h < a.P; ++h)
+        for (int i = 0; i < 16; ++i) codes[16 * h + i] = packed[co + h * 1024 + i];
+    uint16_t scale = packed[so];
+    if (a.sb == 2) scale = (uint16_t)(scale | (packed[so + 1] << 8));
+    uint8_t b[34];
+    packed_to_canon(a.fmt, codes, scale, b);
+    uint8_t *dst = canon + (row * a.nb + blk) * a.bb;
+    for (int i = 0; i < a.bb; ++i) dst[i] = b[i];
+}
+
+// ------------------------------------------------------------ unpack math
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t bits)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// UE8M0 -> fp32 2^(E-127): E = 0 is the subnormal 2^-127, E = 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e)
+{
+    uint32_t b = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : (e << 23));
+    return __builtin_bit_cast(float, b);
+}
+
+__device__ __forceinline__ float i8_at(uint32_t w, int p)
+{
+    return (float)(int8_t)(w >> (8 * p));   // v_cvt_f32_i32 with a sign-extended byte select
+}
+
+// Q4_0 pair k of a packed dword as bf16 (128+q_lo, 128+q_hi).
+__device__ __forceinline__ bf16x2_t q4_pair(uint32_t w, int kk)
+{
+    uint32_t v = ((w >> (4 * kk)) & 0x000F000Fu) | 0x43004300u;
+    return __builtin_bit_cast(bf16x2_t, v);
+}
+
+__device__ __forceinline__ bf16x2_t u32_as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+
+__device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// Byte p of a packed MXFP4 dword as a bf16 pair (element 2p of the dword's
+// eight, element 2p+1), scale 1.0 (the block scale is applied in fp32 later).
+template <int PSEL>
+__device__ __forceinline__ bf16x2_t fp4_pair_bf16(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, PSEL);
+}
+
+template <int PSEL>
+__device__ __forceinline__ f32x2_t fp4_pair_f32(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, PSEL);
+}
+
+// ------------------------------------------------------------- GEMV engine
+// A "pass" of one workgroup: WAVES/KS tiles, each covered by KS waves that
+// split the tile's steps (step j goes to wave j % KS).  Activations for up to
+// M token slots are staged in LDS per window of SW steps.
+struct Geom {
+    const uint8_t *w;            // packed matrix base
+    int32_t n, k, nb;
+    int32_t L, lsh, R, S, tiles;
+    int64_t ctb, stb, soff;
+    int32_t KS, ksh, tpi, ngroups;
+    int32_t SW, nwin, wblk;      // steps per window, windows, blocks per window
+};
+
+// Where the activations of token slot t come from and where its outputs go.
+// Both arrays live in LDS so that the offsets cost no registers.
+struct Slots {
+    const int32_t *xrow;         // activation row of slot t: x + xrow[t] * k
+    const int32_t *yrow;         // output row of slot t:     y + yrow[t] * n + row
+};
+
+template <bool XBF16, bool DOT>
+struct XStage {
+    // Stages window w of M slots: xs[(t*QPB + q)*wblk + bl] (16 B quads), and
+    // corr[t*wblk + bl] = CORR * sum of the block's 32 activations (fp32, index order).
+    template <int M, int FMT>
+    static __device__ __forceinline__ void run(const Geom &g, const void *x, const Slots &sl, int w, uint4 *xs, float *corr)
+    {
+        constexpr int QPB = DOT ? 4 : 8;
+        const int b0 = w * g.SW * g.L;
+        const int total = M * g.wblk;
+        for (int idx = threadIdx.x; idx < total; idx += TPB) {
+            const int t = idx / g.wblk, bl = idx - t * g.wblk, b = b0 + bl;
+            const int64_t xo = (int64_t)sl.xrow[t] * g.k;
+            uint4 q[8];
+            float sum = 0.0f;
+            if (b < g.nb) {
+                if (XBF16) {
+                    const uint4 *src = (const uint4 *)((const uint16_t *)x + xo + (int64_t)b * QK);
+                    uint4 r[4] = {src[0], src[1], src[2], src[3]};
+                    const uint32_t *rw = (const uint32_t *)r;
+                    if (DOT) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) q[i] = r[i];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            uint32_t a0 = rw[2 * i], a1 = rw[2 * i + 1];
+                            q[i] = make_uint4(a0 << 16, a0 & 0xFFFF0000u, a1 << 16, a1 & 0xFFFF0000u);
+                        }
+                    }
+                    if (FMT != QG_Q8_0) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            sum += __builtin_bit_cast(float, rw[i] << 16);
+                            sum += __builtin_bit_cast(float, rw[i] & 0xFFFF0000u);
+                        }
+                    }
+                } else {
+                    const uint4 *src = (const uint4 *)((const float *)x + xo + (int64_t)b * QK);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) q[i] = src[i];
+                    if (FMT != QG_Q8_0) {
+                        const float *f = (const float *)q;
+#pragma unroll
+                        for (int i = 0; i < 32; ++i) sum += f[i];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) q[i] = make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < QPB; ++i) xs[(t * QPB + i) * g.wblk + bl] = q[i];
+            if (FMT == QG_Q4_0) corr[t * g.wblk + bl] = (DOT ? 136.0f : 8.0f) * sum;
+        }
+    }
+};
+
+// Steps per batch (loads in flight per lane before the first use).
+template <int FMT, bool DOT> struct Batch { static constexpr int U = (FMT == QG_Q8_0 || !DOT) ? 4 : 8; };
+
+template <int FMT, bool XBF16, bool DOT, int M>
+struct Engine {
+    static constexpr int P = FMT == QG_Q8_0 ? 2 : 1;
+    static constexpr int U = Batch<FMT, DOT>::U;
+    static constexpr int QPB = DOT ? 4 : 8;
+
+    struct Regs {
+        uint4 c[U][P];
+        uint32_t s[U];
+    };
+
+    static __device__ __forceinline__ void load(const Geom &g, const uint8_t *ct, const uint8_t *st, int lane,
+                                                int jfirst, int cnt, int KS, Regs &r)
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u < cnt) {
+                const int j = jfirst + u * KS;
+                const uint8_t *cp = ct + (int64_t)j * (P * 1024) + lane * 16;
+#pragma unroll
+                for (int h = 0; h < P; ++h) r.c[u][h] = *(const uint4 *)(cp + h * 1024);
+                if (FMT == QG_MXFP4)
+                    r.s[u] = st[(int64_t)j * 64 + lane];
+                else
+                    r.s[u] = ((const uint16_t *)st)[(int64_t)j * 64 + lane];
+            }
+        }
+    }
+
+    // Adds the contributions of one step (block b of this lane's row) to acc.
+    static __device__ __forceinline__ void step(const Geom &g, const uint4 *c, uint32_t sbits, const uint4 *xs,
+                                                const float *corr, int bl, float acc[M])
+    {
+        if (FMT == QG_Q8_0) {
+            const float d = f16_bits_to_f32(sbits);
+            const uint32_t cw[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
+#pragma unroll
+            for (int t = 0; t < M; ++t) {
+                float s = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float4 xq = __builtin_bit_cast(float4, xs[(t * 8 + i) * g.wblk + bl]);
+                    s = __builtin_fmaf(i8_at(cw[i], 0), xq.x, s);
+                    s = __builtin_fmaf(i8_at(cw[i], 1), xq.y, s);
+                    s = __builtin_fmaf(i8_at(cw[i], 2), xq.z, s);
+                    s = __builtin_fmaf(i8_at(cw[i], 3), xq.w, s);
+                }
+                acc[t] = __builtin_fmaf(d, s, acc[t]);
+            }
+        } else if (FMT == QG_Q4_0) {
+            const float d = f16_bits_to_f32(sbits);
+            const uint32_t cw[4] = {c[0].x, c[0].y, c[0].z, c[0].w};
+            if (DOT) {
+                bf16x2_t pr[4][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) pr[i][kk] = q4_pair(cw[i], kk);
+#pragma unroll
+                for (int t = 0; t < M; ++t) {
+                    float s = -corr[t * g.wblk + bl];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint4 xq = xs[(t * 4 + i) * g.wblk + bl];
+                        s = dot2(pr[i][0], u32_as_bf16x2(xq.x), s);
+                        s = dot2(pr[i][1], u32_as_bf16x2(xq.y), s);
+                        s = dot2(pr[i][2], u32_as_bf16x2(xq.z), s);
+                        s = dot2(pr[i][3], u32_as_bf16x2(xq.w), s);
+                    }
+                    acc[t] = __builtin_fmaf(d, s, acc[t]);
+                }
+            } else {
+                // fp32 activations: quad 2i holds elements 8i..8i+3 (nibble bits 0,16,4,20),
+                // quad 2i+1 holds 8i+4..8i+7 (bits 8,24,12,28).
+                float v[32];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int sh[8] = {0, 16, 4, 20, 8, 24, 12, 28};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[8 * i + e] = (float)((cw[i] >> sh[e]) & 15u);
+                }
+#pragma unroll
+                for (int t = 0; t < M; ++t) {
+                    float s = -corr[t * g.wblk + bl];
+#pragma unroll
+                    for (int qd = 0; qd < 8; ++qd) {
+                        const float4 xq = __builtin_bit_cast(float4, xs[(t * 8 + qd) * g.wblk + bl]);
+                        s = __builtin_fmaf(v[4 * qd + 0], xq.x, s);
+                        s = __builtin_fmaf(v[4 * qd + 1], xq.y, s);
+                        s = __builtin_fmaf(v[4 * qd + 2], xq.z, s);
+                        s = __builtin_fmaf(v[4 * qd + 3], xq.w, s);
+                    }
+                    acc[t] = __builtin_fmaf(d, s, acc[t]);
+                }
+            }
+        } else {
+            const float sc = e8m0_to_f32(sbits);
+            const uint32_t cw[4] = {c[0].x, c[0].y, c[0].z, c[0].w};
+            if (DOT) {
+                bf16x2_t pr[4][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pr[i][0] = fp4_pair_bf16<0>(cw[i]);
+                    pr[i][1] = fp4_pair_bf16<1>(cw[i]);
+                    pr[i][2] = fp4_pair_bf16<2>(cw[i]);
+                    pr[i][3] = fp4_pair_bf16<3>(cw[i]);
+                }
+#pragma unroll
+                for (int t = 0; t < M; ++t) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint4 xq = xs[(t * 4 + i) * g.wblk + bl];
+                        s = dot2(pr[i][0], u32_as_bf16x2(xq.x), s);
+                        s = dot2(pr[i][1], u32_as_bf16x2(xq.y), s);
+                        s = dot2(pr[i][2], u32_as_bf16x2(xq.z), s);
+                        s = dot2(pr[i][3], u32_as_bf16x2(xq.w), s);
+                    }
+                    acc[t] = __builtin_fmaf(sc, s, acc[t]);
+                }
+            } else {
+                f32x2_t pr[4][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pr[i][0] = fp4_pair_f32<0>(cw[i]);
+                    pr[i][1] = fp4_pair_f32<1>(cw[i]);
+                    pr[i][2] = fp4_pair_f32<2>(cw[i]);
+                    pr[i][3] = fp4_pair_f32<3>(cw[i]);
+                }
+#pragma unroll
+                for (int t = 0; t < M; ++t) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float4 xa = __builtin_bit_cast(float4, xs[(t * 8 + 2 * i) * g.wblk + bl]);
+                        const float4 xb = __builtin_bit_cast(float4, xs[(t * 8 + 2 * i + 1) * g.wblk + bl]);
+                        s = __builtin_fmaf(pr[i][0].x, xa.x, s);
+                        s = __builtin_fmaf(pr[i][0].y, xa.y, s);
+                        s = __builtin_fmaf(pr[i][1].x, xa.z, s);
+                        s = __builtin_fmaf(pr[i][1].y, xa.w, s);
+                        s = __builtin_fmaf(pr[i][2].x, xb.x, s);
+                        s = __builtin_fmaf(pr[i][2].y, xb.y, s);
+                        s = __builtin_fmaf(pr[i][3].x, xb.z, s);
+                        s = __builtin_fmaf(pr[i][3].y, xb.w, s);
+                    }
+                    acc[t] = __builtin_fmaf(sc, s, acc[t]);
+                }
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void compute(const Geom &g, const Regs &r, int cnt, int jfirst, int KS,
+                                                   int slot, int b0, const uint4 *xs, const float *corr, float acc[M])
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u < cnt) {
+                const int j = jfirst + u * KS;
+                const int bl = j * g.L + slot - b0;
+                step(g, r.c[u], r.s[u], xs, corr, bl, acc);
+            }
+        }
+    }
+
+    // One pass over tile `tile` (or none if tile >= tiles) for this wave; the
+    // whole workgroup calls it together (it contains barriers when staging).
+    // Returns the per-lane partial sums (before the KS and L reductions).
+    static __device__ __forceinline__ void pass(const Geom &g, const void *x, const Slots &sl, int tile, bool &staged,
+                                uint4 *xs, float *corr, float acc[M])
+    {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int KS = g.KS, kpart = wave & (KS - 1);
+        const int slot = lane & (g.L - 1);
+        const bool active = tile < g.tiles;
+        const uint8_t *ct = g.w + (int64_t)tile * g.ctb;
+        const uint8_t *st = g.w + g.soff + (int64_t)tile * g.stb;
+#pragma unroll
+        for (int t = 0; t < M; ++t) acc[t] = 0.0f;
+        for (int w = 0; w < g.nwin; ++w) {
+            const int j0 = w * g.SW;
+            const int j1 = min(g.S, j0 + g.SW);
+            const int jf = j0 + kpart;      // SW is a multiple of KS
+            int nsteps = (active && jf < j1) ? (j1 - jf + KS - 1) / KS : 0;
+            Regs ra, rb;
+            int ca = min(nsteps, U);
+            if (ca > 0) load(g, ct, st, lane, jf, ca, KS, ra);
+            if (g.nwin > 1 || !staged) {
+                __syncthreads();
+                XStage<XBF16, DOT>::template run<M, FMT>(g, x, sl, w, xs, corr);
+                __syncthreads();
+                staged = true;
+            }
+            const int b0 = j0 * g.L;
+            int done = 0;
+            while (done < nsteps) {
+                const int jA = jf + done * KS;
+                const int cA = min(nsteps - done, U);
+                const int cB = min(nsteps - done - cA, U);
+                if (cB > 0) load(g, ct, st, lane, jA + cA * KS, cB, KS, rb);
+                compute(g, ra, cA, jA, KS, slot, b0, xs, corr, acc);
+                done += cA;
+                if (cB <= 0) break;
+                const int cC = min(nsteps - done - cB, U);
+                if (cC > 0) load(g, ct, st, lane, jA + (cA + cB) * KS, cC, KS, ra);
+                compute(g, rb, cB, jA + cA * KS, KS, slot, b0, xs, corr, acc);
+                done += cB;
+            }
+        }
+    }
+};
+
+// Sums the KS per-wave partials (fixed order) and the L lanes of each row.
+// Must be called by the whole workgroup.  Afterwards every lane of a row in a
+// wave with kpart == 0 holds that row's totals.
+template <int M>
+__device__ __forceinline__ void reduce_partials(const Geom &g, float *red, float acc[M])
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kpart = wave & (g.KS - 1);
+    if (g.KS > 1) {
+#pragma unroll
+        for (int t = 0; t < M; ++t) red[(wave * M + t) * 64 + lane] = acc[t];
+        __syncthreads();
+        if (kpart == 0) {
+            for (int q = 1; q < g.KS; ++q)
+#pragma unroll
+                for (int t = 0; t < M; ++t) acc[t] += red[((wave + q) * M + t) * 64 + lane];
+        }
+        __syncthreads();
+    }
+    for (int off = 1; off < g.L; off <<= 1) {
+#pragma unroll
+        for (int t = 0; t < M; ++t) acc[t] += __shfl_xor(acc[t], off, 64);
+    }
+}
+
+inline __host__ __device__ size_t lds_bytes(int M, bool dot, int fmt, int wblk)
+{
+    const int QPB = dot ? 4 : 8;
+    size_t b = (size_t)M * QPB * wblk * 16;
+    if (fmt == QG_Q4_0) b += (size_t)M * wblk * 4;
+    b += (size_t)WAVES * M * 64 * 4;
+    return b;
+}
+
+template <int FMT, bool XBF16, bool DOT, int M>
+__global__ __launch_bounds__(TPB) void k_dense(Geom g, const void *__restrict__ x, float *__restrict__ y)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int QPB = DOT ? 4 : 8;
+    uint4 *xs = (uint4 *)smem;
+    float *corr = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
+    float *red = corr + (FMT == QG_Q4_0 ? M * g.wblk : 0);
+    __shared__ int32_t s_rows[QG_MAX_M];
+    if (threadIdx.x < QG_MAX_M) s_rows[threadIdx.x] = threadIdx.x;   // read only after the staging barrier
+    Slots sl{s_rows, s_rows};
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tsub = wave >> g.ksh, kpart = wave & (g.KS - 1);
+    const int rsub = lane >> g.lsh, slot = lane & (g.L - 1);
+    bool staged = false;
+    for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {
+        const int tile = grp * g.tpi + tsub;
+        float acc[M];
+        Engine<FMT, XBF16, DOT, M>::pass(g, x, sl, tile, staged, xs, corr, acc);
+        reduce_partials<M>(g, red, acc);
+        const int64_t row = (int64_t)tile * g.R + rsub;
+        if (kpart == 0 && tile < g.tiles && row < g.n) {
+#pragma unroll
+            for (int t = 0; t < M; ++t)
+                if ((t & (g.L - 1)) == slot) y[(int64_t)sl.yrow[t] * g.n + row] = acc[t];
+        }
+    }
+}
+
+// ------------------------------------------------------------------- MoE
+// Distinct selected experts, ascending, computed by every workgroup from the
+// device-resident ids (no host round trip).  list[i] for i < *count.
+__device__ inline void distinct_experts(const int32_t *__restrict__ ids, int nslots, int n_experts, int *list, int *count)
+{
+    // nslots <= 64 <= TPB: one thread per slot.
+    __shared__ int s_ids[64];
+    __shared__ int s_first[64];
+    const int t = threadIdx.x;
+    if (t < nslots) s_ids[t] = ids[t];
+    __syncthreads();
+    if (t < nslots) {
+        int e = s_ids[t];
+        bool ok = e >= 0 && e < n_experts;
+        bool first = ok;
+        for (int q = 0; q < t && first; ++q) first = s_ids[q] != e;
+        s_first[t] = first ? 1 : 0;
+    }
+    __syncthreads();
+    if (t < nslots && s_first[t]) {
+        int e = s_ids[t], rank = 0;
+        for (int q = 0; q < nslots; ++q) rank += (s_first[q] && s_ids[q] < e) ? 1 : 0;
+        list[rank] = e;
+    }
+    if (t == 0) {
+        int c = 0;
+        for (int q = 0; q < nslots; ++q) c += s_first[q];
+        *count = c;
+    }
+    __syncthreads();
+}
+
+struct MoeArgs {
+    const uint8_t *experts;
+    int64_t expert_bytes;
+    const int32_t *ids;
+    const float *gw;
+    int32_t n_experts, m, top_k;
+};
+
+// Runs the dense passes of this workgroup over expert `e` for `cnt` slots
+// (1 <= cnt <= 8), dispatched to the engine instantiated for that count.
+template <int FMT, bool XBF16, bool DOT, int M>
+__device__ __forceinline__ void moe_tiles(Geom g, const void *x, const Slots sl, uint4 *xs, float *corr, float *red, int grp,
+                          float *part_out /* [M][tpi*R] or null */, float *y)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tsub = wave >> g.ksh, kpart = wave & (g.KS - 1);
+    const int rsub = lane >> g.lsh, slot = lane & (g.L - 1);
+    bool staged = false;
+    const int tile = grp * g.tpi + tsub;
+    float acc[M];
+    Engine<FMT, XBF16, DOT, M>::pass(g, x, sl, tile, staged, xs, corr, acc);
+    reduce_partials<M>(g, red, acc);
+    const int64_t row = (int64_t)tile * g.R + rsub;
+    if (kpart == 0 && tile < g.tiles && row < g.n) {
+        const int rl = tsub * g.R + rsub;
+#pragma unroll
+        for (int t = 0; t < M; ++t) {
+            if ((t & (g.L - 1)) == slot) {
+                if (part_out)
+                    part_out[t * (g.tpi * g.R) + rl] = acc[t];
+                else
+                    y[(int64_t)sl.yrow[t] * g.n + row] = acc[t];
+            }
+        }
+    }
+}
+
+template <int FMT, bool XBF16, bool DOT>
+__device__ __forceinline__ void moe_dispatch(int cnt, Geom g, const void *x, const Slots sl, uint4 *xs, float *corr, float *red,
+                             int grp, float *part_out, float *y)
+{
+    switch (cnt) {
+    case 1: moe_tiles<FMT, XBF16, DOT, 1>(g, x, sl, xs, corr, red, grp, part_out, y); break;
+    case 2: moe_tiles<FMT, XBF16, DOT, 2>(g, x, sl, xs, corr, red, grp, part_out, y); break;
+    case 3: moe_tiles<FMT, XBF16, DOT, 3>(g, x, sl, xs, corr, red, grp, part_out, y); break;
+    case 4: moe_tiles<FMT, XBF16, DOT, 4>(g, x, sl, xs, corr, red, grp, part_out, y); break;
+    case 5: moe_tiles<FMT, XBF16, DOT, 5>(g, x, sl, xs, corr, red, grp, part_out, y); break;
+    case 6: moe_tiles<FMT, XBF16, DOT, 6>(g, x, sl, xs, corr, red, grp, part_out, y); break;
+    case 7: moe_tiles<FMT, XBF16, DOT, 7>(g, x, sl, xs, corr, red, grp, part_out, y); break;
+    default: moe_tiles<FMT, XBF16, DOT, 8>(g, x, sl, xs, corr, red, grp, part_out, y); break;
+    }
+}
+
+// gate_up mode: grid = (row-tile groups, distinct-expert index).
+template <int FMT, bool XBF16, bool DOT>
+__global__ __launch_bounds__(TPB) void k_moe_gate_up(Geom g, MoeArgs a, const void *__restrict__ x, float *__restrict__ y)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int s_list[64];
+    __shared__ int s_count;
+    __shared__ int s_slots[64];
+    __shared__ int s_nsl;
+    __shared__ int32_t s_xrow[QG_MAX_M], s_yrow[QG_MAX_M];
+    const int nslots = a.m * a.top_k;
+    distinct_experts(a.ids, nslots, a.n_experts, s_list, &s_count);
+    if ((int)blockIdx.y >= s_count) return;      // uniform over the workgroup
+    const int e = s_list[blockIdx.y];
+    if (threadIdx.x == 0) {
+        int c = 0;
+        for (int s = 0; s < nslots; ++s)
+            if (a.ids[s] == e) s_slots[c++] = s;
+        s_nsl = c;
+    }
+    __syncthreads();
+    const int nsl = s_nsl;
+    constexpr int QPB = DOT ? 4 : 8;
+    uint4 *xs = (uint4 *)smem;
+    float *corr = (float *)(smem + (size_t)QG_MAX_M * QPB * g.wblk * 16);
+    float *red = corr + (FMT == QG_Q4_0 ? QG_MAX_M * g.wblk : 0);
+    Geom ge = g;
+    ge.w = a.experts + (int64_t)e * a.expert_bytes;
+    for (int c0 = 0; c0 < nsl; c0 += QG_MAX_M) {
+        const int cnt = min(QG_MAX_M, nsl - c0);
+        __syncthreads();     // earlier passes are done with the slot map
+        if (threadIdx.x < QG_MAX_M) {
+            const int s = s_slots[c0 + min((int)threadIdx.x, cnt - 1)];
+            s_xrow[threadIdx.x] = s / a.top_k;
+            s_yrow[threadIdx.x] = s;
+        }
+        Slots sl{s_xrow, s_yrow};
+        for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {
+            __syncthreads();
+            moe_dispatch<FMT, XBF16, DOT>(cnt, ge, x, sl, xs, corr, red, grp, nullptr, y);
+        }
+    }
+}
+
+// down-combine mode: grid = row-tile groups; each workgroup walks the
+// distinct experts in ascending order, keeps the per-slot partial products
+// of its rows in LDS and combines them with the router weights in slot order.
+template <int FMT, bool XBF16, bool DOT>
+__global__ __launch_bounds__(TPB) void k_moe_down(Geom g, MoeArgs a, const void *__restrict__ x, float *__restrict__ y)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int s_list[64];
+    __shared__ int s_count;
+    __shared__ int s_slots[64];
+    __shared__ int s_nsl;
+    __shared__ int32_t s_xrow[QG_MAX_M], s_yrow[QG_MAX_M];
+    const int nslots = a.m * a.top_k;
+    distinct_experts(a.ids, nslots, a.n_experts, s_list, &s_count);
+    constexpr int QPB = DOT ? 4 : 8;
+    uint4 *xs = (uint4 *)smem;
+    float *corr = (float *)(smem + (size_t)QG_MAX_M * QPB * g.wblk * 16);
+    float *red = corr + (FMT == QG_Q4_0 ? QG_MAX_M * g.wblk : 0);
+    float *part = red + WAVES * QG_MAX_M * 64;           // [nslots][tpi*R]
+    const int rows_pg = g.tpi * g.R;
+    for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {
+        for (int i = threadIdx.x; i < nslots * rows_pg; i += TPB) part[i] = 0.0f;
+        for (int ei = 0; ei < s_count; ++ei) {
+            const int e = s_list[ei];
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                int c = 0;
+                for (int s = 0; s < nslots; ++s)
+                    if (a.ids[s] == e) s_slots[c++] = s;
+                s_nsl = c;
+            }
+            __syncthreads();
+            const int nsl = s_nsl;
+            Geom ge = g;
+            ge.w = a.experts + (int64_t)e * a.expert_bytes;
+            for (int c0 = 0; c0 < nsl; c0 += QG_MAX_M) {
+                const int cnt = min(QG_MAX_M, nsl - c0);
+                __syncthreads();     // earlier passes are done with the slot map
+                if (threadIdx.x < QG_MAX_M) {
+                    // x is [m][top_k][k]: slot s reads row s
+                    s_xrow[threadIdx.x] = s_slots[c0 + min((int)threadIdx.x, cnt - 1)];
+                    s_yrow[threadIdx.x] = 0;
+                }
+                Slots sl{s_xrow, s_yrow};
+                __syncthreads();
+                // partial results land in a staging area, then move to part[slot]
+                float *tmp = part + nslots * rows_pg;    // [8][rows_pg]
+                moe_dispatch<FMT, XBF16, DOT>(cnt, ge, x, sl, xs, corr, red, grp, tmp, nullptr);
+                __syncthreads();
+                for (int i = threadIdx.x; i < cnt * rows_pg; i += TPB) {
+                    const int t = i / rows_pg, rl = i - t * rows_pg;
+                    part[s_slots[c0 + t] * rows_pg + rl] = tmp[t * rows_pg + rl];
+                }
+            }
+        }
+        __syncthreads();
+        // combine: y[t][row] = sum_j w[t][j] * part[t*top_k+j][row], j ascending
+        for (int i = threadIdx.x; i < a.m * rows_pg; i += TPB) {
+            const int t = i / rows_pg, rl = i - t * rows_pg;
+            const int64_t row = (int64_t)grp * rows_pg + rl;
+            if (row < g.n) {
+                float s = 0.0f;
+                for (int j = 0; j < a.top_k; ++j) {
+                    const int sidx = t * a.top_k + j;
+                    const int e = a.ids[sidx];
+                    if (e >= 0 && e < a.n_experts) s = __builtin_fmaf(a.gw[sidx], part[sidx * rows_pg + rl], s);
+                }
+                y[(int64_t)t * g.n + row] = s;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+
+// ------------------------------------------------------------ host plumbing
+struct Plan {
+    Geom g;
+    size_t lds;
+    int grid;
+};
+
+typedef void (*dense_fn)(Geom, const void *, float *);
+
+// Per-format kernel tables (one translation unit each, compiled in parallel).
+dense_fn dense_kernel_q8_0(int xt, int m);
+dense_fn dense_kernel_q4_0(int xt, int m);
+dense_fn dense_kernel_mxfp4(int xt, int m);
+hipError_t launch_moe_q8_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,
+                           const void *x, float *y, hipStream_t s);
+hipError_t launch_moe_q4_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,
+                           const void *x, float *y, hipStream_t s);
+hipError_t launch_moe_mxfp4(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,
+                            const void *x, float *y, hipStream_t s);
+
+template <int FMT, bool XBF16, bool DOT>
+dense_fn pick_dense(int m)
+{
+    switch (m) {
+    case 1: return k_dense<FMT, XBF16, DOT, 1>;
+    case 2: return k_dense<FMT, XBF16, DOT, 2>;
+    case 3: return k_dense<FMT, XBF16, DOT, 3>;
+    case 4: return k_dense<FMT, XBF16, DOT, 4>;
+    case 5: return k_dense<FMT, XBF16, DOT, 5>;
+    case 6: return k_dense<FMT, XBF16, DOT, 6>;
+    case 7: return k_dense<FMT, XBF16, DOT, 7>;
+    default: return k_dense<FMT, XBF16, DOT, 8>;
+    }
+}
+
+// Workgroups may use more than 64 KiB of LDS on gfx950 (160 KiB per CU);
+// larger dynamic allocations are declared to the runtime first.
+inline hipError_t allow_lds(const void *fn, size_t bytes)
+{
+    if (bytes <= 65536) return hipSuccess;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int FMT, bool XBF16, bool DOT>
+hipError_t launch_moe_t(int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds, const void *x,
+                        float *y, hipStream_t s)
+{
+    const void *fn = mode == QG_MOE_GATE_UP ? (const void *)k_moe_gate_up<FMT, XBF16, DOT>
+                                            : (const void *)k_moe_down<FMT, XBF16, DOT>;
+    hipError_t e = allow_lds(fn, lds);
+    if (e != hipSuccess) return e;
+    if (mode == QG_MOE_GATE_UP)
+        hipLaunchKernelGGL((k_moe_gate_up<FMT, XBF16, DOT>), dim3(p.grid, maxdistinct), dim3(TPB), lds, s, p.g, a, x, y);
+    else
+        hipLaunchKernelGGL((k_moe_down<FMT, XBF16, DOT>), dim3(p.grid), dim3(TPB), lds, s, p.g, a, x, y);
+    return hipGetLastError();
+}
+
+} // namespace qg

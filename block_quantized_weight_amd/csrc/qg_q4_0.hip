@@ -1,0 +1,18 @@
+// qg_q4_0.hip -- Q4_0 instantiations of the dense and expert GEMV kernels.
+#include "qg_common.h"
+
+namespace qg {
+
+dense_fn dense_kernel_q4_0(int xt, int m)
+{
+    return xt == QG_BF16 ? pick_dense<QG_Q4_0, true, true>(m) : pick_dense<QG_Q4_0, false, false>(m);
+}
+
+hipError_t launch_moe_q4_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,
+                           const void *x, float *y, hipStream_t s)
+{
+    if (xt == QG_BF16) return launch_moe_t<QG_Q4_0, true, true>(mode, p, a, maxdistinct, lds, x, y, s);
+    return launch_moe_t<QG_Q4_0, false, false>(mode, p, a, maxdistinct, lds, x, y, s);
+}
+
+} // namespace qg

@@ -1,0 +1,172 @@
+/*
+ * qgemv.h -- C ABI of libqgemv.so: block-quantized weight matrix-vector
+ * products for MI355X (gfx950).
+ *
+ * What is computed.  The decode step of an LLM streams every weight matrix
+ * once per generated token through a matrix-vector product; decode is bound by
+ * memory bandwidth (imp README, "Known limitations": a card with less
+ * bandwidth "decodes roughly 25% slower, since decode is bandwidth-bound").
+ * The weights are stored in the block formats the engines serve: Q8_0 and
+ * Q4_0 (Imparo README, opening release notes and the M3 Pro benchmark table;
+ * imp README, "Features" table, Quantization row) and MXFP4, "FP4 E2M1 +
+ * UE8M0 block scales" at 4.25 bits per weight (imp release notes, v0.6).
+ * The top-k expert variant covers mixture-of-experts layers such as
+ * gpt-oss-20b, "MoE (32 experts, top-4)" in MXFP4 (imp README, "Supported
+ * models" table), with expert routing read on the device, not copied to the
+ * host (imp release notes, v0.7.0 "Known issues": host-side MoE routing is
+ * incompatible with graph capture).
+ *
+ * Canonical block formats (32 weights along K per block, little-endian):
+ *   Q8_0  34 B: fp16 scale d, then 32 int8 codes q;              w = d * q
+ *   Q4_0  18 B: fp16 scale d, then 16 bytes; byte j holds code j in its low
+ *               nibble and code j+16 in its high nibble;          w = d * (q - 8)
+ *   MXFP4 17 B: UE8M0 exponent byte E, then 16 bytes with the same nibble
+ *               split; each nibble is an E2M1 code c (sign in bit 3);
+ *                                                                 w = E2M1(c) * 2^(E-127)
+ * A matrix is N rows (outputs) by K columns (inputs), stored as N * (K/32)
+ * canonical blocks, row-major.  E = 255 decodes to NaN; E2M1 has no NaN.
+ *
+ * Packed layout.  The GEMV entry points read weights in a packed layout made
+ * once at load time by qg_pack (device) or qg_pack_host (CPU): per tile of
+ * R = 64/L rows, each wavefront load instruction reads 1 KiB of codes that is
+ * contiguous in memory; scales are a separate stream.  The layout depends only
+ * on (fmt, n, k); qg_layout reports it, qg_packed_bytes its size.  Packing is
+ * bit-exact: qg_unpack(qg_pack(B)) == B byte for byte.
+ *
+ * Conventions for every entry point below:
+ *  - Pointers named as device memory are device memory owned by the caller
+ *    (for example torch tensors).  Pointers named as host memory are host
+ *    memory.  No entry point frees caller memory.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Device work is enqueued on it and the call returns without waiting.
+ *  - Arguments are validated on the host before any HIP call; on error a
+ *    status is returned and nothing is enqueued.  A HIP launch failure returns
+ *    QG_EHIP.  Faults inside kernels surface at the caller's next
+ *    synchronisation, as in HIP.
+ *  - Results are deterministic: the same inputs give the same bits (every
+ *    reduction has a fixed order).
+ *  - Device-resident values are not inspected on the host: expert ids must be
+ *    in [0, n_experts); an id outside that range is skipped (its slot
+ *    contributes nothing and, in gate_up mode, its output rows are left
+ *    unwritten).
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    QG_OK = 0,
+    QG_EINVAL = 1,        /* null pointer, non-positive size, k % 32 != 0, m outside [1, 8], bad enum */
+    QG_EUNSUPPORTED = 2,  /* valid but outside what the kernels serve (see the limits per call) */
+    QG_EALIGN = 3,        /* device pointer misaligned */
+    QG_EHIP = 4           /* a HIP runtime call failed */
+};
+
+/* Weight formats. */
+enum { QG_Q8_0 = 0, QG_Q4_0 = 1, QG_MXFP4 = 2 };
+
+/* Activation element types: fp32, or bf16 bit patterns (uint16). */
+enum { QG_F32 = 0, QG_BF16 = 1 };
+
+/* Expert modes of moe_qgemv_topk. */
+enum { QG_MOE_GATE_UP = 0, QG_MOE_DOWN_COMBINE = 1 };
+
+/* Largest co-batch (tokens per call). */
+#define QG_MAX_M 8
+
+/* Description of the packed layout of one n x k matrix. */
+typedef struct {
+    int32_t fmt;
+    int32_t lanes_per_row;      /* L: lanes of a wavefront that share one row */
+    int32_t rows_per_tile;      /* R = 64 / L */
+    int32_t parts_per_step;     /* 16-byte code loads per lane per step: 2 (Q8_0) or 1 */
+    int32_t scale_bytes;        /* 2 (fp16) or 1 (UE8M0) */
+    int32_t reserved;
+    int64_t n, k;
+    int64_t steps;              /* S: blocks per lane per tile = ceil((k/32) / L) */
+    int64_t tiles;              /* ceil(n / R) */
+    int64_t code_tile_bytes;    /* S * parts * 1024 */
+    int64_t scale_tile_bytes;   /* S * 64 * scale_bytes */
+    int64_t scale_offset;       /* byte offset of the scale stream = tiles * code_tile_bytes */
+    int64_t packed_bytes;       /* total size, rounded up to a multiple of 256 */
+} qg_layout_t;
+
+/* Human-readable name of a status code (static string). */
+const char *qg_status_str(int status);
+
+/* Size in bytes of the packed form of an n x k matrix, or -1 if (fmt, n, k) is invalid. */
+int64_t qg_packed_bytes(int fmt, int64_t n, int64_t k);
+
+/* Fills *out with the packed layout of an n x k matrix.  out: host memory. */
+int qg_layout(int fmt, int64_t n, int64_t k, qg_layout_t *out);
+
+/*
+ * Canonical -> packed (and back) on the host.  canon: host memory,
+ * n * (k/32) canonical blocks.  packed: host memory, qg_packed_bytes bytes;
+ * every padding byte of the packed form is written as zero.
+ */
+int qg_pack_host(int fmt, const void *canon, int64_t n, int64_t k, void *packed);
+int qg_unpack_host(int fmt, const void *packed, int64_t n, int64_t k, void *canon);
+
+/*
+ * The same transforms on the device.  canon, packed: device memory; packed
+ * must be 16-byte aligned (256 recommended).  Bit-identical to the host
+ * versions.
+ */
+int qg_pack(int fmt, const void *canon, int64_t n, int64_t k, void *packed, void *stream);
+int qg_unpack(int fmt, const void *packed, int64_t n, int64_t k, void *canon, void *stream);
+
+/*
+ * Test aid: decodes a packed matrix to fp32 w[n][k] (device memory, row-major)
+ * through the same unpack steps the GEMV kernels use.  Every decoded weight
+ * is exact in fp32 when it is finite, so the result is comparable bit for bit.
+ */
+int qg_dequant_f32(int fmt, const void *w_packed, int64_t n, int64_t k, float *w, void *stream);
+
+/*
+ * Dense product for a co-batch of m tokens (1 <= m <= 8):
+ *     y[t][i] = sum_c W[i][c] * x[t][c]        t < m, i < n
+ * w_packed: device, packed layout of (fmt, n, k), 16-byte aligned (256 recommended).
+ * x: device, [m][k] row-major, fp32 or bf16 (xt), 16-byte aligned.
+ * y: device, fp32 [m][n] row-major, 4-byte aligned, overwritten.
+ * Accumulation is fp32; x is used exactly (bf16 -> fp32 is exact).
+ * Limits: n, k <= 2^31 - 1 and k % 32 == 0.
+ */
+int qgemv_q8_0(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
+               float *y, void *stream);
+int qgemv_q4_0(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
+               float *y, void *stream);
+int qgemv_mxfp4(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
+                float *y, void *stream);
+
+/*
+ * Top-k expert product.  w_experts: device, n_experts packed matrices of
+ * identical shape (fmt, n, k) back to back, expert e at byte offset
+ * e * qg_packed_bytes(fmt, n, k) (a multiple of 256); 16-byte aligned.
+ * topk_ids: device int32 [m][top_k]; topk_w: device fp32 [m][top_k].
+ * Ids should be distinct within a token.
+ *   QG_MOE_GATE_UP:      x [m][k];         y [m][top_k][n],
+ *                        y[t][j][i] = W_{ids[t][j]}[i] . x[t]   (topk_w unused, may be NULL)
+ *   QG_MOE_DOWN_COMBINE: x [m][top_k][k];  y [m][n],
+ *                        y[t][i] = sum over j ascending of topk_w[t][j] * (W_{ids[t][j]}[i] . x[t][j])
+ * Only the selected experts' weights are read; each distinct selected expert
+ * is streamed once per call for all tokens that chose it.
+ * Limits: 1 <= m <= 8, 1 <= top_k <= n_experts, m * top_k <= 64,
+ * n_experts <= 65536.  y is overwritten (rows of invalid ids excepted).
+ */
+int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n, int64_t k,
+                   const int32_t *topk_ids, const float *topk_w, int64_t m, int64_t top_k,
+                   const void *x, int xt, int mode, float *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

@@ -1,0 +1,168 @@
+"""Host-side checks of libqgemv.so: symbols, layout, host packer, argument
+validation.  No call here reaches a kernel launch: every device-side call is
+made with arguments the host validation rejects."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_quantized_weight_amd as q
+import workloads as wl
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qgemv.h")
+
+
+def _declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"qgemv_q8_0", "qgemv_q4_0", "qgemv_mxfp4", "moe_qgemv_topk"} <= set(names)
+    L = ctypes.CDLL(q.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(q.SIGNATURES)
+
+
+def test_status_strings():
+    assert q.status_str(q.QG_OK) == "ok"
+    assert q.status_str(q.QG_EALIGN) == "misaligned device pointer"
+
+
+@pytest.mark.parametrize("fmt", [q.Q8_0, q.Q4_0, q.MXFP4])
+@pytest.mark.parametrize("n,k", [(1, 32), (65, 96), (300, 2048), (19, 608), (2560, 9728)])
+def test_layout_is_consistent(fmt, n, k):
+    lo = q.layout(fmt, n, k)
+    L, R, S = lo["lanes_per_row"], lo["rows_per_tile"], lo["steps"]
+    assert L * R == 64 and L in (1, 2, 4, 8, 16, 32, 64)
+    assert S == -(-(k // 32) // L) and lo["tiles"] == -(-n // R)
+    assert lo["code_tile_bytes"] == S * lo["parts_per_step"] * 1024
+    assert lo["scale_tile_bytes"] == S * 64 * lo["scale_bytes"]
+    raw = lo["tiles"] * (lo["code_tile_bytes"] + lo["scale_tile_bytes"])
+    assert lo["packed_bytes"] == -(-raw // 256) * 256
+    assert lo["packed_bytes"] == q.packed_bytes(fmt, n, k)
+    assert lo["code_tile_bytes"] % 1024 == 0
+    assert lo["packed_bytes"] >= n * (k // 32) * q.BLOCK_BYTES[fmt]
+
+
+def test_workload_shapes_pack_without_padding():
+    shapes = [(q.Q8_0, n, k) for _, _, n, k in wl.c2_sweep_shapes()[:4]] + [(q.Q8_0, 151936, 2560)]
+    shapes += [(q.Q4_0, 19456, 2560), (q.Q4_0, 2560, 9728), (q.Q4_0, 6144, 4096), (q.Q4_0, 24576, 4096),
+               (q.Q4_0, 4096, 12288), (q.MXFP4, 3584, 2048), (q.MXFP4, 2048, 1792)]
+    for fmt, n, k in shapes:
+        assert q.packed_bytes(fmt, n, k) == n * (k // 32) * q.BLOCK_BYTES[fmt], (fmt, n, k)
+
+
+@pytest.mark.parametrize("fmt", [q.Q8_0, q.Q4_0, q.MXFP4])
+@pytest.mark.parametrize("n,k", [(1, 32), (3, 64), (65, 96), (300, 2048), (19, 608), (130, 1792)])
+def test_host_pack_round_trip(fmt, n, k):
+    c = wl.blocks_for(fmt, n, k, config=50, matrix=n).reshape(-1)
+    p = q.pack_host(fmt, c, n, k)
+    assert np.array_equal(q.unpack_host(fmt, p, n, k), c)
+
+
+@pytest.mark.parametrize("fmt", [q.Q8_0, q.Q4_0, q.MXFP4])
+def test_host_pack_round_trip_all_byte_values(fmt):
+    n, k = 64, 256
+    nbytes = n * (k // 32) * q.BLOCK_BYTES[fmt]
+    c = (np.arange(nbytes, dtype=np.int64) * 37 % 256).astype(np.uint8)
+    p = q.pack_host(fmt, c, n, k)
+    assert np.array_equal(q.unpack_host(fmt, p, n, k), c)
+
+
+@pytest.mark.parametrize("fmt", [q.Q8_0, q.Q4_0, q.MXFP4])
+def test_packed_record_placement(fmt):
+    """Every block's bytes land in the (tile, step, lane) record the layout names:
+    lane l of step j in tile t holds block j*L + l%L of row t*R + l/L."""
+    n, k = 70, 320
+    lo = q.layout(fmt, n, k)
+    L, R, S, P, sb = lo["lanes_per_row"], lo["rows_per_tile"], lo["steps"], lo["parts_per_step"], lo["scale_bytes"]
+    nb, bb = k // 32, q.BLOCK_BYTES[fmt]
+    c = np.zeros((n, nb, bb), dtype=np.uint8)
+    rng = np.random.default_rng(3)
+    c[:] = rng.integers(0, 256, size=c.shape, dtype=np.uint8)
+    p = q.pack_host(fmt, c.reshape(-1), n, k)
+    for (row, blk) in [(0, 0), (n - 1, nb - 1), (R, 1), (5, nb // 2)]:
+        t, r = divmod(row, R)
+        j, s = divmod(blk, L)
+        lane = r * L + s
+        # the scale travels unchanged
+        so = lo["scale_offset"] + t * lo["scale_tile_bytes"] + j * 64 * sb + lane * sb
+        assert bytes(p[so:so + sb]) == bytes(c[row, blk, :sb])
+        # the code bytes are a permutation of the block's code nibbles/bytes
+        co = t * lo["code_tile_bytes"] + j * P * 1024 + lane * 16
+        got = np.concatenate([p[co + h * 1024: co + h * 1024 + 16] for h in range(P)])
+        body = c[row, blk, sb:]
+        if fmt == q.Q8_0:
+            assert np.array_equal(got, body)
+        else:
+            nib = lambda a: sorted(list(a & 15) + list(a >> 4))
+            assert nib(got) == nib(body)
+
+
+def test_padding_bytes_are_zero():
+    fmt, n, k = q.Q4_0, 5, 96        # 5 rows -> padded rows in the last tile
+    c = np.full(n * 3 * 18, 0xFF, dtype=np.uint8)
+    p = q.pack_host(fmt, c, n, k)
+    lo = q.layout(fmt, n, k)
+    used = n * 3 * (16 + 2)
+    assert int(np.count_nonzero(p)) == used
+    assert p.size == lo["packed_bytes"]
+
+
+# ------------------------------------------------ validation (nothing launched)
+BAD = ctypes.c_void_p(0)
+ODD = ctypes.c_void_p(0x1001)
+
+
+def test_shape_validation():
+    L = q.lib()
+    assert L.qg_packed_bytes(q.Q8_0, 4, 33) == -1
+    assert L.qg_packed_bytes(q.Q8_0, 0, 32) == -1
+    assert L.qg_packed_bytes(7, 4, 32) == -1
+    assert L.qg_layout(q.Q4_0, 4, 32, None) == q.QG_EINVAL
+    assert L.qg_layout(q.Q4_0, 1 << 32, 32, None) == q.QG_EUNSUPPORTED
+
+
+def test_gemv_argument_validation():
+    L = q.lib()
+    st = L.qgemv_q8_0(BAD, 64, 64, BAD, q.X_F32, 1, BAD, None)
+    assert st == q.QG_EINVAL                              # null pointers
+    a = ctypes.c_void_p(0x100000)
+    assert L.qgemv_q8_0(a, 64, 48, a, q.X_F32, 1, a, None) == q.QG_EINVAL      # k % 32
+    assert L.qgemv_q4_0(a, 64, 64, a, q.X_F32, 0, a, None) == q.QG_EINVAL      # m = 0
+    assert L.qgemv_q4_0(a, 64, 64, a, q.X_F32, 9, a, None) == q.QG_EINVAL      # m = 9
+    assert L.qgemv_mxfp4(a, 64, 64, a, 5, 1, a, None) == q.QG_EINVAL           # bad xt
+    assert L.qgemv_mxfp4(a, -1, 64, a, q.X_BF16, 1, a, None) == q.QG_EINVAL    # n <= 0
+    assert L.qgemv_q8_0(ODD, 64, 64, a, q.X_F32, 1, a, None) == q.QG_EALIGN    # w not 16-aligned
+    assert L.qgemv_q8_0(a, 64, 64, ODD, q.X_F32, 1, a, None) == q.QG_EALIGN    # x not 16-aligned
+    assert L.qgemv_q8_0(a, 64, 64, a, q.X_F32, 1, ODD, None) == q.QG_EALIGN    # y not 4-aligned
+
+
+def test_moe_argument_validation():
+    L = q.lib()
+    a = ctypes.c_void_p(0x100000)
+    f = L.moe_qgemv_topk
+    assert f(q.MXFP4, a, 32, 64, 64, a, a, 1, 4, a, q.X_BF16, 2, a, None) == q.QG_EINVAL      # mode
+    assert f(q.MXFP4, a, 32, 64, 64, a, None, 1, 4, a, q.X_BF16, 1, a, None) == q.QG_EINVAL   # no weights
+    assert f(q.MXFP4, a, 32, 64, 64, a, a, 1, 33, a, q.X_BF16, 0, a, None) == q.QG_EINVAL     # top_k > E
+    assert f(q.MXFP4, a, 32, 64, 64, a, a, 9, 4, a, q.X_BF16, 0, a, None) == q.QG_EINVAL      # m > 8
+    assert f(q.MXFP4, a, 100, 64, 64, a, a, 8, 9, a, q.X_BF16, 0, a, None) == q.QG_EUNSUPPORTED  # m*top_k
+    assert f(q.MXFP4, ODD, 32, 64, 64, a, a, 1, 4, a, q.X_BF16, 0, a, None) == q.QG_EALIGN
+    assert f(q.MXFP4, a, 32, 64, 64, ODD, a, 1, 4, a, q.X_BF16, 0, a, None) == q.QG_EALIGN
+
+
+def test_pack_and_dequant_validation():
+    L = q.lib()
+    a = ctypes.c_void_p(0x100000)
+    assert L.qg_pack(q.Q8_0, a, 4, 40, a, None) == q.QG_EINVAL
+    assert L.qg_pack(q.Q8_0, a, 4, 64, ODD, None) == q.QG_EALIGN
+    assert L.qg_unpack(q.Q8_0, BAD, 4, 64, a, None) == q.QG_EINVAL
+    assert L.qg_dequant_f32(q.Q8_0, a, 4, 64, ODD, None) == q.QG_EALIGN
+    assert L.qg_pack_host(q.Q8_0, None, 4, 64, None) == q.QG_EINVAL
