@@ -36,7 +36,16 @@ SIGNATURES = {
     "qgemv_q4_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_mxfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "moe_qgemv_topk": (_i, [_i, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i, _i, _vp, _vp]),
+    "qg_chain_plan_bytes": (_i64, [_i64]),
+    "qg_chain_plan": (_i, [_i, _i, _i64, _vp, _i64, _vp]),
+    "qgemv_chain": (_i, [_vp, _vp, _vp]),
+    "qg_chain_error": (_i, []),
 }
+
+
+class ChainLinkC(ctypes.Structure):
+    _fields_ = [("w_packed", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
 
 
 class QGError(RuntimeError):
@@ -224,3 +233,48 @@ def moe_qgemv_topk(fmt, w_experts, n_experts, n, k, topk_ids, topk_w, x, mode, y
                               _dev_ptr(y, "y"), _stream(stream))
     _check("moe_qgemv_topk", st)
     return y
+
+
+class Chain:
+    """A chain of dense products run in order by one persistent kernel.
+
+    links: list of (w_packed, n, k, x, y) with device tensors; all share the
+    format, the activation dtype and the token count m.  The plan (built once)
+    holds the tensors' addresses, so they must stay alive and in place.
+    """
+
+    def __init__(self, fmt, links):
+        torch = _torch()
+        if not links:
+            raise ValueError("empty chain")
+        xt = _xt(links[0][3])
+        m = links[0][3].reshape(-1, links[0][2]).shape[0]
+        arr = (ChainLinkC * len(links))()
+        self._keep = []
+        for i, (w, n, k, x, y) in enumerate(links):
+            x2 = x.reshape(-1, k)
+            if _xt(x2) != xt or x2.shape[0] != m or y.numel() != m * n:
+                raise ValueError("chain links must share activation dtype and token count")
+            arr[i] = ChainLinkC(_dev_ptr(w, "w_packed").value, _dev_ptr(x2, "x").value, _dev_ptr(y, "y").value,
+                                n, k)
+            self._keep += [w, x, y]
+        nbytes = lib().qg_chain_plan_bytes(len(links))
+        if nbytes < 0:
+            raise QGError("qg_chain_plan_bytes", QG_EINVAL)
+        self.plan_host = (ctypes.c_uint8 * nbytes)()
+        _check("qg_chain_plan", lib().qg_chain_plan(fmt, xt, m, arr, len(links), self.plan_host))
+        host = torch.frombuffer(bytearray(self.plan_host), dtype=torch.uint8)
+        self.plan_device = host.to(links[0][0].device)
+        torch.cuda.synchronize()
+        self.count = len(links)
+
+    def run(self, stream=None):
+        _check("qgemv_chain", lib().qgemv_chain(self.plan_host, _dev_ptr(self.plan_device, "plan"), _stream(stream)))
+
+
+def chain_error():
+    """1 if a chain barrier timed out since the last call (synchronises), else 0."""
+    v = lib().qg_chain_error()
+    if v < 0:
+        raise QGError("qg_chain_error", QG_EHIP)
+    return v

@@ -1,6 +1,6 @@
 // qg_api.hip -- C ABI of libqgemv.so: argument validation, layout, launch
 // plans, the packer kernels and the dequantization test aid.
-#include "qg_common.h"
+#include "qg_chain.h"
 
 namespace qg {
 namespace {
@@ -162,6 +162,57 @@ int grid_for(int64_t items, int block)
     if (g > 65535 * 8) g = 65535 * 8;
     if (g < 1) g = 1;
     return (int)g;
+}
+
+// Chain plan of one link: the layout, KS for CWAVES waves sized from the
+// tiles each workgroup owns, one activation window (the whole x in LDS).
+int chain_link_plan(int fmt, int xt, int m, int P, const qg_chain_link_t &in, ChainLink *out, size_t *lds)
+{
+    int st = check_shape(fmt, in.n, in.k);
+    if (st) return st;
+    if (!in.w_packed || !in.x || !in.y) return QG_EINVAL;
+    if (!aligned(in.w_packed, 16) || !aligned(in.x, 16) || !aligned(in.y, 4)) return QG_EALIGN;
+    const Layout lo = make_layout(fmt, in.n, in.k);
+    const bool dot = uses_dot(fmt, xt);
+    Geom &g = out->g;
+    memset(out, 0, sizeof(*out));
+    g.w = (const uint8_t *)in.w_packed;
+    g.n = (int32_t)lo.n;
+    g.k = (int32_t)lo.k;
+    g.nb = (int32_t)lo.nb;
+    g.L = lo.L;
+    g.lsh = lo.lsh;
+    g.R = lo.R;
+    g.S = (int32_t)lo.S;
+    g.tiles = (int32_t)lo.tiles;
+    g.ctb = lo.ctb;
+    g.stb = lo.stb;
+    g.soff = lo.soff;
+    const int64_t tpw = (lo.tiles + P - 1) / P;               // tiles per workgroup (max)
+    int tp2 = 1;
+    while (tp2 < tpw && tp2 < CWAVES) tp2 <<= 1;
+    int KS = CWAVES / tp2;
+    while (KS > 1 && KS > lo.S) KS >>= 1;
+    g.KS = KS;
+    g.ksh = ilog2(KS);
+    g.tpi = CWAVES / KS;
+    g.ngroups = 0;
+    const int64_t sw = ((lo.S + KS - 1) / KS) * KS;
+    g.SW = (int32_t)sw;
+    g.nwin = 1;
+    g.wblk = (int32_t)(sw * lo.L);
+    const size_t b = chain_lds_bytes(m, dot, fmt, g.wblk, g.tpi * g.R);
+    if (b > 150 * 1024) return QG_EUNSUPPORTED;
+    *lds = b;
+    out->x = in.x;
+    out->y = in.y;
+    return QG_OK;
+}
+
+const void *chain_kernel(int fmt, int xt, int m)
+{
+    return fmt == QG_Q8_0 ? chain_kernel_q8_0(xt, m) : fmt == QG_Q4_0 ? chain_kernel_q4_0(xt, m)
+                                                                     : chain_kernel_mxfp4(xt, m);
 }
 
 } // namespace
@@ -331,6 +382,69 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
                                     : launch_moe_mxfp4(xt, mode, p, a, maxdistinct, lds, x, y, s);
     if (e != hipSuccess) return QG_EHIP;
     return launch_status();
+}
+
+int64_t qg_chain_plan_bytes(int64_t count)
+{
+    if (count < 1 || count > (1 << 20)) return -1;
+    return (int64_t)(sizeof(ChainHdr) + 16 + (size_t)count * sizeof(ChainLink));
+}
+
+int qg_chain_plan(int fmt, int xt, int64_t m, const qg_chain_link_t *links, int64_t count, void *plan)
+{
+    if (!valid_fmt(fmt) || (xt != QG_F32 && xt != QG_BF16) || m < 1 || m > QG_MAX_M) return QG_EINVAL;
+    if (!links || !plan || count < 1) return QG_EINVAL;
+    if (count > (1 << 20)) return QG_EUNSUPPORTED;
+    int dev = 0, cus = 0, occ = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QG_EHIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return QG_EHIP;
+    ChainHdr *h = (ChainHdr *)plan;
+    ChainLink *L = (ChainLink *)((uint8_t *)plan + sizeof(ChainHdr) + 16);
+    int P = cus < CHAIN_MAX_WG ? cus : CHAIN_MAX_WG;
+    size_t lds = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        size_t b = 0;
+        int st = chain_link_plan(fmt, xt, (int)m, P, links[i], &L[i], &b);
+        if (st) return st;
+        if (b > lds) lds = b;
+    }
+    const void *fn = chain_kernel(fmt, xt, (int)m);
+    if (allow_lds(fn, lds) != hipSuccess) return QG_EHIP;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, CTPB, lds) != hipSuccess) return QG_EHIP;
+    if (occ < 1) return QG_EUNSUPPORTED;
+    memset(h, 0, sizeof(*h));
+    h->magic = CHAIN_MAGIC;
+    h->fmt = fmt;
+    h->xt = xt;
+    h->m = (int32_t)m;
+    h->count = (int32_t)count;
+    h->grid = P;
+    h->lds = (int64_t)lds;
+    return QG_OK;
+}
+
+int qgemv_chain(const void *plan_host, const void *plan_device, void *stream)
+{
+    if (!plan_host || !plan_device) return QG_EINVAL;
+    const ChainHdr *h = (const ChainHdr *)plan_host;
+    if (h->magic != CHAIN_MAGIC || h->count < 1 || h->grid < 1) return QG_EINVAL;
+    if (!aligned(plan_device, 16)) return QG_EALIGN;
+    const ChainLink *links = (const ChainLink *)((const uint8_t *)plan_device + sizeof(ChainHdr) + 16);
+    int nlinks = h->count;
+    const void *fn = chain_kernel(h->fmt, h->xt, h->m);
+    if (allow_lds(fn, (size_t)h->lds) != hipSuccess) return QG_EHIP;
+    void *args[] = {(void *)&links, (void *)&nlinks};
+    hipError_t e = hipLaunchCooperativeKernel(fn, dim3(h->grid), dim3(CTPB), args, (unsigned)h->lds,
+                                              as_stream(stream));
+    return e == hipSuccess ? launch_status() : QG_EHIP;
+}
+
+int qg_chain_error(void)
+{
+    if (hipDeviceSynchronize() != hipSuccess) return -1;
+    int a = chain_error_q8_0(true), b = chain_error_q4_0(true), c = chain_error_mxfp4(true);
+    if (a < 0 || b < 0 || c < 0) return -1;
+    return (a | b | c) ? 1 : 0;
 }
 
 } // extern "C"

@@ -275,6 +275,41 @@ __device__ __forceinline__ bf16x2_t q4_pair(uint32_t w, int kk)
     return __builtin_bit_cast(bf16x2_t, v);
 }
 
+// Global-memory accessors.  Pointers that reach a kernel through memory (not
+// as kernel arguments) are generic; casting them to the global address space
+// keeps the accesses global_* (flat accesses would also count against the LDS
+// wait counter and serialise LDS waits behind weight loads in flight).
+#define QG_GLOBAL __attribute__((address_space(1)))
+typedef unsigned int qg_u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load of weights: read once, so marked nontemporal.
+__device__ __forceinline__ uint4 ld_stream16(const uint8_t *p)
+{
+    const qg_u32x4 v = __builtin_nontemporal_load((const QG_GLOBAL qg_u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t ld_stream_u16(const uint16_t *p)
+{
+    return __builtin_nontemporal_load((const QG_GLOBAL uint16_t *)p);
+}
+
+__device__ __forceinline__ uint32_t ld_stream_u8(const uint8_t *p)
+{
+    return __builtin_nontemporal_load((const QG_GLOBAL uint8_t *)p);
+}
+
+__device__ __forceinline__ uint4 ld_global16(const void *p)
+{
+    const qg_u32x4 v = *(const QG_GLOBAL qg_u32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void st_global_f32(float *p, float v)
+{
+    *(QG_GLOBAL float *)p = v;
+}
+
 __device__ __forceinline__ bf16x2_t u32_as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
 
 __device__ __forceinline__ float dot2(bf16x2_t a, bf16x2_t b, float c)
@@ -326,7 +361,7 @@ struct XStage {
         constexpr int QPB = DOT ? 4 : 8;
         const int b0 = w * g.SW * g.L;
         const int total = M * g.wblk;
-        for (int idx = threadIdx.x; idx < total; idx += TPB) {
+        for (int idx = threadIdx.x; idx < total; idx += (int)blockDim.x) {
             const int t = idx / g.wblk, bl = idx - t * g.wblk, b = b0 + bl;
             const int64_t xo = (int64_t)sl.xrow[t] * g.k;
             uint4 q[8];
@@ -334,7 +369,7 @@ struct XStage {
             if (b < g.nb) {
                 if (XBF16) {
                     const uint4 *src = (const uint4 *)((const uint16_t *)x + xo + (int64_t)b * QK);
-                    uint4 r[4] = {src[0], src[1], src[2], src[3]};
+                    uint4 r[4] = {ld_global16(src), ld_global16(src + 1), ld_global16(src + 2), ld_global16(src + 3)};
                     const uint32_t *rw = (const uint32_t *)r;
                     if (DOT) {
 #pragma unroll
@@ -356,7 +391,7 @@ struct XStage {
                 } else {
                     const uint4 *src = (const uint4 *)((const float *)x + xo + (int64_t)b * QK);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) q[i] = src[i];
+                    for (int i = 0; i < 8; ++i) q[i] = ld_global16(src + i);
                     if (FMT != QG_Q8_0) {
                         const float *f = (const float *)q;
 #pragma unroll
@@ -377,10 +412,10 @@ struct XStage {
 // Steps per batch (loads in flight per lane before the first use).
 template <int FMT, bool DOT> struct Batch { static constexpr int U = (FMT == QG_Q8_0 || !DOT) ? 4 : 8; };
 
-template <int FMT, bool XBF16, bool DOT, int M>
+template <int FMT, bool XBF16, bool DOT, int M, int UB = Batch<FMT, DOT>::U>
 struct Engine {
     static constexpr int P = FMT == QG_Q8_0 ? 2 : 1;
-    static constexpr int U = Batch<FMT, DOT>::U;
+    static constexpr int U = UB;
     static constexpr int QPB = DOT ? 4 : 8;
 
     struct Regs {
@@ -388,21 +423,23 @@ struct Engine {
         uint32_t s[U];
     };
 
+    // Issues the loads of `cnt` (>= 1) steps jfirst, jfirst+KS, ...  Every call
+    // issues exactly U*(P+1) loads: steps past cnt repeat the last one (a cache
+    // hit, never used).  The fixed count keeps the compiler's vmcnt waits exact,
+    // so a batch in flight overlaps the compute of the previous one.
     static __device__ __forceinline__ void load(const Geom &g, const uint8_t *ct, const uint8_t *st, int lane,
                                                 int jfirst, int cnt, int KS, Regs &r)
     {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (u < cnt) {
-                const int j = jfirst + u * KS;
-                const uint8_t *cp = ct + (int64_t)j * (P * 1024) + lane * 16;
+            const int j = jfirst + min(u, cnt - 1) * KS;
+            const uint8_t *cp = ct + (int64_t)j * (P * 1024) + lane * 16;
 #pragma unroll
-                for (int h = 0; h < P; ++h) r.c[u][h] = *(const uint4 *)(cp + h * 1024);
-                if (FMT == QG_MXFP4)
-                    r.s[u] = st[(int64_t)j * 64 + lane];
-                else
-                    r.s[u] = ((const uint16_t *)st)[(int64_t)j * 64 + lane];
-            }
+            for (int h = 0; h < P; ++h) r.c[u][h] = ld_stream16(cp + h * 1024);
+            if (FMT == QG_MXFP4)
+                r.s[u] = ld_stream_u8(st + (int64_t)j * 64 + lane);
+            else
+                r.s[u] = ld_stream_u16((const uint16_t *)st + (int64_t)j * 64 + lane);
         }
     }
 
@@ -545,24 +582,26 @@ struct Engine {
     // whole workgroup calls it together (it contains barriers when staging).
     // Returns the per-lane partial sums (before the KS and L reductions).
     static __device__ __forceinline__ void pass(const Geom &g, const void *x, const Slots &sl, int tile, bool &staged,
-                                uint4 *xs, float *corr, float acc[M])
+                                                uint4 *xs, float *corr, float acc[M])
     {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int KS = g.KS, kpart = wave & (KS - 1);
         const int slot = lane & (g.L - 1);
         const bool active = tile < g.tiles;
-        const uint8_t *ct = g.w + (int64_t)tile * g.ctb;
-        const uint8_t *st = g.w + g.soff + (int64_t)tile * g.stb;
+        // inactive waves load (and ignore) tile 0, step 0, so that loads stay unconditional
+        const int tl = active ? tile : 0;
+        const uint8_t *ct = g.w + (int64_t)tl * g.ctb;
+        const uint8_t *st = g.w + g.soff + (int64_t)tl * g.stb;
 #pragma unroll
         for (int t = 0; t < M; ++t) acc[t] = 0.0f;
         for (int w = 0; w < g.nwin; ++w) {
             const int j0 = w * g.SW;
             const int j1 = min(g.S, j0 + g.SW);
             const int jf = j0 + kpart;      // SW is a multiple of KS
-            int nsteps = (active && jf < j1) ? (j1 - jf + KS - 1) / KS : 0;
+            const int nsteps = (active && jf < j1) ? (j1 - jf + KS - 1) / KS : 0;
+            const int jlast = nsteps > 0 ? jf + (nsteps - 1) * KS : 0;
             Regs ra, rb;
-            int ca = min(nsteps, U);
-            if (ca > 0) load(g, ct, st, lane, jf, ca, KS, ra);
+            load(g, ct, st, lane, nsteps > 0 ? jf : 0, max(1, min(nsteps, U)), KS, ra);
             if (g.nwin > 1 || !staged) {
                 __syncthreads();
                 XStage<XBF16, DOT>::template run<M, FMT>(g, x, sl, w, xs, corr);
@@ -572,16 +611,16 @@ struct Engine {
             const int b0 = j0 * g.L;
             int done = 0;
             while (done < nsteps) {
-                const int jA = jf + done * KS;
                 const int cA = min(nsteps - done, U);
-                const int cB = min(nsteps - done - cA, U);
-                if (cB > 0) load(g, ct, st, lane, jA + cA * KS, cB, KS, rb);
-                compute(g, ra, cA, jA, KS, slot, b0, xs, corr, acc);
+                const int rB = nsteps - done - cA;
+                load(g, ct, st, lane, rB > 0 ? jf + (done + cA) * KS : jlast, rB > 0 ? min(rB, U) : 1, KS, rb);
+                compute(g, ra, cA, jf + done * KS, KS, slot, b0, xs, corr, acc);
                 done += cA;
-                if (cB <= 0) break;
-                const int cC = min(nsteps - done - cB, U);
-                if (cC > 0) load(g, ct, st, lane, jA + (cA + cB) * KS, cC, KS, ra);
-                compute(g, rb, cB, jA + cA * KS, KS, slot, b0, xs, corr, acc);
+                if (done >= nsteps) break;
+                const int cB = min(nsteps - done, U);
+                const int rA = nsteps - done - cB;
+                load(g, ct, st, lane, rA > 0 ? jf + (done + cB) * KS : jlast, rA > 0 ? min(rA, U) : 1, KS, ra);
+                compute(g, rb, cB, jf + done * KS, KS, slot, b0, xs, corr, acc);
                 done += cB;
             }
         }

@@ -1,5 +1,5 @@
 // qg_mxfp4.hip -- MXFP4 instantiations of the dense and expert GEMV kernels.
-#include "qg_common.h"
+#include "qg_chain.h"
 
 namespace qg {
 
@@ -14,5 +14,12 @@ hipError_t launch_moe_mxfp4(int xt, int mode, const Plan &p, const MoeArgs &a, i
     if (xt == QG_BF16) return launch_moe_t<QG_MXFP4, true, true>(mode, p, a, maxdistinct, lds, x, y, s);
     return launch_moe_t<QG_MXFP4, false, false>(mode, p, a, maxdistinct, lds, x, y, s);
 }
+
+const void *chain_kernel_mxfp4(int xt, int m)
+{
+    return xt == QG_BF16 ? pick_chain<QG_MXFP4, true, true>(m) : pick_chain<QG_MXFP4, false, false>(m);
+}
+
+int chain_error_mxfp4(bool clear) { return chain_error_read(clear); }
 
 } // namespace qg

@@ -1,5 +1,5 @@
 // qg_q8_0.hip -- Q8_0 instantiations of the dense and expert GEMV kernels.
-#include "qg_common.h"
+#include "qg_chain.h"
 
 namespace qg {
 
@@ -14,5 +14,12 @@ hipError_t launch_moe_q8_0(int xt, int mode, const Plan &p, const MoeArgs &a, in
     if (xt == QG_BF16) return launch_moe_t<QG_Q8_0, true, false>(mode, p, a, maxdistinct, lds, x, y, s);
     return launch_moe_t<QG_Q8_0, false, false>(mode, p, a, maxdistinct, lds, x, y, s);
 }
+
+const void *chain_kernel_q8_0(int xt, int m)
+{
+    return xt == QG_BF16 ? pick_chain<QG_Q8_0, true, false>(m) : pick_chain<QG_Q8_0, false, false>(m);
+}
+
+int chain_error_q8_0(bool clear) { return chain_error_read(clear); }
 
 } // namespace qg

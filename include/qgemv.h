@@ -165,6 +165,48 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
                    const int32_t *topk_ids, const float *topk_w, int64_t m, int64_t top_k,
                    const void *x, int xt, int mode, float *y, void *stream);
 
+/*
+ * A chain of dense products executed in order by one persistent kernel:
+ * product i+1 starts only after product i has completed on the whole device
+ * (its outputs are visible device-wide), as consecutive projections of one
+ * decode step require.  This removes the per-launch cost between products and
+ * keeps the next product's weights streaming while a product drains, the way
+ * Imparo runs a whole decode layer as one persistent dispatch with a grid
+ * barrier in place of each dispatch boundary (Imparo README, "Megakernel
+ * Decode").
+ *
+ * Use: fill `count` links on the host, size a plan with qg_chain_plan_bytes,
+ * build it with qg_chain_plan (host memory; queries the current device), copy
+ * the plan bytes to device memory once, then call qgemv_chain with both
+ * copies as often as needed (the links' pointers are baked into the plan).
+ * All links share fmt, xt and m (1..8).  Each link's x must fit in LDS
+ * (m * k * 4 bytes for Q8_0 or fp32 activations, m * k * 2 otherwise, up to
+ * about 128 KiB), else QG_EUNSUPPORTED.  The kernel uses one workgroup per
+ * compute unit and is launched cooperatively.  Barrier state lives in static
+ * device memory: chains launched concurrently on one device (different
+ * streams) race and must not overlap.  A barrier that waits too long ends its
+ * wait and records a timeout, so the kernel always finishes; qg_chain_error
+ * reports it.
+ */
+typedef struct {
+    const void *w_packed;   /* device, packed (fmt, n, k) */
+    const void *x;          /* device, [m][k] */
+    float *y;               /* device, [m][n], overwritten */
+    int64_t n, k;
+} qg_chain_link_t;
+
+/* Bytes of a plan for `count` links, or -1. */
+int64_t qg_chain_plan_bytes(int64_t count);
+/* Builds the plan in host memory (`plan`, qg_chain_plan_bytes bytes). */
+int qg_chain_plan(int fmt, int xt, int64_t m, const qg_chain_link_t *links, int64_t count, void *plan);
+/* Launches the chain.  plan_host: the built plan; plan_device: a 16-byte
+ * aligned device copy of the same bytes. */
+int qgemv_chain(const void *plan_host, const void *plan_device, void *stream);
+/* Diagnostic: synchronises the device; returns 1 if any chain barrier timed
+ * out since the previous call (and clears the record), 0 if none, -1 on a
+ * HIP error. */
+int qg_chain_error(void);
+
 #ifdef __cplusplus
 }
 #endif

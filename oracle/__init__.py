@@ -45,6 +45,7 @@ def lib():
         L = ctypes.CDLL(_LIB)
         i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
         for name, rt, args in [
+            ("orc_threads", ctypes.c_int, []),
             ("orc_fp16", ctypes.c_double, [ctypes.c_uint16]),
             ("orc_bf16", ctypes.c_double, [ctypes.c_uint16]),
             ("orc_e8m0", ctypes.c_double, [ctypes.c_uint8]),
@@ -63,6 +64,11 @@ def lib():
 
 def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads():
+    """OpenMP threads the oracle's parallel loops use."""
+    return lib().orc_threads()
 
 
 def fp16(h):

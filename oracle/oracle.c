@@ -30,7 +30,21 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 enum { ORC_Q8_0 = 0, ORC_Q4_0 = 1, ORC_MXFP4 = 2 };
+
+/* Threads an OpenMP region of the oracle uses (1 without OpenMP). */
+int orc_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 enum { ORC_X_F32 = 0, ORC_X_BF16 = 1 };
 enum { ORC_MOE_GATE_UP = 0, ORC_MOE_DOWN = 1 };
 

@@ -72,7 +72,7 @@ def _fp16_bits_uniform(rng, shape, lo, hi):
 
 def q8_0_blocks(n, k, rng_codes, rng_scales, code_lo=-127, code_hi=127, d_lo=1e-3, d_hi=1e-2):
     nb = k // QK
-    codes = rng_codes.integers(code_lo, code_hi + 1, size=(n, nb, QK), dtype=np.int16).astype(np.int8)
+    codes = rng_codes.integers(code_lo, code_hi + 1, size=(n, nb, QK), dtype=np.int8)
     return encode_q8_0(codes, _fp16_bits_uniform(rng_scales, (n, nb), d_lo, d_hi))
 
 
