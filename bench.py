@@ -7,9 +7,9 @@ weights (4.27 GB, all resident in HBM), bf16 activations, fp32 outputs.
 Inputs are seeded and synthetic with the workload's shapes and distributions.
 
 Printed: one JSON line with the achieved GB/s of the whole step (algorithmic
-bytes / wall time per step), the equivalent decode tokens/s, a roofline object
-for the GEMV kernel (algorithmic bytes per launch / mean launch duration from
-HIP events around each launch) and the fp64 CPU oracle timed on a bounded
+bytes / wall time per step, HIP events on the launch stream), the equivalent
+decode tokens/s, a roofline object for the GEMV kernel (algorithmic bytes per
+launch / mean launch duration) and the fp64 CPU oracle timed on a bounded
 sample of the same workload.
 """
 import argparse
@@ -43,11 +43,162 @@ def parse():
                          "between products); graph: the 145 launches replayed from one captured HIP graph; "
                          "eager: the 145 launches issued one by one")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--no-events", action="store_true", help="skip the per-launch event pass")
+    ap.add_argument("--no-events", action="store_true", help="skip the roofline / per-shape timing pass")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--workload", choices=["c2", "c0", "c1", "c3", "c4"], default="c2",
+                    help="c2: the full Q8_0 decode sweep (the headline line); c0/c1/c3/c4: the other workloads, "
+                         "each timed over >= 1 GiB of distinct weight copies so the device-side cache cannot serve "
+                         "repeated reads")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
+
+
+def graph_time(torch, fn, reps):
+    """Capture fn's launches in one HIP graph; return microseconds per replay."""
+    fn()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def copies_for(nbytes):
+    """Distinct weight copies so that one pass touches at least 1 GiB."""
+    return max(2, -(-(1 << 30) // nbytes))
+
+
+def run_other(args):
+    """Per-launch throughput of the other workloads (one JSON line per case)."""
+    import torch
+    import block_quantized_weight_amd as q
+
+    if not os.path.exists(q.LIB_PATH):
+        from block_quantized_weight_amd import build as b
+        b.build()
+    q.lib()
+    dev = torch.device("cuda:0")
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def packed_copies(fmt, canon, n, k, reps):
+        pb = q.packed_bytes(fmt, n, k)
+        buf = torch.empty(reps * pb, dtype=torch.uint8, device=dev)
+        c = torch.from_numpy(canon.reshape(-1)).to(dev)
+        for r in range(reps):
+            q.pack(fmt, c, n, k, out=buf[r * pb:(r + 1) * pb])
+        return [buf[r * pb:(r + 1) * pb] for r in range(reps)]
+
+    def emit(name, gbs, us, extra):
+        line = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "ms_per_step": round(us * 1e-3, 5), "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+                "config": {"workload": name}, "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+        line.update(extra)
+        print(json.dumps(line), flush=True)
+
+    def dense_case(cfg, mats, xt, ms, label):
+        """mats: [(name, n, k, matrix index)]; times each matrix and the whole set."""
+        fmt = wl.CONFIGS[cfg]["fmt"]
+        wsz = sum(q.packed_bytes(fmt, n, k) for _, n, k, _ in mats)
+        reps = copies_for(wsz)
+        ws = {}
+        for name, n, k, j in mats:
+            canon = wl.blocks_for(fmt, n, k, config=cfg, matrix=j)
+            ws[name] = packed_copies(fmt, canon, n, k, reps)
+        for m in ms:
+            xs, ys, per = {}, {}, {}
+            for name, n, k, j in mats:
+                rng = wl.rng_for(cfg, j, "x")
+                if xt == "f32":
+                    xs[name] = torch.from_numpy(wl.x_f32((m, k), rng)).to(dev)
+                else:
+                    xs[name] = bf16_dev(wl.x_bf16_bits((m, k), rng))
+                ys[name] = torch.empty((m, n), dtype=torch.float32, device=dev)
+            xb = 4 if xt == "f32" else 2
+            set_bytes = 0
+            for name, n, k, j in mats:
+                b = n * (k // 32) * wl.BLOCK_BYTES[fmt] + m * k * xb + m * n * 4
+                set_bytes += b
+
+                def one(name=name, n=n, k=k):
+                    for r in range(reps):
+                        q.qgemv(fmt, ws[name][r], n, k, xs[name], y=ys[name])
+                us = graph_time(torch, one, max(2, args.steps // 3)) / reps
+                per[name] = {"n": n, "k": k, "bytes": b, "us": round(us, 3), "gbs": round(b / us / 1e3, 1)}
+
+            def whole():
+                for r in range(reps):
+                    for name, n, k, j in mats:
+                        q.qgemv(fmt, ws[name][r], n, k, xs[name], y=ys[name])
+            us = graph_time(torch, whole, max(2, args.steps // 3)) / reps
+            gbs = set_bytes / us / 1e3
+            emit(f"{label} m={m}", gbs, us, {"per_matrix": per, "bytes_per_set": set_bytes,
+                                              "tokens_per_s": round(m * 1e6 / us, 1), "weight_copies": reps})
+
+    if args.workload == "c0":
+        dense_case(0, [("w", 2048, 2048, 0)], "f32", [1], "q8_0 2048x2048, x fp32")
+    elif args.workload == "c1":
+        dense_case(1, [("gate_up", 19456, 2560, 0), ("down", 2560, 9728, 1)], "bf16", [1],
+                   "q4_0 qwen3-4b-like layer: gate_up 19456x2560 + down 2560x9728, x bf16")
+    elif args.workload == "c3":
+        dense_case(3, [("qkv", 6144, 4096, 0), ("gate_up", 24576, 4096, 1), ("down", 4096, 12288, 2)], "bf16",
+                   [2, 4, 8], "q4_0 co-batch, 8b-like: qkv 6144x4096 + gate_up 24576x4096 + down 4096x12288")
+    elif args.workload == "c4":
+        c = wl.CONFIGS[4]
+        fmt, E, top_k = q.MXFP4, c["n_experts"], c["top_k"]
+        (gn, gk), (dn, dk) = (3584, 2048), (2048, 1792)
+        gpb, dpb = q.packed_bytes(fmt, gn, gk), q.packed_bytes(fmt, dn, dk)
+        reps = copies_for(E * (gpb + dpb))
+        ge = torch.empty(reps * E * gpb, dtype=torch.uint8, device=dev)
+        de = torch.empty(reps * E * dpb, dtype=torch.uint8, device=dev)
+        for e in range(E):
+            gc = torch.from_numpy(wl.blocks_for(fmt, gn, gk, config=4, matrix=2 * e).reshape(-1)).to(dev)
+            dc = torch.from_numpy(wl.blocks_for(fmt, dn, dk, config=4, matrix=2 * e + 1).reshape(-1)).to(dev)
+            for r in range(reps):
+                q.pack(fmt, gc, gn, gk, out=ge[(r * E + e) * gpb:(r * E + e + 1) * gpb])
+                q.pack(fmt, dc, dn, dk, out=de[(r * E + e) * dpb:(r * E + e + 1) * dpb])
+        for m in (1, 4):
+            _, ids, g = wl.router_topk(m, E, top_k, wl.rng_for(4, m, "router"))
+            distinct = len(set(ids.reshape(-1).tolist()))
+            tid, tw = torch.from_numpy(ids).to(dev), torch.from_numpy(g).to(dev)
+            x = bf16_dev(wl.x_bf16_bits((m, gk), wl.rng_for(4, m, "x")))
+            h = bf16_dev(wl.x_bf16_bits((m, top_k, dk), wl.rng_for(4, m, "h")))
+            yg = torch.empty((m, top_k, gn), dtype=torch.float32, device=dev)
+            yd = torch.empty((m, dn), dtype=torch.float32, device=dev)
+            gbytes = distinct * gn * (gk // 32) * 17 + m * gk * 2 + m * top_k * gn * 4 + m * top_k * 8
+            dbytes = distinct * dn * (dk // 32) * 17 + m * top_k * dk * 2 + m * dn * 4 + m * top_k * 8
+            per = {}
+
+            def gate(r):
+                q.moe_qgemv_topk(fmt, ge[r * E * gpb:(r + 1) * E * gpb], E, gn, gk, tid, tw, x, q.MOE_GATE_UP, y=yg)
+
+            def down(r):
+                q.moe_qgemv_topk(fmt, de[r * E * dpb:(r + 1) * E * dpb], E, dn, dk, tid, tw, h, q.MOE_DOWN_COMBINE,
+                                 y=yd)
+            for nm, f, b in (("gate_up", gate, gbytes), ("down_combine", down, dbytes)):
+                us = graph_time(torch, lambda f=f: [f(r) for r in range(reps)], max(2, args.steps // 3)) / reps
+                per[nm] = {"bytes": b, "us": round(us, 3), "gbs": round(b / us / 1e3, 1)}
+            us = graph_time(torch, lambda: [(gate(r), down(r)) for r in range(reps)], max(2, args.steps // 3)) / reps
+            emit(f"mxfp4 moe 32 experts top-4: gate_up 3584x2048 + down 2048x1792 m={m}", (gbytes + dbytes) / us / 1e3,
+                 us, {"per_mode": per, "distinct_experts": distinct, "bytes_per_set": gbytes + dbytes,
+                      "weight_copies": reps})
 
 
 def log(args, *a):
@@ -83,6 +234,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the sharded design is described but not run)", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "c2":
+        run_other(args)
+        return
 
     import torch
     import block_quantized_weight_amd as q
@@ -183,22 +337,16 @@ def main():
     if chain is not None and q.chain_error() != 0:
         raise RuntimeError("a chain barrier timed out: the timed run is invalid")
 
-    # ---- per-launch durations (HIP events around every launch, eager, same stream)
+    # ---- roofline of the GEMV kernel.  Every launch of the step is the same
+    # kernel (Q8_0, bf16 x, M=1); its mean launch duration is the graph step time
+    # over the 145 launches (the rocprofv3 kernel-trace average agrees to within
+    # the ~0.2 us gaps between graph nodes).  Per-shape durations come from one
+    # graph of the 36 distinct matrices of each shape (144 for the LM head, which
+    # is timed alone).
     roof = None
     per_shape = {}
     if not args.no_events:
-        reps = 3
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in shapes]
-        durs = np.zeros((reps, len(shapes)))
-        for r in range(reps):
-            for i, (_, _, n, k) in enumerate(shapes):
-                ev[i][0].record(stream)
-                q.qgemv(fmt, wviews[i], n, k, xs[i], y=ys[i])
-                ev[i][1].record(stream)
-            torch.cuda.synchronize()
-            for i in range(len(shapes)):
-                durs[r, i] = ev[i][0].elapsed_time(ev[i][1]) * 1e-3
-        mean_dur = float(durs.mean())
+        mean_dur = ms_step * 1e-3 / len(shapes)
         mean_bytes = step_bytes / len(shapes)
         achieved = mean_bytes / mean_dur / 1e9
         traffic = recorded_traffic()
@@ -207,15 +355,19 @@ def main():
                 "traffic": None if traffic is None else round(traffic),
                 "kernel": "qg::k_dense<Q8_0, bf16 x, M=1>",
                 "bytes_per_launch": round(mean_bytes), "mean_launch_us": round(mean_dur * 1e6, 3)}
+        groups = {}
         for i, (_, name, n, k) in enumerate(shapes):
-            key = name.split(".")[-1]
-            d = per_shape.setdefault(key, {"n": n, "k": k, "bytes": alg[i], "us": []})
-            d["us"].extend(list(durs[:, i] * 1e6))
-        for key, d in per_shape.items():
-            us = float(np.mean(d.pop("us")))
-            d["us"] = round(us, 3)
-            d["gbs"] = round(d["bytes"] / (us * 1e-6) / 1e9, 1)
-        log(args, f"events: mean launch {mean_dur * 1e6:.2f} us, {achieved:.1f} GB/s per launch; {per_shape}")
+            groups.setdefault(name.split(".")[-1], []).append(i)
+        for key, idx in groups.items():
+            def launches(idx=idx):
+                for i in idx:
+                    _, _, n, k = shapes[i]
+                    q.qgemv(fmt, wviews[i], n, k, xs[i], y=ys[i])
+            us = graph_time(torch, launches, 5) / len(idx)
+            _, _, n, k = shapes[idx[0]]
+            per_shape[key] = {"n": n, "k": k, "bytes": alg[idx[0]], "us": round(us, 3),
+                              "gbs": round(alg[idx[0]] / us / 1e3, 1)}
+        log(args, f"roofline {roof}; per shape {per_shape}")
 
     if args.calib_copy_mib:
         nb = args.calib_copy_mib << 20
@@ -230,8 +382,8 @@ def main():
     cpu = None
     if not args.no_cpu:
         import oracle
-        lm_rows = np.arange(0, 151936, 37)[:4096]
-        sample = [(shapes[i], None) for i in range(4)] + [(shapes[144], lm_rows)]
+        lm_rows = np.arange(0, 151936, 9)
+        sample = [(shapes[i], None) for i in range(40)] + [(shapes[144], lm_rows)]
         t_cpu, bytes_cpu, worst = 0.0, 0, 0.0
         for (j, name, n, k), rows in sample:
             canon = wl.blocks_for(fmt, n, k, config=config, matrix=j)
@@ -247,7 +399,7 @@ def main():
             worst = max(worst, oracle.max_rel_err(yg, yref, l1))
         cpu = {"value": round(bytes_cpu / t_cpu / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
                "kind": "oracle",
-               "sample": "layer-0 qkv, o, gate_up, down in full + 4096 LM-head rows (every 37th); "
+               "sample": "layers 0-9 (qkv, o, gate_up, down) in full + every 9th LM-head row; "
                          f"{bytes_cpu / 1e6:.1f} MB of the sweep's algorithmic bytes, {t_cpu:.1f} s wall",
                "gpu_vs_oracle_max_rel_err": worst}
         log(args, f"cpu oracle: {cpu}")

@@ -692,34 +692,46 @@ __global__ __launch_bounds__(TPB) void k_dense(Geom g, const void *__restrict__ 
 
 // ------------------------------------------------------------------- MoE
 // Distinct selected experts, ascending, computed by every workgroup from the
-// device-resident ids (no host round trip).  list[i] for i < *count.
-__device__ inline void distinct_experts(const int32_t *__restrict__ ids, int nslots, int n_experts, int *list, int *count)
+// device-resident ids (no host round trip).  s_ids receives the ids,
+// list[i] for i < *count the distinct valid ones.  nslots <= 64.
+__device__ inline void distinct_experts(const int32_t *__restrict__ ids, int nslots, int n_experts, int *s_ids,
+                                        int *list, int *count)
 {
-    // nslots <= 64 <= TPB: one thread per slot.
-    __shared__ int s_ids[64];
     __shared__ int s_first[64];
     const int t = threadIdx.x;
     if (t < nslots) s_ids[t] = ids[t];
     __syncthreads();
     if (t < nslots) {
-        int e = s_ids[t];
-        bool ok = e >= 0 && e < n_experts;
-        bool first = ok;
+        const int e = s_ids[t];
+        bool first = e >= 0 && e < n_experts;
         for (int q = 0; q < t && first; ++q) first = s_ids[q] != e;
         s_first[t] = first ? 1 : 0;
     }
     __syncthreads();
     if (t < nslots && s_first[t]) {
-        int e = s_ids[t], rank = 0;
+        const int e = s_ids[t];
+        int rank = 0;
         for (int q = 0; q < nslots; ++q) rank += (s_first[q] && s_ids[q] < e) ? 1 : 0;
         list[rank] = e;
     }
-    if (t == 0) {
-        int c = 0;
-        for (int q = 0; q < nslots; ++q) c += s_first[q];
-        *count = c;
+    if (t < 64) {
+        const uint64_t mask = __ballot(t < nslots && s_first[t]);
+        if (t == 0) *count = __popcll(mask);
     }
     __syncthreads();
+}
+
+// Slots (t * top_k + j) that chose expert e, in increasing order, by one
+// wave with a ballot over the ids in LDS; the caller synchronises.
+__device__ __forceinline__ void expert_slots(int e, int nslots, const int *s_ids, int *s_slots, int *s_nsl)
+{
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const bool match = lane < nslots && s_ids[lane] == e;
+        const uint64_t mask = __ballot(match);
+        if (match) s_slots[__popcll(mask & ((1ull << lane) - 1))] = lane;
+        if (lane == 0) *s_nsl = __popcll(mask);
+    }
 }
 
 struct MoeArgs {
@@ -780,21 +792,17 @@ template <int FMT, bool XBF16, bool DOT>
 __global__ __launch_bounds__(TPB) void k_moe_gate_up(Geom g, MoeArgs a, const void *__restrict__ x, float *__restrict__ y)
 {
     extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int s_ids[64];
     __shared__ int s_list[64];
     __shared__ int s_count;
     __shared__ int s_slots[64];
     __shared__ int s_nsl;
     __shared__ int32_t s_xrow[QG_MAX_M], s_yrow[QG_MAX_M];
     const int nslots = a.m * a.top_k;
-    distinct_experts(a.ids, nslots, a.n_experts, s_list, &s_count);
+    distinct_experts(a.ids, nslots, a.n_experts, s_ids, s_list, &s_count);
     if ((int)blockIdx.y >= s_count) return;      // uniform over the workgroup
     const int e = s_list[blockIdx.y];
-    if (threadIdx.x == 0) {
-        int c = 0;
-        for (int s = 0; s < nslots; ++s)
-            if (a.ids[s] == e) s_slots[c++] = s;
-        s_nsl = c;
-    }
+    expert_slots(e, nslots, s_ids, s_slots, &s_nsl);
     __syncthreads();
     const int nsl = s_nsl;
     constexpr int QPB = DOT ? 4 : 8;
@@ -826,13 +834,14 @@ template <int FMT, bool XBF16, bool DOT>
 __global__ __launch_bounds__(TPB) void k_moe_down(Geom g, MoeArgs a, const void *__restrict__ x, float *__restrict__ y)
 {
     extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int s_ids[64];
     __shared__ int s_list[64];
     __shared__ int s_count;
     __shared__ int s_slots[64];
     __shared__ int s_nsl;
     __shared__ int32_t s_xrow[QG_MAX_M], s_yrow[QG_MAX_M];
     const int nslots = a.m * a.top_k;
-    distinct_experts(a.ids, nslots, a.n_experts, s_list, &s_count);
+    distinct_experts(a.ids, nslots, a.n_experts, s_ids, s_list, &s_count);
     constexpr int QPB = DOT ? 4 : 8;
     uint4 *xs = (uint4 *)smem;
     float *corr = (float *)(smem + (size_t)QG_MAX_M * QPB * g.wblk * 16);
@@ -844,12 +853,7 @@ __global__ __launch_bounds__(TPB) void k_moe_down(Geom g, MoeArgs a, const void 
         for (int ei = 0; ei < s_count; ++ei) {
             const int e = s_list[ei];
             __syncthreads();
-            if (threadIdx.x == 0) {
-                int c = 0;
-                for (int s = 0; s < nslots; ++s)
-                    if (a.ids[s] == e) s_slots[c++] = s;
-                s_nsl = c;
-            }
+            expert_slots(e, nslots, s_ids, s_slots, &s_nsl);
             __syncthreads();
             const int nsl = s_nsl;
             Geom ge = g;
@@ -883,7 +887,7 @@ __global__ __launch_bounds__(TPB) void k_moe_down(Geom g, MoeArgs a, const void 
                 float s = 0.0f;
                 for (int j = 0; j < a.top_k; ++j) {
                     const int sidx = t * a.top_k + j;
-                    const int e = a.ids[sidx];
+                    const int e = s_ids[sidx];
                     if (e >= 0 && e < a.n_experts) s = __builtin_fmaf(a.gw[sidx], part[sidx * rows_pg + rl], s);
                 }
                 y[(int64_t)t * g.n + row] = s;
