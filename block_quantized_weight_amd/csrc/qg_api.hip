@@ -100,8 +100,7 @@ Plan make_plan(const Layout &lo, int M, bool dot, int maxslots_lds)
     g.stb = lo.stb;
     g.soff = lo.soff;
     // activation window: as many steps as fit XBUDGET (at least one)
-    const int QPB = dot ? 4 : 8;
-    const size_t per_block = (size_t)maxslots_lds * QPB * 16 + (lo.fmt == QG_Q4_0 ? (size_t)maxslots_lds * 4 : 0);
+    const size_t per_block = (size_t)maxslots_lds * x_quads(lo.fmt, dot) * 16 + (x_aux(lo.fmt) ? (size_t)maxslots_lds * 4 : 0);
     int64_t sw_max = (int64_t)(XBUDGET / per_block) / lo.L;
     if (sw_max < 1) sw_max = 1;
     // split-K factor: more waves per tile when tiles are few; never more than

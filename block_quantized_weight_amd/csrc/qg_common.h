@@ -58,6 +58,12 @@ struct Layout {
     int64_t ctb, stb, soff, total;
 };
 
+// Staged form of one block of 32 activations in LDS: x_quads() 16-byte quads
+// (fp32, or bf16 pairs for the bf16 dot) plus, for Q4_0, one float per block
+// (the offset correction).
+__host__ __device__ constexpr int x_quads(int fmt, bool dot) { return dot ? 4 : 8; }
+__host__ __device__ constexpr bool x_aux(int fmt) { return fmt == QG_Q4_0; }
+
 inline int block_bytes(int fmt) { return fmt == QG_Q8_0 ? 34 : fmt == QG_Q4_0 ? 18 : 17; }
 
 inline bool valid_fmt(int fmt) { return fmt == QG_Q8_0 || fmt == QG_Q4_0 || fmt == QG_MXFP4; }
@@ -331,6 +337,42 @@ __device__ __forceinline__ f32x2_t fp4_pair_f32(uint32_t w)
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, PSEL);
 }
 
+// Staged form of one block of 32 activations (raw: 4 quads of bf16 or 8
+// quads of fp32, in element order): q[0 .. x_quads) and the per-block float.
+template <int FMT, bool XBF16, bool DOT>
+__device__ __forceinline__ float stage_block(const uint4 (&raw)[8], uint4 (&q)[8])
+{
+    const uint32_t *rw = (const uint32_t *)raw;
+    float sum = 0.0f;
+    if (XBF16) {
+        if (DOT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q[i] = raw[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t a0 = rw[2 * i], a1 = rw[2 * i + 1];
+                q[i] = make_uint4(a0 << 16, a0 & 0xFFFF0000u, a1 << 16, a1 & 0xFFFF0000u);
+            }
+        }
+        if (FMT == QG_Q4_0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                sum += __builtin_bit_cast(float, rw[i] << 16);
+                sum += __builtin_bit_cast(float, rw[i] & 0xFFFF0000u);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = raw[i];
+        if (FMT == QG_Q4_0) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) sum += __builtin_bit_cast(float, rw[i]);
+        }
+    }
+    return FMT == QG_Q4_0 ? (DOT ? 136.0f : 8.0f) * sum : 0.0f;
+}
+
 // ------------------------------------------------------------- GEMV engine
 // A "pass" of one workgroup: WAVES/KS tiles, each covered by KS waves that
 // split the tile's steps (step j goes to wave j % KS).  Activations for up to
@@ -353,58 +395,37 @@ struct Slots {
 
 template <bool XBF16, bool DOT>
 struct XStage {
-    // Stages window w of M slots: xs[(t*QPB + q)*wblk + bl] (16 B quads), and
-    // corr[t*wblk + bl] = CORR * sum of the block's 32 activations (fp32, index order).
+    // Stages window w of M slots: xs[(t*QPB + q)*wblk + bl] (16 B quads) and,
+    // for Q4_0, aux[t*wblk + bl] (the per-block correction of stage_block).
     template <int M, int FMT>
-    static __device__ __forceinline__ void run(const Geom &g, const void *x, const Slots &sl, int w, uint4 *xs, float *corr)
+    static __device__ __forceinline__ void run(const Geom &g, const void *x, const Slots &sl, int w, uint4 *xs, float *aux)
     {
-        constexpr int QPB = DOT ? 4 : 8;
+        constexpr int QPB = x_quads(FMT, DOT);
         const int b0 = w * g.SW * g.L;
         const int total = M * g.wblk;
         for (int idx = threadIdx.x; idx < total; idx += (int)blockDim.x) {
             const int t = idx / g.wblk, bl = idx - t * g.wblk, b = b0 + bl;
             const int64_t xo = (int64_t)sl.xrow[t] * g.k;
-            uint4 q[8];
-            float sum = 0.0f;
+            uint4 raw[8], q[8];
+            float a = 0.0f;
             if (b < g.nb) {
                 if (XBF16) {
                     const uint4 *src = (const uint4 *)((const uint16_t *)x + xo + (int64_t)b * QK);
-                    uint4 r[4] = {ld_global16(src), ld_global16(src + 1), ld_global16(src + 2), ld_global16(src + 3)};
-                    const uint32_t *rw = (const uint32_t *)r;
-                    if (DOT) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) q[i] = r[i];
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            uint32_t a0 = rw[2 * i], a1 = rw[2 * i + 1];
-                            q[i] = make_uint4(a0 << 16, a0 & 0xFFFF0000u, a1 << 16, a1 & 0xFFFF0000u);
-                        }
-                    }
-                    if (FMT != QG_Q8_0) {
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            sum += __builtin_bit_cast(float, rw[i] << 16);
-                            sum += __builtin_bit_cast(float, rw[i] & 0xFFFF0000u);
-                        }
-                    }
+                    for (int i = 0; i < 4; ++i) raw[i] = ld_global16(src + i);
                 } else {
                     const uint4 *src = (const uint4 *)((const float *)x + xo + (int64_t)b * QK);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) q[i] = ld_global16(src + i);
-                    if (FMT != QG_Q8_0) {
-                        const float *f = (const float *)q;
-#pragma unroll
-                        for (int i = 0; i < 32; ++i) sum += f[i];
-                    }
+                    for (int i = 0; i < 8; ++i) raw[i] = ld_global16(src + i);
                 }
+                a = stage_block<FMT, XBF16, DOT>(raw, q);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) q[i] = make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < QPB; ++i) xs[(t * QPB + i) * g.wblk + bl] = q[i];
-            if (FMT == QG_Q4_0) corr[t * g.wblk + bl] = (DOT ? 136.0f : 8.0f) * sum;
+            if (x_aux(FMT)) aux[t * g.wblk + bl] = a;
         }
     }
 };
@@ -416,7 +437,7 @@ template <int FMT, bool XBF16, bool DOT, int M, int UB = Batch<FMT, DOT>::U>
 struct Engine {
     static constexpr int P = FMT == QG_Q8_0 ? 2 : 1;
     static constexpr int U = UB;
-    static constexpr int QPB = DOT ? 4 : 8;
+    static constexpr int QPB = x_quads(FMT, DOT);
 
     struct Regs {
         uint4 c[U][P];
@@ -654,9 +675,8 @@ __device__ __forceinline__ void reduce_partials(const Geom &g, float *red, float
 
 inline __host__ __device__ size_t lds_bytes(int M, bool dot, int fmt, int wblk)
 {
-    const int QPB = dot ? 4 : 8;
-    size_t b = (size_t)M * QPB * wblk * 16;
-    if (fmt == QG_Q4_0) b += (size_t)M * wblk * 4;
+    size_t b = (size_t)M * x_quads(fmt, dot) * wblk * 16;
+    if (x_aux(fmt)) b += (size_t)M * wblk * 4;
     b += (size_t)WAVES * M * 64 * 4;
     return b;
 }
@@ -665,10 +685,10 @@ template <int FMT, bool XBF16, bool DOT, int M>
 __global__ __launch_bounds__(TPB) void k_dense(Geom g, const void *__restrict__ x, float *__restrict__ y)
 {
     extern __shared__ __align__(16) uint8_t smem[];
-    constexpr int QPB = DOT ? 4 : 8;
+    constexpr int QPB = x_quads(FMT, DOT);
     uint4 *xs = (uint4 *)smem;
     float *corr = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
-    float *red = corr + (FMT == QG_Q4_0 ? M * g.wblk : 0);
+    float *red = corr + (x_aux(FMT) ? M * g.wblk : 0);
     __shared__ int32_t s_rows[QG_MAX_M];
     if (threadIdx.x < QG_MAX_M) s_rows[threadIdx.x] = threadIdx.x;   // read only after the staging barrier
     Slots sl{s_rows, s_rows};
@@ -805,10 +825,10 @@ __global__ __launch_bounds__(TPB) void k_moe_gate_up(Geom g, MoeArgs a, const vo
     expert_slots(e, nslots, s_ids, s_slots, &s_nsl);
     __syncthreads();
     const int nsl = s_nsl;
-    constexpr int QPB = DOT ? 4 : 8;
+    constexpr int QPB = x_quads(FMT, DOT);
     uint4 *xs = (uint4 *)smem;
     float *corr = (float *)(smem + (size_t)QG_MAX_M * QPB * g.wblk * 16);
-    float *red = corr + (FMT == QG_Q4_0 ? QG_MAX_M * g.wblk : 0);
+    float *red = corr + (x_aux(FMT) ? QG_MAX_M * g.wblk : 0);
     Geom ge = g;
     ge.w = a.experts + (int64_t)e * a.expert_bytes;
     for (int c0 = 0; c0 < nsl; c0 += QG_MAX_M) {
@@ -842,10 +862,10 @@ __global__ __launch_bounds__(TPB) void k_moe_down(Geom g, MoeArgs a, const void 
     __shared__ int32_t s_xrow[QG_MAX_M], s_yrow[QG_MAX_M];
     const int nslots = a.m * a.top_k;
     distinct_experts(a.ids, nslots, a.n_experts, s_ids, s_list, &s_count);
-    constexpr int QPB = DOT ? 4 : 8;
+    constexpr int QPB = x_quads(FMT, DOT);
     uint4 *xs = (uint4 *)smem;
     float *corr = (float *)(smem + (size_t)QG_MAX_M * QPB * g.wblk * 16);
-    float *red = corr + (FMT == QG_Q4_0 ? QG_MAX_M * g.wblk : 0);
+    float *red = corr + (x_aux(FMT) ? QG_MAX_M * g.wblk : 0);
     float *part = red + WAVES * QG_MAX_M * 64;           // [nslots][tpi*R]
     const int rows_pg = g.tpi * g.R;
     for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {

@@ -227,6 +227,37 @@ def test_config3_cobatch(dev, m, name, n, k, j):
     assert err <= TOL, err
 
 
+# ---------------------------------------------------- activation range
+def _range_case(dev, fmt, x32, xt, n, k, config=68):
+    canon = wl.blocks_for(fmt, n, k, config=config, matrix=fmt)
+    x = wl.f32_to_bf16_bits_rne(x32) if xt == oracle.X_BF16 else x32
+    y = run_dense(fmt, canon, n, k, x, xt, dev)
+    ref, l1 = oracle.gemv(fmt, canon, n, k, x, xt)
+    return oracle.max_rel_err(y, ref, l1)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("xt", [oracle.X_F32, oracle.X_BF16])
+@pytest.mark.parametrize("scale", [1e-30, 1e30])
+def test_activation_magnitudes(dev, fmt, xt, scale):
+    """Tiny and huge activations (every product stays a normal fp32 number)."""
+    say(f"x magnitude fmt={fmt} xt={xt} scale={scale}")
+    x32 = (wl.x_f32((3, 2048), wl.rng_for(68, 1, "x")) * np.float32(scale)).astype(np.float32)
+    err = _range_case(dev, fmt, x32, xt, 257, 2048)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("xt", [oracle.X_F32, oracle.X_BF16])
+def test_mixed_range_activations(dev, fmt, xt):
+    """Twelve decades of magnitude inside every block."""
+    say(f"x mixed range fmt={fmt} xt={xt}")
+    rng = wl.rng_for(68, 2, "x")
+    x32 = (wl.x_f32((4, 4096), rng) * 10.0 ** rng.uniform(-6, 6, size=(4, 4096))).astype(np.float32)
+    err = _range_case(dev, fmt, x32, xt, 129, 4096)
+    assert err <= TOL, err
+
+
 # ------------------------------------------------------------ properties
 def test_deterministic_and_cobatch_invariant(dev):
     fmt, n, k = q.Q4_0, 2560, 9728
