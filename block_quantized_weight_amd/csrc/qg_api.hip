@@ -1,6 +1,7 @@
 // qg_api.hip -- C ABI of libqgemv.so: argument validation, layout, launch
 // plans, the packer kernels and the dequantization test aid.
 #include "qg_chain.h"
+#include "qg_mfma.h"
 
 namespace qg {
 namespace {
@@ -127,6 +128,68 @@ Plan make_plan(const Layout &lo, int M, bool dot, int maxslots_lds)
 
 inline bool uses_dot(int fmt, int xt) { return fmt != QG_Q8_0 && xt == QG_BF16; }
 
+// Co-batches of at least this many bf16 tokens run on the matrix cores
+// (measured crossover on MI355X: the int8 codes' per-weight VALU cost makes
+// Q8_0 gain from two tokens, the 4-bit formats from four).
+inline int mfma_min_m(int fmt) { return fmt == QG_Q8_0 ? 2 : 4; }
+
+// LDS per co-batch workgroup is kept within 80 KiB, so two fit on a CU.
+constexpr int MFMA_WG_LDS = 80 * 1024;
+
+struct MPlan {
+    MGeom g;
+    size_t lds;
+    int grid;
+};
+
+// The matrix-core kernel serves bf16 activations, layouts of 1 to 8 lanes per
+// row, and tiles whose per-lane offsets fit in 32 bits.
+bool mfma_fits(const Layout &lo, int xt, int64_t m)
+{
+    if (xt != QG_BF16 || m < mfma_min_m(lo.fmt) || lo.L > MFMA_MAX_L) return false;
+    const int64_t tpw = lo.L >= 8 ? lo.L / 4 : 1;
+    return lo.ctb * tpw < ((int64_t)1 << 31) && lo.stb * tpw < ((int64_t)1 << 31);
+}
+
+MPlan make_mplan(const Layout &lo, int m)
+{
+    MPlan p{};
+    MGeom &g = p.g;
+    g.n = (int32_t)lo.n;
+    g.k = (int32_t)lo.k;
+    g.nb = (int32_t)lo.nb;
+    g.L = lo.L;
+    g.R = lo.R;
+    g.S = (int32_t)lo.S;
+    g.tiles = (int32_t)lo.tiles;
+    g.ctb = lo.ctb;
+    g.stb = lo.stb;
+    g.soff = lo.soff;
+    g.m = m;
+    const int64_t tpw = lo.L >= 8 ? lo.L / 4 : 1;
+    g.units = (int32_t)((lo.tiles + tpw - 1) / tpw);
+    const size_t per_block = (size_t)m * 64;
+    const int64_t xbudget = (int64_t)MFMA_WG_LDS - (int64_t)mfma_lds_bytes(lo.fmt, m, 0, lo.L);
+    int64_t sw_max = (xbudget / (int64_t)per_block) / lo.L;
+    if (sw_max < 1) sw_max = 1;
+    int KS = 1;
+    if (g.units < 4096) KS = 2;
+    if (g.units < 2048) KS = 4;
+    while (KS > 1 && (lo.S < KS || sw_max < KS)) KS >>= 1;
+    g.KS = KS;
+    g.ksh = ilog2(KS);
+    g.upi = WAVES / KS;
+    g.ngroups = (int32_t)((g.units + g.upi - 1) / g.upi);
+    int64_t sw = sw_max / KS * KS;
+    if (sw >= lo.S) sw = ((lo.S + KS - 1) / KS) * KS;
+    g.SW = (int32_t)sw;
+    g.nwin = (int32_t)((lo.S + sw - 1) / sw);
+    g.wblk = (int32_t)(sw * lo.L);
+    p.lds = mfma_lds_bytes(lo.fmt, m, g.wblk, lo.L);
+    p.grid = g.ngroups > 65535 ? 65535 : g.ngroups;
+    return p;
+}
+
 int launch_status()
 {
     hipError_t e = hipGetLastError();
@@ -142,6 +205,15 @@ int dense(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
     if (m < 1 || m > QG_MAX_M) return QG_EINVAL;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
     const Layout lo = make_layout(fmt, n, k);
+    if (mfma_fits(lo, xt, m)) {
+        MPlan p = make_mplan(lo, (int)m);
+        p.g.w = (const uint8_t *)w;
+        mfma_fn f = fmt == QG_Q8_0 ? mfma_kernel_q8_0(lo.L) : fmt == QG_Q4_0 ? mfma_kernel_q4_0(lo.L) : mfma_kernel_mxfp4(lo.L);
+        void *args[] = {(void *)&p.g, (void *)&x, (void *)&y};
+        if (allow_lds((const void *)f, p.lds) != hipSuccess) return QG_EHIP;
+        hipError_t e = hipLaunchKernel((const void *)f, dim3(p.grid), dim3(TPB), args, p.lds, as_stream(stream));
+        return e == hipSuccess ? launch_status() : QG_EHIP;
+    }
     const bool dot = uses_dot(fmt, xt);
     Plan p = make_plan(lo, (int)m, dot, (int)m);
     p.g.w = (const uint8_t *)w;

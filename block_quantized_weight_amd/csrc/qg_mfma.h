@@ -1,0 +1,331 @@
+#pragma once
+// qg_mfma.h -- co-batch product (several tokens, bf16 activations) on the
+// gfx950 matrix cores.
+//
+// With M tokens the product reuses every decoded weight M times; past a few
+// tokens the per-weight VALU work of the lane-per-block kernel (an unpack plus
+// M dot products, each reading its activations from LDS) becomes the bound.
+// Here one v_mfma_f32_16x16x32_bf16 takes a 32-weight block of 16 rows:
+//   A (16 x 32)  the tokens' activations of that block (A row = token, rows
+//                past M are zero), bf16 exactly as given;
+//   B (32 x 16)  the 16 rows' codes, converted to bf16 in registers (exact:
+//                Q4_0 as 128+q, E2M1 values, int8 codes);
+//   C            for Q4_0, -136 * (sum of the block's activations) per token,
+//                itself one MFMA of A with a constant B of -136 (exact
+//                products, fp32 sums), computed once per block; else zero;
+//   D[t][r]      the block's dot product for token t and row r before the
+//                block scale, which is applied in fp32: acc += d * D.
+// The sum over k inside the instruction is order-free, so any assignment of
+// the 32 k values to operand slots works as long as A and B agree: lane l of
+// both holds 8 consecutive k (octet l/16 of the block), A for token l%16 and
+// B for row l%16; D gives lane l row l%16 and tokens 4*(l/16) .. +3.
+//
+// B needs 8 consecutive k of one row per lane, while the packed layout gives
+// each lane a whole block (16-byte record: row r, block s for lane r*L + s).
+// Weights are loaded exactly as in the lane-per-block kernel (coalesced
+// 16-byte records, nontemporal), then each step's records pass through a
+// small wave-private LDS area from which every lane reads its octets: dword g
+// (4-bit codes) or dwords 2g, 2g+1 (Q8_0) of record r*L + s.  One record of
+// padding after every eight keeps those reads at most two-way bank-conflicted.
+//
+// A "unit" is 16 rows x the whole K: one tile of 16 rows (L = 4), two
+// half-tiles (L = 8, R = 8), or 2 / 4 row groups of a taller tile (L = 2, 1).
+// KS waves of a workgroup split a unit's steps; their partial sums are added
+// in a fixed order through LDS, so results are deterministic.
+#include "qg_common.h"
+
+namespace qg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int MFMA_MAX_L = 8;     // lanes per row served by this kernel
+
+struct MGeom {
+    const uint8_t *w;
+    int32_t n, k, nb, L, R, S, tiles;
+    int64_t ctb, stb, soff;
+    int32_t m;                       // tokens (1 .. 8)
+    int32_t units, KS, ksh, upi, ngroups;
+    int32_t SW, nwin, wblk;
+};
+
+// Compile-time shape of a unit for lanes-per-row LL.
+template <int LL> struct MShape {
+    static constexpr int R = 64 / LL;
+    static constexpr int TPW = LL >= 8 ? LL / 4 : 1;       // tiles per unit
+    static constexpr int RG = LL >= 4 ? 1 : 4 / LL;        // 16-row groups per unit
+    static constexpr int NM = LL >= 4 ? LL : 4;            // MFMAs per step
+    static constexpr int NS = LL;                           // blocks per step
+};
+
+// Per-wave transpose area: one plane of 72 record slots per (tile, part),
+// planes 1168 bytes apart (16 bytes of skew per plane), then the step's
+// scales as fp32 [tile][lane].
+constexpr int MPLANE = 1168;
+inline __host__ __device__ int mfma_wave_bytes(int fmt, int LL)
+{
+    const int tpw = LL >= 8 ? LL / 4 : 1, P = fmt == QG_Q8_0 ? 2 : 1;
+    return tpw * P * MPLANE + tpw * 64 * 4;
+}
+
+inline __host__ __device__ size_t mfma_lds_bytes(int fmt, int m, int wblk, int LL)
+{
+    const int RG = LL >= 4 ? 1 : 4 / LL;
+    size_t b = (size_t)wblk * m * 64;                        // activations: [block][token][octet]
+    b += (size_t)WAVES * RG * 4 * 64 * 4;                    // split-K partials
+    b += (size_t)WAVES * mfma_wave_bytes(fmt, LL);           // transpose areas
+    return b;
+}
+
+template <int FMT, int LL>
+struct MEngine {
+    using Sh = MShape<LL>;
+    static constexpr int P = FMT == QG_Q8_0 ? 2 : 1;        // 16-byte parts per record
+    static constexpr int TPW = Sh::TPW;
+    static constexpr int NM = Sh::NM;
+    static constexpr int U = FMT == QG_Q8_0 ? 2 : 4;        // steps per load batch
+
+    struct Regs {
+        uint4 c[U][TPW][P];
+        uint32_t s[U][TPW];
+    };
+
+    // Issues the loads of cnt (>= 1) steps jfirst, jfirst+KS, ... of the
+    // unit's tiles: always U steps' worth (steps past cnt repeat the last
+    // one), so the vmcnt waits stay exact.  tok[t] is false for a tile past
+    // the end, which then reads the unit's first tile instead (never stored).
+    static __device__ __forceinline__ void load(const MGeom &g, const uint8_t *cb, const uint8_t *sbase, int lane,
+                                                int jfirst, int cnt, int KS, const int (&tofs)[TPW], Regs &r)
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = jfirst + min(u, cnt - 1) * KS;
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                const uint8_t *cp = cb + (int64_t)tofs[tt] * g.ctb + (int64_t)j * (P * 1024) + lane * 16;
+#pragma unroll
+                for (int h = 0; h < P; ++h) r.c[u][tt][h] = ld_stream16(cp + h * 1024);
+                const uint8_t *sp = sbase + (int64_t)tofs[tt] * g.stb;
+                if (FMT == QG_MXFP4)
+                    r.s[u][tt] = ld_stream_u8(sp + (int64_t)j * 64 + lane);
+                else
+                    r.s[u][tt] = ld_stream_u16((const uint16_t *)sp + (int64_t)j * 64 + lane);
+            }
+        }
+    }
+
+    static __device__ __forceinline__ int slot(int sl) { return (sl + (sl >> 3)) * 16; }
+
+    // 8 codes (one octet) -> 8 bf16 values, element order.
+    static __device__ __forceinline__ bf16x8_t unpack(const uint32_t *c)
+    {
+        uint32_t q[4];
+        if (FMT == QG_Q4_0) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) q[kk] = ((c[0] >> (4 * kk)) & 0x000F000Fu) | 0x43004300u;
+        } else if (FMT == QG_MXFP4) {
+            q[0] = __builtin_bit_cast(uint32_t, fp4_pair_bf16<0>(c[0]));
+            q[1] = __builtin_bit_cast(uint32_t, fp4_pair_bf16<1>(c[0]));
+            q[2] = __builtin_bit_cast(uint32_t, fp4_pair_bf16<2>(c[0]));
+            q[3] = __builtin_bit_cast(uint32_t, fp4_pair_bf16<3>(c[0]));
+        } else {
+            // int8 -> fp32 is exact and has at most 8 significant bits, so
+            // its upper half is the exact bf16
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint32_t w = c[kk >> 1];
+                const int b = 2 * (kk & 1);
+                const uint32_t lo = __builtin_bit_cast(uint32_t, i8_at(w, b));
+                const uint32_t hi = __builtin_bit_cast(uint32_t, i8_at(w, b + 1));
+                q[kk] = (lo >> 16) | (hi & 0xFFFF0000u);
+            }
+        }
+        return __builtin_bit_cast(bf16x8_t, make_uint4(q[0], q[1], q[2], q[3]));
+    }
+
+    static __device__ __forceinline__ float scale(uint32_t bits)
+    {
+        return FMT == QG_MXFP4 ? e8m0_to_f32(bits) : f16_bits_to_f32(bits);
+    }
+
+    // The MFMAs of one step (block index jL + s of every row of the unit).
+    // wl: this wave's transpose area.
+    static __device__ __forceinline__ void step(const MGeom &g, const Regs &r, int u, int j, int b0, const uint4 *xs,
+                                                uint8_t *wl, f32x4_t acc[Sh::RG])
+    {
+        const int lane = threadIdx.x & 63, i = lane & 15, oct = lane >> 4;
+        float *wsc = (float *)(wl + TPW * P * MPLANE);
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+#pragma unroll
+            for (int h = 0; h < P; ++h) *(uint4 *)(wl + (tt * P + h) * MPLANE + slot(lane)) = r.c[u][tt][h];
+            wsc[tt * 64 + lane] = scale(r.s[u][tt]);
+        }
+        const int ic = min(i, g.m - 1);
+#pragma unroll
+        for (int s = 0; s < Sh::NS; ++s) {
+            const int bl = j * LL + s - b0;
+            uint4 av = xs[(bl * g.m + ic) * 4 + oct];
+            if (i >= g.m) av = make_uint4(0, 0, 0, 0);
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+            f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (FMT == QG_Q4_0) {
+                const bf16x8_t k136 = __builtin_bit_cast(bf16x8_t, make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, k136, c, 0, 0, 0);    // -136 * sum(x), every row
+            }
+#pragma unroll
+            for (int G = 0; G < Sh::RG; ++G) {
+                const int tt = LL >= 8 ? i / Sh::R : 0;
+                const int rr = LL >= 8 ? i % Sh::R : 16 * G + i;
+                const int sl = rr * LL + s;
+                uint32_t cw[2];
+                if (FMT == QG_Q8_0) {
+                    const uint2 v = *(const uint2 *)(wl + (tt * P + (oct >> 1)) * MPLANE + slot(sl) + 8 * (oct & 1));
+                    cw[0] = v.x;
+                    cw[1] = v.y;
+                } else {
+                    cw[0] = *(const uint32_t *)(wl + tt * MPLANE + slot(sl) + 4 * oct);
+                    cw[1] = 0;
+                }
+                const float sc = wsc[tt * 64 + sl];
+                const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, unpack(cw), c, 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[G][q] = __builtin_fmaf(sc, d[q], acc[G][q]);
+            }
+        }
+    }
+
+    static __device__ __forceinline__ void compute(const MGeom &g, const Regs &r, int cnt, int jfirst, int KS, int b0,
+                                                   const uint4 *xs, uint8_t *wl, f32x4_t acc[Sh::RG])
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (u < cnt) step(g, r, u, jfirst + u * KS, b0, xs, wl, acc);
+    }
+};
+
+// Stages window w of the activations as xs[(bl*m + t)*4 + oct] (bf16 octets).
+__device__ __forceinline__ void mfma_stage(const MGeom &g, const uint16_t *x, int w, uint4 *xs)
+{
+    const int b0 = w * g.SW * g.L;
+    const int total = g.wblk * g.m;
+    for (int idx = threadIdx.x; idx < total; idx += (int)blockDim.x) {
+        const int bl = idx / g.m, t = idx - bl * g.m, b = b0 + bl;
+        uint4 r[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+        if (b < g.nb) {
+            const uint4 *src = (const uint4 *)(x + (int64_t)t * g.k + (int64_t)b * QK);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) r[q] = ld_global16(src + q);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xs[idx * 4 + q] = r[q];
+    }
+}
+
+template <int FMT, int LL>
+__global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restrict__ xv, float *__restrict__ y)
+{
+    using E = MEngine<FMT, LL>;
+    using Sh = MShape<LL>;
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint4 *xs = (uint4 *)smem;
+    float *red = (float *)(smem + (size_t)g.wblk * g.m * 64);
+    const uint16_t *x = (const uint16_t *)xv;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint8_t *wl = (uint8_t *)(red + WAVES * Sh::RG * 4 * 64) + wave * mfma_wave_bytes(FMT, LL);
+    const int usub = wave >> g.ksh, kpart = wave & (g.KS - 1);
+    const int KS = g.KS;
+    bool staged = false;
+    for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {
+        const int unit = grp * g.upi + usub;
+        const bool active = unit < g.units;
+        const int uu = active ? unit : 0;
+        const uint8_t *cb = g.w + (int64_t)uu * Sh::TPW * g.ctb;
+        const uint8_t *sbase = g.w + g.soff + (int64_t)uu * Sh::TPW * g.stb;
+        int tofs[Sh::TPW];
+#pragma unroll
+        for (int tt = 0; tt < Sh::TPW; ++tt) tofs[tt] = uu * Sh::TPW + tt < g.tiles ? tt : 0;
+        f32x4_t acc[Sh::RG];
+#pragma unroll
+        for (int G = 0; G < Sh::RG; ++G) acc[G] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int w = 0; w < g.nwin; ++w) {
+            const int j0 = w * g.SW;
+            const int j1 = min(g.S, j0 + g.SW);
+            const int jf = j0 + kpart;      // SW is a multiple of KS
+            const int nsteps = (active && jf < j1) ? (j1 - jf + KS - 1) / KS : 0;
+            const int jlast = nsteps > 0 ? jf + (nsteps - 1) * KS : 0;
+            typename E::Regs ra, rb;
+            E::load(g, cb, sbase, lane, nsteps > 0 ? jf : 0, max(1, min(nsteps, E::U)), KS, tofs, ra);
+            if (g.nwin > 1 || !staged) {
+                __syncthreads();
+                mfma_stage(g, x, w, xs);
+                __syncthreads();
+                staged = true;
+            }
+            const int b0 = j0 * g.L;
+            int done = 0;
+            while (done < nsteps) {
+                const int cA = min(nsteps - done, E::U);
+                const int rB = nsteps - done - cA;
+                E::load(g, cb, sbase, lane, rB > 0 ? jf + (done + cA) * KS : jlast, rB > 0 ? min(rB, E::U) : 1, KS, tofs, rb);
+                E::compute(g, ra, cA, jf + done * KS, KS, b0, xs, wl, acc);
+                done += cA;
+                if (done >= nsteps) break;
+                const int cB = min(nsteps - done, E::U);
+                const int rA = nsteps - done - cB;
+                E::load(g, cb, sbase, lane, rA > 0 ? jf + (done + cB) * KS : jlast, rA > 0 ? min(rA, E::U) : 1, KS, tofs, ra);
+                E::compute(g, rb, cB, jf + done * KS, KS, b0, xs, wl, acc);
+                done += cB;
+            }
+        }
+        // split-K partials, summed in kpart order
+        if (KS > 1) {
+#pragma unroll
+            for (int G = 0; G < Sh::RG; ++G)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) red[((wave * Sh::RG + G) * 4 + q) * 64 + lane] = acc[G][q];
+            __syncthreads();
+            if (kpart == 0) {
+                for (int qq = 1; qq < KS; ++qq)
+#pragma unroll
+                    for (int G = 0; G < Sh::RG; ++G)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[G][q] += red[(((wave + qq) * Sh::RG + G) * 4 + q) * 64 + lane];
+            }
+            __syncthreads();
+        }
+        if (kpart == 0 && active) {
+            const int i = lane & 15, oct = lane >> 4;
+#pragma unroll
+            for (int G = 0; G < Sh::RG; ++G) {
+                const int64_t row = (int64_t)unit * 16 * Sh::RG + 16 * G + i;
+                if (row >= g.n) continue;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int t = 4 * oct + q;
+                    if (t < g.m) y[(int64_t)t * g.n + row] = acc[G][q];
+                }
+            }
+        }
+    }
+}
+
+typedef void (*mfma_fn)(MGeom, const void *, float *);
+
+template <int FMT>
+mfma_fn pick_mfma(int L)
+{
+    switch (L) {
+    case 1: return k_dense_mfma<FMT, 1>;
+    case 2: return k_dense_mfma<FMT, 2>;
+    case 4: return k_dense_mfma<FMT, 4>;
+    default: return k_dense_mfma<FMT, 8>;
+    }
+}
+
+mfma_fn mfma_kernel_q8_0(int L);
+mfma_fn mfma_kernel_q4_0(int L);
+mfma_fn mfma_kernel_mxfp4(int L);
+
+} // namespace qg

@@ -1,5 +1,6 @@
 // qg_mxfp4.hip -- MXFP4 instantiations of the dense and expert GEMV kernels.
 #include "qg_chain.h"
+#include "qg_mfma.h"
 
 namespace qg {
 
@@ -21,5 +22,7 @@ const void *chain_kernel_mxfp4(int xt, int m)
 }
 
 int chain_error_mxfp4(bool clear) { return chain_error_read(clear); }
+
+mfma_fn mfma_kernel_mxfp4(int L) { return pick_mfma<QG_MXFP4>(L); }
 
 } // namespace qg

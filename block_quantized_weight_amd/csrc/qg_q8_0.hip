@@ -1,5 +1,6 @@
 // qg_q8_0.hip -- Q8_0 instantiations of the dense and expert GEMV kernels.
 #include "qg_chain.h"
+#include "qg_mfma.h"
 
 namespace qg {
 
@@ -21,5 +22,7 @@ const void *chain_kernel_q8_0(int xt, int m)
 }
 
 int chain_error_q8_0(bool clear) { return chain_error_read(clear); }
+
+mfma_fn mfma_kernel_q8_0(int L) { return pick_mfma<QG_Q8_0>(L); }
 
 } // namespace qg

@@ -258,6 +258,51 @@ def test_mixed_range_activations(dev, fmt, xt):
     assert err <= TOL, err
 
 
+# ------------------------------------------------ matrix-core co-batches
+# bf16 co-batches of 4..8 tokens on layouts of 1..8 lanes per row run on the
+# matrix cores.  (n, k) pick each layout class: 33001 rows -> 1 lane per row,
+# 20000 -> 2, 9001 -> 4, 5000 and 4100 -> 8 (odd tile counts leave a half
+# unit); K = 12288 at 8 tokens needs several activation windows.
+MFMA_SHAPES = [(33001, 256, 1), (20000, 2048, 2), (9001, 2048, 4), (5000, 2048, 8), (4100, 12288, 8)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k,L", MFMA_SHAPES)
+@pytest.mark.parametrize("m", [4, 5, 8])
+def test_mfma_cobatch(dev, fmt, n, k, L, m):
+    say(f"mfma fmt={fmt} n={n} k={k} m={m}")
+    assert q.layout(fmt, n, k)["lanes_per_row"] == L
+    canon = wl.blocks_for(fmt, n, k, config=69, matrix=n)
+    x = draw_x((m, k), oracle.X_BF16, 69, n)
+    y = run_dense(fmt, canon, n, k, x, oracle.X_BF16, dev)
+    ref, l1 = oracle.gemv(fmt, canon, n, k, x, oracle.X_BF16)
+    err = oracle.max_rel_err(y, ref, l1)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mfma_deterministic_and_token_consistent(dev, fmt):
+    n, k = 9001, 2048
+    say(f"mfma determinism fmt={fmt}")
+    canon = wl.blocks_for(fmt, n, k, config=70, matrix=fmt)
+    w = packed_dev(fmt, canon, n, k, dev)
+    xb = draw_x((8, k), oracle.X_BF16, 70, fmt)
+    x = bf16_dev(xb, dev)
+    y8a = q.qgemv(fmt, w, n, k, x)
+    y8b = q.qgemv(fmt, w, n, k, x)
+    xr = x[:1].repeat(6, 1).contiguous()
+    yr = q.qgemv(fmt, w, n, k, xr)
+    y1 = q.qgemv(fmt, w, n, k, x[:1].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(y8a, y8b)
+    for t in range(1, 6):
+        assert torch.equal(yr[0], yr[t]), t
+    # a token's row from the matrix cores agrees with the single-token product
+    ref, l1 = oracle.gemv(fmt, canon, n, k, xb[:1], oracle.X_BF16)
+    assert oracle.max_rel_err(y8a[:1].cpu().numpy(), ref, l1) <= TOL
+    assert oracle.max_rel_err(y1.cpu().numpy(), ref, l1) <= TOL
+
+
 # ------------------------------------------------------------ properties
 def test_deterministic_and_cobatch_invariant(dev):
     fmt, n, k = q.Q4_0, 2560, 9728
