@@ -83,6 +83,22 @@ def copies_for(nbytes):
     return max(2, -(-(1 << 30) // nbytes))
 
 
+MFMA_FLOP = 2 * 16 * 16 * 32           # one v_mfma_f32_16x16x32_bf16
+MFMA_BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16
+
+
+def mfma_issued(fmt, n, k):
+    """MFMA instructions one matrix-core launch issues: per 16-row unit and
+    step, one per (row group, block), plus one per block for Q4_0's offset."""
+    import block_quantized_weight_amd as q
+    lo = q.layout(fmt, n, k)
+    L, S, tiles = lo["lanes_per_row"], lo["steps"], lo["tiles"]
+    tpw = L // 4 if L >= 8 else 1
+    units = -(-tiles // tpw)
+    per_step = (L if L >= 4 else 4) + (L if fmt == q.Q4_0 else 0)
+    return units * S * per_step
+
+
 def run_other(args):
     """Per-launch throughput of the other workloads (one JSON line per case)."""
     import torch
@@ -133,15 +149,21 @@ def run_other(args):
                 ys[name] = torch.empty((m, n), dtype=torch.float32, device=dev)
             xb = 4 if xt == "f32" else 2
             set_bytes = 0
+            useful_flop = issued_flop = 0
             for name, n, k, j in mats:
                 b = n * (k // 32) * wl.BLOCK_BYTES[fmt] + m * k * xb + m * n * 4
                 set_bytes += b
+                path = q.dense_path(fmt, n, k, q.X_F32 if xt == "f32" else q.X_BF16, m)
+                if path == q.PATH_MFMA:
+                    useful_flop += 2 * m * n * k
+                    issued_flop += mfma_issued(fmt, n, k) * MFMA_FLOP
 
                 def one(name=name, n=n, k=k):
                     for r in range(reps):
                         q.qgemv(fmt, ws[name][r], n, k, xs[name], y=ys[name])
                 us = graph_time(torch, one, max(2, args.steps // 3)) / reps
-                per[name] = {"n": n, "k": k, "bytes": b, "us": round(us, 3), "gbs": round(b / us / 1e3, 1)}
+                per[name] = {"n": n, "k": k, "bytes": b, "us": round(us, 3), "gbs": round(b / us / 1e3, 1),
+                             "path": "mfma" if path == q.PATH_MFMA else "valu"}
 
             def whole():
                 for r in range(reps):
@@ -149,8 +171,16 @@ def run_other(args):
                         q.qgemv(fmt, ws[name][r], n, k, xs[name], y=ys[name])
             us = graph_time(torch, whole, max(2, args.steps // 3)) / reps
             gbs = set_bytes / us / 1e3
-            emit(f"{label} m={m}", gbs, us, {"per_matrix": per, "bytes_per_set": set_bytes,
-                                              "tokens_per_s": round(m * 1e6 / us, 1), "weight_copies": reps})
+            extra = {"per_matrix": per, "bytes_per_set": set_bytes, "tokens_per_s": round(m * 1e6 / us, 1),
+                     "weight_copies": reps}
+            if issued_flop:
+                # matrix-core work of the set: algorithmic 2*m*n*k against the bf16 dense peak,
+                # and what the MFMAs issue (16 token rows per instruction, plus Q4_0's offset MFMA)
+                extra["mfma"] = {"useful_tflops": round(useful_flop / us / 1e6, 2),
+                                 "issued_tflops": round(issued_flop / us / 1e6, 2),
+                                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                                 "frac": round(useful_flop / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 5)}
+            emit(f"{label} m={m}", gbs, us, extra)
 
     if args.workload == "c0":
         dense_case(0, [("w", 2048, 2048, 0)], "f32", [1], "q8_0 2048x2048, x fp32")

@@ -19,6 +19,7 @@ Q8_0, Q4_0, MXFP4 = 0, 1, 2
 X_F32, X_BF16 = 0, 1
 MOE_GATE_UP, MOE_DOWN_COMBINE = 0, 1
 MAX_M = 8
+PATH_VALU, PATH_MFMA = 0, 1
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17}
 
 # exported functions: name -> (restype, argtypes)
@@ -32,6 +33,7 @@ SIGNATURES = {
     "qg_pack": (_i, [_i, _vp, _i64, _i64, _vp, _vp]),
     "qg_unpack": (_i, [_i, _vp, _i64, _i64, _vp, _vp]),
     "qg_dequant_f32": (_i, [_i, _vp, _i64, _i64, _vp, _vp]),
+    "qg_dense_path": (_i, [_i, _i64, _i64, _i, _i64]),
     "qgemv_q8_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_q4_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_mxfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
@@ -94,6 +96,14 @@ def _check(fn, status):
 
 
 # ------------------------------------------------------------------ layout
+def dense_path(fmt, n, k, xt, m):
+    """PATH_VALU or PATH_MFMA: the kernel family a dense call would run."""
+    v = lib().qg_dense_path(fmt, n, k, xt, m)
+    if v < 0:
+        raise QGError("qg_dense_path", -v)
+    return v
+
+
 def packed_bytes(fmt, n, k):
     v = lib().qg_packed_bytes(fmt, n, k)
     if v < 0:

@@ -400,6 +400,15 @@ int qg_dequant_f32(int fmt, const void *w_packed, int64_t n, int64_t k, float *w
     return launch_status();
 }
 
+int qg_dense_path(int fmt, int64_t n, int64_t k, int xt, int64_t m)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return -st;
+    if (xt != QG_F32 && xt != QG_BF16) return -QG_EINVAL;
+    if (m < 1 || m > QG_MAX_M) return -QG_EINVAL;
+    return mfma_fits(make_layout(fmt, n, k), xt, m) ? QG_PATH_MFMA : QG_PATH_VALU;
+}
+
 int qgemv_q8_0(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
 {
     return dense(QG_Q8_0, w, n, k, x, xt, m, y, stream);

@@ -81,6 +81,9 @@ enum { QG_MOE_GATE_UP = 0, QG_MOE_DOWN_COMBINE = 1 };
 /* Largest co-batch (tokens per call). */
 #define QG_MAX_M 8
 
+/* Kernel families of the dense product (qg_dense_path). */
+enum { QG_PATH_VALU = 0, QG_PATH_MFMA = 1 };
+
 /* Description of the packed layout of one n x k matrix. */
 typedef struct {
     int32_t fmt;
@@ -137,6 +140,11 @@ int qg_dequant_f32(int fmt, const void *w_packed, int64_t n, int64_t k, float *w
  * x: device, [m][k] row-major, fp32 or bf16 (xt), 16-byte aligned.
  * y: device, fp32 [m][n] row-major, 4-byte aligned, overwritten.
  * Accumulation is fp32; x is used exactly (bf16 -> fp32 is exact).
+ * Two kernel families compute it (qg_dense_path says which one a call uses):
+ * lane-per-block vector code, and for bf16 co-batches (Q8_0 from 2 tokens,
+ * Q4_0 and MXFP4 from 4) on layouts of at most 8 lanes per row, the matrix
+ * cores (one bf16 MFMA per 16 rows x 32-weight block, scales applied in
+ * fp32).  Results of the two agree within the rounding of fp32 sums.
  * Limits: n, k <= 2^31 - 1 and k % 32 == 0.
  */
 int qgemv_q8_0(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
@@ -145,6 +153,13 @@ int qgemv_q4_0(const void *w_packed, int64_t n, int64_t k, const void *x, int xt
                float *y, void *stream);
 int qgemv_mxfp4(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
                 float *y, void *stream);
+
+/*
+ * Which kernel family a dense call with these arguments runs: QG_PATH_VALU
+ * or QG_PATH_MFMA, or a negative status (-QG_EINVAL, -QG_EUNSUPPORTED) for
+ * arguments the dense calls would reject.  Host only; no device work.
+ */
+int qg_dense_path(int fmt, int64_t n, int64_t k, int xt, int64_t m);
 
 /*
  * Top-k expert product.  w_experts: device, n_experts packed matrices of

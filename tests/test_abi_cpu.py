@@ -166,3 +166,23 @@ def test_pack_and_dequant_validation():
     assert L.qg_unpack(q.Q8_0, BAD, 4, 64, a, None) == q.QG_EINVAL
     assert L.qg_dequant_f32(q.Q8_0, a, 4, 64, ODD, None) == q.QG_EALIGN
     assert L.qg_pack_host(q.Q8_0, None, 4, 64, None) == q.QG_EINVAL
+
+
+def test_dense_path_rule():
+    """bf16 co-batches on layouts of <= 8 lanes per row take the matrix cores:
+    Q8_0 from 2 tokens, the 4-bit formats from 4; everything else the vector path."""
+    V, M = q.PATH_VALU, q.PATH_MFMA
+    assert q.layout(q.Q4_0, 6144, 4096)["lanes_per_row"] == 8
+    assert q.dense_path(q.Q8_0, 6144, 4096, q.X_BF16, 1) == V
+    assert q.dense_path(q.Q8_0, 6144, 4096, q.X_BF16, 2) == M
+    assert q.dense_path(q.Q4_0, 6144, 4096, q.X_BF16, 3) == V
+    assert q.dense_path(q.Q4_0, 6144, 4096, q.X_BF16, 4) == M
+    assert q.dense_path(q.MXFP4, 6144, 4096, q.X_BF16, 8) == M
+    assert q.dense_path(q.Q4_0, 6144, 4096, q.X_F32, 8) == V          # fp32 activations
+    assert q.layout(q.Q4_0, 2560, 9728)["lanes_per_row"] == 16
+    assert q.dense_path(q.Q4_0, 2560, 9728, q.X_BF16, 8) == V         # 16 lanes per row
+    for bad in [(q.Q8_0, 64, 33, q.X_BF16, 1), (q.Q8_0, 64, 64, q.X_BF16, 0), (q.Q8_0, 64, 64, q.X_BF16, 9),
+                (q.Q8_0, 64, 64, 5, 1), (9, 64, 64, q.X_BF16, 1), (q.Q8_0, 0, 64, q.X_BF16, 1)]:
+        with pytest.raises(q.QGError):
+            q.dense_path(*bad)
+    assert q.lib().qg_dense_path(q.Q8_0, 1 << 32, 64, q.X_BF16, 1) == -q.QG_EUNSUPPORTED

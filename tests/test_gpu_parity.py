@@ -272,6 +272,7 @@ MFMA_SHAPES = [(33001, 256, 1), (20000, 2048, 2), (9001, 2048, 4), (5000, 2048, 
 def test_mfma_cobatch(dev, fmt, n, k, L, m):
     say(f"mfma fmt={fmt} n={n} k={k} m={m}")
     assert q.layout(fmt, n, k)["lanes_per_row"] == L
+    assert q.dense_path(fmt, n, k, q.X_BF16, m) == q.PATH_MFMA
     canon = wl.blocks_for(fmt, n, k, config=69, matrix=n)
     x = draw_x((m, k), oracle.X_BF16, 69, n)
     y = run_dense(fmt, canon, n, k, x, oracle.X_BF16, dev)
