@@ -227,7 +227,7 @@ def qgemv_mxfp4(w_packed, n, k, x, y=None, stream=None):
 
 def moe_qgemv_topk(fmt, w_experts, n_experts, n, k, topk_ids, topk_w, x, mode, y=None, stream=None):
     """Top-k expert GEMV.  GATE_UP: x [m, k] -> y [m, top_k, n];
-    DOWN_COMBINE: x [m, top_k, k] -> y [m, n] (router weights combine, slot order)."""
+    DOWN_COMBINE: x [m, top_k, k] -> y [m, n] (router-weighted sum, fixed order)."""
     torch = _torch()
     m, top_k = topk_ids.shape
     if topk_ids.dtype != torch.int32:

@@ -2,6 +2,7 @@
 // plans, the packer kernels and the dequantization test aid.
 #include "qg_chain.h"
 #include "qg_mfma.h"
+#include "qg_moe_stream.h"
 
 namespace qg {
 namespace {
@@ -441,7 +442,6 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
         return QG_EALIGN;
     const Layout lo = make_layout(fmt, n, k);
     const bool dot = uses_dot(fmt, xt);
-    Plan p = make_plan(lo, QG_MAX_M, dot, QG_MAX_M);
     MoeArgs a;
     a.experts = (const uint8_t *)w_experts;
     a.expert_bytes = lo.total;
@@ -450,13 +450,56 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
     a.n_experts = (int32_t)n_experts;
     a.m = (int32_t)m;
     a.top_k = (int32_t)top_k;
+    hipStream_t s = as_stream(stream);
+    {
+        // streaming kernel: every activation row of the call staged at once
+        const int nrows = (int)(mode == QG_MOE_GATE_UP ? m : m * top_k);
+        const size_t lds = moe_stream_lds(fmt, dot, nrows, (int)(lo.S * lo.L), mode);
+        Geom g{};
+        g.n = (int32_t)lo.n;
+        g.k = (int32_t)lo.k;
+        g.nb = (int32_t)lo.nb;
+        g.L = lo.L;
+        g.lsh = lo.lsh;
+        g.R = lo.R;
+        g.S = (int32_t)lo.S;
+        g.tiles = (int32_t)lo.tiles;
+        g.ctb = lo.ctb;
+        g.stb = lo.stb;
+        g.soff = lo.soff;
+        int KS = 1;
+        if (mode == QG_MOE_DOWN_COMBINE) {
+            if (lo.tiles < 4096) KS = 2;
+            if (lo.tiles < 2048) KS = 4;
+            while (KS > 1 && lo.S < KS) KS >>= 1;
+        }
+        g.KS = KS;
+        g.ksh = ilog2(KS);
+        g.tpi = WAVES / KS;
+        g.ngroups = (int32_t)((lo.tiles + g.tpi - 1) / g.tpi);
+        g.SW = (int32_t)lo.S;
+        g.nwin = 1;
+        g.wblk = (int32_t)(lo.S * lo.L);
+        if (lds <= MOE_STREAM_LDS && g.ngroups <= 65535) {
+            g.w = (const uint8_t *)w_experts;
+            const int ms = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
+            moe_stream_fn f = fmt == QG_Q8_0 ? moe_stream_kernel_q8_0(xt, mode, ms)
+                              : fmt == QG_Q4_0 ? moe_stream_kernel_q4_0(xt, mode, ms)
+                                               : moe_stream_kernel_mxfp4(xt, mode, ms);
+            void *args[] = {(void *)&g, (void *)&a, (void *)&x, (void *)&y};
+            if (allow_lds((const void *)f, lds) != hipSuccess) return QG_EHIP;
+            hipError_t e = hipLaunchKernel((const void *)f, dim3(g.ngroups), dim3(TPB), args, lds, s);
+            return e == hipSuccess ? launch_status() : QG_EHIP;
+        }
+    }
+    // general kernels: activations staged per expert in windows
+    Plan p = make_plan(lo, QG_MAX_M, dot, QG_MAX_M);
     const int maxdistinct = (int)((m * top_k < n_experts) ? m * top_k : n_experts);
     size_t lds = p.lds;
     if (mode == QG_MOE_DOWN_COMBINE) {
         const size_t rows_pg = (size_t)p.g.tpi * p.g.R;
         lds += (size_t)(m * top_k + QG_MAX_M) * rows_pg * 4;
     }
-    hipStream_t s = as_stream(stream);
     hipError_t e = fmt == QG_Q8_0 ? launch_moe_q8_0(xt, mode, p, a, maxdistinct, lds, x, y, s)
                    : fmt == QG_Q4_0 ? launch_moe_q4_0(xt, mode, p, a, maxdistinct, lds, x, y, s)
                                     : launch_moe_mxfp4(xt, mode, p, a, maxdistinct, lds, x, y, s);

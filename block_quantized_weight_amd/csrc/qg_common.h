@@ -430,6 +430,12 @@ struct XStage {
     }
 };
 
+// Slot -> staged activation row map of the dense product: slot t reads row t.
+struct IdMap {
+    __device__ __forceinline__ int operator()(int t) const { return t; }
+    __device__ __forceinline__ int count() const { return QG_MAX_M; }
+};
+
 // Steps per batch (loads in flight per lane before the first use).
 template <int FMT, bool DOT> struct Batch { static constexpr int U = (FMT == QG_Q8_0 || !DOT) ? 4 : 8; };
 
@@ -465,18 +471,22 @@ struct Engine {
     }
 
     // Adds the contributions of one step (block b of this lane's row) to acc.
+    // Slot t reads staged activation row xm(t) (the identity for the dense
+    // product); slots t >= xm.count() are skipped.
+    template <typename XMap = IdMap>
     static __device__ __forceinline__ void step(const Geom &g, const uint4 *c, uint32_t sbits, const uint4 *xs,
-                                                const float *corr, int bl, float acc[M])
+                                                const float *corr, int bl, float acc[M], const XMap &xm = XMap())
     {
         if (FMT == QG_Q8_0) {
             const float d = f16_bits_to_f32(sbits);
             const uint32_t cw[8] = {c[0].x, c[0].y, c[0].z, c[0].w, c[1].x, c[1].y, c[1].z, c[1].w};
 #pragma unroll
             for (int t = 0; t < M; ++t) {
+                if (t >= xm.count()) break;
                 float s = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float4 xq = __builtin_bit_cast(float4, xs[(t * 8 + i) * g.wblk + bl]);
+                    const float4 xq = __builtin_bit_cast(float4, xs[(xm(t) * 8 + i) * g.wblk + bl]);
                     s = __builtin_fmaf(i8_at(cw[i], 0), xq.x, s);
                     s = __builtin_fmaf(i8_at(cw[i], 1), xq.y, s);
                     s = __builtin_fmaf(i8_at(cw[i], 2), xq.z, s);
@@ -495,10 +505,11 @@ struct Engine {
                     for (int kk = 0; kk < 4; ++kk) pr[i][kk] = q4_pair(cw[i], kk);
 #pragma unroll
                 for (int t = 0; t < M; ++t) {
-                    float s = -corr[t * g.wblk + bl];
+                    if (t >= xm.count()) break;
+                    float s = -corr[xm(t) * g.wblk + bl];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint4 xq = xs[(t * 4 + i) * g.wblk + bl];
+                        const uint4 xq = xs[(xm(t) * 4 + i) * g.wblk + bl];
                         s = dot2(pr[i][0], u32_as_bf16x2(xq.x), s);
                         s = dot2(pr[i][1], u32_as_bf16x2(xq.y), s);
                         s = dot2(pr[i][2], u32_as_bf16x2(xq.z), s);
@@ -518,10 +529,11 @@ struct Engine {
                 }
 #pragma unroll
                 for (int t = 0; t < M; ++t) {
-                    float s = -corr[t * g.wblk + bl];
+                    if (t >= xm.count()) break;
+                    float s = -corr[xm(t) * g.wblk + bl];
 #pragma unroll
                     for (int qd = 0; qd < 8; ++qd) {
-                        const float4 xq = __builtin_bit_cast(float4, xs[(t * 8 + qd) * g.wblk + bl]);
+                        const float4 xq = __builtin_bit_cast(float4, xs[(xm(t) * 8 + qd) * g.wblk + bl]);
                         s = __builtin_fmaf(v[4 * qd + 0], xq.x, s);
                         s = __builtin_fmaf(v[4 * qd + 1], xq.y, s);
                         s = __builtin_fmaf(v[4 * qd + 2], xq.z, s);
@@ -544,10 +556,11 @@ struct Engine {
                 }
 #pragma unroll
                 for (int t = 0; t < M; ++t) {
+                    if (t >= xm.count()) break;
                     float s = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint4 xq = xs[(t * 4 + i) * g.wblk + bl];
+                        const uint4 xq = xs[(xm(t) * 4 + i) * g.wblk + bl];
                         s = dot2(pr[i][0], u32_as_bf16x2(xq.x), s);
                         s = dot2(pr[i][1], u32_as_bf16x2(xq.y), s);
                         s = dot2(pr[i][2], u32_as_bf16x2(xq.z), s);
@@ -566,11 +579,12 @@ struct Engine {
                 }
 #pragma unroll
                 for (int t = 0; t < M; ++t) {
+                    if (t >= xm.count()) break;
                     float s = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float4 xa = __builtin_bit_cast(float4, xs[(t * 8 + 2 * i) * g.wblk + bl]);
-                        const float4 xb = __builtin_bit_cast(float4, xs[(t * 8 + 2 * i + 1) * g.wblk + bl]);
+                        const float4 xa = __builtin_bit_cast(float4, xs[(xm(t) * 8 + 2 * i) * g.wblk + bl]);
+                        const float4 xb = __builtin_bit_cast(float4, xs[(xm(t) * 8 + 2 * i + 1) * g.wblk + bl]);
                         s = __builtin_fmaf(pr[i][0].x, xa.x, s);
                         s = __builtin_fmaf(pr[i][0].y, xa.y, s);
                         s = __builtin_fmaf(pr[i][1].x, xa.z, s);
@@ -586,15 +600,17 @@ struct Engine {
         }
     }
 
+    template <typename XMap = IdMap>
     static __device__ __forceinline__ void compute(const Geom &g, const Regs &r, int cnt, int jfirst, int KS,
-                                                   int slot, int b0, const uint4 *xs, const float *corr, float acc[M])
+                                                   int slot, int b0, const uint4 *xs, const float *corr, float acc[M],
+                                                   const XMap &xm = XMap())
     {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (u < cnt) {
                 const int j = jfirst + u * KS;
                 const int bl = j * g.L + slot - b0;
-                step(g, r.c[u], r.s[u], xs, corr, bl, acc);
+                step(g, r.c[u], r.s[u], xs, corr, bl, acc, xm);
             }
         }
     }

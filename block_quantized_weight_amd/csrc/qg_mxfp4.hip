@@ -1,6 +1,7 @@
 // qg_mxfp4.hip -- MXFP4 instantiations of the dense and expert GEMV kernels.
 #include "qg_chain.h"
 #include "qg_mfma.h"
+#include "qg_moe_stream.h"
 
 namespace qg {
 
@@ -24,5 +25,10 @@ const void *chain_kernel_mxfp4(int xt, int m)
 int chain_error_mxfp4(bool clear) { return chain_error_read(clear); }
 
 mfma_fn mfma_kernel_mxfp4(int L) { return pick_mfma<QG_MXFP4>(L); }
+
+moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms)
+{
+    return xt == QG_BF16 ? pick_moe_stream<QG_MXFP4, true, true>(mode, ms) : pick_moe_stream<QG_MXFP4, false, false>(mode, ms);
+}
 
 } // namespace qg

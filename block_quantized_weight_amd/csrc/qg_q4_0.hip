@@ -1,6 +1,7 @@
 // qg_q4_0.hip -- Q4_0 instantiations of the dense and expert GEMV kernels.
 #include "qg_chain.h"
 #include "qg_mfma.h"
+#include "qg_moe_stream.h"
 
 namespace qg {
 
@@ -24,5 +25,10 @@ const void *chain_kernel_q4_0(int xt, int m)
 int chain_error_q4_0(bool clear) { return chain_error_read(clear); }
 
 mfma_fn mfma_kernel_q4_0(int L) { return pick_mfma<QG_Q4_0>(L); }
+
+moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms)
+{
+    return xt == QG_BF16 ? pick_moe_stream<QG_Q4_0, true, true>(mode, ms) : pick_moe_stream<QG_Q4_0, false, false>(mode, ms);
+}
 
 } // namespace qg

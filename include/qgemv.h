@@ -166,15 +166,18 @@ int qg_dense_path(int fmt, int64_t n, int64_t k, int xt, int64_t m);
  * identical shape (fmt, n, k) back to back, expert e at byte offset
  * e * qg_packed_bytes(fmt, n, k) (a multiple of 256); 16-byte aligned.
  * topk_ids: device int32 [m][top_k]; topk_w: device fp32 [m][top_k].
- * Ids should be distinct within a token.
+ * Ids should be distinct within a token (repeated ids still follow the
+ * formulas below); an id outside [0, n_experts) contributes nothing.
  *   QG_MOE_GATE_UP:      x [m][k];         y [m][top_k][n],
  *                        y[t][j][i] = W_{ids[t][j]}[i] . x[t]   (topk_w unused, may be NULL)
  *   QG_MOE_DOWN_COMBINE: x [m][top_k][k];  y [m][n],
- *                        y[t][i] = sum over j ascending of topk_w[t][j] * (W_{ids[t][j]}[i] . x[t][j])
- * Only the selected experts' weights are read; each distinct selected expert
- * is streamed once per call for all tokens that chose it.
+ *                        y[t][i] = sum over j of topk_w[t][j] * (W_{ids[t][j]}[i] . x[t][j])
+ * fp32 accumulation in a fixed order (ascending expert id, then slot), so
+ * the same inputs give the same bits.  Only the selected experts' weights
+ * are read; each distinct selected expert is streamed once per call for all
+ * tokens that chose it.
  * Limits: 1 <= m <= 8, 1 <= top_k <= n_experts, m * top_k <= 64,
- * n_experts <= 65536.  y is overwritten (rows of invalid ids excepted).
+ * n_experts <= 65536.  y is overwritten, except gate_up rows of invalid ids.
  */
 int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n, int64_t k,
                    const int32_t *topk_ids, const float *topk_w, int64_t m, int64_t top_k,

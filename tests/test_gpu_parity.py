@@ -441,6 +441,59 @@ def test_moe_all_tokens_same_experts(dev):
         assert oracle.max_rel_err(y, ref, l1) <= TOL
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_moe_repeated_expert_in_a_token(dev, fmt):
+    """Ids repeated inside a token (outside the documented precondition) still
+    follow the definition: expert 5 takes 6 of 8 slots, more than one work
+    item's worth for two tokens."""
+    E, n, k = 8, 200, 512
+    say(f"moe repeated ids fmt={fmt}")
+    ids = np.array([[5, 5, 5, 5], [5, 2, 5, 2]], dtype=np.int32)
+    g = np.array([[0.1, 0.2, 0.3, 0.4], [0.4, 0.3, 0.2, 0.1]], dtype=np.float32)
+    for mode in (q.MOE_GATE_UP, q.MOE_DOWN_COMBINE):
+        y, ref, l1 = _moe_case(dev, fmt, E, n, k, ids, g, oracle.X_BF16, mode, 73)
+        assert oracle.max_rel_err(y, ref, l1) <= TOL, mode
+
+
+def test_moe_invalid_ids_contribute_nothing(dev):
+    """An id outside [0, n_experts) adds nothing to down-combine and leaves its
+    gate_up rows untouched."""
+    fmt, E, n, k = q.MXFP4, 8, 256, 1024
+    say("moe invalid ids")
+    ids = np.array([[3, -1, 7, 40], [1, 3, 99, 2]], dtype=np.int32)
+    g = np.array([[0.4, 0.3, 0.2, 0.1], [0.25, 0.25, 0.25, 0.25]], dtype=np.float32)
+    valid = (ids >= 0) & (ids < E)
+    experts = _experts(fmt, E, n, k, 74)
+    wexp = _experts_dev(fmt, experts, E, n, k, dev)
+    ids_ref = np.where(valid, ids, 0).astype(np.int32)
+    g_ref = np.where(valid, g, 0).astype(np.float32)
+    h = draw_x((2, 4, k), oracle.X_BF16, 74, 0, "h")
+    y = q.moe_qgemv_topk(fmt, wexp, E, n, k, to_dev(ids, dev), to_dev(g, dev), x_dev(h, oracle.X_BF16, dev),
+                         q.MOE_DOWN_COMBINE)
+    ref, l1 = oracle.moe(fmt, experts, E, n, k, ids_ref, g_ref, h, oracle.X_BF16, q.MOE_DOWN_COMBINE)
+    assert oracle.max_rel_err(y.cpu().numpy(), ref, l1) <= TOL
+    x = draw_x((2, k), oracle.X_BF16, 74, 0, "x")
+    yg = torch.full((2, 4, n), float("nan"), device=dev)
+    q.moe_qgemv_topk(fmt, wexp, E, n, k, to_dev(ids, dev), None, x_dev(x, oracle.X_BF16, dev), q.MOE_GATE_UP, y=yg)
+    yg = yg.cpu().numpy()
+    ref, l1 = oracle.moe(fmt, experts, E, n, k, ids_ref, g_ref, x, oracle.X_BF16, q.MOE_GATE_UP)
+    assert np.isnan(yg[~valid]).all()
+    assert oracle.max_rel_err(yg[valid], ref[valid], l1[valid]) <= TOL
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("mode", [q.MOE_GATE_UP, q.MOE_DOWN_COMBINE])
+def test_moe_general_kernels(dev, fmt, mode):
+    """Activation rows too large to stage at once (fp32, 8 tokens x 8 slots or
+    K = 8192) take the kernels that stage per expert in windows."""
+    E, n, m, top_k = 16, 130, 8, 8
+    k = 8192 if mode == q.MOE_GATE_UP else 4096
+    say(f"moe general fmt={fmt} mode={mode}")
+    _, ids, g = wl.router_topk(m, E, top_k, wl.rng_for(75, fmt, "router"))
+    y, ref, l1 = _moe_case(dev, fmt, E, n, k, ids, g, oracle.X_F32, mode, 75)
+    assert oracle.max_rel_err(y, ref, l1) <= TOL
+
+
 def test_moe_deterministic(dev):
     fmt, E, n, k, m, top_k = q.MXFP4, 32, 2048, 1792, 4, 4
     say("moe determinism")
