@@ -450,6 +450,7 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
     a.n_experts = (int32_t)n_experts;
     a.m = (int32_t)m;
     a.top_k = (int32_t)top_k;
+    a.isplit = 1;
     hipStream_t s = as_stream(stream);
     {
         // streaming kernel: every activation row of the call staged at once
@@ -467,15 +468,16 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
         g.ctb = lo.ctb;
         g.stb = lo.stb;
         g.soff = lo.soff;
-        int KS = 1;
-        if (mode == QG_MOE_DOWN_COMBINE) {
-            if (lo.tiles < 4096) KS = 2;
-            if (lo.tiles < 2048) KS = 4;
-            while (KS > 1 && lo.S < KS) KS >>= 1;
-        }
-        g.KS = KS;
-        g.ksh = ilog2(KS);
-        g.tpi = WAVES / KS;
+        // waves per tile, splitting its items.  down-combine: more when tiles
+        // are few; gate_up: one (a wave streams every item of its tile, which
+        // measured faster than splitting on MI355X)
+        int IS = 1;
+        if (mode == QG_MOE_DOWN_COMBINE && lo.tiles < 4096) IS = 2;
+        if (mode == QG_MOE_DOWN_COMBINE && lo.tiles < 2048) IS = 4;
+        a.isplit = IS;
+        g.KS = 1;
+        g.ksh = 0;
+        g.tpi = WAVES / IS;
         g.ngroups = (int32_t)((lo.tiles + g.tpi - 1) / g.tpi);
         g.SW = (int32_t)lo.S;
         g.nwin = 1;

@@ -776,6 +776,7 @@ struct MoeArgs {
     const int32_t *ids;
     const float *gw;
     int32_t n_experts, m, top_k;
+    int32_t isplit;              // streaming kernel: waves that share a tile, splitting its items
 };
 
 // Runs the dense passes of this workgroup over expert `e` for `cnt` slots

@@ -5,18 +5,19 @@
 // experts in ascending order (imp keeps routing on the device so the decode
 // graph holds no host round trip: imp release notes v0.7.0, known issues),
 // and splits every expert's slots into "items" of at most MS slots.  All the
-// activation rows the call needs are staged once.  A wave then owns one
-// (row tile, k-part) of the expert shape and streams that tile of every item
-// back to back: the first weight batch of item i+1 is loaded while item i is
-// computed, so the weight stream does not drain at expert boundaries and no
-// barrier sits inside it.
-//   gate_up:      no split-K; after each item the wave reduces across its
-//                 row's lanes and stores the item's slot rows.
+// activation rows the call needs are staged once.  IS waves share a row tile
+// of the expert shape and split its items (wave p takes items p, p+IS, ...);
+// each wave streams all steps of its items back to back, the first weight
+// batch of its next item being loaded while the current one is computed, so
+// the weight stream does not drain at expert boundaries and no barrier sits
+// inside it.
+//   gate_up:      after each item the wave reduces across its row's lanes
+//                 and stores the item's slot rows.
 //   down-combine: the wave folds router-weighted slot results into per-token
-//                 registers; at the end the KS waves of a tile add their
+//                 registers; at the end the IS waves of a tile add their
 //                 partials in a fixed order through LDS.
-// Only selected experts are read, each once per workgroup; the result is
-// deterministic (fixed item order and reduction order).
+// Only selected experts are read, each once per tile; the result is
+// deterministic (fixed item assignment and reduction order).
 #include "qg_common.h"
 
 namespace qg {
@@ -115,8 +116,8 @@ inline __host__ __device__ size_t moe_stream_lds(int fmt, bool dot, int nrows, i
     return b;
 }
 
-// grid = ceil(tiles / tpi) workgroups, one (tile, k-part) per wave.
-// gate_up: KS = 1.  Geom: one activation window covering all of K.
+// grid = ceil(tiles / tpi) workgroups, tpi = WAVES / IS tiles each; one
+// (tile, item subset) per wave.  Geom: KS = 1, one activation window over K.
 template <int FMT, bool XBF16, bool DOT, int MS, int MODE>
 __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const void *__restrict__ x, float *__restrict__ y)
 {
@@ -133,7 +134,8 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
     float *corr = (float *)(smem + (size_t)nrows * QPB * g.wblk * 16);
     float *red = corr + (x_aux(FMT) ? nrows * g.wblk : 0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int tsub = wave >> g.ksh, kpart = wave & (g.KS - 1);
+    const int IS = a.isplit;
+    const int tsub = wave / IS, ipart = wave - tsub * IS;
     const int rsub = lane >> g.lsh, slot = lane & (g.L - 1);
 
     distinct_experts(a.ids, nslots, a.n_experts, s_ids, s_list, &s_count);
@@ -142,21 +144,21 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
 
     const int tile = blockIdx.x * g.tpi + tsub;
     const int tl = tile < g.tiles ? tile : 0;
-    const int nsteps = (tile < g.tiles && kpart < g.S && ni > 0) ? (g.S - kpart + g.KS - 1) / g.KS : 0;
+    const int nsteps = (tile < g.tiles && ipart < ni) ? g.S : 0;
     auto work = [&](int i) {
         const uint8_t *w = a.experts + (int64_t)it.e[i] * a.expert_bytes;
         ItemWork iw;
         iw.ct = w + (int64_t)tl * g.ctb;
         iw.st = w + g.soff + (int64_t)tl * g.stb;
-        iw.jf = kpart;
+        iw.jf = 0;
         iw.nsteps = nsteps;
-        iw.KS = g.KS;
+        iw.KS = 1;
         return iw;
     };
     typename E::Regs ra, rb;
     if (nsteps > 0) {
-        const ItemWork w0 = work(0);
-        E::load(g, w0.ct, w0.st, lane, w0.jf, min(nsteps, E::U), g.KS, ra);
+        const ItemWork w0 = work(ipart);
+        E::load(g, w0.ct, w0.st, lane, w0.jf, min(nsteps, E::U), 1, ra);
     }
 
     // stage every activation row of the call (row r = token for gate_up,
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
 #pragma unroll
     for (int t = 0; t < QG_MAX_M; ++t) tok[t] = 0.0f;
     bool in_a = true;               // the current item's first batch is in ra
-    for (int i = 0; i < ni; ++i) {
+    for (int i = ipart; i < ni; i += IS) {
         SlotMap<MS> sm;
         sm.n = it.n[i];
 #pragma unroll
@@ -209,8 +211,8 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
         if (nsteps > 0) {
             const ItemWork w = work(i);
             ItemWork nx = w;
-            if (i + 1 < ni) {
-                nx = work(i + 1);
+            if (i + IS < ni) {
+                nx = work(i + IS);
             } else {
                 nx.nsteps = 1;      // nothing follows: repeat this item's first step
             }
@@ -242,13 +244,13 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
         }
     }
     if (MODE == QG_MOE_DOWN_COMBINE) {
-        // split-K partials of the tile, added in kpart order
-        if (g.KS > 1) {
+        // the IS waves' partials of the tile, added in ipart order
+        if (IS > 1) {
 #pragma unroll
             for (int t = 0; t < QG_MAX_M; ++t) red[(wave * QG_MAX_M + t) * 64 + lane] = tok[t];
             __syncthreads();
-            if (kpart == 0) {
-                for (int q = 1; q < g.KS; ++q)
+            if (ipart == 0) {
+                for (int q = 1; q < IS; ++q)
 #pragma unroll
                     for (int t = 0; t < QG_MAX_M; ++t) tok[t] += red[((wave + q) * QG_MAX_M + t) * 64 + lane];
             }
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
 #pragma unroll
             for (int t = 0; t < QG_MAX_M; ++t) tok[t] += __shfl_xor(tok[t], off, 64);
         }
-        if (kpart == 0 && tile < g.tiles && row < g.n) {
+        if (ipart == 0 && tile < g.tiles && row < g.n) {
 #pragma unroll
             for (int t = 0; t < QG_MAX_M; ++t)
                 if (t < a.m && (t & (g.L - 1)) == slot) y[(int64_t)t * g.n + row] = tok[t];
