@@ -106,10 +106,15 @@ Plan make_plan(const Layout &lo, int M, bool dot, int maxslots_lds)
     int64_t sw_max = (int64_t)(XBUDGET / per_block) / lo.L;
     if (sw_max < 1) sw_max = 1;
     // split-K factor: more waves per tile when tiles are few; never more than
-    // the steps of a tile or of a window
+    // the steps of a tile or of a window.  A single token over short rows (at
+    // most 20 steps per lane) runs unsplit: the cross-wave reduction then
+    // costs more than it saves (MI355X: -0.7 to -1.0 us per launch on the
+    // 2560..6144-row decode matrices).  Co-batches keep the split, which also
+    // spreads their heavier per-step arithmetic.
     int KS = 1;
     if (lo.tiles < 4096) KS = 2;
     if (lo.tiles < 2048) KS = 4;
+    if (M == 1 && lo.S <= 20) KS = 1;
     while (KS > 1 && (lo.S < KS || sw_max < KS)) KS >>= 1;
     g.KS = KS;
     g.ksh = ilog2(KS);
