@@ -205,9 +205,12 @@ def run_other(args):
                 q.pack(fmt, gc, gn, gk, out=ge[(r * E + e) * gpb:(r * E + e + 1) * gpb])
                 q.pack(fmt, dc, dn, dk, out=de[(r * E + e) * dpb:(r * E + e + 1) * dpb])
         for m in (1, 4):
-            _, ids, g = wl.router_topk(m, E, top_k, wl.rng_for(4, m, "router"))
+            logits, ids, g = wl.router_topk(m, E, top_k, wl.rng_for(4, m, "router"))
             distinct = len(set(ids.reshape(-1).tolist()))
             tid, tw = torch.from_numpy(ids).to(dev), torch.from_numpy(g).to(dev)
+            lg = torch.from_numpy(logits).to(dev)
+            rid = torch.empty_like(tid)
+            rw = torch.empty_like(tw)
             x = bf16_dev(wl.x_bf16_bits((m, gk), wl.rng_for(4, m, "x")))
             h = bf16_dev(wl.x_bf16_bits((m, top_k, dk), wl.rng_for(4, m, "h")))
             yg = torch.empty((m, top_k, gn), dtype=torch.float32, device=dev)
@@ -226,9 +229,17 @@ def run_other(args):
                 us = graph_time(torch, lambda f=f: [f(r) for r in range(reps)], max(2, args.steps // 3)) / reps
                 per[nm] = {"bytes": b, "us": round(us, 3), "gbs": round(b / us / 1e3, 1)}
             us = graph_time(torch, lambda: [(gate(r), down(r)) for r in range(reps)], max(2, args.steps // 3)) / reps
+
+            # the device router (top-k + softmax of the logits), alone and in front of the two products
+            def route():
+                q.moe_router_topk(lg, top_k, ids=rid, weights=rw)
+            rus = graph_time(torch, lambda: [route() for _ in range(reps)], max(2, args.steps // 3)) / reps
+            wus = graph_time(torch, lambda: [(route(), gate(r), down(r)) for r in range(reps)],
+                             max(2, args.steps // 3)) / reps
+            per["router"] = {"us": round(rus, 3)}
             emit(f"mxfp4 moe 32 experts top-4: gate_up 3584x2048 + down 2048x1792 m={m}", (gbytes + dbytes) / us / 1e3,
                  us, {"per_mode": per, "distinct_experts": distinct, "bytes_per_set": gbytes + dbytes,
-                      "weight_copies": reps})
+                      "weight_copies": reps, "us_with_device_router": round(wus, 3)})
 
 
 def log(args, *a):

@@ -38,6 +38,7 @@ SIGNATURES = {
     "qgemv_q4_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_mxfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "moe_qgemv_topk": (_i, [_i, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i, _i, _vp, _vp]),
+    "moe_router_topk": (_i, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "qg_chain_plan_bytes": (_i64, [_i64]),
     "qg_chain_plan": (_i, [_i, _i, _i64, _vp, _i64, _vp]),
     "qgemv_chain": (_i, [_vp, _vp, _vp]),
@@ -243,6 +244,23 @@ def moe_qgemv_topk(fmt, w_experts, n_experts, n, k, topk_ids, topk_w, x, mode, y
                               _dev_ptr(y, "y"), _stream(stream))
     _check("moe_qgemv_topk", st)
     return y
+
+
+def moe_router_topk(logits, top_k, ids=None, weights=None, stream=None):
+    """Device top-k routing: logits fp32 [m, n_experts] -> (ids int32 [m, top_k],
+    weights fp32 [m, top_k]), ready for moe_qgemv_topk."""
+    torch = _torch()
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be float32 [m, n_experts]")
+    m, n_experts = logits.shape
+    if ids is None:
+        ids = torch.empty((m, top_k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((m, top_k), dtype=torch.float32, device=logits.device)
+    st = lib().moe_router_topk(_dev_ptr(logits, "logits"), m, n_experts, top_k, _dev_ptr(ids, "ids"),
+                               _dev_ptr(weights, "weights"), _stream(stream))
+    _check("moe_router_topk", st)
+    return ids, weights
 
 
 class Chain:

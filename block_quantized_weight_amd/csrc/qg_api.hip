@@ -73,6 +73,93 @@ __global__ void k_unpack(LayoutArgs a, const uint8_t *__restrict__ packed, uint8
         unpack_record(a, packed, canon, r);
 }
 
+// ----------------------------------------------------------------- router
+// Top-k routing on the device, one wavefront per token.  Each logit becomes a
+// 64-bit key: the float's bits in an order-preserving unsigned form (NaN taken
+// as -inf), then the complement of the expert id, so the largest key is the
+// largest logit with the lower id first among equals.  top_k rounds of a
+// wave-wide key maximum (within rows of 16 lanes by DPP rotations, across
+// the four rows by lane reads) pick the experts in order; the softmax of the
+// selected logits is taken in fp32.
+constexpr int ROUTER_MAX_EXPERTS = 1024;
+constexpr int ROUTER_MAX_K = 64;
+
+__device__ __forceinline__ uint32_t order_bits(float f)
+{
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if (f != f) u = 0xFF800000u;                            // NaN ranks as -inf
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_float(uint32_t o)
+{
+    return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ uint64_t max_key(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the wave, returned to every lane.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k)
+{
+    // rows of 16 lanes: rotate by 8, 4, 2, 1 (row_ror:n is DPP control 0x120 + n)
+#define QG_ROR(N)                                                                                          \
+    {                                                                                                      \
+        const uint32_t lo = __builtin_amdgcn_update_dpp(0, (uint32_t)k, 0x120 + (N), 0xF, 0xF, false);     \
+        const uint32_t hi = __builtin_amdgcn_update_dpp(0, (uint32_t)(k >> 32), 0x120 + (N), 0xF, 0xF, false); \
+        k = max_key(k, ((uint64_t)hi << 32) | lo);                                                         \
+    }
+    QG_ROR(8) QG_ROR(4) QG_ROR(2) QG_ROR(1)
+#undef QG_ROR
+    uint64_t r = 0;
+#pragma unroll
+    for (int row = 0; row < 4; ++row) {
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 16 * row);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 16 * row);
+        r = max_key(r, ((uint64_t)hi << 32) | lo);
+    }
+    return r;
+}
+
+template <int NV>
+__global__ __launch_bounds__(64) void k_router(const float *__restrict__ logits, int ne, int topk,
+                                               int32_t *__restrict__ ids, float *__restrict__ w)
+{
+    const int lane = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    const float *lt = logits + t * ne;
+    uint64_t key[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + 64 * i;
+        const float f = lt[e < ne ? e : 0];
+        key[i] = e < ne ? (((uint64_t)order_bits(f) << 32) | (uint32_t)~e) : 0;   // 0: not an expert
+    }
+    int my_id = 0;
+    float my_v = 0.0f;
+    for (int j = 0; j < topk; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < NV; ++i) best = max_key(best, key[i]);
+        best = wave_max_key(best);
+        const int e = (int)~(uint32_t)best;
+        if (lane == j) {
+            my_id = e;
+            my_v = order_float((uint32_t)(best >> 32));
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (key[i] == best) key[i] = 0;                // taken (keys are unique)
+    }
+    const float top = __shfl(my_v, 0, 64);
+    const float ex = lane < topk ? expf(my_v - top) : 0.0f;
+    float sum = ex;
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (lane < topk) {
+        ids[t * topk + lane] = my_id;
+        w[t * topk + lane] = ex / sum;
+    }
+}
+
 // ------------------------------------------------------------ host side
 hipStream_t as_stream(void *s) { return (hipStream_t)s; }
 
@@ -511,6 +598,22 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
                    : fmt == QG_Q4_0 ? launch_moe_q4_0(xt, mode, p, a, maxdistinct, lds, x, y, s)
                                     : launch_moe_mxfp4(xt, mode, p, a, maxdistinct, lds, x, y, s);
     if (e != hipSuccess) return QG_EHIP;
+    return launch_status();
+}
+
+int moe_router_topk(const float *logits, int64_t m, int64_t n_experts, int64_t top_k, int32_t *ids, float *weights,
+                    void *stream)
+{
+    if (!logits || !ids || !weights) return QG_EINVAL;
+    if (m < 1 || n_experts < 1 || top_k < 1 || top_k > n_experts) return QG_EINVAL;
+    if (n_experts > ROUTER_MAX_EXPERTS || top_k > ROUTER_MAX_K || m > 0x7FFFFFFF) return QG_EUNSUPPORTED;
+    if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4)) return QG_EALIGN;
+    const int nv = (int)((n_experts + 63) / 64);
+    void (*f)(const float *, int, int, int32_t *, float *) = nv <= 1 ? k_router<1> : nv <= 2 ? k_router<2>
+                                                             : nv <= 4 ? k_router<4> : nv <= 8 ? k_router<8>
+                                                                                    : k_router<16>;
+    hipLaunchKernelGGL(f, dim3((unsigned)m), dim3(64), 0, as_stream(stream), logits, (int)n_experts, (int)top_k, ids,
+                       weights);
     return launch_status();
 }
 

@@ -184,6 +184,21 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
                    const void *x, int xt, int mode, float *y, void *stream);
 
 /*
+ * Top-k routing on the device, producing moe_qgemv_topk's ids and weights
+ * without a host round trip (imp keeps MoE routing on the device so the
+ * decode graph stays capturable: imp release notes v0.7.0, known issues).
+ * logits: device fp32 [m][n_experts].  ids: device int32 [m][top_k], the
+ * top_k experts of each token by descending logit, a lower expert id first
+ * among equal logits.  weights: device fp32 [m][top_k], the softmax of the
+ * selected logits (exp(l - l_max) / sum, fp32).  NaN logits rank as -inf; a
+ * token whose selected logits are all -inf gets NaN weights.
+ * Limits: 1 <= top_k <= min(n_experts, 64), n_experts <= 1024.  4-byte
+ * aligned pointers; ids and weights are overwritten.
+ */
+int moe_router_topk(const float *logits, int64_t m, int64_t n_experts, int64_t top_k, int32_t *ids, float *weights,
+                    void *stream);
+
+/*
  * A chain of dense products executed in order by one persistent kernel:
  * product i+1 starts only after product i has completed on the whole device
  * (its outputs are visible device-wide), as consecutive projections of one

@@ -151,6 +151,36 @@ def moe(fmt, experts, n_experts, n, k, ids, g, x, xt, mode, rows=None):
     return y, l1
 
 
+def router_topk(logits, top_k):
+    """Top-k routing by definition, in fp64.
+
+    For each token: the top_k experts by descending logit, the lower expert id
+    first among equal logits; weights = softmax over the selected logits
+    (exp(l - l_max) / sum).  The pages route each token to 4 of 32 experts
+    (tests/golden/page_facts.txt); the softmax domain (the selected logits) is
+    a reading.  logits: float32 [m, n_experts], no NaN.  Returns ids int64
+    [m, top_k] and weights float64 [m, top_k].
+    """
+    la = np.asarray(logits, dtype=np.float32)
+    if la.ndim != 2 or not 1 <= top_k <= la.shape[1]:
+        raise ValueError("router_topk: logits [m, n_experts] and 1 <= top_k <= n_experts")
+    if np.isnan(la).any():
+        raise ValueError("router_topk: NaN logit")
+    m, n_experts = la.shape
+    ids = np.empty((m, top_k), dtype=np.int64)
+    w = np.empty((m, top_k), dtype=np.float64)
+    for t in range(m):
+        ranked = sorted(range(n_experts), key=lambda e: (-float(la[t, e]), e))
+        chosen = ranked[:top_k]
+        vals = [float(la[t, e]) for e in chosen]
+        top = vals[0]
+        ex = [np.exp(v - top) for v in vals]
+        total = sum(ex)
+        ids[t] = chosen
+        w[t] = [v / total for v in ex]
+    return ids, w
+
+
 def max_rel_err(yhat, y, l1):
     """max |yhat - y| / l1; where l1 == 0 the output must be exactly 0 (else inf)."""
     yhat = np.asarray(yhat, dtype=np.float64)

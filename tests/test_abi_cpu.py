@@ -186,3 +186,17 @@ def test_dense_path_rule():
         with pytest.raises(q.QGError):
             q.dense_path(*bad)
     assert q.lib().qg_dense_path(q.Q8_0, 1 << 32, 64, q.X_BF16, 1) == -q.QG_EUNSUPPORTED
+
+
+def test_router_argument_validation():
+    """Rejected before any device work (no GPU needed)."""
+    L = q.lib()
+    a = ctypes.c_void_p(1 << 20)
+    ODD = ctypes.c_void_p((1 << 20) + 2)
+    assert L.moe_router_topk(None, 1, 32, 4, a, a, None) == q.QG_EINVAL
+    assert L.moe_router_topk(a, 0, 32, 4, a, a, None) == q.QG_EINVAL
+    assert L.moe_router_topk(a, 1, 32, 0, a, a, None) == q.QG_EINVAL
+    assert L.moe_router_topk(a, 1, 4, 5, a, a, None) == q.QG_EINVAL
+    assert L.moe_router_topk(a, 1, 2048, 4, a, a, None) == q.QG_EUNSUPPORTED
+    assert L.moe_router_topk(a, 1, 128, 65, a, a, None) == q.QG_EUNSUPPORTED
+    assert L.moe_router_topk(ODD, 1, 32, 4, a, a, None) == q.QG_EALIGN

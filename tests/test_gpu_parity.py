@@ -517,3 +517,55 @@ def test_moe_deterministic(dev):
     b = q.moe_qgemv_topk(fmt, wexp, E, n, k, tid, tw, h, q.MOE_DOWN_COMBINE)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ router
+def _router_check(dev, logits_np, top_k):
+    lg = to_dev(logits_np.astype(np.float32), dev)
+    ids, w = q.moe_router_topk(lg, top_k)
+    torch.cuda.synchronize()
+    ref_in = np.where(np.isnan(logits_np), -np.inf, logits_np).astype(np.float32)
+    rid, rw = oracle.router_topk(ref_in, top_k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    got = w.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - rw) <= 1e-6 * rw + 1e-7), np.max(np.abs(got - rw))
+
+
+@pytest.mark.parametrize("m,E,k", [(1, 32, 4), (4, 32, 4), (8, 128, 8), (1000, 64, 2), (3, 1024, 64),
+                                   (5, 7, 7), (2, 1, 1), (6, 100, 1)])
+def test_router_matches_oracle(dev, m, E, k):
+    say(f"router m={m} E={E} k={k}")
+    _router_check(dev, wl.x_f32((m, E), wl.rng_for(76, E, "router")), k)
+
+
+def test_router_ties_and_special_values(dev):
+    """Many equal logits (lower id first), -inf entries and NaN (ranked as -inf)."""
+    say("router ties")
+    rng = np.random.default_rng(77)
+    lg = rng.integers(-2, 3, size=(64, 40)).astype(np.float32)
+    lg[3, :] = 0.0
+    lg[5, ::3] = -np.inf
+    lg[7, 1::4] = np.nan
+    for k in (1, 4, 13, 40):
+        _router_check(dev, lg, k)
+
+
+def test_router_feeds_expert_product(dev):
+    """Device routing straight into the expert product (C4 shapes): ids and
+    weights never leave the device; the result matches the oracle routed on
+    the same logits."""
+    c = wl.CONFIGS[4]
+    E, top_k, m = c["n_experts"], c["top_k"], 4
+    fmt, n, k = q.MXFP4, 2048, 1792
+    say("router -> moe down")
+    logits = wl.x_f32((m, E), wl.rng_for(78, 0, "router"))
+    ids, w = q.moe_router_topk(to_dev(logits, dev), top_k)
+    experts = _experts(fmt, E, n, k, 78)
+    wexp = _experts_dev(fmt, experts, E, n, k, dev)
+    h = draw_x((m, top_k, k), oracle.X_BF16, 78, 0, "h")
+    y = q.moe_qgemv_topk(fmt, wexp, E, n, k, ids, w, x_dev(h, oracle.X_BF16, dev), q.MOE_DOWN_COMBINE)
+    torch.cuda.synchronize()
+    rid, rw = oracle.router_topk(logits, top_k)
+    ref, l1 = oracle.moe(fmt, experts, E, n, k, rid.astype(np.int32), rw.astype(np.float32), h, oracle.X_BF16,
+                         q.MOE_DOWN_COMBINE)
+    assert oracle.max_rel_err(y.cpu().numpy(), ref, l1) <= TOL

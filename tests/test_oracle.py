@@ -300,3 +300,42 @@ def test_oracle_rejects_bad_arguments():
         oracle.gemv(oracle.Q8_0, blk, 1, 32, np.ones((1, 32), np.float32), 7)
     with pytest.raises(ValueError):
         oracle.gemv(oracle.Q8_0, blk, 1, 32, np.ones((1, 32), np.float32), oracle.X_F32, rows=[1])
+
+
+# ------------------------------------------------------------------ router
+def test_router_hand_example_with_tie():
+    """logits (0.5, 2, 2, -1, 3), top 3: expert 4 first, then the tie 2.0
+    resolved to the lower id (1 before 2); weights e^0, e^-1, e^-1 normalised."""
+    ids, w = oracle.router_topk(np.array([[0.5, 2.0, 2.0, -1.0, 3.0]], dtype=np.float32), 3)
+    assert ids.tolist() == [[4, 1, 2]]
+    den = 1.0 + 2.0 * math.exp(-1.0)
+    assert np.allclose(w[0], [1.0 / den, math.exp(-1.0) / den, math.exp(-1.0) / den], rtol=1e-15, atol=0)
+
+
+def test_router_closed_forms():
+    ids, w = oracle.router_topk(np.zeros((2, 6), dtype=np.float32), 4)        # all equal
+    assert ids.tolist() == [[0, 1, 2, 3]] * 2 and np.all(w == 0.25)
+    ids, w = oracle.router_topk(np.array([[1.0, -np.inf, 7.0]], dtype=np.float32), 1)
+    assert ids.tolist() == [[2]] and w.tolist() == [[1.0]]
+    ids, w = oracle.router_topk(np.array([[0.0, -np.inf, np.log(3.0)]], dtype=np.float32), 3)
+    assert ids.tolist() == [[2, 0, 1]]
+    assert abs(w[0, 0] - 0.75) < 1e-7 and abs(w[0, 1] - 0.25) < 1e-7 and w[0, 2] == 0.0
+    with pytest.raises(ValueError):
+        oracle.router_topk(np.array([[0.0, np.nan]], dtype=np.float32), 1)
+
+
+def test_router_against_exhaustive_search():
+    """Small cases with repeated values: the chosen list is the lexicographic
+    maximum of (logit, -id) over all ordered selections."""
+    import itertools
+    rng = np.random.default_rng(5)
+    for trial in range(200):
+        n_experts = int(rng.integers(1, 7))
+        top_k = int(rng.integers(1, n_experts + 1))
+        logits = rng.integers(-2, 3, size=(1, n_experts)).astype(np.float32)
+        ids, w = oracle.router_topk(logits, top_k)
+        best = max(itertools.permutations(range(n_experts), top_k),
+                   key=lambda p: [(float(logits[0, e]), -e) for e in p])
+        assert ids[0].tolist() == list(best)
+        assert abs(w.sum() - 1.0) < 1e-15
+        assert np.all(np.diff(w[0]) <= 0)
