@@ -68,7 +68,18 @@ struct ChainHdr {
     int64_t lds;
 };
 
-template <int FMT, bool DOT> struct ChainBatch { static constexpr int U = FMT == QG_Q8_0 ? 4 : (DOT ? 8 : 4); };
+// Steps per weight batch.  Two batches stay live across a whole pass (one in
+// flight, one computing) beside the control wave's staging registers, so the
+// wider compute variants (fp32 activations, more than 4 tokens) take smaller
+// batches to stay within the 168 registers this launch shape allows without
+// spilling (Q4_0 with fp32 activations and one token spills even at 2).
+template <int FMT, bool XBF16, bool DOT, int M> struct ChainBatch {
+    static constexpr int U = !XBF16 && FMT == QG_Q4_0 && M == 1 ? 1
+                             : !XBF16 || (FMT == QG_Q8_0 && M > 4) ? 2
+                             : FMT == QG_Q8_0                      ? 4
+                             : DOT                                 ? (M > 4 ? 4 : 8)
+                                                                   : 4;
+};
 
 // LDS carve-up of one link: staged activations, Q4_0 block sums, split-K
 // partials, and a double-buffered block of finished rows for the control wave.
@@ -129,7 +140,7 @@ template <int M, int FMT, bool XBF16, bool DOT>
 __device__ __forceinline__ void chain_stage(const Geom &g, const void *x, uint4 *xs, float *corr)
 {
     constexpr int QPB = DOT ? 4 : 8;
-    constexpr int CH = 2;
+    constexpr int CH = XBF16 ? 2 : 1;       // blocks per lane in flight (fp32 blocks are twice the registers)
     constexpr int NLD = XBF16 ? 4 : 8;       // 16-byte loads per block
     const int lane = threadIdx.x & 63;
     const int total = M * g.wblk;
@@ -277,7 +288,7 @@ __device__ __forceinline__ bool chain_pass_loop(const Geom &g, const PassWork &w
 template <int FMT, bool XBF16, bool DOT, int M>
 __global__ __launch_bounds__(CTPB) void k_chain(const ChainLink *__restrict__ links, int nlinks)
 {
-    using E = Engine<FMT, XBF16, DOT, M, ChainBatch<FMT, DOT>::U>;
+    using E = Engine<FMT, XBF16, DOT, M, ChainBatch<FMT, XBF16, DOT, M>::U>;
     using LdsT = ChainLds<M, DOT, FMT>;
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ uint32_t s_base;
