@@ -1,0 +1,116 @@
+"""Graph capture: every kernel family recorded in one HIP graph (through
+torch.cuda.CUDAGraph), replayed several times with the program's own eager
+work and synchronisations in between; each replay must reproduce the eager
+results bit for bit (all kernels are deterministic), and replays must read
+inputs rewritten in place between them."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+torch = pytest.importorskip("torch")
+q = pytest.importorskip("block_quantized_weight_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    q.lib()
+    return torch.device("cuda:0")
+
+
+def _bf16(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def _packed(fmt, n, k, config, matrix, dev):
+    canon = wl.blocks_for(fmt, n, k, config=config, matrix=matrix)
+    return q.pack(fmt, torch.from_numpy(canon.reshape(-1)).to(dev), n, k)
+
+
+def test_graph_replays_match_eager(dev):
+    print("graph capture", flush=True)
+    # dense, vector path: Q8_0, one token
+    n1, k1 = 6144, 2560
+    w1 = _packed(q.Q8_0, n1, k1, 90, 0, dev)
+    x1 = _bf16(wl.x_bf16_bits((1, k1), wl.rng_for(90, 0, "x")), dev)
+    y1 = torch.empty((1, n1), device=dev)
+    # dense, matrix cores: Q4_0, four tokens
+    n2, k2 = 5000, 2048
+    w2 = _packed(q.Q4_0, n2, k2, 90, 1, dev)
+    x2 = _bf16(wl.x_bf16_bits((4, k2), wl.rng_for(90, 1, "x")), dev)
+    y2 = torch.empty((4, n2), device=dev)
+    assert q.dense_path(q.Q4_0, n2, k2, q.X_BF16, 4) == q.PATH_MFMA
+    # experts: router -> gate_up and down-combine (MXFP4, 16 experts, top-4, 2 tokens)
+    fmt, E, top_k, m = q.MXFP4, 16, 4, 2
+    gn, gk, dn, dk = 512, 1024, 1024, 512
+    gpb, dpb = q.packed_bytes(fmt, gn, gk), q.packed_bytes(fmt, dn, dk)
+    ge = torch.empty(E * gpb, dtype=torch.uint8, device=dev)
+    de = torch.empty(E * dpb, dtype=torch.uint8, device=dev)
+    for e in range(E):
+        q.pack(fmt, torch.from_numpy(wl.blocks_for(fmt, gn, gk, config=91, matrix=2 * e).reshape(-1)).to(dev),
+               gn, gk, out=ge[e * gpb:(e + 1) * gpb])
+        q.pack(fmt, torch.from_numpy(wl.blocks_for(fmt, dn, dk, config=91, matrix=2 * e + 1).reshape(-1)).to(dev),
+               dn, dk, out=de[e * dpb:(e + 1) * dpb])
+    logits = torch.from_numpy(wl.x_f32((m, E), wl.rng_for(91, 0, "router"))).to(dev)
+    xg = _bf16(wl.x_bf16_bits((m, gk), wl.rng_for(91, 0, "x")), dev)
+    hd = _bf16(wl.x_bf16_bits((m, top_k, dk), wl.rng_for(91, 0, "h")), dev)
+    ids = torch.empty((m, top_k), dtype=torch.int32, device=dev)
+    gw = torch.empty((m, top_k), device=dev)
+    yg = torch.empty((m, top_k, gn), device=dev)
+    yd = torch.empty((m, dn), device=dev)
+
+    def step():
+        q.qgemv(q.Q8_0, w1, n1, k1, x1, y=y1)
+        q.qgemv(q.Q4_0, w2, n2, k2, x2, y=y2)
+        q.moe_router_topk(logits, top_k, ids=ids, weights=gw)
+        q.moe_qgemv_topk(fmt, ge, E, gn, gk, ids, gw, xg, q.MOE_GATE_UP, y=yg)
+        q.moe_qgemv_topk(fmt, de, E, dn, dk, ids, gw, hd, q.MOE_DOWN_COMBINE, y=yd)
+
+    outs = (y1, y2, ids, gw, yg, yd)
+
+    def eager():
+        step()
+        torch.cuda.synchronize()
+        return [o.clone() for o in outs]
+
+    ref = eager()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    other_w = _packed(q.Q8_0, 256, 512, 92, 0, dev)
+    other_x = _bf16(wl.x_bf16_bits((1, 512), wl.rng_for(92, 0, "x")), dev)
+    for rep in range(5):
+        for o in outs:
+            o.fill_(-1 if o.dtype == torch.int32 else float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), rep
+        q.qgemv(q.Q8_0, other_w, 256, 512, other_x)      # eager work between replays
+        torch.cuda.synchronize()
+
+    # new inputs, written in place: replays see them
+    x1.copy_(_bf16(wl.x_bf16_bits((1, k1), wl.rng_for(90, 5, "x")), dev))
+    logits.copy_(torch.from_numpy(wl.x_f32((m, E), wl.rng_for(91, 5, "router"))).to(dev))
+    torch.cuda.synchronize()
+    ref2 = eager()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref2):
+            assert torch.equal(a, b), rep
+    assert not torch.equal(ref2[0], ref[0])
+    rid, _ = oracle.router_topk(logits.cpu().numpy(), top_k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
