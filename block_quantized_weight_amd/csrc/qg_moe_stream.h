@@ -41,32 +41,44 @@ struct SlotMap {
     __device__ __forceinline__ int count() const { return n; }
 };
 
-// Splits the distinct experts' slots into items of at most ms slots, in
-// ascending expert order and ascending slot order.  Called by the whole
-// workgroup after distinct_experts; ends with a barrier.
-__device__ __forceinline__ void build_items(const int *s_ids, const int *s_list, int nexp, int nslots, int ms,
-                                            MoeItems *it)
+// The work list, built by wave 0 from the routing ids held in registers
+// (lane s holds slot s's id): the distinct valid experts in ascending order,
+// each expert's slots split into items of at most ms slots in ascending slot
+// order.  Two passes of lane reads (v_readlane) in which every lane works out
+// its own slot's place -- one over the slots, one over the distinct experts
+// -- so no step waits on LDS.  The caller synchronises afterwards.
+__device__ __forceinline__ void route_items(int id, int nslots, int n_experts, int ms, MoeItems *it)
 {
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        int ni = 0;
-        for (int d = 0; d < nexp; ++d) {
-            const int e = s_list[d];
-            const bool match = lane < nslots && s_ids[lane] == e;
-            const uint64_t mask = __ballot(match);
-            const int cnt = __popcll(mask);
-            const int rank = __popcll(mask & ((1ull << lane) - 1));
-            for (int c0 = 0; c0 < cnt; c0 += ms, ++ni) {
-                if (match && rank >= c0 && rank < c0 + ms) it->s[ni][rank - c0] = lane;
-                if (lane == 0) {
-                    it->e[ni] = e;
-                    it->n[ni] = min(ms, cnt - c0);
-                }
-            }
-        }
-        if (lane == 0) it->count = ni;
+    const int lane = threadIdx.x & 63;
+    const bool valid = lane < nslots && id >= 0 && id < n_experts;
+    const int e = valid ? id : 0x7FFFFFFF;
+    // pass over the slots: slots of the same expert before this one, and in all
+    int before = 0, same = 0;
+    for (int q = 0; q < nslots; ++q) {
+        const bool eq = __builtin_amdgcn_readlane(e, q) == e;
+        same += eq ? 1 : 0;
+        before += (eq && q < lane) ? 1 : 0;
     }
-    __syncthreads();
+    const bool first = valid && before == 0;
+    const int nit = (same + ms - 1) / ms;                // items of this lane's expert
+    // pass over the distinct experts: items of smaller experts come first
+    int base = 0, total = 0;
+    for (uint64_t b = __ballot(first); b; b &= b - 1) {
+        const int q = __builtin_ctzll(b);
+        const int eq = __builtin_amdgcn_readlane(e, q);
+        const int nq = __builtin_amdgcn_readlane(nit, q);
+        base += eq < e ? nq : 0;
+        total += nq;
+    }
+    if (valid) {
+        const int item = base + before / ms, pos = before - (before / ms) * ms;
+        it->s[item][pos] = lane;
+        if (pos == 0) {
+            it->e[item] = e;
+            it->n[item] = min(ms, same - before);
+        }
+    }
+    if (lane == 0) it->count = total;
 }
 
 // Where a wave's tile of one item lives.
@@ -123,9 +135,6 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
 {
     using E = Engine<FMT, XBF16, DOT, MS>;
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ int s_ids[64];
-    __shared__ int s_list[64];
-    __shared__ int s_count;
     __shared__ MoeItems it;
     constexpr int QPB = x_quads(FMT, DOT);
     const int nslots = a.m * a.top_k;
@@ -138,10 +147,34 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
     const int tsub = wave / IS, ipart = wave - tsub * IS;
     const int rsub = lane >> g.lsh, slot = lane & (g.L - 1);
 
-    distinct_experts(a.ids, nslots, a.n_experts, s_ids, s_list, &s_count);
-    build_items(s_ids, s_list, s_count, nslots, MS, &it);
-    const int ni = it.count;
+    // Activations do not depend on the routing: every thread issues the loads
+    // of its first PF staging units before the ids are even known.  (LDS
+    // already limits this kernel to one workgroup per compute unit, so the
+    // registers cost no occupancy.)
+    constexpr int PF = XBF16 ? 4 : 2;
+    constexpr int NLD = XBF16 ? 4 : 8;
+    const int total = nrows * g.wblk;
+    auto unit_src = [&](int idx) {
+        const int r = idx / g.wblk, bl = idx - r * g.wblk;
+        return (const uint8_t *)x + ((int64_t)r * g.k + (int64_t)min(bl, g.nb - 1) * QK) * (XBF16 ? 2 : 4);
+    };
+    const int my_id = a.ids[min(lane, nslots - 1)];    // lanes past the slots are ignored by the routing
+    // keep this load ahead of the activation loads (the memory counter is in
+    // order, so the routing would otherwise wait for all of them)
+    __builtin_amdgcn_sched_barrier(0);
+    // a fixed number of loads (units past the end repeat the last one), so
+    // the wait for the ids below does not also wait for these
+    uint4 pre[PF][8];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const uint8_t *src = unit_src(min((int)threadIdx.x + p * (int)blockDim.x, total - 1));
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) pre[p][i] = ld_global16(src + 16 * i);
+    }
 
+    if (wave == 0) route_items(my_id, nslots, a.n_experts, MS, &it);
+    __syncthreads();
+    const int ni = it.count;
     const int tile = blockIdx.x * g.tpi + tsub;
     const int tl = tile < g.tiles ? tile : 0;
     const int nsteps = (tile < g.tiles && ipart < ni) ? g.S : 0;
@@ -163,32 +196,31 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
 
     // stage every activation row of the call (row r = token for gate_up,
     // slot for down), one window over all of K
-    {
-        const int total = nrows * g.wblk;
-        for (int idx = threadIdx.x; idx < total; idx += (int)blockDim.x) {
-            const int r = idx / g.wblk, bl = idx - r * g.wblk;
-            uint4 raw[8], q[8];
-            float av = 0.0f;
-            if (bl < g.nb) {
-                const int64_t off = (int64_t)r * g.k + (int64_t)bl * QK;
-                if (XBF16) {
-                    const uint4 *src = (const uint4 *)((const uint16_t *)x + off);
+    auto stage_unit = [&](int idx, const uint4 (&raw)[8]) {
+        const int r = idx / g.wblk, bl = idx - r * g.wblk;
+        uint4 q[8];
+        float av = 0.0f;
+        if (bl < g.nb) {
+            av = stage_block<FMT, XBF16, DOT>(raw, q);
+        } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) raw[i] = ld_global16(src + i);
-                } else {
-                    const uint4 *src = (const uint4 *)((const float *)x + off);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) raw[i] = ld_global16(src + i);
-                }
-                av = stage_block<FMT, XBF16, DOT>(raw, q);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) q[i] = make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < QPB; ++i) xs[(r * QPB + i) * g.wblk + bl] = q[i];
-            if (x_aux(FMT)) corr[r * g.wblk + bl] = av;
+            for (int i = 0; i < 8; ++i) q[i] = make_uint4(0, 0, 0, 0);
         }
+#pragma unroll
+        for (int i = 0; i < QPB; ++i) xs[(r * QPB + i) * g.wblk + bl] = q[i];
+        if (x_aux(FMT)) corr[r * g.wblk + bl] = av;
+    };
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const int idx = (int)threadIdx.x + p * (int)blockDim.x;
+        if (idx < total) stage_unit(idx, pre[p]);
+    }
+    for (int idx = (int)threadIdx.x + PF * (int)blockDim.x; idx < total; idx += (int)blockDim.x) {
+        uint4 raw[8];
+        const uint8_t *src = unit_src(idx);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) raw[i] = ld_global16(src + 16 * i);
+        stage_unit(idx, raw);
     }
     __syncthreads();
 
