@@ -22,6 +22,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 Q8_0, Q4_0, MXFP4 = 0, 1, 2
 X_F32, X_BF16 = 0, 1
 MOE_GATE_UP, MOE_DOWN = 0, 1
+ACT_NONE, ACT_SWIGLU = 0, 1
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17}
 
 
@@ -192,5 +193,109 @@ def max_rel_err(yhat, y, l1):
     nz = ~zero
     err[nz] = diff[nz] / l1[nz]
     err[zero & (yhat != 0)] = np.inf
+    err[~np.isfinite(yhat)] = np.inf
+    return float(err.max()) if err.size else 0.0
+
+
+# ------------------------------------------------------------ fused steps
+# The decode step around a quantized product: RMS normalisation of the
+# activations before it, and a gated activation (SwiGLU) or a residual add
+# after it.  The pages report such fusions (imp release notes v0.4: a fused
+# RMSNorm-gated + SiLU kernel; Imparo README, "Bonsai CUDA Validation": an
+# RMS/Add tail fusion reviewed and deferred; "Design Rules": fusion by hand
+# where a measurement justifies it) but define neither operation; the
+# definitions below are the published ones (RMSNorm: Zhang and Sennrich,
+# "Root Mean Square Layer Normalization", 2019; SwiGLU: Shazeer, "GLU
+# Variants Improve Transformer", 2020, with SiLU v * sigmoid(v)).  The
+# pages' fused matrices pair a gate_up product of N = 2F rows with a down
+# product of K = F columns; the reading taken is gate rows [0, F), up rows
+# [F, 2F).  Everything is fp64 and follows the definitions in order.
+
+
+def x_values(x, xt):
+    """Activations as float64 [m, k]: fp32 as is, bf16 bit patterns as the
+    upper half of an fp32 (exact)."""
+    if xt == X_F32:
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << 16
+    return bits.view(np.float32).astype(np.float64)
+
+
+def silu(v):
+    """SiLU(v) = v / (1 + exp(-v)), fp64 (exp overflow gives the limit 0)."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def rmsnorm(x, gamma, eps):
+    """RMSNorm of each row of x (float64 [m, k]): x * r * gamma with
+    r = 1 / sqrt(mean(x^2) + eps).  Returns (normalised x, r [m])."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(gamma, dtype=np.float32).astype(np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=1) + float(eps))
+    return x * r[:, None] * g[None, :], r
+
+
+def _row_weights(fmt, blocks, n, k, rows):
+    """Decoded weights of the given rows, float64 [len(rows), k]."""
+    b = _blocks(fmt, blocks, n, k).reshape(n, -1)
+    sub = np.ascontiguousarray(b[np.asarray(rows, dtype=np.int64)])
+    return decode(fmt, sub.reshape(-1), len(rows), k)
+
+
+def dense_fused(fmt, blocks, n, k, x, xt, norm_weight=None, eps=0.0, act=ACT_NONE, residual=None, rows=None):
+    """Fused dense step, by definition in fp64:
+        x' = RMSNorm(x) if norm_weight is given, else x
+        z  = W x'                          (all n rows)
+        o  = SiLU(z[:F]) * z[F:]           if act == ACT_SWIGLU (F = n / 2)
+             z                             otherwise
+        o += residual                      if given ([m, n_out], fp32)
+    Returns (o, scale) as float64 [m, nrows] over the output rows `rows`
+    (default all n_out).  scale bounds the output's sensitivity to fp32
+    rounding of the products: L1 = sum |w x'| of the row without the gate.
+    With it, products off by |dg| <= e * L1_gate and |du| <= e * L1_up
+    (e <= 2e-3) move o by at most e * scale with
+        scale = 1.1 * L1_gate * (|u| + 2e-3 * L1_up) + |SiLU(g)| * L1_up,
+    since |SiLU'| < 1.1 everywhere (the last term of the first product is
+    the cross term dg * du)."""
+    xv = x_values(x, xt).reshape(-1, k)
+    if norm_weight is not None:
+        xv, _ = rmsnorm(xv, norm_weight, eps)
+    if act == ACT_SWIGLU:
+        if n % 2:
+            raise ValueError("SwiGLU needs an even row count")
+        n_out = n // 2
+    else:
+        n_out = n
+    r = np.arange(n_out) if rows is None else np.asarray(rows, dtype=np.int64)
+    if act == ACT_SWIGLU:
+        wg = _row_weights(fmt, blocks, n, k, r)
+        wu = _row_weights(fmt, blocks, n, k, r + n_out)
+        g, l1g = xv @ wg.T, np.abs(xv) @ np.abs(wg).T
+        u, l1u = xv @ wu.T, np.abs(xv) @ np.abs(wu).T
+        o = silu(g) * u
+        scale = 1.1 * l1g * (np.abs(u) + 2e-3 * l1u) + np.abs(silu(g)) * l1u
+    else:
+        w = _row_weights(fmt, blocks, n, k, r)
+        o, scale = xv @ w.T, np.abs(xv) @ np.abs(w).T
+    if residual is not None:
+        o = o + np.asarray(residual, dtype=np.float32).astype(np.float64).reshape(-1, n_out)[:, r]
+    return o, scale
+
+
+def fused_err(yhat, o, scale, y_bf16=False):
+    """max over outputs of (|yhat - o| - out_rel * |o|) / scale: the product
+    error against its rounding scale once the output's own rounding is
+    allowed for (out_rel = 2^-8 for bf16 outputs, 2^-20 for fp32, which also
+    covers the few ulp of exp and the division in SiLU), the remainder
+    clamped at 0.  Where scale == 0 the remainder must be 0; non-finite
+    outputs give inf."""
+    yhat = np.asarray(yhat, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    scale = np.asarray(scale, dtype=np.float64)
+    out_rel = 2.0 ** -8 if y_bf16 else 2.0 ** -20
+    rest = np.maximum(np.abs(yhat - o) - out_rel * np.abs(o), 0.0)
+    err = np.where(scale > 0, rest / np.where(scale > 0, scale, 1.0), np.where(rest > 0, np.inf, 0.0))
     err[~np.isfinite(yhat)] = np.inf
     return float(err.max()) if err.size else 0.0

@@ -339,3 +339,119 @@ def test_router_against_exhaustive_search():
         assert ids[0].tolist() == list(best)
         assert abs(w.sum() - 1.0) < 1e-15
         assert np.all(np.diff(w[0]) <= 0)
+
+
+# ------------------------------------------------------- fused steps (SwiGLU, RMSNorm, residual)
+def test_silu_against_torch_and_identities():
+    torch = pytest.importorskip("torch")
+    v = np.concatenate([np.linspace(-60, 60, 2401), [0.0, 1e-300, -1e-300, 700.0, -700.0, 1e4, -1e4]])
+    ref = torch.nn.functional.silu(torch.from_numpy(v)).numpy()
+    got = oracle.silu(v)
+    assert np.all(np.abs(got - ref) <= 4e-16 * np.maximum(np.abs(ref), 1e-300))
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1e4) == 1e4 and oracle.silu(-1e4) == 0.0            # the limits
+    w = np.linspace(-30, 30, 601)
+    assert np.allclose(oracle.silu(-w), oracle.silu(w) - w, rtol=0, atol=1e-13)   # sigma(-v) = 1 - sigma(v)
+    assert abs(oracle.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+    # |SiLU'| < 1.1 (the error scale of the fused oracle rests on it)
+    h = 1e-6
+    d = (oracle.silu(w + h) - oracle.silu(w - h)) / (2 * h)
+    assert np.max(np.abs(d)) < 1.1 and np.max(d) > 1.09
+
+
+def test_rmsnorm_against_torch_and_closed_forms():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((3, 256)) * np.array([[1.0], [1e-3], [50.0]])
+    gamma = rng.uniform(0.5, 1.5, 256).astype(np.float32)
+    for eps in (0.0, 1e-6, 1e-2):
+        got, r = oracle.rmsnorm(x, gamma, eps)
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (256,),
+                                           torch.from_numpy(gamma.astype(np.float64)), eps).numpy()
+        assert np.allclose(got, ref, rtol=1e-14, atol=0)
+        assert np.allclose(r, [1.0 / math.sqrt(math.fsum(row * row) / 256 + eps) for row in x], rtol=1e-15)
+    # a constant row c with eps = 0 normalises to sign(c) * gamma exactly; scaling x changes nothing
+    c = np.full((2, 64), [[-3.0], [0.5]])
+    got, _ = oracle.rmsnorm(c, np.full(64, 2.0, np.float32), 0.0)
+    assert np.array_equal(got, np.full((2, 64), [[-2.0], [2.0]]))
+    a, _ = oracle.rmsnorm(x, gamma, 0.0)
+    b, _ = oracle.rmsnorm(1024.0 * x, gamma, 0.0)
+    assert np.allclose(a, b, rtol=1e-14, atol=0)
+
+
+def test_x_values_decodes_bf16_and_fp32():
+    bits = np.array([[0x3F80, 0xC000, 0x0001, 0x7F7F]], dtype=np.uint16)
+    want = [1.0, -2.0, struct.unpack("<f", struct.pack("<I", 0x00010000))[0],
+            struct.unpack("<f", struct.pack("<I", 0x7F7F0000))[0]]
+    assert np.array_equal(oracle.x_values(bits, oracle.X_BF16)[0], want)
+    f = np.array([[1.5, -0.1]], dtype=np.float32)
+    assert np.array_equal(oracle.x_values(f, oracle.X_F32), f.astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", [oracle.Q8_0, oracle.Q4_0, oracle.MXFP4])
+def test_dense_fused_reduces_to_the_c_product(fmt):
+    n, k, m = 96, 256, 3
+    blocks = wl.blocks_for(fmt, n, k, config=94, matrix=fmt)
+    x = wl.x_bf16_bits((m, k), wl.rng_for(94, fmt, "x"))
+    y, l1 = oracle.gemv(fmt, blocks, n, k, x, oracle.X_BF16)            # the C loop
+    o, scale = oracle.dense_fused(fmt, blocks, n, k, x, oracle.X_BF16)   # decode + numpy product
+    assert np.max(np.abs(o - y) / l1) < 1e-13 and np.allclose(scale, l1, rtol=1e-13)
+    # SwiGLU: gate rows first, up rows second
+    torch = pytest.importorskip("torch")
+    o, _ = oracle.dense_fused(fmt, blocks, n, k, x, oracle.X_BF16, act=oracle.ACT_SWIGLU)
+    g, u = y[:, : n // 2], y[:, n // 2:]
+    want = torch.nn.functional.silu(torch.from_numpy(g)).numpy() * u
+    assert np.allclose(o, want, rtol=1e-12, atol=1e-12 * np.max(l1))
+    # residual: added after everything else
+    res = wl.x_f32((m, n // 2), wl.rng_for(94, fmt, "res"))
+    o2, _ = oracle.dense_fused(fmt, blocks, n, k, x, oracle.X_BF16, act=oracle.ACT_SWIGLU, residual=res)
+    assert np.allclose(o2 - res.astype(np.float64), o, rtol=0, atol=1e-12 * np.max(np.abs(o2)))
+    # row subsets
+    rows = np.array([47, 0, 5])
+    o3, s3 = oracle.dense_fused(fmt, blocks, n, k, x, oracle.X_BF16, act=oracle.ACT_SWIGLU, residual=res, rows=rows)
+    _, s2 = oracle.dense_fused(fmt, blocks, n, k, x, oracle.X_BF16, act=oracle.ACT_SWIGLU, residual=res)
+    assert np.array_equal(o3, o2[:, rows]) and np.array_equal(s3, s2[:, rows])
+
+
+def test_dense_fused_norm_is_a_scaled_product():
+    # with gamma a power of two, x * gamma is exact in fp32, so the C product of
+    # x * gamma times r (computed here with math.fsum) must give the same rows
+    fmt, n, k, m = oracle.Q8_0, 64, 512, 2
+    blocks = wl.blocks_for(fmt, n, k, config=95, matrix=0)
+    x = wl.x_f32((m, k), wl.rng_for(95, 0, "x"))
+    gamma = np.where(np.arange(k) % 3 == 0, 0.5, 4.0).astype(np.float32)
+    eps = 1e-5
+    o, scale = oracle.dense_fused(fmt, blocks, n, k, x, oracle.X_F32, norm_weight=gamma, eps=eps)
+    y, l1 = oracle.gemv(fmt, blocks, n, k, (x * gamma).astype(np.float32), oracle.X_F32)
+    xd = x.astype(np.float64)
+    r = np.array([1.0 / math.sqrt(math.fsum(row * row) / k + eps) for row in xd])
+    assert np.max(np.abs(o - r[:, None] * y) / (r[:, None] * l1)) < 1e-13
+    assert np.allclose(scale, r[:, None] * l1, rtol=1e-13)
+
+
+def test_fused_verdict_catches_plausible_mistakes():
+    fmt, n, k, m = oracle.Q4_0, 128, 512, 2
+    blocks = wl.blocks_for(fmt, n, k, config=96, matrix=0)
+    # activations with an RMS far from 1, so that the normalisation matters
+    x = (5.0 * wl.x_f32((m, k), wl.rng_for(96, 0, "x"))).astype(np.float32)
+    gamma = wl.x_f32((1, k), wl.rng_for(96, 0, "gamma"))[0]
+    o, scale = oracle.dense_fused(fmt, blocks, n, k, x, oracle.X_F32, norm_weight=gamma, eps=1e-6,
+                                  act=oracle.ACT_SWIGLU)
+    assert oracle.fused_err(o, o, scale) == 0.0
+    # fp32 rounding of the output passes; bf16 rounding passes only under the bf16 allowance
+    assert oracle.fused_err(o.astype(np.float32), o, scale) == 0.0
+    ob = ((o.astype(np.float32).view(np.uint32) + 0x8000) & 0xFFFF0000).view(np.float32)
+    assert oracle.fused_err(ob, o, scale, y_bf16=True) == 0.0
+    # gate and up swapped, the normalisation dropped, gamma dropped: each fails by
+    # more than ten times the 2e-3 tolerance
+    xv = oracle.x_values(x, oracle.X_F32)
+    _, r = oracle.rmsnorm(xv, gamma, 1e-6)
+    yn, _ = oracle.dense_fused(fmt, blocks, n, k, x, oracle.X_F32, norm_weight=gamma, eps=1e-6)
+    swapped = oracle.silu(yn[:, n // 2:]) * yn[:, : n // 2]
+    assert oracle.fused_err(swapped, o, scale) > 10 * 2e-3
+    no_norm = oracle.silu(yn[:, : n // 2] / r[:, None]) * (yn[:, n // 2:] / r[:, None])
+    assert oracle.fused_err(no_norm, o, scale) > 10 * 2e-3
+    ones = np.ones(k, dtype=np.float32)
+    no_gamma, _ = oracle.dense_fused(fmt, blocks, n, k, x, oracle.X_F32, norm_weight=ones, eps=1e-6,
+                                     act=oracle.ACT_SWIGLU)
+    assert oracle.fused_err(no_gamma, o, scale) > 10 * 2e-3

@@ -8,7 +8,7 @@ oracle and the HIP path cannot agree with each other through it.
 from .gen import (  # noqa: F401
     FMT_Q8_0, FMT_Q4_0, FMT_MXFP4, FMT_NAMES, BLOCK_BYTES, QK,
     rng_for, q8_0_blocks, q4_0_blocks, mxfp4_blocks, blocks_for,
-    x_f32, x_bf16_bits, f32_to_bf16_bits_rne, router_topk,
+    x_f32, x_bf16_bits, f32_to_bf16_bits_rne, router_topk, norm_weight_f32,
     encode_q8_0, encode_q4_0, encode_mxfp4,
 )
 from .configs import CONFIGS, c2_sweep_shapes  # noqa: F401

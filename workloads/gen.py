@@ -21,7 +21,7 @@ FMT_Q8_0, FMT_Q4_0, FMT_MXFP4 = 0, 1, 2
 FMT_NAMES = {FMT_Q8_0: "q8_0", FMT_Q4_0: "q4_0", FMT_MXFP4: "mxfp4"}
 BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4_0: 18, FMT_MXFP4: 17}
 
-ROLES = {"codes": 0, "scales": 1, "x": 2, "router": 3, "h": 4}
+ROLES = {"codes": 0, "scales": 1, "x": 2, "router": 3, "h": 4, "gamma": 5, "res": 6}
 
 
 def rng_for(config, matrix, role):
@@ -114,6 +114,12 @@ def x_f32(shape, rng):
 
 def x_bf16_bits(shape, rng):
     return f32_to_bf16_bits_rne(x_f32(shape, rng))
+
+
+def norm_weight_f32(k, rng, lo=0.25, hi=2.0):
+    """RMSNorm weights: fp32 uniform in [lo, hi] (positive, around 1, as a
+    trained norm's are)."""
+    return rng.uniform(lo, hi, size=k).astype(np.float32)
 
 
 def router_topk(m, n_experts, top_k, rng):
