@@ -46,10 +46,11 @@ def parse():
     ap.add_argument("--no-events", action="store_true", help="skip the roofline / per-shape timing pass")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", choices=["c2", "c0", "c1", "c3", "c4"], default="c2",
-                    help="c2: the full Q8_0 decode sweep (the headline line); c0/c1/c3/c4: the other workloads, "
-                         "each timed over >= 1 GiB of distinct weight copies so the device-side cache cannot serve "
-                         "repeated reads")
+    ap.add_argument("--workload", choices=["c2", "c2f", "c0", "c1", "c3", "c4"], default="c2",
+                    help="c2: the full Q8_0 decode sweep (the headline line); c2f: the same sweep with the decode "
+                         "step's neighbours fused in (RMSNorm, SwiGLU, residual; qgemv_fused) next to the plain "
+                         "sweep; c0/c1/c3/c4: the other workloads, each timed over >= 1 GiB of distinct weight "
+                         "copies so the device-side cache cannot serve repeated reads")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -269,13 +270,117 @@ def recorded_traffic():
     return float(m_val.group(1))
 
 
+def run_fused_sweep(args, torch, q, dev, shapes, wviews, xs, ys, fmt, config):
+    """The decode sweep with its neighbours fused in, against the plain sweep.
+
+    Dataflow per layer (attention itself is not part of the path; its output
+    is a fixed synthetic bf16 vector per layer):
+        qkv     = W_qkv RMSNorm(h)                        (fp32 out)
+        h       = W_o attn + h                            (residual, in place)
+        a       = SwiGLU(W_gate_up RMSNorm(h))            (bf16 out, F = 9728)
+        h       = W_down a + h                            (residual, in place)
+    then logits = W_lm RMSNorm(h).  h is the fp32 hidden state (2560).
+    Algorithmic bytes per launch: weights + activations read + norm weights +
+    residual read + outputs written."""
+    hidden = 2560
+    h = torch.from_numpy(wl.x_f32((1, hidden), wl.rng_for(config, 200, "x"))).to(dev)
+    a = torch.empty((1, 9728), dtype=torch.bfloat16, device=dev)
+    calls, alg = [], []
+    for i, (j, name, n, k) in enumerate(shapes):
+        kind = name.split(".")[-1]
+        wb = n * (k // 32) * 34
+        if kind in ("qkv", "gate_up", "lm_head"):
+            g = torch.from_numpy(wl.norm_weight_f32(k, wl.rng_for(config, j, "gamma"))).to(dev)
+            if kind == "gate_up":
+                calls.append(dict(i=i, x=h, norm_weight=g, act=q.ACT_SWIGLU, residual=None, y=a))
+                alg.append(wb + 4 * k + 4 * k + 2 * (n // 2))
+            else:
+                calls.append(dict(i=i, x=h, norm_weight=g, act=q.ACT_NONE, residual=None, y=ys[i]))
+                alg.append(wb + 4 * k + 4 * k + 4 * n)
+        else:
+            x = xs[i] if kind == "o" else a
+            calls.append(dict(i=i, x=x, norm_weight=None, act=q.ACT_NONE, residual=h, y=h))
+            alg.append(wb + 2 * k + 4 * n + 4 * n)
+    plain_alg = [n * (k // 32) * 34 + 2 * k + 4 * n for (_, _, n, k) in shapes]
+
+    def fused(idx=None):
+        for c in calls if idx is None else [calls[t] for t in idx]:
+            _, _, n, k = shapes[c["i"]]
+            q.qgemv_fused(fmt, wviews[c["i"]], n, k, c["x"], norm_weight=c["norm_weight"], eps=1e-6,
+                          act=c["act"], residual=c["residual"], y=c["y"])
+
+    def plain(idx=None):
+        for i in range(len(shapes)) if idx is None else idx:
+            _, _, n, k = shapes[i]
+            q.qgemv(fmt, wviews[i], n, k, xs[i], y=ys[i])
+
+    # the same dataflow unfused, for comparison only: the plain products with
+    # the norm, gate and residual steps done by separate torch kernels
+    # (bf16 copies of the normalised activations feed the plain products)
+    gam = {c["i"]: c["norm_weight"] for c in calls if c["norm_weight"] is not None}
+    xb = {i: torch.empty((1, k), dtype=torch.bfloat16, device=dev) for i, (_, _, n, k) in enumerate(shapes)}
+    gu_out = torch.empty((1, 19456), dtype=torch.float32, device=dev)
+
+    def unfused():
+        for i, (_, name, n, k) in enumerate(shapes):
+            kind = name.split(".")[-1]
+            if kind in ("qkv", "gate_up", "lm_head"):
+                xb[i].copy_(torch.nn.functional.rms_norm(h, (k,), gam[i], 1e-6))
+                if kind == "gate_up":
+                    q.qgemv(fmt, wviews[i], n, k, xb[i], y=gu_out)
+                    a.copy_(torch.nn.functional.silu(gu_out[:, : n // 2]) * gu_out[:, n // 2:])
+                else:
+                    q.qgemv(fmt, wviews[i], n, k, xb[i], y=ys[i])
+            else:
+                q.qgemv(fmt, wviews[i], n, k, xs[i] if kind == "o" else a, y=ys[i])
+                h.add_(ys[i])
+
+    reps = max(1, args.steps)
+    us_f = graph_time(torch, fused, reps)
+    us_p = graph_time(torch, plain, reps)
+    us_u = graph_time(torch, unfused, reps)
+    log(args, f"unfused (plain products + torch norm / SwiGLU / add kernels) {us_u:.1f} us")
+    fb, pb = sum(alg), sum(plain_alg)
+    log(args, f"fused sweep {us_f:.1f} us ({fb / us_f / 1e3:.1f} GB/s); plain {us_p:.1f} us ({pb / us_p / 1e3:.1f} GB/s)")
+    groups = {}
+    for i, (_, name, n, k) in enumerate(shapes):
+        groups.setdefault(name.split(".")[-1], []).append(i)
+    per_shape = {}
+    for key, idx in groups.items():
+        uf = graph_time(torch, lambda idx=idx: fused(idx), 5) / len(idx)
+        up = graph_time(torch, lambda idx=idx: plain(idx), 5) / len(idx)
+        _, _, n, k = shapes[idx[0]]
+        per_shape[key] = {"n": n, "k": k, "fused": {"bytes": alg[idx[0]], "us": round(uf, 3),
+                                                    "gbs": round(alg[idx[0]] / uf / 1e3, 1)},
+                          "plain": {"bytes": plain_alg[idx[0]], "us": round(up, 3),
+                                    "gbs": round(plain_alg[idx[0]] / up / 1e3, 1)}}
+    log(args, f"per shape {per_shape}")
+    out = {
+        "metric": METRIC, "value": round(fb / us_f / 1e3, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": reps, "warmup": args.warmup, "ms_per_step": round(us_f * 1e-3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "q8_0 full decode sweep with RMSNorm / SwiGLU / residual fused (qgemv_fused), "
+                               "M=1: 36 x {qkv+norm, o+residual, gate_up+norm+SwiGLU->bf16, down+residual} "
+                               "+ lm_head+norm", "launches_per_step": len(shapes), "bytes_per_step": fb},
+        "pct_of_peak": round(100.0 * fb / us_f / 1e3 / HBM_PEAK_GBS, 2),
+        "equiv_decode_tok_s": round(1e6 / us_f, 1),
+        "plain_sweep": {"us": round(us_p, 1), "gbs": round(pb / us_p / 1e3, 1), "bytes": pb},
+        "fused_over_plain_time": round(us_f / us_p, 4),
+        "unfused_sweep": {"us": round(us_u, 1), "what": "plain products + torch rms_norm / silu*mul / add "
+                                                        "kernels between them, one graph"},
+        "fused_over_unfused_time": round(us_f / us_u, 4),
+        "per_shape": per_shape,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the sharded design is described but not run)", file=sys.stderr)
         sys.exit(2)
-    if args.workload != "c2":
+    if args.workload not in ("c2", "c2f"):
         run_other(args)
         return
 
@@ -322,6 +427,9 @@ def main():
     log(args, f"inputs generated, packed and resident in {time.time() - t0:.1f} s")
 
     wviews = [wbuf[offs[i]:offs[i] + q.packed_bytes(fmt, n, k)] for i, (_, _, n, k) in enumerate(shapes)]
+    if args.workload == "c2f":
+        run_fused_sweep(args, torch, q, dev, shapes, wviews, xs, ys, fmt, config)
+        return
     # algorithmic bytes: canonical weights + x (bf16) + y (fp32)
     alg = [n * (k // 32) * 34 + 2 * k + 4 * n for (_, _, n, k) in shapes]
     step_bytes = sum(alg)

@@ -20,6 +20,7 @@ X_F32, X_BF16 = 0, 1
 MOE_GATE_UP, MOE_DOWN_COMBINE = 0, 1
 MAX_M = 8
 PATH_VALU, PATH_MFMA = 0, 1
+ACT_NONE, ACT_SWIGLU = 0, 1
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17}
 
 # exported functions: name -> (restype, argtypes)
@@ -37,6 +38,7 @@ SIGNATURES = {
     "qgemv_q8_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_q4_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_mxfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
+    "qgemv_fused": (_i, [_i, _vp, _i64, _i64, _vp, _i, _i64, _vp, ctypes.c_float, _i, _vp, _vp, _i, _vp]),
     "moe_qgemv_topk": (_i, [_i, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i, _i, _vp, _vp]),
     "moe_router_topk": (_i, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "qg_chain_plan_bytes": (_i64, [_i64]),
@@ -224,6 +226,42 @@ def qgemv_q4_0(w_packed, n, k, x, y=None, stream=None):
 
 def qgemv_mxfp4(w_packed, n, k, x, y=None, stream=None):
     return qgemv(MXFP4, w_packed, n, k, x, y, stream)
+
+
+def qgemv_fused(fmt, w_packed, n, k, x, norm_weight=None, eps=1e-6, act=ACT_NONE, residual=None, y=None,
+                out_dtype=None, stream=None):
+    """Dense product with the decode step's neighbours fused in:
+    y = [SwiGLU](W RMSNorm(x)) [+ residual], each part optional.
+    x float32 or bfloat16 [m, k]; norm_weight float32 [k] or None; act
+    ACT_NONE or ACT_SWIGLU (gate rows first, y has n / 2 columns); residual
+    float32 [m, n_out] or None (may be y itself when y is float32); y float32
+    or bfloat16 [m, n_out] (out_dtype when y is None, default float32)."""
+    torch = _torch()
+    x2 = x.reshape(-1, k)
+    m = x2.shape[0]
+    n_out = n // 2 if act == ACT_SWIGLU else n
+    if y is None:
+        y = torch.empty((m, n_out), dtype=out_dtype or torch.float32, device=x.device)
+    if y.dtype == torch.float32:
+        yt = X_F32
+    elif y.dtype == torch.bfloat16:
+        yt = X_BF16
+    else:
+        raise ValueError("y must be float32 or bfloat16")
+    gp = None
+    if norm_weight is not None:
+        if norm_weight.dtype != torch.float32:
+            raise ValueError("norm_weight must be float32")
+        gp = _dev_ptr(norm_weight, "norm_weight")
+    rp = None
+    if residual is not None:
+        if residual.dtype != torch.float32:
+            raise ValueError("residual must be float32")
+        rp = _dev_ptr(residual, "residual")
+    st = lib().qgemv_fused(fmt, _dev_ptr(w_packed, "w_packed"), n, k, _dev_ptr(x2, "x"), _xt(x2), m, gp,
+                           float(eps), act, rp, _dev_ptr(y, "y"), yt, _stream(stream))
+    _check("qgemv_fused", st)
+    return y
 
 
 def moe_qgemv_topk(fmt, w_experts, n_experts, n, k, topk_ids, topk_w, x, mode, y=None, stream=None):

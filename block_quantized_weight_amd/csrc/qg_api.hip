@@ -3,6 +3,7 @@
 #include "qg_chain.h"
 #include "qg_mfma.h"
 #include "qg_moe_stream.h"
+#include "qg_fused.h"
 
 namespace qg {
 namespace {
@@ -515,6 +516,65 @@ int qgemv_q4_0(const void *w, int64_t n, int64_t k, const void *x, int xt, int64
 int qgemv_mxfp4(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
 {
     return dense(QG_MXFP4, w, n, k, x, xt, m, y, stream);
+}
+
+static bool overlaps(const void *a, size_t abytes, const void *b, size_t bbytes)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+int qgemv_fused(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m,
+                const float *norm_weight, float norm_eps, int act, const float *residual,
+                void *y, int yt, void *stream)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return st;
+    if (!w || !x || !y) return QG_EINVAL;
+    if (xt != QG_F32 && xt != QG_BF16) return QG_EINVAL;
+    if (yt != QG_F32 && yt != QG_BF16) return QG_EINVAL;
+    if (act != QG_ACT_NONE && act != QG_ACT_SWIGLU) return QG_EINVAL;
+    if (m < 1 || m > QG_MAX_M) return QG_EINVAL;
+    if (norm_weight && !(norm_eps >= 0.0f && norm_eps <= 3.4e38f)) return QG_EINVAL;    // rejects NaN too
+    if (act == QG_ACT_SWIGLU && (n % 2) != 0) return QG_EINVAL;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, yt == QG_F32 ? 4 : 2)) return QG_EALIGN;
+    if ((norm_weight && !aligned(norm_weight, 16)) || (residual && !aligned(residual, 4))) return QG_EALIGN;
+    const int64_t n_out = act == QG_ACT_SWIGLU ? n / 2 : n;
+    if (residual && !(yt == QG_F32 && (const void *)residual == y) &&
+        overlaps(residual, (size_t)(m * n_out * 4), y, (size_t)(m * n_out * (yt == QG_F32 ? 4 : 2))))
+        return QG_EINVAL;
+    const Layout lo = make_layout(fmt, n, k);
+    if (act == QG_ACT_SWIGLU && (n_out % lo.R) != 0) return QG_EUNSUPPORTED;
+    const bool norm = norm_weight != nullptr;
+    const bool dot = !norm && uses_dot(fmt, xt);
+    Plan p = make_plan(lo, (int)m, dot, (int)m);
+    p.g.w = (const uint8_t *)w;
+    EpiArgs e{};
+    e.gamma = norm_weight;
+    e.eps = norm_eps;
+    e.residual = residual;
+    e.y = y;
+    e.n_out = (int32_t)n_out;
+    e.half_tiles = act == QG_ACT_SWIGLU ? (int32_t)(n_out / lo.R) : 0;
+    e.y_bf16 = yt == QG_BF16;
+    const bool glu = e.half_tiles > 0;
+    int block = TPB;
+    if (glu) {
+        // GLU_WAVES waves: KS per tile, gate and up tiles in equal numbers
+        p.g.tpi = GLU_WAVES / p.g.KS;
+        const int pp = p.g.tpi / 2;
+        p.g.ngroups = (e.half_tiles + pp - 1) / pp;
+        p.grid = p.g.ngroups > 65535 ? 65535 : p.g.ngroups;
+        p.lds += (size_t)(GLU_WAVES - WAVES) * m * 64 * 4;     // split-K partials of the extra waves
+        block = 64 * GLU_WAVES;
+    }
+    dense_ep_fn f = fmt == QG_Q8_0 ? dense_ep_kernel_q8_0(xt, (int)m, norm, glu)
+                    : fmt == QG_Q4_0 ? dense_ep_kernel_q4_0(xt, (int)m, norm, glu)
+                                     : dense_ep_kernel_mxfp4(xt, (int)m, norm, glu);
+    void *args[] = {(void *)&p.g, (void *)&e, (void *)&x};
+    if (allow_lds((const void *)f, p.lds) != hipSuccess) return QG_EHIP;
+    hipError_t err = hipLaunchKernel((const void *)f, dim3(p.grid), dim3(block), args, p.lds, as_stream(stream));
+    return err == hipSuccess ? launch_status() : QG_EHIP;
 }
 
 int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n, int64_t k,

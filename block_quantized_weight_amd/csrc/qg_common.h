@@ -621,6 +621,17 @@ struct Engine {
     static __device__ __forceinline__ void pass(const Geom &g, const void *x, const Slots &sl, int tile, bool &staged,
                                                 uint4 *xs, float *corr, float acc[M])
     {
+        XStage<XBF16, DOT> st;
+        pass_st(g, x, sl, tile, staged, xs, corr, acc, st);
+    }
+
+    // The same with a given stager: an object whose run<M, FMT>(g, x, sl, w,
+    // xs, corr) fills window w's staged activations in this engine's form; the
+    // whole workgroup calls it between two barriers.
+    template <class ST>
+    static __device__ __forceinline__ void pass_st(const Geom &g, const void *x, const Slots &sl, int tile, bool &staged,
+                                                   uint4 *xs, float *corr, float acc[M], ST &stg)
+    {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int KS = g.KS, kpart = wave & (KS - 1);
         const int slot = lane & (g.L - 1);
@@ -641,7 +652,7 @@ struct Engine {
             load(g, ct, st, lane, nsteps > 0 ? jf : 0, max(1, min(nsteps, U)), KS, ra);
             if (g.nwin > 1 || !staged) {
                 __syncthreads();
-                XStage<XBF16, DOT>::template run<M, FMT>(g, x, sl, w, xs, corr);
+                stg.template run<M, FMT>(g, x, sl, w, xs, corr);
                 __syncthreads();
                 staged = true;
             }

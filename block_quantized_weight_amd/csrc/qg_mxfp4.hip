@@ -1,5 +1,6 @@
 // qg_mxfp4.hip -- MXFP4 instantiations of the dense and expert GEMV kernels.
 #include "qg_chain.h"
+#include "qg_fused.h"
 #include "qg_mfma.h"
 #include "qg_moe_stream.h"
 
@@ -29,6 +30,11 @@ mfma_fn mfma_kernel_mxfp4(int L) { return pick_mfma<QG_MXFP4>(L); }
 moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms)
 {
     return xt == QG_BF16 ? pick_moe_stream<QG_MXFP4, true, true>(mode, ms) : pick_moe_stream<QG_MXFP4, false, false>(mode, ms);
+}
+
+dense_ep_fn dense_ep_kernel_mxfp4(int xt, int m, bool norm, bool glu)
+{
+    return pick_dense_ep_fmt<QG_MXFP4>(xt, m, norm, glu);
 }
 
 } // namespace qg

@@ -1,5 +1,6 @@
 // qg_q4_0.hip -- Q4_0 instantiations of the dense and expert GEMV kernels.
 #include "qg_chain.h"
+#include "qg_fused.h"
 #include "qg_mfma.h"
 #include "qg_moe_stream.h"
 
@@ -29,6 +30,11 @@ mfma_fn mfma_kernel_q4_0(int L) { return pick_mfma<QG_Q4_0>(L); }
 moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms)
 {
     return xt == QG_BF16 ? pick_moe_stream<QG_Q4_0, true, true>(mode, ms) : pick_moe_stream<QG_Q4_0, false, false>(mode, ms);
+}
+
+dense_ep_fn dense_ep_kernel_q4_0(int xt, int m, bool norm, bool glu)
+{
+    return pick_dense_ep_fmt<QG_Q4_0>(xt, m, norm, glu);
 }
 
 } // namespace qg

@@ -84,6 +84,9 @@ enum { QG_MOE_GATE_UP = 0, QG_MOE_DOWN_COMBINE = 1 };
 /* Kernel families of the dense product (qg_dense_path). */
 enum { QG_PATH_VALU = 0, QG_PATH_MFMA = 1 };
 
+/* Activation of the fused product's epilogue (qgemv_fused). */
+enum { QG_ACT_NONE = 0, QG_ACT_SWIGLU = 1 };
+
 /* Description of the packed layout of one n x k matrix. */
 typedef struct {
     int32_t fmt;
@@ -160,6 +163,34 @@ int qgemv_mxfp4(const void *w_packed, int64_t n, int64_t k, const void *x, int x
  * arguments the dense calls would reject.  Host only; no device work.
  */
 int qg_dense_path(int fmt, int64_t n, int64_t k, int xt, int64_t m);
+
+/*
+ * Dense product with its decode-step neighbours fused in (the pages report
+ * such hand-made fusions: imp release notes v0.4, a fused RMSNorm-gated +
+ * SiLU kernel; Imparo README, "Bonsai CUDA Validation", an RMS/Add tail
+ * fusion; the operations themselves are the published ones):
+ *     x'  = norm_weight ? x * r * norm_weight : x,
+ *           r = 1 / sqrt(mean over c of x[t][c]^2 + norm_eps)    (RMSNorm)
+ *     z   = W x'                                                   (n rows)
+ *     o   = act == QG_ACT_SWIGLU ? SiLU(z[0 .. F)) * z[F .. 2F) : z,
+ *           F = n / 2, SiLU(v) = v / (1 + exp(-v))   (gate rows first)
+ *     y   = o + residual (if residual) ;  y [m][n_out], n_out = F or n
+ * fmt: weight format of the packed w (as qgemv_*); x, xt, m as qgemv_*.
+ * norm_weight: device fp32 [k], 16-byte aligned, or NULL (no normalisation);
+ * norm_eps: finite, >= 0.  residual: device fp32 [m][n_out], 4-byte aligned,
+ * or NULL; with an fp32 output it may be y itself (in-place add), otherwise
+ * it must not overlap y.  y: device [m][n_out], fp32 (yt = QG_F32, 4-byte
+ * aligned) or bf16 round-to-nearest-even (yt = QG_BF16, 2-byte aligned),
+ * overwritten.  Runs the vector kernel family for every m: normalised
+ * activations are kept in fp32 (a bf16 copy for the matrix cores would
+ * round each by up to 2^-9).  r is computed in fp32 per workgroup, in a
+ * fixed order, so the same inputs give the same bits.
+ * Limits: those of qgemv_*; with SwiGLU n is even and F a multiple of the
+ * layout's rows per tile (QG_EUNSUPPORTED otherwise).
+ */
+int qgemv_fused(int fmt, const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
+                const float *norm_weight, float norm_eps, int act, const float *residual,
+                void *y, int yt, void *stream);
 
 /*
  * Top-k expert product.  w_experts: device, n_experts packed matrices of

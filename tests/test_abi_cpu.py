@@ -200,3 +200,34 @@ def test_router_argument_validation():
     assert L.moe_router_topk(a, 1, 2048, 4, a, a, None) == q.QG_EUNSUPPORTED
     assert L.moe_router_topk(a, 1, 128, 65, a, a, None) == q.QG_EUNSUPPORTED
     assert L.moe_router_topk(ODD, 1, 32, 4, a, a, None) == q.QG_EALIGN
+
+
+def test_fused_argument_validation():
+    """qgemv_fused rejects bad arguments before any device work (no GPU needed)."""
+    L = q.lib()
+    a = ctypes.c_void_p(1 << 20)
+    b = ctypes.c_void_p(1 << 24)
+    ODD = ctypes.c_void_p((1 << 20) + 2)
+    f = ctypes.c_float
+
+    def call(fmt=q.Q8_0, w=a, n=256, k=512, x=a, xt=q.X_BF16, m=1, g=None, eps=1e-6, act=q.ACT_NONE, res=None,
+             y=b, yt=q.X_F32):
+        return L.qgemv_fused(fmt, w, n, k, x, xt, m, g, f(eps), act, res, y, yt, None)
+
+    assert call(w=None) == q.QG_EINVAL and call(x=None) == q.QG_EINVAL and call(y=None) == q.QG_EINVAL
+    assert call(fmt=7) == q.QG_EINVAL and call(k=100) == q.QG_EINVAL and call(n=0) == q.QG_EINVAL
+    assert call(xt=2) == q.QG_EINVAL and call(yt=2) == q.QG_EINVAL and call(act=2) == q.QG_EINVAL
+    assert call(m=0) == q.QG_EINVAL and call(m=9) == q.QG_EINVAL
+    assert call(g=a, eps=-1.0) == q.QG_EINVAL and call(g=a, eps=float("nan")) == q.QG_EINVAL
+    assert call(g=a, eps=float("inf")) == q.QG_EINVAL
+    assert call(act=q.ACT_SWIGLU, n=255) == q.QG_EINVAL
+    assert call(x=ODD) == q.QG_EALIGN and call(g=ODD) == q.QG_EALIGN
+    assert call(y=ctypes.c_void_p((1 << 24) + 2)) == q.QG_EALIGN
+    assert call(res=ctypes.c_void_p((1 << 24) + 2), y=ctypes.c_void_p(1 << 26)) == q.QG_EALIGN
+    # residual overlapping y: only the exact alias with an fp32 output is allowed
+    assert call(res=ctypes.c_void_p((1 << 24) + 4)) == q.QG_EINVAL
+    assert call(res=b, yt=q.X_BF16) == q.QG_EINVAL
+    # SwiGLU needs F to be a multiple of the layout's rows per tile
+    lo = q.layout(q.Q8_0, 2 * 4100, 2560)
+    assert 4100 % lo["rows_per_tile"] != 0
+    assert call(act=q.ACT_SWIGLU, n=2 * 4100, k=2560) == q.QG_EUNSUPPORTED
