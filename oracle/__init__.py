@@ -268,17 +268,8 @@ def dense_fused(fmt, blocks, n, k, x, xt, norm_weight=None, eps=0.0, act=ACT_NON
         n_out = n // 2
     else:
         n_out = n
+    o, scale = _fused_rows(fmt, blocks, n, k, xv, act, rows)
     r = np.arange(n_out) if rows is None else np.asarray(rows, dtype=np.int64)
-    if act == ACT_SWIGLU:
-        wg = _row_weights(fmt, blocks, n, k, r)
-        wu = _row_weights(fmt, blocks, n, k, r + n_out)
-        g, l1g = xv @ wg.T, np.abs(xv) @ np.abs(wg).T
-        u, l1u = xv @ wu.T, np.abs(xv) @ np.abs(wu).T
-        o = silu(g) * u
-        scale = 1.1 * l1g * (np.abs(u) + 2e-3 * l1u) + np.abs(silu(g)) * l1u
-    else:
-        w = _row_weights(fmt, blocks, n, k, r)
-        o, scale = xv @ w.T, np.abs(xv) @ np.abs(w).T
     if residual is not None:
         o = o + np.asarray(residual, dtype=np.float32).astype(np.float64).reshape(-1, n_out)[:, r]
     return o, scale
@@ -299,3 +290,87 @@ def fused_err(yhat, o, scale, y_bf16=False):
     err = np.where(scale > 0, rest / np.where(scale > 0, scale, 1.0), np.where(rest > 0, np.inf, 0.0))
     err[~np.isfinite(yhat)] = np.inf
     return float(err.max()) if err.size else 0.0
+
+
+def moe_fused(fmt, experts, n_experts, n, k, ids, g, x, xt, mode, norm_weight=None, eps=0.0, act=ACT_NONE,
+              residual=None, rows=None):
+    """Fused top-k expert step, by definition in fp64 (the definitions of
+    dense_fused, per slot):
+      MOE_GATE_UP:  x [m, k];  for each token t and slot j with a valid id
+                    e = ids[t, j]:  z = W_e RMSNorm(x_t) (RMSNorm optional),
+                    o[t, j] = SiLU(z[:F]) * z[F:] with ACT_SWIGLU, else z.
+                    Slots with an invalid id get NaN (they have no output).
+      MOE_DOWN:     x [m, top_k, k];  o[t] = sum over j ascending of
+                    g[t, j] * W_{ids[t, j]} x[t, j]  (+ residual[t]).
+    Returns (o, scale): gate_up [m, top_k, nrows], down [m, nrows]; scale as
+    in dense_fused, for down the sum over slots of |g| * row L1."""
+    ida = np.asarray(ids, dtype=np.int64)
+    m, top_k = ida.shape
+    bb = BLOCK_BYTES[fmt]
+    per = n * (k // 32) * bb
+    e_all = np.ascontiguousarray(experts, dtype=np.uint8)
+    if e_all.size != n_experts * per:
+        raise ValueError("expert array size does not match")
+
+    def expert(e):
+        return e_all[e * per:(e + 1) * per]
+
+    xv = x_values(x, xt)
+    if mode == MOE_GATE_UP:
+        xv = xv.reshape(m, k)
+        if residual is not None:
+            raise ValueError("gate_up takes no residual")
+        n_out = n // 2 if act == ACT_SWIGLU else n
+        nr = n_out if rows is None else len(rows)
+        o = np.full((m, top_k, nr), np.nan)
+        scale = np.zeros((m, top_k, nr))
+        for t in range(m):
+            for j in range(top_k):
+                e = int(ida[t, j])
+                if not 0 <= e < n_experts:
+                    continue
+                xt_row = xv[t:t + 1]
+                if norm_weight is not None:
+                    xt_row, _ = rmsnorm(xt_row, norm_weight, eps)
+                # the product of the (normalised) fp64 row, as dense_fused does
+                oo, ss = _fused_rows(fmt, expert(e), n, k, xt_row, act, rows)
+                o[t, j], scale[t, j] = oo[0], ss[0]
+        return o, scale
+    if norm_weight is not None or act != ACT_NONE:
+        raise ValueError("down-combine takes neither a normalisation nor a gate")
+    xv = xv.reshape(m, top_k, k)
+    ga = np.asarray(g, dtype=np.float32).astype(np.float64).reshape(m, top_k)
+    nr = n if rows is None else len(rows)
+    r = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((m, nr))
+    scale = np.zeros((m, nr))
+    for t in range(m):
+        for j in range(top_k):
+            e = int(ida[t, j])
+            if not 0 <= e < n_experts:
+                continue
+            w = _row_weights(fmt, expert(e), n, k, r)
+            o[t] += ga[t, j] * (w @ xv[t, j])
+            scale[t] += abs(ga[t, j]) * (np.abs(w) @ np.abs(xv[t, j]))
+    if residual is not None:
+        o += np.asarray(residual, dtype=np.float32).astype(np.float64).reshape(m, n)[:, r]
+    return o, scale
+
+
+def _fused_rows(fmt, blocks, n, k, xv, act, rows):
+    """dense_fused's product and gate for activations already in fp64."""
+    if act == ACT_SWIGLU:
+        if n % 2:
+            raise ValueError("SwiGLU needs an even row count")
+        n_out = n // 2
+    else:
+        n_out = n
+    r = np.arange(n_out) if rows is None else np.asarray(rows, dtype=np.int64)
+    if act == ACT_SWIGLU:
+        wg = _row_weights(fmt, blocks, n, k, r)
+        wu = _row_weights(fmt, blocks, n, k, r + n_out)
+        g, l1g = xv @ wg.T, np.abs(xv) @ np.abs(wg).T
+        u, l1u = xv @ wu.T, np.abs(xv) @ np.abs(wu).T
+        return silu(g) * u, 1.1 * l1g * (np.abs(u) + 2e-3 * l1u) + np.abs(silu(g)) * l1u
+    w = _row_weights(fmt, blocks, n, k, r)
+    return xv @ w.T, np.abs(xv) @ np.abs(w).T

@@ -455,3 +455,63 @@ def test_fused_verdict_catches_plausible_mistakes():
     no_gamma, _ = oracle.dense_fused(fmt, blocks, n, k, x, oracle.X_F32, norm_weight=ones, eps=1e-6,
                                      act=oracle.ACT_SWIGLU)
     assert oracle.fused_err(no_gamma, o, scale) > 10 * 2e-3
+
+
+def _moe_case(fmt=oracle.Q4_0, E=6, n=64, k=128, m=3, top_k=2, config=97):
+    experts = np.concatenate([wl.blocks_for(fmt, n, k, config=config, matrix=e).reshape(-1) for e in range(E)])
+    _, ids, g = wl.router_topk(m, E, top_k, wl.rng_for(config, 0, "router"))
+    return fmt, E, n, k, m, top_k, experts, ids, g
+
+
+def test_moe_fused_reduces_to_the_c_expert_product():
+    torch = pytest.importorskip("torch")
+    fmt, E, n, k, m, top_k, experts, ids, g = _moe_case()
+    x = wl.x_bf16_bits((m, k), wl.rng_for(97, 0, "x"))
+    h = wl.x_bf16_bits((m, top_k, k), wl.rng_for(97, 0, "h"))
+    yg, l1g = oracle.moe(fmt, experts, E, n, k, ids, g, x, oracle.X_BF16, oracle.MOE_GATE_UP)   # the C loop
+    o, s = oracle.moe_fused(fmt, experts, E, n, k, ids, g, x, oracle.X_BF16, oracle.MOE_GATE_UP)
+    assert np.max(np.abs(o - yg) / l1g) < 1e-13 and np.allclose(s, l1g, rtol=1e-13)
+    o, _ = oracle.moe_fused(fmt, experts, E, n, k, ids, g, x, oracle.X_BF16, oracle.MOE_GATE_UP, act=oracle.ACT_SWIGLU)
+    want = torch.nn.functional.silu(torch.from_numpy(yg[..., : n // 2])).numpy() * yg[..., n // 2:]
+    assert np.allclose(o, want, rtol=1e-12, atol=1e-12 * np.max(l1g))
+    yd, l1d = oracle.moe(fmt, experts, E, n, k, ids, g, h, oracle.X_BF16, oracle.MOE_DOWN)
+    res = wl.x_f32((m, n), wl.rng_for(97, 0, "res"))
+    o, s = oracle.moe_fused(fmt, experts, E, n, k, ids, g, h, oracle.X_BF16, oracle.MOE_DOWN, residual=res)
+    assert np.max(np.abs(o - res - yd) / l1d) < 1e-13 and np.allclose(s, l1d, rtol=1e-13)
+    rows = np.array([5, 0, 63])
+    o2, s2 = oracle.moe_fused(fmt, experts, E, n, k, ids, g, h, oracle.X_BF16, oracle.MOE_DOWN, residual=res, rows=rows)
+    assert np.array_equal(o2, o[:, rows]) and np.array_equal(s2, s[:, rows])
+
+
+def test_moe_fused_norm_is_a_scaled_expert_product():
+    # gamma a power of two: x * gamma is exact in fp32, so the C expert product
+    # of x * gamma, times r (math.fsum), gives the normalised rows
+    fmt, E, n, k, m, top_k, experts, ids, g = _moe_case(fmt=oracle.MXFP4, config=98)
+    x = (4.0 * wl.x_f32((m, k), wl.rng_for(98, 0, "x"))).astype(np.float32)
+    gamma = np.where(np.arange(k) % 5 == 0, 2.0, 0.25).astype(np.float32)
+    eps = 1e-4
+    o, s = oracle.moe_fused(fmt, experts, E, n, k, ids, g, x, oracle.X_F32, oracle.MOE_GATE_UP,
+                            norm_weight=gamma, eps=eps)
+    y, l1 = oracle.moe(fmt, experts, E, n, k, ids, g, (x * gamma).astype(np.float32), oracle.X_F32,
+                       oracle.MOE_GATE_UP)
+    r = np.array([1.0 / math.sqrt(math.fsum(row * row) / k + eps) for row in x.astype(np.float64)])
+    assert np.max(np.abs(o - r[:, None, None] * y) / (r[:, None, None] * l1)) < 1e-13
+    assert np.allclose(s, r[:, None, None] * l1, rtol=1e-13)
+
+
+def test_moe_fused_invalid_ids():
+    fmt, E, n, k, m, top_k, experts, ids, g = _moe_case(config=99)
+    ids = ids.copy()
+    ids[0, 1] = -1
+    ids[1, 0] = E
+    x = wl.x_bf16_bits((m, k), wl.rng_for(99, 0, "x"))
+    o, _ = oracle.moe_fused(fmt, experts, E, n, k, ids, g, x, oracle.X_BF16, oracle.MOE_GATE_UP, act=oracle.ACT_SWIGLU)
+    assert np.all(np.isnan(o[0, 1])) and np.all(np.isnan(o[1, 0])) and np.all(np.isfinite(o[2]))
+    # down: every id invalid leaves the residual exactly
+    h = wl.x_bf16_bits((m, top_k, k), wl.rng_for(99, 0, "h"))
+    res = wl.x_f32((m, n), wl.rng_for(99, 0, "res"))
+    o, s = oracle.moe_fused(fmt, experts, E, n, k, np.full_like(ids, -1), g, h, oracle.X_BF16, oracle.MOE_DOWN,
+                            residual=res)
+    assert np.array_equal(o, res.astype(np.float64)) and not s.any()
+    with pytest.raises(ValueError):
+        oracle.moe_fused(fmt, experts, E, n, k, ids, g, h, oracle.X_BF16, oracle.MOE_DOWN, act=oracle.ACT_SWIGLU)
