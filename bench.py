@@ -238,9 +238,32 @@ def run_other(args):
             wus = graph_time(torch, lambda: [(route(), gate(r), down(r)) for r in range(reps)],
                              max(2, args.steps // 3)) / reps
             per["router"] = {"us": round(rus, 3)}
+
+            # the expert FFN fused (moe_qgemv_topk_fused): fp32 hidden state ->
+            # gate_up with RMSNorm + SwiGLU -> bf16 -> down-combine + residual (in place)
+            hid = torch.from_numpy(wl.x_f32((m, gk), wl.rng_for(4, m, "x"))).to(dev)
+            gam = torch.from_numpy(wl.norm_weight_f32(gk, wl.rng_for(4, m, "gamma"))).to(dev)
+            act = torch.empty((m, top_k, gn // 2), dtype=torch.bfloat16, device=dev)
+
+            def fgate(r):
+                q.moe_qgemv_topk_fused(fmt, ge[r * E * gpb:(r + 1) * E * gpb], E, gn, gk, tid, tw, hid, q.MOE_GATE_UP,
+                                       norm_weight=gam, eps=1e-6, act=q.ACT_SWIGLU, y=act)
+
+            def fdown(r):
+                q.moe_qgemv_topk_fused(fmt, de[r * E * dpb:(r + 1) * E * dpb], E, dn, dk, tid, tw, act,
+                                       q.MOE_DOWN_COMBINE, residual=hid, y=hid)
+            fg_bytes = distinct * gn * (gk // 32) * 17 + m * gk * 4 + gk * 4 + m * top_k * (gn // 2) * 2 + m * top_k * 8
+            fd_bytes = distinct * dn * (dk // 32) * 17 + m * top_k * dk * 2 + 2 * m * dn * 4 + m * top_k * 8
+            fused = {}
+            for nm, f, b in (("gate_up_norm_swiglu", fgate, fg_bytes), ("down_combine_residual", fdown, fd_bytes)):
+                fu = graph_time(torch, lambda f=f: [f(r) for r in range(reps)], max(2, args.steps // 3)) / reps
+                fused[nm] = {"bytes": b, "us": round(fu, 3), "gbs": round(b / fu / 1e3, 1)}
+            fused["router_and_both"] = {"us": round(graph_time(torch, lambda: [(route(), fgate(r), fdown(r))
+                                                                              for r in range(reps)],
+                                                               max(2, args.steps // 3)) / reps, 3)}
             emit(f"mxfp4 moe 32 experts top-4: gate_up 3584x2048 + down 2048x1792 m={m}", (gbytes + dbytes) / us / 1e3,
                  us, {"per_mode": per, "distinct_experts": distinct, "bytes_per_set": gbytes + dbytes,
-                      "weight_copies": reps, "us_with_device_router": round(wus, 3)})
+                      "weight_copies": reps, "us_with_device_router": round(wus, 3), "fused_ffn": fused})
 
 
 def log(args, *a):

@@ -40,6 +40,8 @@ SIGNATURES = {
     "qgemv_mxfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_fused": (_i, [_i, _vp, _i64, _i64, _vp, _i, _i64, _vp, ctypes.c_float, _i, _vp, _vp, _i, _vp]),
     "moe_qgemv_topk": (_i, [_i, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i, _i, _vp, _vp]),
+    "moe_qgemv_topk_fused": (_i, [_i, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i, _i, _vp, ctypes.c_float,
+                                  _i, _vp, _vp, _i, _vp]),
     "moe_router_topk": (_i, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "qg_chain_plan_bytes": (_i64, [_i64]),
     "qg_chain_plan": (_i, [_i, _i, _i64, _vp, _i64, _vp]),
@@ -281,6 +283,46 @@ def moe_qgemv_topk(fmt, w_experts, n_experts, n, k, topk_ids, topk_w, x, mode, y
                               _dev_ptr(topk_ids, "topk_ids"), wp, m, top_k, _dev_ptr(x, "x"), _xt(x), mode,
                               _dev_ptr(y, "y"), _stream(stream))
     _check("moe_qgemv_topk", st)
+    return y
+
+
+def moe_qgemv_topk_fused(fmt, w_experts, n_experts, n, k, topk_ids, topk_w, x, mode, norm_weight=None, eps=1e-6,
+                         act=ACT_NONE, residual=None, y=None, out_dtype=None, stream=None):
+    """Top-k expert product with the neighbours fused in.  GATE_UP: x [m, k]
+    -> y [m, top_k, n_out], optionally RMSNorm(x) and SwiGLU (n_out = n / 2);
+    DOWN_COMBINE: x [m, top_k, k] -> y [m, n], optionally + residual float32
+    [m, n] (may be y).  y float32 or bfloat16 (out_dtype when y is None)."""
+    torch = _torch()
+    m, top_k = topk_ids.shape
+    if topk_ids.dtype != torch.int32:
+        raise ValueError("topk_ids must be int32")
+    if topk_w is not None and topk_w.dtype != torch.float32:
+        raise ValueError("topk_w must be float32")
+    n_out = n // 2 if act == ACT_SWIGLU else n
+    if y is None:
+        shape = (m, top_k, n_out) if mode == MOE_GATE_UP else (m, n)
+        y = torch.empty(shape, dtype=out_dtype or torch.float32, device=x.device)
+    if y.dtype == torch.float32:
+        yt = X_F32
+    elif y.dtype == torch.bfloat16:
+        yt = X_BF16
+    else:
+        raise ValueError("y must be float32 or bfloat16")
+    gp = None
+    if norm_weight is not None:
+        if norm_weight.dtype != torch.float32:
+            raise ValueError("norm_weight must be float32")
+        gp = _dev_ptr(norm_weight, "norm_weight")
+    rp = None
+    if residual is not None:
+        if residual.dtype != torch.float32:
+            raise ValueError("residual must be float32")
+        rp = _dev_ptr(residual, "residual")
+    wp = None if topk_w is None else _dev_ptr(topk_w, "topk_w")
+    st = lib().moe_qgemv_topk_fused(fmt, _dev_ptr(w_experts, "w_experts"), n_experts, n, k,
+                                    _dev_ptr(topk_ids, "topk_ids"), wp, m, top_k, _dev_ptr(x, "x"), _xt(x), mode,
+                                    gp, float(eps), act, rp, _dev_ptr(y, "y"), yt, _stream(stream))
+    _check("moe_qgemv_topk_fused", st)
     return y
 
 

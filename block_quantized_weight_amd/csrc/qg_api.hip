@@ -577,22 +577,40 @@ int qgemv_fused(int fmt, const void *w, int64_t n, int64_t k, const void *x, int
     return err == hipSuccess ? launch_status() : QG_EHIP;
 }
 
-int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n, int64_t k,
-                   const int32_t *topk_ids, const float *topk_w, int64_t m, int64_t top_k,
-                   const void *x, int xt, int mode, float *y, void *stream)
+// The expert product, plain or fused (norm, gate, residual or a bf16 output
+// requested): fused calls run only on the streaming kernel.
+static int moe_impl(int fmt, const void *w_experts, int64_t n_experts, int64_t n, int64_t k,
+                    const int32_t *topk_ids, const float *topk_w, int64_t m, int64_t top_k, const void *x, int xt,
+                    int mode, const float *norm_weight, float norm_eps, int act, const float *residual, void *y, int yt,
+                    void *stream)
 {
     int st = check_shape(fmt, n, k);
     if (st) return st;
     if (!w_experts || !topk_ids || !x || !y) return QG_EINVAL;
     if (xt != QG_F32 && xt != QG_BF16) return QG_EINVAL;
+    if (yt != QG_F32 && yt != QG_BF16) return QG_EINVAL;
     if (mode != QG_MOE_GATE_UP && mode != QG_MOE_DOWN_COMBINE) return QG_EINVAL;
     if (mode == QG_MOE_DOWN_COMBINE && !topk_w) return QG_EINVAL;
+    if (act != QG_ACT_NONE && act != QG_ACT_SWIGLU) return QG_EINVAL;
+    if (mode == QG_MOE_GATE_UP && residual) return QG_EINVAL;
+    if (mode == QG_MOE_DOWN_COMBINE && (norm_weight || act != QG_ACT_NONE)) return QG_EINVAL;
+    if (norm_weight && !(norm_eps >= 0.0f && norm_eps <= 3.4e38f)) return QG_EINVAL;
+    if (act == QG_ACT_SWIGLU && (n % 2) != 0) return QG_EINVAL;
     if (m < 1 || m > QG_MAX_M || n_experts < 1 || top_k < 1 || top_k > n_experts) return QG_EINVAL;
     if (m * top_k > 64 || n_experts > 65536) return QG_EUNSUPPORTED;
-    if (!aligned(w_experts, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(topk_ids, 4) ||
-        (topk_w && !aligned(topk_w, 4)))
+    if (!aligned(w_experts, 16) || !aligned(x, 16) || !aligned(y, yt == QG_F32 ? 4 : 2) || !aligned(topk_ids, 4) ||
+        (topk_w && !aligned(topk_w, 4)) || (norm_weight && !aligned(norm_weight, 16)) ||
+        (residual && !aligned(residual, 4)))
         return QG_EALIGN;
+    const int64_t n_out = act == QG_ACT_SWIGLU ? n / 2 : n;
+    const int64_t ny = mode == QG_MOE_GATE_UP ? m * top_k * n_out : m * n_out;
+    if (residual && !(yt == QG_F32 && (const void *)residual == y) &&
+        overlaps(residual, (size_t)(ny * 4), y, (size_t)(ny * (yt == QG_F32 ? 4 : 2))))
+        return QG_EINVAL;
+    const bool fused = norm_weight || act != QG_ACT_NONE || residual || yt != QG_F32;
     const Layout lo = make_layout(fmt, n, k);
+    if (act == QG_ACT_SWIGLU && (n_out % lo.R) != 0) return QG_EUNSUPPORTED;
+    const bool norm = norm_weight != nullptr, glu = act == QG_ACT_SWIGLU;
     const bool dot = uses_dot(fmt, xt);
     MoeArgs a;
     a.experts = (const uint8_t *)w_experts;
@@ -603,11 +621,21 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
     a.m = (int32_t)m;
     a.top_k = (int32_t)top_k;
     a.isplit = 1;
+    EpiArgs e{};
+    e.gamma = norm_weight;
+    e.eps = norm_eps;
+    e.residual = residual;
+    e.y = y;
+    e.n_out = (int32_t)n_out;
+    e.half_tiles = glu ? (int32_t)(n_out / lo.R) : 0;
+    e.y_bf16 = yt == QG_BF16;
     hipStream_t s = as_stream(stream);
     {
         // streaming kernel: every activation row of the call staged at once
+        // (normalised rows in fp32)
         const int nrows = (int)(mode == QG_MOE_GATE_UP ? m : m * top_k);
-        const size_t lds = moe_stream_lds(fmt, dot, nrows, (int)(lo.S * lo.L), mode);
+        const size_t lds = moe_stream_lds(fmt, dot && !norm, nrows, (int)(lo.S * lo.L), mode,
+                                          glu ? (int)(m * top_k) : 0, lo.R);
         Geom g{};
         g.n = (int32_t)lo.n;
         g.k = (int32_t)lo.k;
@@ -630,23 +658,27 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
         g.KS = 1;
         g.ksh = 0;
         g.tpi = WAVES / IS;
-        g.ngroups = (int32_t)((lo.tiles + g.tpi - 1) / g.tpi);
+        // with the gate a workgroup holds WAVES / 2 gate/up tile pairs
+        g.ngroups = glu ? (int32_t)((e.half_tiles + WAVES / 2 - 1) / (WAVES / 2))
+                        : (int32_t)((lo.tiles + g.tpi - 1) / g.tpi);
         g.SW = (int32_t)lo.S;
         g.nwin = 1;
         g.wblk = (int32_t)(lo.S * lo.L);
-        if (lds <= MOE_STREAM_LDS && g.ngroups <= 65535) {
+        if (lds <= (glu ? MOE_STREAM_LDS_GLU : MOE_STREAM_LDS) && g.ngroups <= 65535) {
             g.w = (const uint8_t *)w_experts;
             const int ms = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
-            moe_stream_fn f = fmt == QG_Q8_0 ? moe_stream_kernel_q8_0(xt, mode, ms)
-                              : fmt == QG_Q4_0 ? moe_stream_kernel_q4_0(xt, mode, ms)
-                                               : moe_stream_kernel_mxfp4(xt, mode, ms);
-            void *args[] = {(void *)&g, (void *)&a, (void *)&x, (void *)&y};
+            moe_stream_fn f = fmt == QG_Q8_0 ? moe_stream_kernel_q8_0(xt, mode, ms, norm, glu)
+                              : fmt == QG_Q4_0 ? moe_stream_kernel_q4_0(xt, mode, ms, norm, glu)
+                                               : moe_stream_kernel_mxfp4(xt, mode, ms, norm, glu);
+            void *args[] = {(void *)&g, (void *)&a, (void *)&e, (void *)&x};
             if (allow_lds((const void *)f, lds) != hipSuccess) return QG_EHIP;
-            hipError_t e = hipLaunchKernel((const void *)f, dim3(g.ngroups), dim3(TPB), args, lds, s);
-            return e == hipSuccess ? launch_status() : QG_EHIP;
+            hipError_t err = hipLaunchKernel((const void *)f, dim3(g.ngroups), dim3(TPB), args, lds, s);
+            return err == hipSuccess ? launch_status() : QG_EHIP;
         }
     }
+    if (fused) return QG_EUNSUPPORTED;     // the per-expert kernels have no fused epilogue
     // general kernels: activations staged per expert in windows
+    float *yf = (float *)y;
     Plan p = make_plan(lo, QG_MAX_M, dot, QG_MAX_M);
     const int maxdistinct = (int)((m * top_k < n_experts) ? m * top_k : n_experts);
     size_t lds = p.lds;
@@ -654,11 +686,28 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
         const size_t rows_pg = (size_t)p.g.tpi * p.g.R;
         lds += (size_t)(m * top_k + QG_MAX_M) * rows_pg * 4;
     }
-    hipError_t e = fmt == QG_Q8_0 ? launch_moe_q8_0(xt, mode, p, a, maxdistinct, lds, x, y, s)
-                   : fmt == QG_Q4_0 ? launch_moe_q4_0(xt, mode, p, a, maxdistinct, lds, x, y, s)
-                                    : launch_moe_mxfp4(xt, mode, p, a, maxdistinct, lds, x, y, s);
-    if (e != hipSuccess) return QG_EHIP;
+    hipError_t err = fmt == QG_Q8_0 ? launch_moe_q8_0(xt, mode, p, a, maxdistinct, lds, x, yf, s)
+                     : fmt == QG_Q4_0 ? launch_moe_q4_0(xt, mode, p, a, maxdistinct, lds, x, yf, s)
+                                      : launch_moe_mxfp4(xt, mode, p, a, maxdistinct, lds, x, yf, s);
+    if (err != hipSuccess) return QG_EHIP;
     return launch_status();
+}
+
+int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n, int64_t k,
+                   const int32_t *topk_ids, const float *topk_w, int64_t m, int64_t top_k,
+                   const void *x, int xt, int mode, float *y, void *stream)
+{
+    return moe_impl(fmt, w_experts, n_experts, n, k, topk_ids, topk_w, m, top_k, x, xt, mode, nullptr, 0.0f,
+                    QG_ACT_NONE, nullptr, y, QG_F32, stream);
+}
+
+int moe_qgemv_topk_fused(int fmt, const void *w_experts, int64_t n_experts, int64_t n, int64_t k,
+                         const int32_t *topk_ids, const float *topk_w, int64_t m, int64_t top_k,
+                         const void *x, int xt, int mode, const float *norm_weight, float norm_eps, int act,
+                         const float *residual, void *y, int yt, void *stream)
+{
+    return moe_impl(fmt, w_experts, n_experts, n, k, topk_ids, topk_w, m, top_k, x, xt, mode, norm_weight, norm_eps,
+                    act, residual, y, yt, stream);
 }
 
 int moe_router_topk(const float *logits, int64_t m, int64_t n_experts, int64_t top_k, int32_t *ids, float *weights,

@@ -18,11 +18,20 @@
 //                 partials in a fixed order through LDS.
 // Only selected experts are read, each once per tile; the result is
 // deterministic (fixed item assignment and reduction order).
-#include "qg_common.h"
+//
+// Fused neighbours (the definitions of qg_fused.h): gate_up may normalise
+// the token rows (x * gamma staged in fp32, sum of x^2 formed while staging,
+// 1/rms applied to the row totals) and gate its output (SwiGLU: a workgroup
+// holds two gate/up tile pairs, one wave per tile; every wave streams its
+// tile for all items and leaves its per-slot row totals in LDS, and after
+// one barrier the workgroup combines gate and up and writes F outputs per
+// slot); down-combine may add a residual; either writes fp32 or bf16.
+#include "qg_fused.h"
 
 namespace qg {
 
 constexpr int MOE_STREAM_LDS = 96 * 1024;   // staged activations + partials per workgroup
+constexpr int MOE_STREAM_LDS_GLU = 144 * 1024;   // the same plus the gate's per-slot row totals
 
 // Work items (expert, up to MS slots), built in LDS by wave 0.
 struct MoeItems {
@@ -120,28 +129,38 @@ __device__ __forceinline__ bool stream_item(const Geom &g, const ItemWork &w, co
     }
 }
 
-inline __host__ __device__ size_t moe_stream_lds(int fmt, bool dot, int nrows, int wblk, int mode)
+// Dynamic LDS: staged rows, Q4_0 corrections, then down-combine's split
+// partials or, with the gate, the per-slot row totals of the tile pairs.
+inline __host__ __device__ size_t moe_stream_lds(int fmt, bool dot, int nrows, int wblk, int mode, int glu_slots = 0,
+                                                 int rows_per_tile = 0)
 {
     size_t b = (size_t)nrows * x_quads(fmt, dot) * wblk * 16;
     if (x_aux(fmt)) b += (size_t)nrows * wblk * 4;
     if (mode == QG_MOE_DOWN_COMBINE) b += (size_t)WAVES * QG_MAX_M * 64 * 4;
+    if (glu_slots) b += (size_t)WAVES * glu_slots * rows_per_tile * 4;
     return b;
 }
 
-// grid = ceil(tiles / tpi) workgroups, tpi = WAVES / IS tiles each; one
-// (tile, item subset) per wave.  Geom: KS = 1, one activation window over K.
-template <int FMT, bool XBF16, bool DOT, int MS, int MODE>
-__global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const void *__restrict__ x, float *__restrict__ y)
+// grid = ceil(tiles / tpi) workgroups, tpi = WAVES / IS tiles each (with
+// the gate: gate tiles, e.half_tiles of them); one (tile, item subset) per
+// wave.  Geom: KS = 1, one activation window over K.  NORM (gate_up only):
+// stage x * gamma in fp32 (DOT false).  GLU (gate_up only): SwiGLU.
+template <int FMT, bool XBF16, bool DOT, int MS, int MODE, bool NORM, bool GLU>
+__global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e, const void *__restrict__ x)
 {
+    static_assert(!NORM || !DOT, "normalised rows are staged in fp32");
+    static_assert(MODE == QG_MOE_GATE_UP || (!NORM && !GLU), "down-combine fuses only the residual");
     using E = Engine<FMT, XBF16, DOT, MS>;
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ MoeItems it;
+    __shared__ float s_part[WAVES * QG_MAX_M];
     constexpr int QPB = x_quads(FMT, DOT);
     const int nslots = a.m * a.top_k;
     const int nrows = MODE == QG_MOE_GATE_UP ? a.m : nslots;
     uint4 *xs = (uint4 *)smem;
     float *corr = (float *)(smem + (size_t)nrows * QPB * g.wblk * 16);
     float *red = corr + (x_aux(FMT) ? nrows * g.wblk : 0);
+    float *res = red;               // GLU: [2][PP][nslots][R] row totals (gate_up has no down partials)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int IS = a.isplit;
     const int tsub = wave / IS, ipart = wave - tsub * IS;
@@ -175,7 +194,13 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
     if (wave == 0) route_items(my_id, nslots, a.n_experts, MS, &it);
     __syncthreads();
     const int ni = it.count;
-    const int tile = blockIdx.x * g.tpi + tsub;
+    // with the gate (IS = 1, WAVES / 2 pairs per workgroup): waves [0, pp)
+    // hold gate tiles, waves [pp, 2 pp) the matching up tiles
+    constexpr int PP = WAVES / 2;
+    const int gpair = blockIdx.x * PP + (tsub % PP);
+    const bool upw = GLU && tsub >= PP;
+    const int tile = GLU ? (gpair < e.half_tiles ? gpair + (upw ? e.half_tiles : 0) : g.tiles)
+                         : blockIdx.x * g.tpi + tsub;
     const int tl = tile < g.tiles ? tile : 0;
     const int nsteps = (tile < g.tiles && ipart < ni) ? g.S : 0;
     auto work = [&](int i) {
@@ -196,12 +221,49 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
 
     // stage every activation row of the call (row r = token for gate_up,
     // slot for down), one window over all of K
+    float ss[QG_MAX_M];             // NORM: this thread's sums of x^2 per token row
+#pragma unroll
+    for (int t = 0; t < QG_MAX_M; ++t) ss[t] = 0.0f;
     auto stage_unit = [&](int idx, const uint4 (&raw)[8]) {
         const int r = idx / g.wblk, bl = idx - r * g.wblk;
         uint4 q[8];
         float av = 0.0f;
         if (bl < g.nb) {
-            av = stage_block<FMT, XBF16, DOT>(raw, q);
+            if constexpr (NORM) {
+                // x (exact in fp32) times gamma, in the fp32 form; x^2 summed per row
+                uint4 xf[8];
+                if (XBF16) {
+                    const uint32_t *rw = (const uint32_t *)raw;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        xf[i] = make_uint4(rw[2 * i] << 16, rw[2 * i] & 0xFFFF0000u, rw[2 * i + 1] << 16,
+                                           rw[2 * i + 1] & 0xFFFF0000u);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xf[i] = raw[i];
+                }
+                const uint4 *gs = (const uint4 *)(e.gamma + (int64_t)bl * QK);
+                float sq = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint4 gv = ld_global16(gs + i);
+                    const float x0 = __builtin_bit_cast(float, xf[i].x), x1 = __builtin_bit_cast(float, xf[i].y);
+                    const float x2 = __builtin_bit_cast(float, xf[i].z), x3 = __builtin_bit_cast(float, xf[i].w);
+                    sq = fmaf(x0, x0, sq);
+                    sq = fmaf(x1, x1, sq);
+                    sq = fmaf(x2, x2, sq);
+                    sq = fmaf(x3, x3, sq);
+                    xf[i] = make_uint4(__builtin_bit_cast(uint32_t, x0 * __builtin_bit_cast(float, gv.x)),
+                                       __builtin_bit_cast(uint32_t, x1 * __builtin_bit_cast(float, gv.y)),
+                                       __builtin_bit_cast(uint32_t, x2 * __builtin_bit_cast(float, gv.z)),
+                                       __builtin_bit_cast(uint32_t, x3 * __builtin_bit_cast(float, gv.w)));
+                }
+#pragma unroll
+                for (int t = 0; t < QG_MAX_M; ++t) ss[t] += t == r ? sq : 0.0f;
+                av = stage_block<FMT, false, false>(xf, q);
+            } else {
+                av = stage_block<FMT, XBF16, DOT>(raw, q);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) q[i] = make_uint4(0, 0, 0, 0);
@@ -222,6 +284,7 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
         for (int i = 0; i < NLD; ++i) raw[i] = ld_global16(src + 16 * i);
         stage_unit(idx, raw);
     }
+    if constexpr (NORM) NormStage<XBF16>::template publish<QG_MAX_M>(ss, s_part);
     __syncthreads();
 
     const int64_t row = (int64_t)tile * g.R + rsub;
@@ -257,10 +320,22 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
 #pragma unroll
                 for (int t = 0; t < MS; ++t) acc[t] += __shfl_xor(acc[t], off, 64);
             }
-            if (nsteps > 0 && row < g.n) {
+            if constexpr (GLU) {
+                // row totals of this wave's tile per slot: res[up][pair][slot][row in tile]
+                if (nsteps > 0) {
 #pragma unroll
-                for (int t = 0; t < MS; ++t)
-                    if (t < sm.n && (t & (g.L - 1)) == slot) y[(int64_t)it.s[i][t] * g.n + row] = acc[t];
+                    for (int t = 0; t < MS; ++t)
+                        if (t < sm.n && (t & (g.L - 1)) == slot)
+                            res[(((upw ? PP : 0) + tsub % PP) * nslots + it.s[i][t]) * g.R + rsub] = acc[t];
+                }
+            } else if (nsteps > 0 && row < e.n_out) {
+#pragma unroll
+                for (int t = 0; t < MS; ++t) {
+                    if (t < sm.n && (t & (g.L - 1)) == slot) {
+                        const float v = NORM ? acc[t] * rinv_of<WAVES>(s_part, sm.r[t], g.k, e.eps) : acc[t];
+                        store_out(e, (int64_t)it.s[i][t] * e.n_out + row, v);
+                    }
+                }
             }
         } else {
 #pragma unroll
@@ -273,6 +348,25 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
                 for (int q = 0; q < QG_MAX_M; ++q)
                     if (q == tk) tok[q] = __builtin_fmaf(gw, acc[t], tok[q]);
             }
+        }
+    }
+    if constexpr (GLU) {
+        // every wave has left its totals; the workgroup writes SiLU(g) * u
+        __syncthreads();
+        const int per = nslots * g.R;
+        for (int idx = threadIdx.x; idx < PP * per; idx += (int)blockDim.x) {
+            const int pr = idx / per, rem = idx - pr * per;
+            const int sid = rem / g.R, rs = rem - sid * g.R;
+            const int pair = blockIdx.x * PP + pr;
+            const int id = a.ids[sid];
+            if (pair >= e.half_tiles || id < 0 || id >= a.n_experts) continue;     // no such pair, or no output
+            float gv = res[(pr * nslots + sid) * g.R + rs], uv = res[((PP + pr) * nslots + sid) * g.R + rs];
+            if (NORM) {
+                const float r = rinv_of<WAVES>(s_part, sid / a.top_k, g.k, e.eps);
+                gv *= r;
+                uv *= r;
+            }
+            store_out(e, (int64_t)sid * e.n_out + (int64_t)pair * g.R + rs, silu(gv) * uv);
         }
     }
     if (MODE == QG_MOE_DOWN_COMBINE) {
@@ -294,34 +388,40 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, const voi
         if (ipart == 0 && tile < g.tiles && row < g.n) {
 #pragma unroll
             for (int t = 0; t < QG_MAX_M; ++t)
-                if (t < a.m && (t & (g.L - 1)) == slot) y[(int64_t)t * g.n + row] = tok[t];
+                if (t < a.m && (t & (g.L - 1)) == slot) store_out(e, (int64_t)t * g.n + row, tok[t]);
         }
     }
 }
 
-typedef void (*moe_stream_fn)(Geom, MoeArgs, const void *, float *);
+typedef void (*moe_stream_fn)(Geom, MoeArgs, EpiArgs, const void *);
 
-template <int FMT, bool XBF16, bool DOT>
-moe_stream_fn pick_moe_stream(int mode, int ms)
+template <int FMT, bool XBF16, bool DOT, int MODE, bool NORM, bool GLU>
+moe_stream_fn pick_moe_stream_ms(int ms)
 {
-    if (mode == QG_MOE_GATE_UP) {
-        switch (ms) {
-        case 1: return k_moe_stream<FMT, XBF16, DOT, 1, QG_MOE_GATE_UP>;
-        case 2: return k_moe_stream<FMT, XBF16, DOT, 2, QG_MOE_GATE_UP>;
-        case 4: return k_moe_stream<FMT, XBF16, DOT, 4, QG_MOE_GATE_UP>;
-        default: return k_moe_stream<FMT, XBF16, DOT, 8, QG_MOE_GATE_UP>;
-        }
-    }
     switch (ms) {
-    case 1: return k_moe_stream<FMT, XBF16, DOT, 1, QG_MOE_DOWN_COMBINE>;
-    case 2: return k_moe_stream<FMT, XBF16, DOT, 2, QG_MOE_DOWN_COMBINE>;
-    case 4: return k_moe_stream<FMT, XBF16, DOT, 4, QG_MOE_DOWN_COMBINE>;
-    default: return k_moe_stream<FMT, XBF16, DOT, 8, QG_MOE_DOWN_COMBINE>;
+    case 1: return k_moe_stream<FMT, XBF16, DOT, 1, MODE, NORM, GLU>;
+    case 2: return k_moe_stream<FMT, XBF16, DOT, 2, MODE, NORM, GLU>;
+    case 4: return k_moe_stream<FMT, XBF16, DOT, 4, MODE, NORM, GLU>;
+    default: return k_moe_stream<FMT, XBF16, DOT, 8, MODE, NORM, GLU>;
     }
 }
 
-moe_stream_fn moe_stream_kernel_q8_0(int xt, int mode, int ms);
-moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms);
-moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms);
+// gate_up: the plain form, or normalised and/or gated (normalised rows are
+// staged in fp32, so those kernels take DOT false); down-combine: one form
+// (residual and output type are arguments).
+template <int FMT, bool XBF16, bool DOT>
+moe_stream_fn pick_moe_stream(int mode, int ms, bool norm, bool glu)
+{
+    if (mode == QG_MOE_DOWN_COMBINE) return pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_DOWN_COMBINE, false, false>(ms);
+    if (norm)
+        return glu ? pick_moe_stream_ms<FMT, XBF16, false, QG_MOE_GATE_UP, true, true>(ms)
+                   : pick_moe_stream_ms<FMT, XBF16, false, QG_MOE_GATE_UP, true, false>(ms);
+    return glu ? pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_GATE_UP, false, true>(ms)
+               : pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_GATE_UP, false, false>(ms);
+}
+
+moe_stream_fn moe_stream_kernel_q8_0(int xt, int mode, int ms, bool norm, bool glu);
+moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms, bool norm, bool glu);
+moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms, bool norm, bool glu);
 
 } // namespace qg

@@ -27,9 +27,10 @@ int chain_error_mxfp4(bool clear) { return chain_error_read(clear); }
 
 mfma_fn mfma_kernel_mxfp4(int L) { return pick_mfma<QG_MXFP4>(L); }
 
-moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms)
+moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms, bool norm, bool glu)
 {
-    return xt == QG_BF16 ? pick_moe_stream<QG_MXFP4, true, true>(mode, ms) : pick_moe_stream<QG_MXFP4, false, false>(mode, ms);
+    return xt == QG_BF16 ? pick_moe_stream<QG_MXFP4, true, true>(mode, ms, norm, glu)
+                         : pick_moe_stream<QG_MXFP4, false, false>(mode, ms, norm, glu);
 }
 
 dense_ep_fn dense_ep_kernel_mxfp4(int xt, int m, bool norm, bool glu)

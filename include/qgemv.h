@@ -215,6 +215,28 @@ int moe_qgemv_topk(int fmt, const void *w_experts, int64_t n_experts, int64_t n,
                    const void *x, int xt, int mode, float *y, void *stream);
 
 /*
+ * Top-k expert product with its decode-step neighbours fused in (the
+ * definitions of qgemv_fused, per slot; the pages' MoE layers are gated
+ * FFNs whose gate_up matrices have twice the down matrix's K rows):
+ *   QG_MOE_GATE_UP:      y[t][j] = act(W_{ids[t][j]} x'_t), x'_t = RMSNorm(x_t) when
+ *                        norm_weight is given; act = SwiGLU (gate rows first,
+ *                        n_out = n / 2) or none.  y [m][top_k][n_out]; residual
+ *                        must be NULL.  Rows of slots with invalid ids are not written.
+ *   QG_MOE_DOWN_COMBINE: y[t] = sum over j of topk_w[t][j] * W_{ids[t][j]} x[t][j]
+ *                        (+ residual[t]); y [m][n]; norm_weight must be NULL and
+ *                        act QG_ACT_NONE.  residual: fp32 [m][n] or NULL; with an
+ *                        fp32 y it may be y itself.
+ * Other arguments as moe_qgemv_topk; norm_weight, norm_eps, yt as qgemv_fused.
+ * Only the streaming kernel serves these calls: QG_EUNSUPPORTED when the
+ * call's activation rows (fp32 when normalised) exceed its 96 KiB of LDS,
+ * or with SwiGLU when F is not a multiple of the layout's rows per tile.
+ */
+int moe_qgemv_topk_fused(int fmt, const void *w_experts, int64_t n_experts, int64_t n, int64_t k,
+                         const int32_t *topk_ids, const float *topk_w, int64_t m, int64_t top_k,
+                         const void *x, int xt, int mode, const float *norm_weight, float norm_eps, int act,
+                         const float *residual, void *y, int yt, void *stream);
+
+/*
  * Top-k routing on the device, producing moe_qgemv_topk's ids and weights
  * without a host round trip (imp keeps MoE routing on the device so the
  * decode graph stays capturable: imp release notes v0.7.0, known issues).

@@ -231,3 +231,32 @@ def test_fused_argument_validation():
     lo = q.layout(q.Q8_0, 2 * 4100, 2560)
     assert 4100 % lo["rows_per_tile"] != 0
     assert call(act=q.ACT_SWIGLU, n=2 * 4100, k=2560) == q.QG_EUNSUPPORTED
+
+
+def test_moe_fused_argument_validation():
+    """moe_qgemv_topk_fused rejects bad arguments before any device work."""
+    L = q.lib()
+    a = ctypes.c_void_p(1 << 20)
+    b = ctypes.c_void_p(1 << 24)
+    ODD = ctypes.c_void_p((1 << 20) + 2)
+    f = ctypes.c_float
+
+    def call(fmt=q.MXFP4, n=1024, k=512, m=2, top_k=4, mode=q.MOE_GATE_UP, g=None, eps=1e-6, act=q.ACT_NONE,
+             res=None, y=b, yt=q.X_F32, w=a, x=a):
+        return L.moe_qgemv_topk_fused(fmt, w, 16, n, k, a, a, m, top_k, x, q.X_BF16, mode, g, f(eps), act, res, y,
+                                      yt, None)
+
+    assert call(res=a) == q.QG_EINVAL                                  # gate_up takes no residual
+    assert call(mode=q.MOE_DOWN_COMBINE, g=a) == q.QG_EINVAL           # down takes no normalisation
+    assert call(mode=q.MOE_DOWN_COMBINE, act=q.ACT_SWIGLU) == q.QG_EINVAL
+    assert call(act=3) == q.QG_EINVAL and call(yt=5) == q.QG_EINVAL
+    assert call(g=a, eps=-1.0) == q.QG_EINVAL and call(g=a, eps=float("nan")) == q.QG_EINVAL
+    assert call(act=q.ACT_SWIGLU, n=1023) == q.QG_EINVAL
+    assert call(g=ODD) == q.QG_EALIGN and call(y=ctypes.c_void_p((1 << 24) + 2)) == q.QG_EALIGN
+    assert call(mode=q.MOE_DOWN_COMBINE, res=ctypes.c_void_p((1 << 24) + 8)) == q.QG_EINVAL   # overlaps y
+    assert call(mode=q.MOE_DOWN_COMBINE, res=b, yt=q.X_BF16) == q.QG_EINVAL
+    lo = q.layout(q.Q8_0, 2 * 4100, 2560)
+    assert 4100 % lo["rows_per_tile"] != 0
+    assert call(fmt=q.Q8_0, n=2 * 4100, k=2560, act=q.ACT_SWIGLU) == q.QG_EUNSUPPORTED
+    # eight normalised (fp32-staged) rows of K = 4096 need 128 KiB of LDS: refused, not run elsewhere
+    assert call(k=4096, m=8, top_k=2, g=a) == q.QG_EUNSUPPORTED
