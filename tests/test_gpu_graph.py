@@ -63,6 +63,16 @@ def test_graph_replays_match_eager(dev):
     gw = torch.empty((m, top_k), device=dev)
     yg = torch.empty((m, top_k, gn), device=dev)
     yd = torch.empty((m, dn), device=dev)
+    # fused: dense RMSNorm + SwiGLU -> bf16 (Q4_0 gate_up 2 x 1024 rows, K 2048), expert gate_up
+    # with RMSNorm + SwiGLU -> bf16, expert down-combine with the residual added in place
+    w3 = _packed(q.Q4_0, 2048, 2048, 90, 2, dev)
+    gam3 = torch.from_numpy(wl.norm_weight_f32(2048, wl.rng_for(90, 2, "gamma"))).to(dev)
+    y3 = torch.empty((4, 1024), dtype=torch.bfloat16, device=dev)
+    hid = torch.from_numpy(wl.x_f32((m, gk), wl.rng_for(91, 1, "x"))).to(dev)
+    gam4 = torch.from_numpy(wl.norm_weight_f32(gk, wl.rng_for(91, 1, "gamma"))).to(dev)
+    ya = torch.empty((m, top_k, gn // 2), dtype=torch.bfloat16, device=dev)
+    res = torch.from_numpy(wl.x_f32((m, dn), wl.rng_for(91, 1, "res"))).to(dev)
+    yr = torch.empty((m, dn), device=dev)
 
     def step():
         q.qgemv(q.Q8_0, w1, n1, k1, x1, y=y1)
@@ -70,8 +80,13 @@ def test_graph_replays_match_eager(dev):
         q.moe_router_topk(logits, top_k, ids=ids, weights=gw)
         q.moe_qgemv_topk(fmt, ge, E, gn, gk, ids, gw, xg, q.MOE_GATE_UP, y=yg)
         q.moe_qgemv_topk(fmt, de, E, dn, dk, ids, gw, hd, q.MOE_DOWN_COMBINE, y=yd)
+        q.qgemv_fused(q.Q4_0, w3, 2048, 2048, x2, norm_weight=gam3, act=q.ACT_SWIGLU, y=y3)
+        q.moe_qgemv_topk_fused(fmt, ge, E, gn, gk, ids, gw, hid, q.MOE_GATE_UP, norm_weight=gam4,
+                               act=q.ACT_SWIGLU, y=ya)
+        yr.copy_(res)
+        q.moe_qgemv_topk_fused(fmt, de, E, dn, dk, ids, gw, hd, q.MOE_DOWN_COMBINE, residual=yr, y=yr)
 
-    outs = (y1, y2, ids, gw, yg, yd)
+    outs = (y1, y2, ids, gw, yg, yd, y3, ya, yr)
 
     def eager():
         step()
