@@ -46,11 +46,12 @@ def parse():
     ap.add_argument("--no-events", action="store_true", help="skip the roofline / per-shape timing pass")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", choices=["c2", "c2f", "c0", "c1", "c3", "c4"], default="c2",
+    ap.add_argument("--workload", choices=["c2", "c2f", "c0", "c1", "c3", "c4", "gemm"], default="c2",
                     help="c2: the full Q8_0 decode sweep (the headline line); c2f: the same sweep with the decode "
                          "step's neighbours fused in (RMSNorm, SwiGLU, residual; qgemv_fused) next to the plain "
                          "sweep; c0/c1/c3/c4: the other workloads, each timed over >= 1 GiB of distinct weight "
-                         "copies so the device-side cache cannot serve repeated reads")
+                         "copies so the device-side cache cannot serve repeated reads; gemm: qgemm on the c3 "
+                         "matrices at 16..128 tokens")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -183,7 +184,54 @@ def run_other(args):
                                  "frac": round(useful_flop / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 5)}
             emit(f"{label} m={m}", gbs, us, extra)
 
-    if args.workload == "c0":
+    def gemm_case(cfg, mats, ms, label):
+        """qgemm on bf16 tokens: each matrix and the whole set per token count, against the
+        same tokens as co-batch calls of 8 (qgemv)."""
+        fmt = wl.CONFIGS[cfg]["fmt"]
+        wsz = sum(q.packed_bytes(fmt, n, k) for _, n, k, _ in mats)
+        reps = copies_for(wsz)
+        ws = {}
+        for name, n, k, j in mats:
+            ws[name] = packed_copies(fmt, wl.blocks_for(fmt, n, k, config=cfg, matrix=j), n, k, reps)
+        for m in ms:
+            xs = {name: bf16_dev(wl.x_bf16_bits((m, k), wl.rng_for(cfg, j, "x"))) for name, n, k, j in mats}
+            ys = {name: torch.empty((m, n), dtype=torch.float32, device=dev) for name, n, k, j in mats}
+            set_bytes = sum(n * (k // 32) * wl.BLOCK_BYTES[fmt] + m * k * 2 + m * n * 4 for _, n, k, _ in mats)
+            flop = sum(2 * m * n * k for _, n, k, _ in mats)
+            per = {}
+            for name, n, k, j in mats:
+                def one(name=name, n=n, k=k):
+                    for r in range(reps):
+                        q.qgemm(fmt, ws[name][r], n, k, xs[name], y=ys[name])
+                us = graph_time(torch, one, max(2, args.steps // 3)) / reps
+                b = n * (k // 32) * wl.BLOCK_BYTES[fmt] + m * k * 2 + m * n * 4
+                per[name] = {"n": n, "k": k, "us": round(us, 3), "gbs": round(b / us / 1e3, 1),
+                             "tflops": round(2 * m * n * k / us / 1e6, 2),
+                             "path": "mfma" if q.gemm_path(fmt, n, k, q.X_BF16, m) == q.PATH_MFMA else "valu"}
+
+            def whole():
+                for r in range(reps):
+                    for name, n, k, j in mats:
+                        q.qgemm(fmt, ws[name][r], n, k, xs[name], y=ys[name])
+
+            def cobatch():
+                for r in range(reps):
+                    for name, n, k, j in mats:
+                        for t0 in range(0, m, 8):
+                            q.qgemv(fmt, ws[name][r], n, k, xs[name][t0:t0 + 8], y=ys[name][t0:t0 + 8])
+            us = graph_time(torch, whole, max(2, args.steps // 3)) / reps
+            us8 = graph_time(torch, cobatch, max(2, args.steps // 3)) / reps
+            emit(f"{label} m={m}", set_bytes / us / 1e3, us,
+                 {"per_matrix": per, "bytes_per_set": set_bytes, "tokens_per_s": round(m * 1e6 / us, 1),
+                  "weight_copies": reps,
+                  "mfma": {"useful_tflops": round(flop / us / 1e6, 2), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                           "frac": round(flop / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 5)},
+                  "as_cobatches_of_8": {"us": round(us8, 3), "tokens_per_s": round(m * 1e6 / us8, 1)}})
+
+    if args.workload == "gemm":
+        gemm_case(3, [("qkv", 6144, 4096, 0), ("gate_up", 24576, 4096, 1), ("down", 4096, 12288, 2)],
+                  [16, 32, 64, 128], "q4_0 qgemm, 8b-like: qkv 6144x4096 + gate_up 24576x4096 + down 4096x12288")
+    elif args.workload == "c0":
         dense_case(0, [("w", 2048, 2048, 0)], "f32", [1], "q8_0 2048x2048, x fp32")
     elif args.workload == "c1":
         dense_case(1, [("gate_up", 19456, 2560, 0), ("down", 2560, 9728, 1)], "bf16", [1],

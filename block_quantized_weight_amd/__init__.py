@@ -19,6 +19,7 @@ Q8_0, Q4_0, MXFP4 = 0, 1, 2
 X_F32, X_BF16 = 0, 1
 MOE_GATE_UP, MOE_DOWN_COMBINE = 0, 1
 MAX_M = 8
+MAX_GEMM_M = 128
 PATH_VALU, PATH_MFMA = 0, 1
 ACT_NONE, ACT_SWIGLU = 0, 1
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17}
@@ -38,6 +39,8 @@ SIGNATURES = {
     "qgemv_q8_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_q4_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_mxfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
+    "qgemm": (_i, [_i, _vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
+    "qg_gemm_path": (_i, [_i, _i64, _i64, _i, _i64]),
     "qgemv_fused": (_i, [_i, _vp, _i64, _i64, _vp, _i, _i64, _vp, ctypes.c_float, _i, _vp, _vp, _i, _vp]),
     "moe_qgemv_topk": (_i, [_i, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i, _i, _vp, _vp]),
     "moe_qgemv_topk_fused": (_i, [_i, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _i, _i, _vp, ctypes.c_float,
@@ -228,6 +231,27 @@ def qgemv_q4_0(w_packed, n, k, x, y=None, stream=None):
 
 def qgemv_mxfp4(w_packed, n, k, x, y=None, stream=None):
     return qgemv(MXFP4, w_packed, n, k, x, y, stream)
+
+
+def gemm_path(fmt, n, k, xt, m):
+    """PATH_VALU or PATH_MFMA: the kernel family a qgemm call would run."""
+    v = lib().qg_gemm_path(fmt, n, k, xt, m)
+    if v < 0:
+        raise QGError("qg_gemm_path", -v)
+    return v
+
+
+def qgemm(fmt, w_packed, n, k, x, y=None, stream=None):
+    """y[m, n] = W x[m, k]^T for 1 <= m <= MAX_GEMM_M tokens (float32 or bfloat16 x)."""
+    torch = _torch()
+    x2 = x.reshape(-1, k)
+    m = x2.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    st = lib().qgemm(fmt, _dev_ptr(w_packed, "w_packed"), n, k, _dev_ptr(x2, "x"), _xt(x2), m, _dev_ptr(y, "y"),
+                     _stream(stream))
+    _check("qgemm", st)
+    return y
 
 
 def qgemv_fused(fmt, w_packed, n, k, x, norm_weight=None, eps=1e-6, act=ACT_NONE, residual=None, y=None,

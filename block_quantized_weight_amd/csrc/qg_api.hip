@@ -245,7 +245,12 @@ bool mfma_fits(const Layout &lo, int xt, int64_t m)
     return lo.ctb * tpw < ((int64_t)1 << 31) && lo.stb * tpw < ((int64_t)1 << 31);
 }
 
-MPlan make_mplan(const Layout &lo, int m)
+// m: tokens the LDS holds (one group of at most 16); groups > 0 (the
+// many-token product): the split-K factor is the smallest that still gives
+// ~512 workgroups over all groups, since each workgroup stages the
+// activations once for its WAVES / KS units (more units per workgroup means
+// fewer re-reads of the activations).
+MPlan make_mplan(const Layout &lo, int m, int groups = 0)
 {
     MPlan p{};
     MGeom &g = p.g;
@@ -263,13 +268,21 @@ MPlan make_mplan(const Layout &lo, int m)
     const int64_t tpw = lo.L >= 8 ? lo.L / 4 : 1;
     g.units = (int32_t)((lo.tiles + tpw - 1) / tpw);
     const size_t per_block = (size_t)m * 64;
-    const int64_t xbudget = (int64_t)MFMA_WG_LDS - (int64_t)mfma_lds_bytes(lo.fmt, m, 0, lo.L);
-    int64_t sw_max = (xbudget / (int64_t)per_block) / lo.L;
-    if (sw_max < 1) sw_max = 1;
+    // activation window: as many steps as fit beside the fixed areas (at least one)
+    auto sw_for = [&](int ks) {
+        const int64_t xbudget = (int64_t)MFMA_WG_LDS - (int64_t)mfma_lds_bytes(lo.fmt, m, 0, lo.L, ks);
+        const int64_t v = (xbudget / (int64_t)per_block) / lo.L;
+        return v < 1 ? (int64_t)1 : v;
+    };
     int KS = 1;
-    if (g.units < 4096) KS = 2;
-    if (g.units < 2048) KS = 4;
-    while (KS > 1 && (lo.S < KS || sw_max < KS)) KS >>= 1;
+    if (groups > 0) {
+        while (KS < WAVES && ((g.units + WAVES / KS - 1) / (WAVES / KS)) * groups < 512) KS <<= 1;
+    } else {
+        if (g.units < 4096) KS = 2;
+        if (g.units < 2048) KS = 4;
+    }
+    while (KS > 1 && (lo.S < KS || sw_for(KS) < KS)) KS >>= 1;
+    const int64_t sw_max = sw_for(KS);
     g.KS = KS;
     g.ksh = ilog2(KS);
     g.upi = WAVES / KS;
@@ -279,7 +292,7 @@ MPlan make_mplan(const Layout &lo, int m)
     g.SW = (int32_t)sw;
     g.nwin = (int32_t)((lo.S + sw - 1) / sw);
     g.wblk = (int32_t)(sw * lo.L);
-    p.lds = mfma_lds_bytes(lo.fmt, m, g.wblk, lo.L);
+    p.lds = mfma_lds_bytes(lo.fmt, m, g.wblk, lo.L, KS);
     p.grid = g.ngroups > 65535 ? 65535 : g.ngroups;
     return p;
 }
@@ -516,6 +529,56 @@ int qgemv_q4_0(const void *w, int64_t n, int64_t k, const void *x, int xt, int64
 int qgemv_mxfp4(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
 {
     return dense(QG_MXFP4, w, n, k, x, xt, m, y, stream);
+}
+
+// Token groups on the matrix cores: bf16 activations, layouts of at most
+// GEMM_MAX_L lanes per row, 32-bit per-lane tile offsets.
+static bool gemm_fits(const Layout &lo, int xt)
+{
+    if (xt != QG_BF16 || lo.L > GEMM_MAX_L) return false;
+    const int64_t tpw = lo.L >= 8 ? lo.L / 4 : 1;
+    return lo.ctb * tpw < ((int64_t)1 << 31) && lo.stb * tpw < ((int64_t)1 << 31);
+}
+
+int qg_gemm_path(int fmt, int64_t n, int64_t k, int xt, int64_t m)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return -st;
+    if (xt != QG_F32 && xt != QG_BF16) return -QG_EINVAL;
+    if (m < 1 || m > QG_MAX_GEMM_M) return -QG_EINVAL;
+    return gemm_fits(make_layout(fmt, n, k), xt) ? QG_PATH_MFMA : QG_PATH_VALU;
+}
+
+int qgemm(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
+{
+    int st = check_shape(fmt, n, k);
+    if (st) return st;
+    if (!w || !x || !y) return QG_EINVAL;
+    if (xt != QG_F32 && xt != QG_BF16) return QG_EINVAL;
+    if (m < 1 || m > QG_MAX_GEMM_M) return QG_EINVAL;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
+    const Layout lo = make_layout(fmt, n, k);
+    if (gemm_fits(lo, xt)) {
+        // one launch: grid.y = token groups of 16, LDS planned for one group
+        const int groups = (int)((m + 15) / 16);
+        MPlan p = make_mplan(lo, (int)(m < 16 ? m : 16), groups);
+        p.g.m = (int32_t)m;
+        p.g.w = (const uint8_t *)w;
+        mfma_fn f = fmt == QG_Q8_0 ? mfma_kernel_q8_0(lo.L) : fmt == QG_Q4_0 ? mfma_kernel_q4_0(lo.L) : mfma_kernel_mxfp4(lo.L);
+        void *args[] = {(void *)&p.g, (void *)&x, (void *)&y};
+        if (allow_lds((const void *)f, p.lds) != hipSuccess) return QG_EHIP;
+        hipError_t e = hipLaunchKernel((const void *)f, dim3(p.grid, (unsigned)groups), dim3(TPB), args, p.lds,
+                                       as_stream(stream));
+        return e == hipSuccess ? launch_status() : QG_EHIP;
+    }
+    // otherwise the dense product, QG_MAX_M tokens per launch
+    const size_t xsz = xt == QG_BF16 ? 2 : 4;
+    for (int64_t t0 = 0; t0 < m; t0 += QG_MAX_M) {
+        const int64_t mt = m - t0 < QG_MAX_M ? m - t0 : QG_MAX_M;
+        st = dense(fmt, w, n, k, (const uint8_t *)x + t0 * k * xsz, xt, mt, y + t0 * n, stream);
+        if (st) return st;
+    }
+    return QG_OK;
 }
 
 static bool overlaps(const void *a, size_t abytes, const void *b, size_t bbytes)

@@ -39,13 +39,14 @@ namespace qg {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int MFMA_MAX_L = 8;     // lanes per row served by this kernel
+constexpr int MFMA_MAX_L = 8;     // lanes per row served for co-batches of up to 8 tokens
+constexpr int GEMM_MAX_L = 16;    // lanes per row served for token groups (qgemm)
 
 struct MGeom {
     const uint8_t *w;
     int32_t n, k, nb, L, R, S, tiles;
     int64_t ctb, stb, soff;
-    int32_t m;                       // tokens (1 .. 8)
+    int32_t m;                       // tokens of the call; each blockIdx.y runs a group of up to 16
     int32_t units, KS, ksh, upi, ngroups;
     int32_t SW, nwin, wblk;
 };
@@ -69,11 +70,17 @@ inline __host__ __device__ int mfma_wave_bytes(int fmt, int LL)
     return tpw * P * MPLANE + tpw * 64 * 4;
 }
 
-inline __host__ __device__ size_t mfma_lds_bytes(int fmt, int m, int wblk, int LL)
+// Split-K partials (present only when KS > 1).
+inline __host__ __device__ size_t mfma_red_bytes(int LL)
 {
     const int RG = LL >= 4 ? 1 : 4 / LL;
+    return (size_t)WAVES * RG * 4 * 64 * 4;
+}
+
+inline __host__ __device__ size_t mfma_lds_bytes(int fmt, int m, int wblk, int LL, int KS)
+{
     size_t b = (size_t)wblk * m * 64;                        // activations: [block][token][octet]
-    b += (size_t)WAVES * RG * 4 * 64 * 4;                    // split-K partials
+    if (KS > 1) b += mfma_red_bytes(LL);                     // split-K partials
     b += (size_t)WAVES * mfma_wave_bytes(fmt, LL);           // transpose areas
     return b;
 }
@@ -84,7 +91,8 @@ struct MEngine {
     static constexpr int P = FMT == QG_Q8_0 ? 2 : 1;        // 16-byte parts per record
     static constexpr int TPW = Sh::TPW;
     static constexpr int NM = Sh::NM;
-    static constexpr int U = FMT == QG_Q8_0 ? 2 : 4;        // steps per load batch
+    // steps per load batch (16 lanes per row load 4 tiles per step: fewer steps)
+    static constexpr int U = LL >= 16 ? (FMT == QG_Q8_0 ? 1 : 2) : (FMT == QG_Q8_0 ? 2 : 4);
 
     struct Regs {
         uint4 c[U][TPW][P];
@@ -149,10 +157,10 @@ struct MEngine {
         return FMT == QG_MXFP4 ? e8m0_to_f32(bits) : f16_bits_to_f32(bits);
     }
 
-    // The MFMAs of one step (block index jL + s of every row of the unit).
-    // wl: this wave's transpose area.
+    // The MFMAs of one step (block index jL + s of every row of the unit)
+    // for the mp (<= 16) tokens of the group.  wl: this wave's transpose area.
     static __device__ __forceinline__ void step(const MGeom &g, const Regs &r, int u, int j, int b0, const uint4 *xs,
-                                                uint8_t *wl, f32x4_t acc[Sh::RG])
+                                                uint8_t *wl, f32x4_t (&acc)[Sh::RG], int mp)
     {
         const int lane = threadIdx.x & 63, i = lane & 15, oct = lane >> 4;
         float *wsc = (float *)(wl + TPW * P * MPLANE);
@@ -162,18 +170,12 @@ struct MEngine {
             for (int h = 0; h < P; ++h) *(uint4 *)(wl + (tt * P + h) * MPLANE + slot(lane)) = r.c[u][tt][h];
             wsc[tt * 64 + lane] = scale(r.s[u][tt]);
         }
-        const int ic = min(i, g.m - 1);
 #pragma unroll
         for (int s = 0; s < Sh::NS; ++s) {
             const int bl = j * LL + s - b0;
-            uint4 av = xs[(bl * g.m + ic) * 4 + oct];
-            if (i >= g.m) av = make_uint4(0, 0, 0, 0);
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
-            f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (FMT == QG_Q4_0) {
-                const bf16x8_t k136 = __builtin_bit_cast(bf16x8_t, make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, k136, c, 0, 0, 0);    // -136 * sum(x), every row
-            }
+            // the rows' weight operands and scales
+            bf16x8_t bw[Sh::RG];
+            float sc[Sh::RG];
 #pragma unroll
             for (int G = 0; G < Sh::RG; ++G) {
                 const int tt = LL >= 8 ? i / Sh::R : 0;
@@ -188,30 +190,43 @@ struct MEngine {
                     cw[0] = *(const uint32_t *)(wl + tt * MPLANE + slot(sl) + 4 * oct);
                     cw[1] = 0;
                 }
-                const float sc = wsc[tt * 64 + sl];
-                const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, unpack(cw), c, 0, 0, 0);
+                bw[G] = unpack(cw);
+                sc[G] = wsc[tt * 64 + sl];
+            }
+            uint4 av = xs[(bl * mp + min(i, mp - 1)) * 4 + oct];
+            if (i >= mp) av = make_uint4(0, 0, 0, 0);
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+            f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (FMT == QG_Q4_0) {
+                const bf16x8_t k136 = __builtin_bit_cast(bf16x8_t, make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, k136, c, 0, 0, 0);    // -136 * sum(x), every row
+            }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[G][q] = __builtin_fmaf(sc, d[q], acc[G][q]);
+            for (int G = 0; G < Sh::RG; ++G) {
+                const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[G], c, 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[G][q] = __builtin_fmaf(sc[G], d[q], acc[G][q]);
             }
         }
     }
 
     static __device__ __forceinline__ void compute(const MGeom &g, const Regs &r, int cnt, int jfirst, int KS, int b0,
-                                                   const uint4 *xs, uint8_t *wl, f32x4_t acc[Sh::RG])
+                                                   const uint4 *xs, uint8_t *wl, f32x4_t (&acc)[Sh::RG], int mp)
     {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (u < cnt) step(g, r, u, jfirst + u * KS, b0, xs, wl, acc);
+            if (u < cnt) step(g, r, u, jfirst + u * KS, b0, xs, wl, acc, mp);
     }
 };
 
-// Stages window w of the activations as xs[(bl*m + t)*4 + oct] (bf16 octets).
-__device__ __forceinline__ void mfma_stage(const MGeom &g, const uint16_t *x, int w, uint4 *xs)
+// Stages window w of the mp tokens' activations (x already offset to the
+// group's first token) as xs[(bl*mp + t)*4 + oct] (bf16 octets).
+__device__ __forceinline__ void mfma_stage(const MGeom &g, const uint16_t *x, int w, uint4 *xs, int mp)
 {
     const int b0 = w * g.SW * g.L;
-    const int total = g.wblk * g.m;
+    const int total = g.wblk * mp;
     for (int idx = threadIdx.x; idx < total; idx += (int)blockDim.x) {
-        const int bl = idx / g.m, t = idx - bl * g.m, b = b0 + bl;
+        const int bl = idx / mp, t = idx - bl * mp, b = b0 + bl;
         uint4 r[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
         if (b < g.nb) {
             const uint4 *src = (const uint4 *)(x + (int64_t)t * g.k + (int64_t)b * QK);
@@ -223,17 +238,23 @@ __device__ __forceinline__ void mfma_stage(const MGeom &g, const uint16_t *x, in
     }
 }
 
+// blockIdx.y: token group (tokens 16*y .. 16*y + 15 of the call); the
+// co-batch calls have one group.  LDS is planned for min(m, 16) tokens.
 template <int FMT, int LL>
-__global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restrict__ xv, float *__restrict__ y)
+__global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restrict__ xv, float *__restrict__ yv)
 {
     using E = MEngine<FMT, LL>;
     using Sh = MShape<LL>;
     extern __shared__ __align__(16) uint8_t smem[];
+    const int tb = (int)blockIdx.y * 16;
+    const int mp = min(16, g.m - tb);
+    const int mplan = min(16, g.m);
     uint4 *xs = (uint4 *)smem;
-    float *red = (float *)(smem + (size_t)g.wblk * g.m * 64);
-    const uint16_t *x = (const uint16_t *)xv;
+    float *red = (float *)(smem + (size_t)g.wblk * mplan * 64);
+    const uint16_t *x = (const uint16_t *)xv + (int64_t)tb * g.k;
+    float *y = yv + (int64_t)tb * g.n;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint8_t *wl = (uint8_t *)(red + WAVES * Sh::RG * 4 * 64) + wave * mfma_wave_bytes(FMT, LL);
+    uint8_t *wl = (uint8_t *)red + (g.KS > 1 ? mfma_red_bytes(LL) : 0) + wave * mfma_wave_bytes(FMT, LL);
     const int usub = wave >> g.ksh, kpart = wave & (g.KS - 1);
     const int KS = g.KS;
     bool staged = false;
@@ -259,7 +280,7 @@ __global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restr
             E::load(g, cb, sbase, lane, nsteps > 0 ? jf : 0, max(1, min(nsteps, E::U)), KS, tofs, ra);
             if (g.nwin > 1 || !staged) {
                 __syncthreads();
-                mfma_stage(g, x, w, xs);
+                mfma_stage(g, x, w, xs, mp);
                 __syncthreads();
                 staged = true;
             }
@@ -269,13 +290,13 @@ __global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restr
                 const int cA = min(nsteps - done, E::U);
                 const int rB = nsteps - done - cA;
                 E::load(g, cb, sbase, lane, rB > 0 ? jf + (done + cA) * KS : jlast, rB > 0 ? min(rB, E::U) : 1, KS, tofs, rb);
-                E::compute(g, ra, cA, jf + done * KS, KS, b0, xs, wl, acc);
+                E::compute(g, ra, cA, jf + done * KS, KS, b0, xs, wl, acc, mp);
                 done += cA;
                 if (done >= nsteps) break;
                 const int cB = min(nsteps - done, E::U);
                 const int rA = nsteps - done - cB;
                 E::load(g, cb, sbase, lane, rA > 0 ? jf + (done + cB) * KS : jlast, rA > 0 ? min(rA, E::U) : 1, KS, tofs, ra);
-                E::compute(g, rb, cB, jf + done * KS, KS, b0, xs, wl, acc);
+                E::compute(g, rb, cB, jf + done * KS, KS, b0, xs, wl, acc, mp);
                 done += cB;
             }
         }
@@ -304,7 +325,7 @@ __global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restr
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int t = 4 * oct + q;
-                    if (t < g.m) y[(int64_t)t * g.n + row] = acc[G][q];
+                    if (t < mp) y[(int64_t)t * g.n + row] = acc[G][q];
                 }
             }
         }
@@ -313,6 +334,7 @@ __global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restr
 
 typedef void (*mfma_fn)(MGeom, const void *, float *);
 
+// L = 16 serves only the many-token product (qgemm); the co-batch calls take L <= 8.
 template <int FMT>
 mfma_fn pick_mfma(int L)
 {
@@ -320,7 +342,8 @@ mfma_fn pick_mfma(int L)
     case 1: return k_dense_mfma<FMT, 1>;
     case 2: return k_dense_mfma<FMT, 2>;
     case 4: return k_dense_mfma<FMT, 4>;
-    default: return k_dense_mfma<FMT, 8>;
+    case 8: return k_dense_mfma<FMT, 8>;
+    default: return k_dense_mfma<FMT, 16>;
     }
 }
 

@@ -78,8 +78,11 @@ enum { QG_F32 = 0, QG_BF16 = 1 };
 /* Expert modes of moe_qgemv_topk. */
 enum { QG_MOE_GATE_UP = 0, QG_MOE_DOWN_COMBINE = 1 };
 
-/* Largest co-batch (tokens per call). */
+/* Largest co-batch (tokens per call) of the GEMV entry points. */
 #define QG_MAX_M 8
+
+/* Largest token count of qgemm. */
+#define QG_MAX_GEMM_M 128
 
 /* Kernel families of the dense product (qg_dense_path). */
 enum { QG_PATH_VALU = 0, QG_PATH_MFMA = 1 };
@@ -163,6 +166,22 @@ int qgemv_mxfp4(const void *w_packed, int64_t n, int64_t k, const void *x, int x
  * arguments the dense calls would reject.  Host only; no device work.
  */
 int qg_dense_path(int fmt, int64_t n, int64_t k, int xt, int64_t m);
+
+/*
+ * Dense product for 1 <= m <= QG_MAX_GEMM_M tokens (the prefill side of the
+ * co-batch route: Imparo README, "Bonsai CUDA Validation", whose tensor-core
+ * projections serve M 9..128 while small M keeps its own routes):
+ *     y[t][i] = sum_c W[i][c] * x[t][c]        t < m, i < n
+ * Arguments, layouts and limits as qgemv_* except m.  bf16 activations on
+ * layouts of at most 16 lanes per row run on the matrix cores in one launch:
+ * each group of 16 tokens is one MFMA operand, groups are a grid dimension
+ * (they share each weight tile through the device caches).  Other calls
+ * (fp32 activations, shorter matrices with more lanes per row) run the
+ * dense product QG_MAX_M tokens per launch.  qg_gemm_path says which.
+ */
+int qgemm(int fmt, const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y,
+          void *stream);
+int qg_gemm_path(int fmt, int64_t n, int64_t k, int xt, int64_t m);
 
 /*
  * Dense product with its decode-step neighbours fused in (the pages report

@@ -260,3 +260,23 @@ def test_moe_fused_argument_validation():
     assert call(fmt=q.Q8_0, n=2 * 4100, k=2560, act=q.ACT_SWIGLU) == q.QG_EUNSUPPORTED
     # eight normalised (fp32-staged) rows of K = 4096 need 128 KiB of LDS: refused, not run elsewhere
     assert call(k=4096, m=8, top_k=2, g=a) == q.QG_EUNSUPPORTED
+
+
+def test_gemm_argument_validation_and_path():
+    """qgemm rejects bad arguments before any device work; qg_gemm_path's rule."""
+    L = q.lib()
+    a = ctypes.c_void_p(1 << 20)
+    ODD = ctypes.c_void_p((1 << 20) + 2)
+    assert L.qgemm(q.Q4_0, a, 256, 512, a, q.X_BF16, 0, a, None) == q.QG_EINVAL
+    assert L.qgemm(q.Q4_0, a, 256, 512, a, q.X_BF16, q.MAX_GEMM_M + 1, a, None) == q.QG_EINVAL
+    assert L.qgemm(q.Q4_0, a, 256, 500, a, q.X_BF16, 16, a, None) == q.QG_EINVAL
+    assert L.qgemm(q.Q4_0, None, 256, 512, a, q.X_BF16, 16, a, None) == q.QG_EINVAL
+    assert L.qgemm(q.Q4_0, a, 256, 512, a, 7, 16, a, None) == q.QG_EINVAL
+    assert L.qgemm(q.Q4_0, a, 256, 512, ODD, q.X_BF16, 16, a, None) == q.QG_EALIGN
+    # matrix cores for bf16 on layouts of <= 16 lanes per row, else the dense product in passes
+    for fmt in (q.Q8_0, q.Q4_0, q.MXFP4):
+        for n, k in [(32768, 256), (16384, 512), (8192, 256), (4096, 4096), (2048, 4096), (1024, 4096), (300, 4096)]:
+            lanes = q.layout(fmt, n, k)["lanes_per_row"]
+            want = q.PATH_MFMA if lanes <= 16 else q.PATH_VALU
+            assert q.gemm_path(fmt, n, k, q.X_BF16, 64) == want, (fmt, n, k, lanes)
+            assert q.gemm_path(fmt, n, k, q.X_F32, 64) == q.PATH_VALU

@@ -208,6 +208,18 @@ def test_numpy_blas_cross_check_c0_size():
     assert np.allclose(l1[0], np.abs(W) @ np.abs(x.astype(np.float64)[0]), rtol=1e-13)
 
 
+def test_numpy_blas_cross_check_many_tokens():
+    # the product for a prefill-sized token count (128) against numpy's matmul
+    fmt, n, k, m = oracle.Q4_0, 96, 512, 128
+    blocks = wl.blocks_for(fmt, n, k, config=93, matrix=1)
+    x = wl.x_bf16_bits((m, k), wl.rng_for(93, 1, "x"))
+    W = oracle.decode(fmt, blocks, n, k)
+    xv = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    y, l1 = oracle.gemv(fmt, blocks, n, k, x, oracle.X_BF16)
+    assert np.max(np.abs(xv @ W.T - y) / l1) < 1e-13
+    assert np.allclose(l1, np.abs(xv) @ np.abs(W).T, rtol=1e-13)
+
+
 def test_row_subset_matches_full():
     n, k = 64, 256
     blocks = wl.blocks_for(oracle.Q4_0, n, k, config=92, matrix=0)
