@@ -73,6 +73,9 @@ def test_graph_replays_match_eager(dev):
     ya = torch.empty((m, top_k, gn // 2), dtype=torch.bfloat16, device=dev)
     res = torch.from_numpy(wl.x_f32((m, dn), wl.rng_for(91, 1, "res"))).to(dev)
     yr = torch.empty((m, dn), device=dev)
+    # many-token product: 40 tokens on the matrix cores
+    x5 = _bf16(wl.x_bf16_bits((40, k2), wl.rng_for(90, 6, "x")), dev)
+    y5 = torch.empty((40, n2), device=dev)
 
     def step():
         q.qgemv(q.Q8_0, w1, n1, k1, x1, y=y1)
@@ -85,8 +88,9 @@ def test_graph_replays_match_eager(dev):
                                act=q.ACT_SWIGLU, y=ya)
         yr.copy_(res)
         q.moe_qgemv_topk_fused(fmt, de, E, dn, dk, ids, gw, hd, q.MOE_DOWN_COMBINE, residual=yr, y=yr)
+        q.qgemm(q.Q4_0, w2, n2, k2, x5, y=y5)
 
-    outs = (y1, y2, ids, gw, yg, yd, y3, ya, yr)
+    outs = (y1, y2, ids, gw, yg, yd, y3, ya, yr, y5)
 
     def eager():
         step()
