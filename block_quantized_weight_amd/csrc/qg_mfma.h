@@ -1,6 +1,6 @@
 #pragma once
 // qg_mfma.h -- co-batch product (several tokens, bf16 activations) on the
-// gfx950 matrix cores.
+// gfx950 matrix cores, and the many-token product (qgemm) built on it.
 //
 // With M tokens the product reuses every decoded weight M times; past a few
 // tokens the per-weight VALU work of the lane-per-block kernel (an unpack plus
@@ -29,9 +29,14 @@
 // padding after every eight keeps those reads at most two-way bank-conflicted.
 //
 // A "unit" is 16 rows x the whole K: one tile of 16 rows (L = 4), two
-// half-tiles (L = 8, R = 8), or 2 / 4 row groups of a taller tile (L = 2, 1).
-// KS waves of a workgroup split a unit's steps; their partial sums are added
-// in a fixed order through LDS, so results are deterministic.
+// half-tiles (L = 8, R = 8), four quarter-tiles (L = 16, R = 4), or 2 / 4
+// row groups of a taller tile (L = 2, 1).  KS waves of a workgroup split a
+// unit's steps; their partial sums are added in a fixed order through LDS,
+// so results are deterministic.
+//
+// More than 16 tokens: each group of 16 is one A operand and one grid row
+// (blockIdx.y); every group reads the unit's weights again, and those
+// repeats can be served by the device caches.
 #include "qg_common.h"
 
 namespace qg {
