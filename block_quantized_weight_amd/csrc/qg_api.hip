@@ -711,18 +711,19 @@ static int moe_impl(int fmt, const void *w_experts, int64_t n_experts, int64_t n
         g.ctb = lo.ctb;
         g.stb = lo.stb;
         g.soff = lo.soff;
-        // waves per tile, splitting its items.  down-combine: more when tiles
-        // are few; gate_up: one (a wave streams every item of its tile, which
-        // measured faster than splitting on MI355X)
+        // waves per tile, splitting its items, when tiles are few: down-combine
+        // up to four, gate_up two (MI355X, the MXFP4 expert shapes at one and
+        // four tokens: gate_up 11.4 / 32.6 us with one wave per tile, 9.5 /
+        // 24.6 with two, 12.2 / 28.4 with four)
         int IS = 1;
-        if (mode == QG_MOE_DOWN_COMBINE && lo.tiles < 4096) IS = 2;
+        if (lo.tiles < 4096) IS = 2;
         if (mode == QG_MOE_DOWN_COMBINE && lo.tiles < 2048) IS = 4;
         a.isplit = IS;
         g.KS = 1;
         g.ksh = 0;
         g.tpi = WAVES / IS;
-        // with the gate a workgroup holds WAVES / 2 gate/up tile pairs
-        g.ngroups = glu ? (int32_t)((e.half_tiles + WAVES / 2 - 1) / (WAVES / 2))
+        // with the gate a workgroup holds tpi / 2 gate/up tile pairs
+        g.ngroups = glu ? (int32_t)((e.half_tiles + g.tpi / 2 - 1) / (g.tpi / 2))
                         : (int32_t)((lo.tiles + g.tpi - 1) / g.tpi);
         g.SW = (int32_t)lo.S;
         g.nwin = 1;

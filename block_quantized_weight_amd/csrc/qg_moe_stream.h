@@ -22,10 +22,10 @@
 // Fused neighbours (the definitions of qg_fused.h): gate_up may normalise
 // the token rows (x * gamma staged in fp32, sum of x^2 formed while staging,
 // 1/rms applied to the row totals) and gate its output (SwiGLU: a workgroup
-// holds two gate/up tile pairs, one wave per tile; every wave streams its
-// tile for all items and leaves its per-slot row totals in LDS, and after
-// one barrier the workgroup combines gate and up and writes F outputs per
-// slot); down-combine may add a residual; either writes fp32 or bf16.
+// holds tpi / 2 gate/up tile pairs; the waves of each tile stream their
+// items and leave their per-slot row totals in LDS, and after one barrier
+// the workgroup combines gate and up and writes F outputs per slot);
+// down-combine may add a residual; either writes fp32 or bf16.
 #include "qg_fused.h"
 
 namespace qg {
@@ -194,9 +194,9 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
     if (wave == 0) route_items(my_id, nslots, a.n_experts, MS, &it);
     __syncthreads();
     const int ni = it.count;
-    // with the gate (IS = 1, WAVES / 2 pairs per workgroup): waves [0, pp)
-    // hold gate tiles, waves [pp, 2 pp) the matching up tiles
-    constexpr int PP = WAVES / 2;
+    // with the gate (PP = tpi / 2 pairs per workgroup): tile slots [0, PP)
+    // hold gate tiles, [PP, 2 PP) the matching up tiles, IS waves each
+    const int PP = g.tpi / 2;
     const int gpair = blockIdx.x * PP + (tsub % PP);
     const bool upw = GLU && tsub >= PP;
     const int tile = GLU ? (gpair < e.half_tiles ? gpair + (upw ? e.half_tiles : 0) : g.tiles)
