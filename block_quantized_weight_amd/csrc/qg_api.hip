@@ -620,10 +620,12 @@ int qgemv_fused(int fmt, const void *w, int64_t n, int64_t k, const void *x, int
     e.n_out = (int32_t)n_out;
     e.half_tiles = act == QG_ACT_SWIGLU ? (int32_t)(n_out / lo.R) : 0;
     e.y_bf16 = yt == QG_BF16;
-    const bool glu = e.half_tiles > 0;
+    // the gate: 0 none; 1 gate and up halves in one wave (the plain grid: the
+    // work units are as many as the tiles); 2 for one-row tiles (64 lanes per
+    // row), GLU_WAVES-wave workgroups whose halves hold gate and up tiles
+    const int glu = e.half_tiles == 0 ? 0 : lo.L <= 32 ? 1 : 2;
     int block = TPB;
-    if (glu) {
-        // GLU_WAVES waves: KS per tile, gate and up tiles in equal numbers
+    if (glu == 2) {
         p.g.tpi = GLU_WAVES / p.g.KS;
         const int pp = p.g.tpi / 2;
         p.g.ngroups = (e.half_tiles + pp - 1) / pp;

@@ -632,14 +632,25 @@ struct Engine {
     static __device__ __forceinline__ void pass_st(const Geom &g, const void *x, const Slots &sl, int tile, bool &staged,
                                                    uint4 *xs, float *corr, float acc[M], ST &stg)
     {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int KS = g.KS, kpart = wave & (KS - 1);
-        const int slot = lane & (g.L - 1);
         const bool active = tile < g.tiles;
         // inactive waves load (and ignore) tile 0, step 0, so that loads stay unconditional
         const int tl = active ? tile : 0;
-        const uint8_t *ct = g.w + (int64_t)tl * g.ctb;
-        const uint8_t *st = g.w + g.soff + (int64_t)tl * g.stb;
+        pass_core(g, x, sl, g.w + (int64_t)tl * g.ctb, g.w + g.soff + (int64_t)tl * g.stb, threadIdx.x & 63, active,
+                  staged, xs, corr, acc, stg);
+    }
+
+    // The pass with the lane's own tile bases (ct, st) and record lane rl:
+    // the lane reads 16-byte record rl of each step of that tile (its row
+    // rl / L, block rl % L).  With rl = the lane, a whole tile per wave.
+    // Requires rl % L == lane % L (the staged activations are indexed by it).
+    template <class ST>
+    static __device__ __forceinline__ void pass_core(const Geom &g, const void *x, const Slots &sl, const uint8_t *ct,
+                                                     const uint8_t *st, int rl, bool active, bool &staged, uint4 *xs,
+                                                     float *corr, float acc[M], ST &stg)
+    {
+        const int lane = rl, wave = threadIdx.x >> 6;
+        const int KS = g.KS, kpart = wave & (KS - 1);
+        const int slot = rl & (g.L - 1);
 #pragma unroll
         for (int t = 0; t < M; ++t) acc[t] = 0.0f;
         for (int w = 0; w < g.nwin; ++w) {

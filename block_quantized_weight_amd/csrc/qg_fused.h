@@ -25,11 +25,13 @@
 //    partials, a xor butterfly, then the waves in order), with the first
 //    weight loads already in flight; all workgroups hold the same r and no
 //    extra launch is needed.
-//  * SwiGLU.  Workgroups of eight waves: half of them split gate tiles, the
-//    other half the matching up tiles (F is a multiple of the tile's rows,
-//    so the up tile is the gate tile plus a fixed offset), each wave with as
-//    many steps as in the plain product; the up totals reach the gate waves
-//    through LDS and only F outputs are written.
+//  * SwiGLU.  F is a multiple of the tile's rows, so the up tile of gate
+//    tile t is t + F/R.  A wave takes half a gate tile in its lanes 0..31 and
+//    the same half of the up tile in lanes 32..63, so the work units are as
+//    many as the tiles and the grid is the plain product's; the gate and up
+//    totals of a row meet by one lane swap, and only F outputs are written.
+//    (Layouts of 64 lanes per row have one-row tiles: there eight-wave
+//    workgroups split gate and up tiles and meet through LDS.)
 //  * Residual and bf16 output in the store.
 #include <type_traits>
 
@@ -252,7 +254,68 @@ __global__ __launch_bounds__(TPB) void k_dense_ep(Geom g, EpiArgs e, const void 
     }
 }
 
-// With the SwiGLU gate: workgroups of GLU_WAVES waves.  The first half of the
+// With the SwiGLU gate, layouts of at most 32 lanes per row: the plain
+// product's grid of TPB-thread workgroups over work units u = 2 t + h, one
+// per tile count.  A wave's lanes 0..31 read records 32 h .. 32 h + 31 of gate
+// tile t (rows 32 h / L .. of the tile), lanes 32..63 the same records of up
+// tile t + half_tiles; each load instruction reads two contiguous 512-byte
+// halves.  After the split-K and row reductions (within 32-lane halves, as
+// L <= 32) a row's gate and up totals are 32 lanes apart, one lane swap.
+template <int FMT, bool XBF16, bool DOT, int M, bool NORM>
+__global__ __launch_bounds__(TPB) void k_dense_glu_lanes(Geom g, EpiArgs e, const void *__restrict__ x)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int QPB = x_quads(FMT, DOT);
+    uint4 *xs = (uint4 *)smem;
+    float *corr = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
+    float *red = corr + (x_aux(FMT) ? M * g.wblk : 0);
+    __shared__ int32_t s_rows[QG_MAX_M];
+    __shared__ float s_part[WAVES * QG_MAX_M];
+    if (threadIdx.x < QG_MAX_M) s_rows[threadIdx.x] = threadIdx.x;   // read only after the first barrier
+    Slots sl{s_rows, s_rows};
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tsub = wave >> g.ksh, kpart = wave & (g.KS - 1);
+    const int slot = lane & (g.L - 1);
+    const bool upl = lane >= 32;
+    typedef typename std::conditional<NORM, NormStage<XBF16>, PlainStage<XBF16, DOT>>::type Stager;
+    Stager st;
+    if constexpr (NORM) {
+        st.gamma = e.gamma;
+        st.s_part = s_part;
+        st.have = false;
+    }
+    bool staged = false;
+    for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {
+        const int u = grp * g.tpi + tsub;
+        const int t = u >> 1, h = u & 1;
+        const bool active = t < e.half_tiles;
+        const int tile = active ? t + (upl ? e.half_tiles : 0) : 0;
+        const int rl = 32 * h + (lane & 31);
+        float acc[M];
+        Engine<FMT, XBF16, DOT, M>::pass_core(g, x, sl, g.w + (int64_t)tile * g.ctb, g.w + g.soff + (int64_t)tile * g.stb,
+                                              rl, active, staged, xs, corr, acc, st);
+        reduce_partials<M>(g, red, acc);
+        float up[M];
+#pragma unroll
+        for (int q = 0; q < M; ++q) up[q] = __shfl_xor(acc[q], 32, 64);
+        const int64_t row = (int64_t)t * g.R + rl / g.L;
+        if (!upl && kpart == 0 && active && row < e.n_out) {
+#pragma unroll
+            for (int q = 0; q < M; ++q) {
+                if ((q & (g.L - 1)) != slot) continue;
+                float gv = acc[q], uv = up[q];
+                if (NORM) {
+                    const float r = rinv_of<WAVES>(s_part, q, g.k, e.eps);
+                    gv *= r;
+                    uv *= r;
+                }
+                store_out(e, (int64_t)q * e.n_out + row, silu(gv) * uv);
+            }
+        }
+    }
+}
+
+// With the SwiGLU gate, 64 lanes per row (one-row tiles): workgroups of GLU_WAVES waves.  The first half of the
 // waves runs g.tpi / 2 gate tiles (KS waves each), the second half the up
 // tiles of the same rows (gate tile + half_tiles); the up waves hand their
 // row totals to the gate waves through LDS, which finish the outputs.
@@ -318,16 +381,19 @@ __global__ __launch_bounds__(64 * GLU_WAVES) void k_dense_glu(Geom g, EpiArgs e,
 
 typedef void (*dense_ep_fn)(Geom, EpiArgs, const void *);
 
-template <int FMT, bool XBF16, bool DOT, bool NORM, bool GLU, int M>
+// GLU: 0 none, 1 lanes (<= 32 lanes per row), 2 eight-wave workgroups.
+template <int FMT, bool XBF16, bool DOT, bool NORM, int GLU, int M>
 dense_ep_fn ep_kernel()
 {
-    if constexpr (GLU)
+    if constexpr (GLU == 1)
+        return k_dense_glu_lanes<FMT, XBF16, DOT, M, NORM>;
+    else if constexpr (GLU == 2)
         return k_dense_glu<FMT, XBF16, DOT, M, NORM>;
     else
         return k_dense_ep<FMT, XBF16, DOT, M, NORM>;
 }
 
-template <int FMT, bool XBF16, bool DOT, bool NORM, bool GLU>
+template <int FMT, bool XBF16, bool DOT, bool NORM, int GLU>
 dense_ep_fn pick_dense_ep(int m)
 {
     switch (m) {
@@ -342,7 +408,7 @@ dense_ep_fn pick_dense_ep(int m)
     }
 }
 
-template <int FMT, bool GLU>
+template <int FMT, int GLU>
 dense_ep_fn pick_dense_ep_glu(int xt, int m, bool norm)
 {
     constexpr bool DOTB = FMT != QG_Q8_0;
@@ -354,13 +420,14 @@ dense_ep_fn pick_dense_ep_glu(int xt, int m, bool norm)
 // Normalising kernels stage fp32 (x * gamma); the others stage as the plain
 // product does (bf16 pairs for 4-bit codes with bf16 activations).
 template <int FMT>
-dense_ep_fn pick_dense_ep_fmt(int xt, int m, bool norm, bool glu)
+dense_ep_fn pick_dense_ep_fmt(int xt, int m, bool norm, int glu)
 {
-    return glu ? pick_dense_ep_glu<FMT, true>(xt, m, norm) : pick_dense_ep_glu<FMT, false>(xt, m, norm);
+    return glu == 1 ? pick_dense_ep_glu<FMT, 1>(xt, m, norm)
+           : glu == 2 ? pick_dense_ep_glu<FMT, 2>(xt, m, norm) : pick_dense_ep_glu<FMT, 0>(xt, m, norm);
 }
 
-dense_ep_fn dense_ep_kernel_q8_0(int xt, int m, bool norm, bool glu);
-dense_ep_fn dense_ep_kernel_q4_0(int xt, int m, bool norm, bool glu);
-dense_ep_fn dense_ep_kernel_mxfp4(int xt, int m, bool norm, bool glu);
+dense_ep_fn dense_ep_kernel_q8_0(int xt, int m, bool norm, int glu);
+dense_ep_fn dense_ep_kernel_q4_0(int xt, int m, bool norm, int glu);
+dense_ep_fn dense_ep_kernel_mxfp4(int xt, int m, bool norm, int glu);
 
 } // namespace qg

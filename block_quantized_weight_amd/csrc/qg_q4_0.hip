@@ -33,7 +33,7 @@ moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms, bool norm, bool g
                          : pick_moe_stream<QG_Q4_0, false, false>(mode, ms, norm, glu);
 }
 
-dense_ep_fn dense_ep_kernel_q4_0(int xt, int m, bool norm, bool glu)
+dense_ep_fn dense_ep_kernel_q4_0(int xt, int m, bool norm, int glu)
 {
     return pick_dense_ep_fmt<QG_Q4_0>(xt, m, norm, glu);
 }

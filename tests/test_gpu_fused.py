@@ -187,3 +187,17 @@ def test_fused_decode_shapes_sampled(dev, case):
     o, scale = c.oracle(rows=rows)
     err = oracle.fused_err(y_host(y)[:, rows], o, scale, y_bf16=ybf16)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [1, 4])
+def test_fused_gate_on_one_row_tiles(dev, fmt, m):
+    # 64 lanes per row (one-row tiles): the gate runs on eight-wave workgroups
+    n, k = 600, 4096
+    assert q.layout(fmt, n, k)["lanes_per_row"] == 64
+    c = Case(fmt, n, k, m, oracle.X_BF16, True, SWIGLU, True, True, matrix=53)
+    say(c.label(), "one-row tiles")
+    _, y = c.run(dev)
+    o, scale = c.oracle()
+    err = oracle.fused_err(y_host(y), o, scale, y_bf16=True)
+    assert err <= TOL, err
