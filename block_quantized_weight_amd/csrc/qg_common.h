@@ -4,8 +4,8 @@
 //
 // The decode step of an LLM streams each weight matrix once per token through
 // a matrix-vector product, so the product is bound by HBM bandwidth (imp
-// README, "Known limitations": lower bandwidth "decodes roughly 25% slower,
-// since decode is bandwidth-bound").  Everything here is shaped for that:
+// README, "Known limitations": a card with less bandwidth decodes
+// proportionally slower).  Everything here is shaped for that:
 //
 //  * Packed layout (built once at load time).  A tile holds R = 64/L rows.
 //    Lane l of a wavefront owns row l/L of the tile and, at step j, block

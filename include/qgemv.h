@@ -4,15 +4,16 @@
  *
  * What is computed.  The decode step of an LLM streams every weight matrix
  * once per generated token through a matrix-vector product; decode is bound by
- * memory bandwidth (imp README, "Known limitations": a card with less
- * bandwidth "decodes roughly 25% slower, since decode is bandwidth-bound").
+ * memory bandwidth (imp README, "Known limitations": a card with a quarter
+ * less bandwidth decodes about a quarter slower).
  * The weights are stored in the block formats the engines serve: Q8_0 and
  * Q4_0 (Imparo README, opening release notes and the M3 Pro benchmark table;
- * imp README, "Features" table, Quantization row) and MXFP4, "FP4 E2M1 +
- * UE8M0 block scales" at 4.25 bits per weight (imp release notes, v0.6).
+ * imp README, "Features" table, Quantization row) and MXFP4, 4-bit E2M1
+ * values with UE8M0 block scales at 4.25 bits per weight (imp release notes,
+ * v0.6).
  * The top-k expert variant covers mixture-of-experts layers such as
- * gpt-oss-20b, "MoE (32 experts, top-4)" in MXFP4 (imp README, "Supported
- * models" table), with expert routing read on the device, not copied to the
+ * gpt-oss-20b, 32 experts of which 4 serve each token, in MXFP4 (imp README,
+ * "Supported models" table), with expert routing read on the device, not copied to the
  * host (imp release notes, v0.7.0 "Known issues": host-side MoE routing is
  * incompatible with graph capture).
  *
@@ -276,9 +277,9 @@ int moe_router_topk(const float *logits, int64_t m, int64_t n_experts, int64_t t
  * (its outputs are visible device-wide), as consecutive projections of one
  * decode step require.  This removes the per-launch cost between products and
  * keeps the next product's weights streaming while a product drains, the way
- * Imparo runs a whole decode layer as one persistent dispatch with a grid
- * barrier in place of each dispatch boundary (Imparo README, "Megakernel
- * Decode").
+ * Imparo's decode puts a layer's work into a single persistent launch whose
+ * grid barriers stand where dispatch boundaries were (Imparo README,
+ * "Megakernel Decode").
  *
  * Use: fill `count` links on the host, size a plan with qg_chain_plan_bytes,
  * build it with qg_chain_plan (host memory; queries the current device), copy

@@ -17,8 +17,8 @@
  *     table, Quantization row).  Their block layouts (32 weights, one fp16
  *     scale, Q4_0 zero point 8, nibble split) are the workload definitions;
  *     the pages print no byte layout.
- *   - MXFP4 is "FP4 E2M1 + UE8M0 block scales" at 4.25 bits per weight (imp
- *     release notes, v0.6, "Highlights" and "Features").  4.25 = 4 + 8/32, so a
+ *   - MXFP4 is 4-bit E2M1 values with UE8M0 block scales at 4.25 bits per
+ *     weight (imp release notes, v0.6, "Highlights" and "Features").  4.25 = 4 + 8/32, so a
  *     block is 32 E2M1 codes plus one 8-bit power-of-two scale.
  *   - E2M1 values follow from the name: 1 sign bit, 2 exponent bits with bias
  *     1, 1 mantissa bit, exponent field 0 subnormal, no inf/NaN codes.
