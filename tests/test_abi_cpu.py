@@ -260,6 +260,9 @@ def test_moe_fused_argument_validation():
     assert call(fmt=q.Q8_0, n=2 * 4100, k=2560, act=q.ACT_SWIGLU) == q.QG_EUNSUPPORTED
     # eight normalised (fp32-staged) rows of K = 4096 need 128 KiB of LDS: refused, not run elsewhere
     assert call(k=4096, m=8, top_k=2, g=a) == q.QG_EUNSUPPORTED
+    # more than 64 slots per call
+    assert call(m=8, top_k=9) == q.QG_EUNSUPPORTED
+    assert call(m=0) == q.QG_EINVAL and call(top_k=17) == q.QG_EINVAL
 
 
 def test_gemm_argument_validation_and_path():

@@ -75,7 +75,7 @@ def test_gemm_layout_classes(dev, fmt, lanes, m):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("m", [1, 5, 8, 12, 33])
+@pytest.mark.parametrize("m", [1, 5, 8, 12, 33, 100])
 def test_gemm_ragged_rows_and_small_m(dev, fmt, m):
     # ragged row counts (tiles past the end, partial 16-row units)
     for n, k in [(1000, 256), (4100, 512), (2060, 4096)]:

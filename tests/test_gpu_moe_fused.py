@@ -191,3 +191,24 @@ def test_moe_ffn_on_device_at_full_size(dev, m):
     a_bits = a.cpu().view(torch.int16).numpy().view(np.uint16)
     o, s = oracle.moe_fused(fmt, down.canon, E, dn, dk, ids, g, a_bits, oracle.X_BF16, DOWN, residual=hidden)
     check(out.cpu().numpy().astype(np.float64), o, s, False)
+
+
+@pytest.mark.parametrize("fmt", [q.MXFP4, q.Q4_0])
+def test_moe_fused_largest_call(dev, fmt):
+    # 8 tokens x top-8 of 16 experts = 64 slots, the most one call takes
+    E, top_k, m, n, k = 16, 8, 8, 512, 256
+    ex = Experts(fmt, E, n, k, 180 + fmt, dev)
+    ids, g = routing(m, E, top_k, 180)
+    x = draw((m, k), oracle.X_BF16, 180, 0, "x", 3.0)
+    gamma = wl.norm_weight_f32(k, wl.rng_for(180, 0, "gamma"))
+    say(f"moe fused largest fmt={fmt}")
+    y = run(ex, ids, g, x, oracle.X_BF16, GATE, dev, gamma=gamma, act=SWIGLU, ybf16=True)
+    o, s = oracle.moe_fused(fmt, ex.canon, E, n, k, ids, g, x, oracle.X_BF16, GATE, norm_weight=gamma, eps=1e-5,
+                            act=SWIGLU)
+    check(y.float().cpu().numpy().astype(np.float64), o, s, True)
+    exd = Experts(fmt, E, k, n // 2, 181 + fmt, dev)            # down: K = F
+    h = draw((m, top_k, n // 2), oracle.X_BF16, 181, 0, "h", 1.0)
+    res = wl.x_f32((m, k), wl.rng_for(181, 0, "res"))
+    yd = run(exd, ids, g, h, oracle.X_BF16, DOWN, dev, res=res)
+    o, s = oracle.moe_fused(fmt, exd.canon, E, k, n // 2, ids, g, h, oracle.X_BF16, DOWN, residual=res)
+    check(yd.cpu().numpy().astype(np.float64), o, s, False)
