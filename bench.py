@@ -52,6 +52,8 @@ def parse():
                          "sweep; c0/c1/c3/c4: the other workloads, each timed over >= 1 GiB of distinct weight "
                          "copies so the device-side cache cannot serve repeated reads; gemm: qgemm on the c3 "
                          "matrices at 16..128 tokens")
+    ap.add_argument("--tokens", default="16,32,64,128",
+                    help="gemm workload: the token counts to run (comma-separated, 1..128)")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -230,7 +232,8 @@ def run_other(args):
 
     if args.workload == "gemm":
         gemm_case(3, [("qkv", 6144, 4096, 0), ("gate_up", 24576, 4096, 1), ("down", 4096, 12288, 2)],
-                  [16, 32, 64, 128], "q4_0 qgemm, 8b-like: qkv 6144x4096 + gate_up 24576x4096 + down 4096x12288")
+                  [int(t) for t in args.tokens.split(",")],
+                  "q4_0 qgemm, 8b-like: qkv 6144x4096 + gate_up 24576x4096 + down 4096x12288")
     elif args.workload == "c0":
         dense_case(0, [("w", 2048, 2048, 0)], "f32", [1], "q8_0 2048x2048, x fp32")
     elif args.workload == "c1":
