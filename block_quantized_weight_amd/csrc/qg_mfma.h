@@ -34,9 +34,11 @@
 // unit's steps; their partial sums are added in a fixed order through LDS,
 // so results are deterministic.
 //
-// More than 16 tokens: each group of 16 is one A operand and one grid row
-// (blockIdx.y); every group reads the unit's weights again, and those
-// repeats can be served by the device caches.
+// More than 16 tokens: each group of 16 is one A operand; a workgroup pass
+// (grid row blockIdx.y) takes one group, or two that share each unpacked
+// weight operand where a wave holds several 16-row groups; every pass reads
+// the unit's weights again, and those repeats can be served by the device
+// caches.
 #include "qg_common.h"
 
 namespace qg {
@@ -75,22 +77,31 @@ inline __host__ __device__ int mfma_wave_bytes(int fmt, int LL)
     return tpw * P * MPLANE + tpw * 64 * 4;
 }
 
+// Token groups of 16 per workgroup pass in the many-token product: two where
+// a wave holds several 16-row groups (L <= 2) and there are more than 16
+// tokens, so every unpacked weight operand serves two A operands; one
+// elsewhere.  Measured on MI355X (Q4_0,
+// 64 / 128 tokens): 24576x4096 at 2 lanes per row 72.4 / 119.2 us with one
+// group, 60.1 / 98.7 with two; at 8 lanes per row two groups were slower
+// (4096x12288: 73.7 -> 93.2 us at 128 tokens), four slower everywhere.
+inline __host__ __device__ int gemm_groups(int LL, int64_t m) { return LL <= 2 && m > 16 ? 2 : 1; }
+
 // Split-K partials (present only when KS > 1).
-inline __host__ __device__ size_t mfma_red_bytes(int LL)
+inline __host__ __device__ size_t mfma_red_bytes(int LL, int TG = 1)
 {
     const int RG = LL >= 4 ? 1 : 4 / LL;
-    return (size_t)WAVES * RG * 4 * 64 * 4;
+    return (size_t)WAVES * TG * RG * 4 * 64 * 4;
 }
 
-inline __host__ __device__ size_t mfma_lds_bytes(int fmt, int m, int wblk, int LL, int KS)
+inline __host__ __device__ size_t mfma_lds_bytes(int fmt, int m, int wblk, int LL, int KS, int TG = 1)
 {
     size_t b = (size_t)wblk * m * 64;                        // activations: [block][token][octet]
-    if (KS > 1) b += mfma_red_bytes(LL);                     // split-K partials
+    if (KS > 1) b += mfma_red_bytes(LL, TG);                 // split-K partials
     b += (size_t)WAVES * mfma_wave_bytes(fmt, LL);           // transpose areas
     return b;
 }
 
-template <int FMT, int LL>
+template <int FMT, int LL, int TG = 1>
 struct MEngine {
     using Sh = MShape<LL>;
     static constexpr int P = FMT == QG_Q8_0 ? 2 : 1;        // 16-byte parts per record
@@ -165,7 +176,7 @@ struct MEngine {
     // The MFMAs of one step (block index jL + s of every row of the unit)
     // for the mp (<= 16) tokens of the group.  wl: this wave's transpose area.
     static __device__ __forceinline__ void step(const MGeom &g, const Regs &r, int u, int j, int b0, const uint4 *xs,
-                                                uint8_t *wl, f32x4_t (&acc)[Sh::RG], int mp)
+                                                uint8_t *wl, f32x4_t (&acc)[TG][Sh::RG], int mp)
     {
         const int lane = threadIdx.x & 63, i = lane & 15, oct = lane >> 4;
         float *wsc = (float *)(wl + TPW * P * MPLANE);
@@ -198,25 +209,30 @@ struct MEngine {
                 bw[G] = unpack(cw);
                 sc[G] = wsc[tt * 64 + sl];
             }
-            uint4 av = xs[(bl * mp + min(i, mp - 1)) * 4 + oct];
-            if (i >= mp) av = make_uint4(0, 0, 0, 0);
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
-            f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (FMT == QG_Q4_0) {
-                const bf16x8_t k136 = __builtin_bit_cast(bf16x8_t, make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, k136, c, 0, 0, 0);    // -136 * sum(x), every row
-            }
+            // every token group, unconditionally (tokens past mp read zeros)
 #pragma unroll
-            for (int G = 0; G < Sh::RG; ++G) {
-                const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[G], c, 0, 0, 0);
+            for (int tg = 0; tg < TG; ++tg) {
+                const int tok = 16 * tg + i;
+                uint4 av = xs[(bl * mp + min(tok, mp - 1)) * 4 + oct];
+                if (tok >= mp) av = make_uint4(0, 0, 0, 0);
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+                f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (FMT == QG_Q4_0) {
+                    const bf16x8_t k136 = __builtin_bit_cast(bf16x8_t, make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, k136, c, 0, 0, 0);    // -136 * sum(x), every row
+                }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[G][q] = __builtin_fmaf(sc[G], d[q], acc[G][q]);
+                for (int G = 0; G < Sh::RG; ++G) {
+                    const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[G], c, 0, 0, 0);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[tg][G][q] = __builtin_fmaf(sc[G], d[q], acc[tg][G][q]);
+                }
             }
         }
     }
 
     static __device__ __forceinline__ void compute(const MGeom &g, const Regs &r, int cnt, int jfirst, int KS, int b0,
-                                                   const uint4 *xs, uint8_t *wl, f32x4_t (&acc)[Sh::RG], int mp)
+                                                   const uint4 *xs, uint8_t *wl, f32x4_t (&acc)[TG][Sh::RG], int mp)
     {
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -243,23 +259,24 @@ __device__ __forceinline__ void mfma_stage(const MGeom &g, const uint16_t *x, in
     }
 }
 
-// blockIdx.y: token group (tokens 16*y .. 16*y + 15 of the call); the
-// co-batch calls have one group.  LDS is planned for min(m, 16) tokens.
-template <int FMT, int LL>
+// blockIdx.y: a pass over TG token groups of 16 (tokens 16*TG*y .. of the
+// call); the co-batch calls have one pass of one group.  LDS is planned for
+// min(m, 16*TG) tokens.
+template <int FMT, int LL, int TG>
 __global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restrict__ xv, float *__restrict__ yv)
 {
-    using E = MEngine<FMT, LL>;
+    using E = MEngine<FMT, LL, TG>;
     using Sh = MShape<LL>;
     extern __shared__ __align__(16) uint8_t smem[];
-    const int tb = (int)blockIdx.y * 16;
-    const int mp = min(16, g.m - tb);
-    const int mplan = min(16, g.m);
+    const int tb = (int)blockIdx.y * 16 * TG;
+    const int mp = min(16 * TG, g.m - tb);
+    const int mplan = min(16 * TG, g.m);
     uint4 *xs = (uint4 *)smem;
     float *red = (float *)(smem + (size_t)g.wblk * mplan * 64);
     const uint16_t *x = (const uint16_t *)xv + (int64_t)tb * g.k;
     float *y = yv + (int64_t)tb * g.n;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint8_t *wl = (uint8_t *)red + (g.KS > 1 ? mfma_red_bytes(LL) : 0) + wave * mfma_wave_bytes(FMT, LL);
+    uint8_t *wl = (uint8_t *)red + (g.KS > 1 ? mfma_red_bytes(LL, TG) : 0) + wave * mfma_wave_bytes(FMT, LL);
     const int usub = wave >> g.ksh, kpart = wave & (g.KS - 1);
     const int KS = g.KS;
     bool staged = false;
@@ -272,9 +289,11 @@ __global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restr
         int tofs[Sh::TPW];
 #pragma unroll
         for (int tt = 0; tt < Sh::TPW; ++tt) tofs[tt] = uu * Sh::TPW + tt < g.tiles ? tt : 0;
-        f32x4_t acc[Sh::RG];
+        f32x4_t acc[TG][Sh::RG];
 #pragma unroll
-        for (int G = 0; G < Sh::RG; ++G) acc[G] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+            for (int G = 0; G < Sh::RG; ++G) acc[tg][G] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         for (int w = 0; w < g.nwin; ++w) {
             const int j0 = w * g.SW;
             const int j1 = min(g.S, j0 + g.SW);
@@ -308,29 +327,38 @@ __global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restr
         // split-K partials, summed in kpart order
         if (KS > 1) {
 #pragma unroll
-            for (int G = 0; G < Sh::RG; ++G)
+            for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) red[((wave * Sh::RG + G) * 4 + q) * 64 + lane] = acc[G][q];
+                for (int G = 0; G < Sh::RG; ++G)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        red[(((wave * TG + tg) * Sh::RG + G) * 4 + q) * 64 + lane] = acc[tg][G][q];
             __syncthreads();
             if (kpart == 0) {
                 for (int qq = 1; qq < KS; ++qq)
 #pragma unroll
-                    for (int G = 0; G < Sh::RG; ++G)
+                    for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[G][q] += red[(((wave + qq) * Sh::RG + G) * 4 + q) * 64 + lane];
+                        for (int G = 0; G < Sh::RG; ++G)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                acc[tg][G][q] += red[((((wave + qq) * TG + tg) * Sh::RG + G) * 4 + q) * 64 + lane];
             }
             __syncthreads();
         }
         if (kpart == 0 && active) {
             const int i = lane & 15, oct = lane >> 4;
 #pragma unroll
-            for (int G = 0; G < Sh::RG; ++G) {
-                const int64_t row = (int64_t)unit * 16 * Sh::RG + 16 * G + i;
-                if (row >= g.n) continue;
+            for (int tg = 0; tg < TG; ++tg) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int t = 4 * oct + q;
-                    if (t < mp) y[(int64_t)t * g.n + row] = acc[G][q];
+                for (int G = 0; G < Sh::RG; ++G) {
+                    const int64_t row = (int64_t)unit * 16 * Sh::RG + 16 * G + i;
+                    if (row >= g.n) continue;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int t = 16 * tg + 4 * oct + q;
+                        if (t < mp) y[(int64_t)t * g.n + row] = acc[tg][G][q];
+                    }
                 }
             }
         }
@@ -339,21 +367,23 @@ __global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restr
 
 typedef void (*mfma_fn)(MGeom, const void *, float *);
 
-// L = 16 serves only the many-token product (qgemm); the co-batch calls take L <= 8.
+// tg: token groups per pass, 1 (co-batch calls, and qgemm where L > 2) or 2
+// (qgemm, L <= 2: gemm_groups).  L = 16 serves only qgemm.
 template <int FMT>
-mfma_fn pick_mfma(int L)
+mfma_fn pick_mfma(int L, int tg = 1)
 {
+    if (tg == 2) return L == 1 ? k_dense_mfma<FMT, 1, 2> : k_dense_mfma<FMT, 2, 2>;
     switch (L) {
-    case 1: return k_dense_mfma<FMT, 1>;
-    case 2: return k_dense_mfma<FMT, 2>;
-    case 4: return k_dense_mfma<FMT, 4>;
-    case 8: return k_dense_mfma<FMT, 8>;
-    default: return k_dense_mfma<FMT, 16>;
+    case 1: return k_dense_mfma<FMT, 1, 1>;
+    case 2: return k_dense_mfma<FMT, 2, 1>;
+    case 4: return k_dense_mfma<FMT, 4, 1>;
+    case 8: return k_dense_mfma<FMT, 8, 1>;
+    default: return k_dense_mfma<FMT, 16, 1>;
     }
 }
 
-mfma_fn mfma_kernel_q8_0(int L);
-mfma_fn mfma_kernel_q4_0(int L);
-mfma_fn mfma_kernel_mxfp4(int L);
+mfma_fn mfma_kernel_q8_0(int L, int tg = 1);
+mfma_fn mfma_kernel_q4_0(int L, int tg = 1);
+mfma_fn mfma_kernel_mxfp4(int L, int tg = 1);
 
 } // namespace qg

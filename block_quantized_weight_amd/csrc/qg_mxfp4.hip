@@ -25,7 +25,7 @@ const void *chain_kernel_mxfp4(int xt, int m)
 
 int chain_error_mxfp4(bool clear) { return chain_error_read(clear); }
 
-mfma_fn mfma_kernel_mxfp4(int L) { return pick_mfma<QG_MXFP4>(L); }
+mfma_fn mfma_kernel_mxfp4(int L, int tg) { return pick_mfma<QG_MXFP4>(L, tg); }
 
 moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms, bool norm, bool glu)
 {

@@ -25,7 +25,7 @@ const void *chain_kernel_q8_0(int xt, int m)
 
 int chain_error_q8_0(bool clear) { return chain_error_read(clear); }
 
-mfma_fn mfma_kernel_q8_0(int L) { return pick_mfma<QG_Q8_0>(L); }
+mfma_fn mfma_kernel_q8_0(int L, int tg) { return pick_mfma<QG_Q8_0>(L, tg); }
 
 moe_stream_fn moe_stream_kernel_q8_0(int xt, int mode, int ms, bool norm, bool glu)
 {
