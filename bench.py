@@ -167,7 +167,7 @@ def run_other(args):
                         q.qgemv(fmt, ws[name][r], n, k, xs[name], y=ys[name])
                 us = graph_time(torch, one, max(2, args.steps // 3)) / reps
                 per[name] = {"n": n, "k": k, "bytes": b, "us": round(us, 3), "gbs": round(b / us / 1e3, 1),
-                             "path": "mfma" if path == q.PATH_MFMA else "valu"}
+                             "path": {q.PATH_MFMA: "mfma", q.PATH_VALU_ONE: "valu_one"}.get(path, "valu")}
 
             def whole():
                 for r in range(reps):
@@ -560,10 +560,11 @@ def main():
     if chain is not None and q.chain_error() != 0:
         raise RuntimeError("a chain barrier timed out: the timed run is invalid")
 
-    # ---- roofline of the GEMV kernel.  Every launch of the step is the same
-    # kernel (Q8_0, bf16 x, M=1); its mean launch duration is the graph step time
-    # over the 145 launches (the rocprofv3 kernel-trace average agrees to within
-    # the ~0.2 us gaps between graph nodes).  Per-shape durations come from one
+    # ---- roofline of the GEMV kernel.  Every launch of the step is the vector
+    # GEMV (Q8_0, bf16 x, M=1: o in its one-batch form k_dense_one, the other
+    # shapes in k_dense); its mean launch duration is the graph step time over
+    # the 145 launches (the rocprofv3 kernel-trace average agrees to within the
+    # ~0.2 us gaps between graph nodes).  Per-shape durations come from one
     # graph of the 36 distinct matrices of each shape (144 for the LM head, which
     # is timed alone).
     roof = None
@@ -576,7 +577,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else round(traffic),
-                "kernel": "qg::k_dense<Q8_0, bf16 x, M=1>",
+                "kernel": "qg::k_dense / k_dense_one<Q8_0, bf16 x, M=1>",
                 "bytes_per_launch": round(mean_bytes), "mean_launch_us": round(mean_dur * 1e6, 3)}
         groups = {}
         for i, (_, name, n, k) in enumerate(shapes):

@@ -20,7 +20,7 @@ X_F32, X_BF16 = 0, 1
 MOE_GATE_UP, MOE_DOWN_COMBINE = 0, 1
 MAX_M = 8
 MAX_GEMM_M = 128
-PATH_VALU, PATH_MFMA = 0, 1
+PATH_VALU, PATH_MFMA, PATH_VALU_ONE = 0, 1, 2
 ACT_NONE, ACT_SWIGLU = 0, 1
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17}
 
@@ -105,7 +105,7 @@ def _check(fn, status):
 
 # ------------------------------------------------------------------ layout
 def dense_path(fmt, n, k, xt, m):
-    """PATH_VALU or PATH_MFMA: the kernel family a dense call would run."""
+    """PATH_VALU, PATH_MFMA or PATH_VALU_ONE: the kernel family a dense call would run."""
     v = lib().qg_dense_path(fmt, n, k, xt, m)
     if v < 0:
         raise QGError("qg_dense_path", -v)

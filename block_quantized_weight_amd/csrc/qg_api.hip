@@ -300,6 +300,16 @@ MPlan make_mplan(const Layout &lo, int m, int passes = 0, int TG = 1)
     return p;
 }
 
+// Steps in flight of the one-batch kernel for this plan, or 0 where it does
+// not apply: one token, one activation window held by the workgroup's threads,
+// at most ONE_MAX_U steps per wave, one tile group per workgroup.
+int one_batch(int fmt, const Plan &p, int64_t m)
+{
+    const Geom &g = p.g;
+    if (m != 1 || g.nwin != 1 || (int64_t)m * g.wblk > (int64_t)ONE_XR * TPB || g.ngroups != p.grid) return 0;
+    return one_batch_u(fmt, (g.S + g.KS - 1) / g.KS);
+}
+
 int launch_status()
 {
     hipError_t e = hipGetLastError();
@@ -327,8 +337,11 @@ int dense(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
     const bool dot = uses_dot(fmt, xt);
     Plan p = make_plan(lo, (int)m, dot, (int)m);
     p.g.w = (const uint8_t *)w;
-    dense_fn f = fmt == QG_Q8_0 ? dense_kernel_q8_0(xt, (int)m)
-                 : fmt == QG_Q4_0 ? dense_kernel_q4_0(xt, (int)m) : dense_kernel_mxfp4(xt, (int)m);
+    const int u = one_batch(fmt, p, m);
+    dense_fn f = u ? (fmt == QG_Q8_0 ? dense_one_kernel_q8_0(xt, u)
+                      : fmt == QG_Q4_0 ? dense_one_kernel_q4_0(xt, u) : dense_one_kernel_mxfp4(xt, u))
+                   : (fmt == QG_Q8_0 ? dense_kernel_q8_0(xt, (int)m)
+                      : fmt == QG_Q4_0 ? dense_kernel_q4_0(xt, (int)m) : dense_kernel_mxfp4(xt, (int)m));
     void *args[] = {(void *)&p.g, (void *)&x, (void *)&y};
     if (allow_lds((const void *)f, p.lds) != hipSuccess) return QG_EHIP;
     hipError_t e = hipLaunchKernel((const void *)f, dim3(p.grid), dim3(TPB), args, p.lds, as_stream(stream));
@@ -516,7 +529,9 @@ int qg_dense_path(int fmt, int64_t n, int64_t k, int xt, int64_t m)
     if (st) return -st;
     if (xt != QG_F32 && xt != QG_BF16) return -QG_EINVAL;
     if (m < 1 || m > QG_MAX_M) return -QG_EINVAL;
-    return mfma_fits(make_layout(fmt, n, k), xt, m) ? QG_PATH_MFMA : QG_PATH_VALU;
+    const Layout lo = make_layout(fmt, n, k);
+    if (mfma_fits(lo, xt, m)) return QG_PATH_MFMA;
+    return one_batch(fmt, make_plan(lo, (int)m, uses_dot(fmt, xt), (int)m), m) ? QG_PATH_VALU_ONE : QG_PATH_VALU;
 }
 
 int qgemv_q8_0(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)

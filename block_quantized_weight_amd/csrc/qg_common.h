@@ -748,6 +748,95 @@ __global__ __launch_bounds__(TPB) void k_dense(Geom g, const void *__restrict__ 
     }
 }
 
+// ------------------------------------------------- one-batch dense product
+// For matrices whose per-wave share of a tile is short (at most U steps, one
+// activation window, every activation block of the call held by the
+// workgroup's threads at ONE_XR blocks each), each wave issues all of its
+// weight loads at once, directly after the loads of its threads' activation
+// blocks.  HBM then has the whole matrix requested from the start of the
+// launch (the batched pass above requests one batch ahead of the arithmetic,
+// and its second batch only after the staging barrier), the staging of x
+// overlaps the weight stream, and the arithmetic of each step follows the
+// arrival of its data.  A wave's loads complete in issue order, so the
+// activations, needed first, are issued first.  Same arithmetic, reduction
+// and output as k_dense.
+constexpr int ONE_XR = 2;
+constexpr int ONE_MAX_U = 20;
+
+template <int FMT, bool XBF16, bool DOT, int M, int U>
+__global__ __launch_bounds__(TPB) void k_dense_one(Geom g, const void *__restrict__ x, float *__restrict__ y)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    using E = Engine<FMT, XBF16, DOT, M, U>;
+    constexpr int QPB = x_quads(FMT, DOT);
+    constexpr int XQ = XBF16 ? 4 : 8;       // 16-byte loads per activation block
+    uint4 *xs = (uint4 *)smem;
+    float *corr = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
+    float *red = corr + (x_aux(FMT) ? M * g.wblk : 0);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tsub = wave >> g.ksh, kpart = wave & (g.KS - 1);
+    const int rsub = lane >> g.lsh, slot = lane & (g.L - 1);
+    const int tile = blockIdx.x * g.tpi + tsub;
+    const int total = M * g.wblk;
+
+    // activation blocks idx = thread + r * TPB: token idx / wblk, block idx % wblk
+    // (blocks past the row or past the call load block 0 of token 0 and stage zeros)
+    uint4 raw[ONE_XR][8];
+#pragma unroll
+    for (int r = 0; r < ONE_XR; ++r) {
+        const int idx = threadIdx.x + r * TPB;
+        const int t = idx / g.wblk, bl = idx - t * g.wblk;
+        const bool ok = idx < total && bl < g.nb;
+        const int64_t off = ok ? (int64_t)t * g.k + (int64_t)bl * QK : 0;
+        const uint4 *src = XBF16 ? (const uint4 *)((const uint16_t *)x + off) : (const uint4 *)((const float *)x + off);
+#pragma unroll
+        for (int i = 0; i < XQ; ++i) raw[r][i] = ld_global16(src + i);
+#pragma unroll
+        for (int i = XQ; i < 8; ++i) raw[r][i] = make_uint4(0, 0, 0, 0);
+    }
+
+    // every weight step of this wave: steps kpart, kpart + KS, ... of its tile
+    const bool active = tile < g.tiles;
+    const int tl = active ? tile : 0;
+    const uint8_t *ct = g.w + (int64_t)tl * g.ctb;
+    const uint8_t *st = g.w + g.soff + (int64_t)tl * g.stb;
+    const int nsteps = (active && kpart < g.S) ? (g.S - kpart + g.KS - 1) / g.KS : 0;
+    typename E::Regs rw;
+    E::load(g, ct, st, lane, nsteps > 0 ? kpart : 0, max(1, nsteps), g.KS, rw);
+
+#pragma unroll
+    for (int r = 0; r < ONE_XR; ++r) {
+        const int idx = threadIdx.x + r * TPB;
+        if (idx < total) {
+            const int t = idx / g.wblk, bl = idx - t * g.wblk;
+            uint4 q[8];
+            float a = 0.0f;
+            if (bl < g.nb) {
+                a = stage_block<FMT, XBF16, DOT>(raw[r], q);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) q[i] = make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < QPB; ++i) xs[(t * QPB + i) * g.wblk + bl] = q[i];
+            if (x_aux(FMT)) corr[t * g.wblk + bl] = a;
+        }
+    }
+    __syncthreads();
+
+    float acc[M];
+#pragma unroll
+    for (int t = 0; t < M; ++t) acc[t] = 0.0f;
+    E::compute(g, rw, nsteps, kpart, g.KS, slot, 0, xs, corr, acc);
+    reduce_partials<M>(g, red, acc);
+    const int64_t row = (int64_t)tile * g.R + rsub;
+    if (kpart == 0 && tile < g.tiles && row < g.n) {
+#pragma unroll
+        for (int t = 0; t < M; ++t)
+            if ((t & (g.L - 1)) == slot) y[(int64_t)t * g.n + row] = acc[t];
+    }
+}
+
 // ------------------------------------------------------------------- MoE
 // Distinct selected experts, ascending, computed by every workgroup from the
 // device-resident ids (no host round trip).  s_ids receives the ids,
@@ -970,6 +1059,9 @@ typedef void (*dense_fn)(Geom, const void *, float *);
 dense_fn dense_kernel_q8_0(int xt, int m);
 dense_fn dense_kernel_q4_0(int xt, int m);
 dense_fn dense_kernel_mxfp4(int xt, int m);
+dense_fn dense_one_kernel_q8_0(int xt, int u);
+dense_fn dense_one_kernel_q4_0(int xt, int u);
+dense_fn dense_one_kernel_mxfp4(int xt, int u);
 hipError_t launch_moe_q8_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,
                            const void *x, float *y, hipStream_t s);
 hipError_t launch_moe_q4_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,
@@ -989,6 +1081,32 @@ dense_fn pick_dense(int m)
     case 6: return k_dense<FMT, XBF16, DOT, 6>;
     case 7: return k_dense<FMT, XBF16, DOT, 7>;
     default: return k_dense<FMT, XBF16, DOT, 8>;
+    }
+}
+
+// Steps in flight of the one-batch kernel for one token whose waves each
+// stream `need` steps, or 0 where the batched pass is faster.  Measured on
+// MI355X (graph replay, 36 distinct copies, µs per launch, batched -> one
+// batch): Q4_0 6144x2560 7.04 -> 5.91, 2560x4096 5.95 -> 5.03, 19456x2560
+// (4 waves per tile) 11.54 -> 10.58, 2560x9728 (19 steps) 9.44 -> 8.69;
+// MXFP4 alike.  Q8_0 (twice the bytes and the arithmetic per step) gains
+// only on short streams: 2560x4096 (8 steps) 6.27 -> 5.89, while 6144x2560
+// (10 steps) 7.04 -> 7.21 and 2560x9728 (19 steps) 10.00 -> 10.65 lose.
+inline int one_batch_u(int fmt, int need)
+{
+    if (need <= 8) return 8;
+    if (fmt == QG_Q8_0) return 0;
+    return need <= 12 ? 12 : need <= ONE_MAX_U ? ONE_MAX_U : 0;
+}
+
+template <int FMT, bool XBF16, bool DOT>
+dense_fn pick_dense_one(int u)
+{
+    if constexpr (FMT == QG_Q8_0) {
+        return k_dense_one<FMT, XBF16, DOT, 1, 8>;
+    } else {
+        return u == 8 ? k_dense_one<FMT, XBF16, DOT, 1, 8>
+                      : u == 12 ? k_dense_one<FMT, XBF16, DOT, 1, 12> : k_dense_one<FMT, XBF16, DOT, 1, ONE_MAX_U>;
     }
 }
 

@@ -11,6 +11,11 @@ dense_fn dense_kernel_q4_0(int xt, int m)
     return xt == QG_BF16 ? pick_dense<QG_Q4_0, true, true>(m) : pick_dense<QG_Q4_0, false, false>(m);
 }
 
+dense_fn dense_one_kernel_q4_0(int xt, int u)
+{
+    return xt == QG_BF16 ? pick_dense_one<QG_Q4_0, true, true>(u) : pick_dense_one<QG_Q4_0, false, false>(u);
+}
+
 hipError_t launch_moe_q4_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,
                            const void *x, float *y, hipStream_t s)
 {

@@ -85,8 +85,10 @@ enum { QG_MOE_GATE_UP = 0, QG_MOE_DOWN_COMBINE = 1 };
 /* Largest token count of qgemm. */
 #define QG_MAX_GEMM_M 128
 
-/* Kernel families of the dense product (qg_dense_path). */
-enum { QG_PATH_VALU = 0, QG_PATH_MFMA = 1 };
+/* Kernel families of the dense product (qg_dense_path): the vector code
+ * with a few steps in flight per wave, the matrix cores, and the vector code
+ * with each wave's whole stream requested at once (one token, short rows). */
+enum { QG_PATH_VALU = 0, QG_PATH_MFMA = 1, QG_PATH_VALU_ONE = 2 };
 
 /* Activation of the fused product's epilogue (qgemv_fused). */
 enum { QG_ACT_NONE = 0, QG_ACT_SWIGLU = 1 };
@@ -151,7 +153,9 @@ int qg_dequant_f32(int fmt, const void *w_packed, int64_t n, int64_t k, float *w
  * lane-per-block vector code, and for bf16 co-batches (Q8_0 from 2 tokens,
  * Q4_0 and MXFP4 from 4) on layouts of at most 8 lanes per row, the matrix
  * cores (one bf16 MFMA per 16 rows x 32-weight block, scales applied in
- * fp32).  Results of the two agree within the rounding of fp32 sums.
+ * fp32).  Results of the two agree within the rounding of fp32 sums.  For
+ * one token over short rows the vector code requests each wave's whole
+ * weight stream at once (same arithmetic, same bits).
  * Limits: n, k <= 2^31 - 1 and k % 32 == 0.
  */
 int qgemv_q8_0(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
@@ -162,8 +166,8 @@ int qgemv_mxfp4(const void *w_packed, int64_t n, int64_t k, const void *x, int x
                 float *y, void *stream);
 
 /*
- * Which kernel family a dense call with these arguments runs: QG_PATH_VALU
- * or QG_PATH_MFMA, or a negative status (-QG_EINVAL, -QG_EUNSUPPORTED) for
+ * Which kernel family a dense call with these arguments runs: QG_PATH_VALU,
+ * QG_PATH_MFMA or QG_PATH_VALU_ONE, or a negative status (-QG_EINVAL, -QG_EUNSUPPORTED) for
  * arguments the dense calls would reject.  Host only; no device work.
  */
 int qg_dense_path(int fmt, int64_t n, int64_t k, int xt, int64_t m);

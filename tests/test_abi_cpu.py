@@ -170,7 +170,8 @@ def test_pack_and_dequant_validation():
 
 def test_dense_path_rule():
     """bf16 co-batches on layouts of <= 8 lanes per row take the matrix cores:
-    Q8_0 from 2 tokens, the 4-bit formats from 4; everything else the vector path."""
+    Q8_0 from 2 tokens, the 4-bit formats from 4; everything else the vector path,
+    one token over short rows its one-batch form."""
     V, M = q.PATH_VALU, q.PATH_MFMA
     assert q.layout(q.Q4_0, 6144, 4096)["lanes_per_row"] == 8
     assert q.dense_path(q.Q8_0, 6144, 4096, q.X_BF16, 1) == V
@@ -181,6 +182,17 @@ def test_dense_path_rule():
     assert q.dense_path(q.Q4_0, 6144, 4096, q.X_F32, 8) == V          # fp32 activations
     assert q.layout(q.Q4_0, 2560, 9728)["lanes_per_row"] == 16
     assert q.dense_path(q.Q4_0, 2560, 9728, q.X_BF16, 8) == V         # 16 lanes per row
+    # one token over short rows: the one-batch vector kernel (4-bit formats up to
+    # 20 steps per wave, Q8_0 up to 8)
+    O = q.PATH_VALU_ONE
+    assert q.dense_path(q.Q8_0, 2560, 4096, q.X_BF16, 1) == O         # 8 steps per lane
+    assert q.dense_path(q.Q8_0, 6144, 2560, q.X_BF16, 1) == V         # 10
+    assert q.dense_path(q.Q8_0, 2048, 2048, q.X_F32, 1) == O
+    assert q.dense_path(q.Q4_0, 2560, 9728, q.X_BF16, 1) == O         # 19
+    assert q.dense_path(q.Q4_0, 19456, 2560, q.X_BF16, 1) == O        # 40 over 4 waves
+    assert q.dense_path(q.Q4_0, 2560, 9728, q.X_BF16, 2) == V         # two tokens
+    assert q.dense_path(q.Q8_0, 151936, 2560, q.X_BF16, 1) == V       # 40 per wave
+    assert q.dense_path(q.MXFP4, 6144, 4096, q.X_F32, 1) == O
     for bad in [(q.Q8_0, 64, 33, q.X_BF16, 1), (q.Q8_0, 64, 64, q.X_BF16, 0), (q.Q8_0, 64, 64, q.X_BF16, 9),
                 (q.Q8_0, 64, 64, 5, 1), (9, 64, 64, q.X_BF16, 1), (q.Q8_0, 0, 64, q.X_BF16, 1)]:
         with pytest.raises(q.QGError):

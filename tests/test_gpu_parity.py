@@ -217,6 +217,24 @@ def test_config2_sweep_shapes(dev, idx):
     assert err <= TOL, err
 
 
+# one token over short rows: each wave's whole weight stream requested at once.
+# k = 4096 / 2560 / 9728 / 1056 give 8 / 10 / 19 / 33 steps per lane at 16 / 8 /
+# 16 / 1 lanes per row (the last split over 4 waves); rows ragged past the last tile
+ONE_SHAPES = [(2060, 4096), (4100, 2560), (2000, 9728), (1000, 1056)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("xt", [oracle.X_F32, oracle.X_BF16])
+def test_one_batch_path(dev, fmt, xt):
+    O, V = q.PATH_VALU_ONE, q.PATH_VALU
+    want = [O, V, V, V] if fmt == q.Q8_0 else [O, O, O, O]    # Q8_0 only up to 8 steps per wave
+    for (n, k), path in zip(ONE_SHAPES, want):
+        assert q.dense_path(fmt, n, k, xt, 1) == path, (n, k)
+        say(f"one-batch fmt={fmt} xt={xt} n={n} k={k} path={path}")
+        err = _config_dense(dev, 68, fmt, xt, n, k, 1, n % 89)
+        assert err <= TOL, (n, k, err)
+
+
 @pytest.mark.parametrize("m", [2, 4, 8])
 @pytest.mark.parametrize("name,n,k,j", [("qkv", 6144, 4096, 0), ("gate_up", 24576, 4096, 1),
                                         ("down", 4096, 12288, 2)])
@@ -338,9 +356,10 @@ def test_deterministic_and_cobatch_invariant(dev):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_every_output_written_and_nothing_else(dev, fmt):
-    n, k, m = 333, 2048, 5
-    say(f"canary fmt={fmt}")
+@pytest.mark.parametrize("m", [1, 5])
+def test_every_output_written_and_nothing_else(dev, fmt, m):
+    n, k = 333, 2048
+    say(f"canary fmt={fmt} m={m}")
     canon = wl.blocks_for(fmt, n, k, config=67, matrix=fmt)
     w = packed_dev(fmt, canon, n, k, dev)
     x = bf16_dev(draw_x((m, k), oracle.X_BF16, 67, fmt), dev)
