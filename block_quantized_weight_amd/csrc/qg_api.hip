@@ -301,13 +301,23 @@ MPlan make_mplan(const Layout &lo, int m, int passes = 0, int TG = 1)
 }
 
 // Steps in flight of the one-batch kernel for this plan, or 0 where it does
-// not apply: one token, one activation window held by the workgroup's threads,
-// at most ONE_MAX_U steps per wave, one tile group per workgroup.
-int one_batch(int fmt, const Plan &p, int64_t m)
+// not apply: few tokens (one_batch_u), one activation window held by the
+// workgroup's threads, at most ONE_MAX_U steps per wave, one tile group per
+// workgroup, and every workgroup resident at once (its registers allow
+// one_waves per compute unit, its LDS may allow fewer).  A grid that needs
+// two rounds loses to the batched pass (MI355X, Q4_0 24576x4096 at two
+// tokens, 768 workgroups of 16 steps per wave: 18.9 us batched, 21.2 one
+// batch at 2 per compute unit).
+int one_batch(int fmt, int xt, const Plan &p, int64_t m)
 {
     const Geom &g = p.g;
-    if (m != 1 || g.nwin != 1 || (int64_t)m * g.wblk > (int64_t)ONE_XR * TPB || g.ngroups != p.grid) return 0;
-    return one_batch_u(fmt, (g.S + g.KS - 1) / g.KS);
+    if (g.nwin != 1 || m * g.wblk > (int64_t)ONE_XR * TPB || g.ngroups != p.grid) return 0;
+    const int u = one_batch_u(fmt, (int)m, (g.S + g.KS - 1) / g.KS);
+    if (!u) return 0;
+    int per_cu = one_waves(fmt, xt == QG_BF16, u);
+    const int lds_cu = p.lds > 0 ? (int)((160 * 1024) / p.lds) : per_cu;
+    if (lds_cu < per_cu) per_cu = lds_cu;
+    return p.grid <= per_cu * QG_CUS ? u : 0;
 }
 
 int launch_status()
@@ -337,9 +347,9 @@ int dense(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
     const bool dot = uses_dot(fmt, xt);
     Plan p = make_plan(lo, (int)m, dot, (int)m);
     p.g.w = (const uint8_t *)w;
-    const int u = one_batch(fmt, p, m);
-    dense_fn f = u ? (fmt == QG_Q8_0 ? dense_one_kernel_q8_0(xt, u)
-                      : fmt == QG_Q4_0 ? dense_one_kernel_q4_0(xt, u) : dense_one_kernel_mxfp4(xt, u))
+    const int u = one_batch(fmt, xt, p, m);
+    dense_fn f = u ? (fmt == QG_Q8_0 ? dense_one_kernel_q8_0(xt, (int)m, u)
+                      : fmt == QG_Q4_0 ? dense_one_kernel_q4_0(xt, (int)m, u) : dense_one_kernel_mxfp4(xt, (int)m, u))
                    : (fmt == QG_Q8_0 ? dense_kernel_q8_0(xt, (int)m)
                       : fmt == QG_Q4_0 ? dense_kernel_q4_0(xt, (int)m) : dense_kernel_mxfp4(xt, (int)m));
     void *args[] = {(void *)&p.g, (void *)&x, (void *)&y};
@@ -531,7 +541,7 @@ int qg_dense_path(int fmt, int64_t n, int64_t k, int xt, int64_t m)
     if (m < 1 || m > QG_MAX_M) return -QG_EINVAL;
     const Layout lo = make_layout(fmt, n, k);
     if (mfma_fits(lo, xt, m)) return QG_PATH_MFMA;
-    return one_batch(fmt, make_plan(lo, (int)m, uses_dot(fmt, xt), (int)m), m) ? QG_PATH_VALU_ONE : QG_PATH_VALU;
+    return one_batch(fmt, xt, make_plan(lo, (int)m, uses_dot(fmt, xt), (int)m), m) ? QG_PATH_VALU_ONE : QG_PATH_VALU;
 }
 
 int qgemv_q8_0(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)

@@ -760,11 +760,20 @@ __global__ __launch_bounds__(TPB) void k_dense(Geom g, const void *__restrict__ 
 // arrival of its data.  A wave's loads complete in issue order, so the
 // activations, needed first, are issued first.  Same arithmetic, reduction
 // and output as k_dense.
-constexpr int ONE_XR = 2;
+constexpr int ONE_XR = 3;
 constexpr int ONE_MAX_U = 20;
+constexpr int QG_CUS = 256;             // compute units of the MI355X / MI350X
+
+// Waves per SIMD each variant is compiled to allow (its register budget):
+// a workgroup has one wave per SIMD, so a compute unit holds this many.
+__host__ __device__ constexpr int one_waves(int fmt, bool xbf16, int u)
+{
+    return !xbf16 ? 2 : fmt == QG_Q8_0 ? 3 : u <= 8 ? 4 : u <= 12 ? 3 : 2;
+}
 
 template <int FMT, bool XBF16, bool DOT, int M, int U>
-__global__ __launch_bounds__(TPB) void k_dense_one(Geom g, const void *__restrict__ x, float *__restrict__ y)
+__global__ __launch_bounds__(TPB, one_waves(FMT, XBF16, U)) void k_dense_one(Geom g, const void *__restrict__ x,
+                                                                              float *__restrict__ y)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     using E = Engine<FMT, XBF16, DOT, M, U>;
@@ -1059,9 +1068,9 @@ typedef void (*dense_fn)(Geom, const void *, float *);
 dense_fn dense_kernel_q8_0(int xt, int m);
 dense_fn dense_kernel_q4_0(int xt, int m);
 dense_fn dense_kernel_mxfp4(int xt, int m);
-dense_fn dense_one_kernel_q8_0(int xt, int u);
-dense_fn dense_one_kernel_q4_0(int xt, int u);
-dense_fn dense_one_kernel_mxfp4(int xt, int u);
+dense_fn dense_one_kernel_q8_0(int xt, int m, int u);
+dense_fn dense_one_kernel_q4_0(int xt, int m, int u);
+dense_fn dense_one_kernel_mxfp4(int xt, int m, int u);
 hipError_t launch_moe_q8_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,
                            const void *x, float *y, hipStream_t s);
 hipError_t launch_moe_q4_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,
@@ -1092,21 +1101,33 @@ dense_fn pick_dense(int m)
 // MXFP4 alike.  Q8_0 (twice the bytes and the arithmetic per step) gains
 // only on short streams: 2560x4096 (8 steps) 6.27 -> 5.89, while 6144x2560
 // (10 steps) 7.04 -> 7.21 and 2560x9728 (19 steps) 10.00 -> 10.65 lose.
-inline int one_batch_u(int fmt, int need)
+// The 4-bit formats use it for co-batches of up to ONE_MAX_M tokens too (the
+// vector co-batch range of bf16 activations).
+constexpr int ONE_MAX_M = 3;
+
+inline int one_batch_u(int fmt, int m, int need)
 {
-    if (need <= 8) return 8;
-    if (fmt == QG_Q8_0) return 0;
-    return need <= 12 ? 12 : need <= ONE_MAX_U ? ONE_MAX_U : 0;
+    if (fmt == QG_Q8_0) return m == 1 && need <= 8 ? 8 : 0;
+    if (m > ONE_MAX_M) return 0;
+    return need <= 8 ? 8 : need <= 12 ? 12 : need <= ONE_MAX_U ? ONE_MAX_U : 0;
 }
 
+template <int FMT, bool XBF16, bool DOT, int M>
+dense_fn pick_dense_one_u(int u)
+{
+    return u == 8 ? k_dense_one<FMT, XBF16, DOT, M, 8>
+                  : u == 12 ? k_dense_one<FMT, XBF16, DOT, M, 12> : k_dense_one<FMT, XBF16, DOT, M, ONE_MAX_U>;
+}
+
+// m tokens (1..ONE_MAX_M; Q8_0 one), u steps in flight (one_batch_u).
 template <int FMT, bool XBF16, bool DOT>
-dense_fn pick_dense_one(int u)
+dense_fn pick_dense_one(int m, int u)
 {
     if constexpr (FMT == QG_Q8_0) {
         return k_dense_one<FMT, XBF16, DOT, 1, 8>;
     } else {
-        return u == 8 ? k_dense_one<FMT, XBF16, DOT, 1, 8>
-                      : u == 12 ? k_dense_one<FMT, XBF16, DOT, 1, 12> : k_dense_one<FMT, XBF16, DOT, 1, ONE_MAX_U>;
+        return m == 1 ? pick_dense_one_u<FMT, XBF16, DOT, 1>(u)
+                      : m == 2 ? pick_dense_one_u<FMT, XBF16, DOT, 2>(u) : pick_dense_one_u<FMT, XBF16, DOT, 3>(u);
     }
 }
 

@@ -11,9 +11,9 @@ dense_fn dense_kernel_mxfp4(int xt, int m)
     return xt == QG_BF16 ? pick_dense<QG_MXFP4, true, true>(m) : pick_dense<QG_MXFP4, false, false>(m);
 }
 
-dense_fn dense_one_kernel_mxfp4(int xt, int u)
+dense_fn dense_one_kernel_mxfp4(int xt, int m, int u)
 {
-    return xt == QG_BF16 ? pick_dense_one<QG_MXFP4, true, true>(u) : pick_dense_one<QG_MXFP4, false, false>(u);
+    return xt == QG_BF16 ? pick_dense_one<QG_MXFP4, true, true>(m, u) : pick_dense_one<QG_MXFP4, false, false>(m, u);
 }
 
 hipError_t launch_moe_mxfp4(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,

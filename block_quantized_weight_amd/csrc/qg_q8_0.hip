@@ -11,9 +11,9 @@ dense_fn dense_kernel_q8_0(int xt, int m)
     return xt == QG_BF16 ? pick_dense<QG_Q8_0, true, false>(m) : pick_dense<QG_Q8_0, false, false>(m);
 }
 
-dense_fn dense_one_kernel_q8_0(int xt, int u)
+dense_fn dense_one_kernel_q8_0(int xt, int m, int u)
 {
-    return xt == QG_BF16 ? pick_dense_one<QG_Q8_0, true, false>(u) : pick_dense_one<QG_Q8_0, false, false>(u);
+    return xt == QG_BF16 ? pick_dense_one<QG_Q8_0, true, false>(m, u) : pick_dense_one<QG_Q8_0, false, false>(m, u);
 }
 
 hipError_t launch_moe_q8_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,

@@ -176,21 +176,23 @@ def test_dense_path_rule():
     assert q.layout(q.Q4_0, 6144, 4096)["lanes_per_row"] == 8
     assert q.dense_path(q.Q8_0, 6144, 4096, q.X_BF16, 1) == V
     assert q.dense_path(q.Q8_0, 6144, 4096, q.X_BF16, 2) == M
-    assert q.dense_path(q.Q4_0, 6144, 4096, q.X_BF16, 3) == V
+    assert q.dense_path(q.Q4_0, 6144, 4096, q.X_BF16, 3) == q.PATH_VALU_ONE
     assert q.dense_path(q.Q4_0, 6144, 4096, q.X_BF16, 4) == M
     assert q.dense_path(q.MXFP4, 6144, 4096, q.X_BF16, 8) == M
     assert q.dense_path(q.Q4_0, 6144, 4096, q.X_F32, 8) == V          # fp32 activations
     assert q.layout(q.Q4_0, 2560, 9728)["lanes_per_row"] == 16
     assert q.dense_path(q.Q4_0, 2560, 9728, q.X_BF16, 8) == V         # 16 lanes per row
-    # one token over short rows: the one-batch vector kernel (4-bit formats up to
-    # 20 steps per wave, Q8_0 up to 8)
+    # one token (4-bit formats: up to 3) over short rows: the one-batch vector
+    # kernel (4-bit formats up to 20 steps per wave, Q8_0 up to 8)
     O = q.PATH_VALU_ONE
     assert q.dense_path(q.Q8_0, 2560, 4096, q.X_BF16, 1) == O         # 8 steps per lane
     assert q.dense_path(q.Q8_0, 6144, 2560, q.X_BF16, 1) == V         # 10
     assert q.dense_path(q.Q8_0, 2048, 2048, q.X_F32, 1) == O
     assert q.dense_path(q.Q4_0, 2560, 9728, q.X_BF16, 1) == O         # 19
     assert q.dense_path(q.Q4_0, 19456, 2560, q.X_BF16, 1) == O        # 40 over 4 waves
-    assert q.dense_path(q.Q4_0, 2560, 9728, q.X_BF16, 2) == V         # two tokens
+    assert q.dense_path(q.Q4_0, 2560, 9728, q.X_BF16, 2) == O         # two tokens (4-bit: up to 3)
+    assert q.dense_path(q.Q4_0, 2560, 9728, q.X_BF16, 3) == V         # 3 x 304 blocks > 3 per thread
+    assert q.dense_path(q.Q8_0, 2560, 4096, q.X_F32, 2) == V          # Q8_0: one token only
     assert q.dense_path(q.Q8_0, 151936, 2560, q.X_BF16, 1) == V       # 40 per wave
     assert q.dense_path(q.MXFP4, 6144, 4096, q.X_F32, 1) == O
     for bad in [(q.Q8_0, 64, 33, q.X_BF16, 1), (q.Q8_0, 64, 64, q.X_BF16, 0), (q.Q8_0, 64, 64, q.X_BF16, 9),

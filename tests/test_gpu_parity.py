@@ -235,6 +235,21 @@ def test_one_batch_path(dev, fmt, xt):
         assert err <= TOL, (n, k, err)
 
 
+@pytest.mark.parametrize("fmt", [q.Q4_0, q.MXFP4])
+@pytest.mark.parametrize("m", [2, 3])
+def test_one_batch_cobatch(dev, fmt, m):
+    # the 4-bit formats' vector co-batches: one batch while the call's activation
+    # blocks fit three per thread (m x k / 32 <= 768) in one window
+    for n, k in ONE_SHAPES[:3]:
+        for xt in (oracle.X_BF16, oracle.X_F32):
+            path = q.dense_path(fmt, n, k, xt, m)
+            if xt == oracle.X_BF16:
+                assert path == (q.PATH_VALU_ONE if m * (k // 32) <= 768 else q.PATH_VALU), (n, k)
+            say(f"one-batch co-batch fmt={fmt} m={m} xt={xt} n={n} k={k} path={path}")
+            err = _config_dense(dev, 69, fmt, xt, n, k, m, n % 83)
+            assert err <= TOL, (n, k, xt, err)
+
+
 @pytest.mark.parametrize("m", [2, 4, 8])
 @pytest.mark.parametrize("name,n,k,j", [("qkv", 6144, 4096, 0), ("gate_up", 24576, 4096, 1),
                                         ("down", 4096, 12288, 2)])
