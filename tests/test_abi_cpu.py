@@ -195,6 +195,11 @@ def test_dense_path_rule():
     assert q.dense_path(q.Q8_0, 2560, 4096, q.X_F32, 2) == V          # Q8_0: one token only
     assert q.dense_path(q.Q8_0, 151936, 2560, q.X_BF16, 1) == V       # 40 per wave
     assert q.dense_path(q.MXFP4, 6144, 4096, q.X_F32, 1) == O
+    # only when every workgroup is resident at once: 768 workgroups of 16 steps per
+    # wave need 3 per compute unit, the 20-step variant holds 2
+    assert q.dense_path(q.Q4_0, 24576, 4096, q.X_BF16, 2) == V
+    assert q.dense_path(q.Q4_0, 24576, 4096, q.X_BF16, 1) == V
+    assert q.dense_path(q.Q4_0, 6144, 4096, q.X_BF16, 2) == O          # 768 of 4 steps: 4 per unit
     for bad in [(q.Q8_0, 64, 33, q.X_BF16, 1), (q.Q8_0, 64, 64, q.X_BF16, 0), (q.Q8_0, 64, 64, q.X_BF16, 9),
                 (q.Q8_0, 64, 64, 5, 1), (9, 64, 64, q.X_BF16, 1), (q.Q8_0, 0, 64, q.X_BF16, 1)]:
         with pytest.raises(q.QGError):
