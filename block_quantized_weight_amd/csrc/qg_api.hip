@@ -664,9 +664,14 @@ int qgemv_fused(int fmt, const void *w, int64_t n, int64_t k, const void *x, int
         p.lds += (size_t)(GLU_WAVES - WAVES) * m * 64 * 4;     // split-K partials of the extra waves
         block = 64 * GLU_WAVES;
     }
-    dense_ep_fn f = fmt == QG_Q8_0 ? dense_ep_kernel_q8_0(xt, (int)m, norm, glu)
-                    : fmt == QG_Q4_0 ? dense_ep_kernel_q4_0(xt, (int)m, norm, glu)
-                                     : dense_ep_kernel_mxfp4(xt, (int)m, norm, glu);
+    // without normalisation or gate, the plain product's one-batch form where it applies
+    const int u = !norm && glu == 0 ? one_batch(fmt, xt, p, m) : 0;
+    dense_ep_fn f = u ? (fmt == QG_Q8_0 ? dense_one_ep_kernel_q8_0(xt, (int)m, u)
+                         : fmt == QG_Q4_0 ? dense_one_ep_kernel_q4_0(xt, (int)m, u)
+                                          : dense_one_ep_kernel_mxfp4(xt, (int)m, u))
+                      : fmt == QG_Q8_0 ? dense_ep_kernel_q8_0(xt, (int)m, norm, glu)
+                      : fmt == QG_Q4_0 ? dense_ep_kernel_q4_0(xt, (int)m, norm, glu)
+                                       : dense_ep_kernel_mxfp4(xt, (int)m, norm, glu);
     void *args[] = {(void *)&p.g, (void *)&e, (void *)&x};
     if (allow_lds((const void *)f, p.lds) != hipSuccess) return QG_EHIP;
     hipError_t err = hipLaunchKernel((const void *)f, dim3(p.grid), dim3(block), args, p.lds, as_stream(stream));

@@ -771,9 +771,11 @@ __host__ __device__ constexpr int one_waves(int fmt, bool xbf16, int u)
     return !xbf16 ? 2 : fmt == QG_Q8_0 ? 3 : u <= 8 ? 4 : u <= 12 ? 3 : 2;
 }
 
+// The workgroup's one-batch pass over its tile group (grid = ngroups): on
+// return acc holds what reduce_partials leaves (row totals in the lanes of
+// waves with kpart == 0).
 template <int FMT, bool XBF16, bool DOT, int M, int U>
-__global__ __launch_bounds__(TPB, one_waves(FMT, XBF16, U)) void k_dense_one(Geom g, const void *__restrict__ x,
-                                                                              float *__restrict__ y)
+__device__ __forceinline__ void dense_one_pass(const Geom &g, const void *__restrict__ x, float acc[M])
 {
     extern __shared__ __align__(16) uint8_t smem[];
     using E = Engine<FMT, XBF16, DOT, M, U>;
@@ -784,7 +786,7 @@ __global__ __launch_bounds__(TPB, one_waves(FMT, XBF16, U)) void k_dense_one(Geo
     float *red = corr + (x_aux(FMT) ? M * g.wblk : 0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tsub = wave >> g.ksh, kpart = wave & (g.KS - 1);
-    const int rsub = lane >> g.lsh, slot = lane & (g.L - 1);
+    const int slot = lane & (g.L - 1);
     const int tile = blockIdx.x * g.tpi + tsub;
     const int total = M * g.wblk;
 
@@ -833,16 +835,25 @@ __global__ __launch_bounds__(TPB, one_waves(FMT, XBF16, U)) void k_dense_one(Geo
     }
     __syncthreads();
 
-    float acc[M];
 #pragma unroll
     for (int t = 0; t < M; ++t) acc[t] = 0.0f;
     E::compute(g, rw, nsteps, kpart, g.KS, slot, 0, xs, corr, acc);
     reduce_partials<M>(g, red, acc);
-    const int64_t row = (int64_t)tile * g.R + rsub;
-    if (kpart == 0 && tile < g.tiles && row < g.n) {
+}
+
+template <int FMT, bool XBF16, bool DOT, int M, int U>
+__global__ __launch_bounds__(TPB, one_waves(FMT, XBF16, U)) void k_dense_one(Geom g, const void *__restrict__ x,
+                                                                              float *__restrict__ y)
+{
+    float acc[M];
+    dense_one_pass<FMT, XBF16, DOT, M, U>(g, x, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tile = blockIdx.x * g.tpi + (wave >> g.ksh);
+    const int64_t row = (int64_t)tile * g.R + (lane >> g.lsh);
+    if ((wave & (g.KS - 1)) == 0 && tile < g.tiles && row < g.n) {
 #pragma unroll
         for (int t = 0; t < M; ++t)
-            if ((t & (g.L - 1)) == slot) y[(int64_t)t * g.n + row] = acc[t];
+            if ((t & (g.L - 1)) == (lane & (g.L - 1))) y[(int64_t)t * g.n + row] = acc[t];
     }
 }
 

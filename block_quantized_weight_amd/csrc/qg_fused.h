@@ -254,6 +254,24 @@ __global__ __launch_bounds__(TPB) void k_dense_ep(Geom g, EpiArgs e, const void 
     }
 }
 
+// Without normalisation or gate, where the plain product takes its one-batch
+// form (one_batch_u): the same pass, then the residual / output-type epilogue.
+template <int FMT, bool XBF16, bool DOT, int M, int U>
+__global__ __launch_bounds__(TPB, one_waves(FMT, XBF16, U)) void k_dense_one_ep(Geom g, EpiArgs e,
+                                                                                 const void *__restrict__ x)
+{
+    float acc[M];
+    dense_one_pass<FMT, XBF16, DOT, M, U>(g, x, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tile = blockIdx.x * g.tpi + (wave >> g.ksh);
+    const int64_t row = (int64_t)tile * g.R + (lane >> g.lsh);
+    if ((wave & (g.KS - 1)) == 0 && tile < g.tiles && row < e.n_out) {
+#pragma unroll
+        for (int t = 0; t < M; ++t)
+            if ((t & (g.L - 1)) == (lane & (g.L - 1))) store_out(e, (int64_t)t * e.n_out + row, acc[t]);
+    }
+}
+
 // With the SwiGLU gate, layouts of at most 32 lanes per row: the plain
 // product's grid of TPB-thread workgroups over work units u = 2 t + h, one
 // per tile count.  A wave's lanes 0..31 read records 32 h .. 32 h + 31 of gate
@@ -426,8 +444,33 @@ dense_ep_fn pick_dense_ep_fmt(int xt, int m, bool norm, int glu)
            : glu == 2 ? pick_dense_ep_glu<FMT, 2>(xt, m, norm) : pick_dense_ep_glu<FMT, 0>(xt, m, norm);
 }
 
+template <int FMT, bool XBF16, bool DOT, int M>
+dense_ep_fn pick_dense_one_ep_u(int u)
+{
+    return u == 8 ? k_dense_one_ep<FMT, XBF16, DOT, M, 8>
+                  : u == 12 ? k_dense_one_ep<FMT, XBF16, DOT, M, 12> : k_dense_one_ep<FMT, XBF16, DOT, M, ONE_MAX_U>;
+}
+
+// m tokens, u steps in flight, as pick_dense_one.
+template <int FMT>
+dense_ep_fn pick_dense_one_ep(int xt, int m, int u)
+{
+    if constexpr (FMT == QG_Q8_0) {
+        return xt == QG_BF16 ? k_dense_one_ep<FMT, true, false, 1, 8> : k_dense_one_ep<FMT, false, false, 1, 8>;
+    } else {
+        if (xt == QG_BF16)
+            return m == 1 ? pick_dense_one_ep_u<FMT, true, true, 1>(u)
+                   : m == 2 ? pick_dense_one_ep_u<FMT, true, true, 2>(u) : pick_dense_one_ep_u<FMT, true, true, 3>(u);
+        return m == 1 ? pick_dense_one_ep_u<FMT, false, false, 1>(u)
+               : m == 2 ? pick_dense_one_ep_u<FMT, false, false, 2>(u) : pick_dense_one_ep_u<FMT, false, false, 3>(u);
+    }
+}
+
 dense_ep_fn dense_ep_kernel_q8_0(int xt, int m, bool norm, int glu);
 dense_ep_fn dense_ep_kernel_q4_0(int xt, int m, bool norm, int glu);
 dense_ep_fn dense_ep_kernel_mxfp4(int xt, int m, bool norm, int glu);
+dense_ep_fn dense_one_ep_kernel_q8_0(int xt, int m, int u);
+dense_ep_fn dense_one_ep_kernel_q4_0(int xt, int m, int u);
+dense_ep_fn dense_one_ep_kernel_mxfp4(int xt, int m, int u);
 
 } // namespace qg

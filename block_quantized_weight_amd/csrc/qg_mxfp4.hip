@@ -38,6 +38,8 @@ moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms, bool norm, bool 
                          : pick_moe_stream<QG_MXFP4, false, false>(mode, ms, norm, glu);
 }
 
+dense_ep_fn dense_one_ep_kernel_mxfp4(int xt, int m, int u) { return pick_dense_one_ep<QG_MXFP4>(xt, m, u); }
+
 dense_ep_fn dense_ep_kernel_mxfp4(int xt, int m, bool norm, int glu)
 {
     return pick_dense_ep_fmt<QG_MXFP4>(xt, m, norm, glu);

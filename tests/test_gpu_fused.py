@@ -128,8 +128,8 @@ def test_fused_plain_matches_qgemv_bitwise_on_the_vector_path(dev, fmt, m):
 @pytest.mark.parametrize("n,k", [(4100, 2560), (2000, 9728), (1000, 1056)])
 @pytest.mark.parametrize("m", [1, 2])
 def test_fused_plain_matches_one_batch_bitwise(dev, fmt, n, k, m):
-    # qgemv requests each wave's whole stream at once (one token: 10, 19 and
-    # 33/4 steps per wave), the fused kernel streams it in batches; same bits
+    # one batch (one token: 10, 19 and 33/4 steps per wave): the fused call with
+    # nothing fused runs the same pass as qgemv, then its own epilogue; same bits
     assert q.dense_path(fmt, n, k, q.X_BF16, m) == q.PATH_VALU_ONE
     c = Case(fmt, n, k, m, oracle.X_BF16, False, NONE, False, False, matrix=60 + n % 7, xscale=1.0)
     say(c.label(), "vs one-batch qgemv")

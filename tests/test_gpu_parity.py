@@ -250,6 +250,26 @@ def test_one_batch_cobatch(dev, fmt, m):
             assert err <= TOL, (n, k, xt, err)
 
 
+@pytest.mark.parametrize("fmt", [q.Q4_0, q.MXFP4])
+@pytest.mark.parametrize("n,k", [(1100, 2560), (1000, 1056)])
+def test_one_batch_matches_batched_bitwise(dev, fmt, n, k):
+    # fp32 activations: two tokens take the one-batch kernel, four the batched one.
+    # These shapes (16 and 1 lanes per row, >= 4 steps per lane, windows of >= 4
+    # steps at four tokens, < 2048 tiles) get the same split-K (4 waves per tile)
+    # at both token counts; each token's arithmetic is then the same, so are its bits
+    assert q.dense_path(fmt, n, k, q.X_F32, 2) == q.PATH_VALU_ONE
+    assert q.dense_path(fmt, n, k, q.X_F32, 4) == q.PATH_VALU
+    say(f"one-batch vs batched fmt={fmt} n={n} k={k}")
+    canon = wl.blocks_for(fmt, n, k, config=70, matrix=n % 79)
+    x = draw_x((4, k), oracle.X_F32, 70, n % 79)
+    w = packed_dev(fmt, canon, n, k, dev)
+    xd = to_dev(x, dev)
+    y4 = q.qgemv(fmt, w, n, k, xd)
+    y2 = q.qgemv(fmt, w, n, k, xd[:2])
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y4[:2])
+
+
 @pytest.mark.parametrize("m", [2, 4, 8])
 @pytest.mark.parametrize("name,n,k,j", [("qkv", 6144, 4096, 0), ("gate_up", 24576, 4096, 1),
                                         ("down", 4096, 12288, 2)])
