@@ -34,7 +34,7 @@ def _packed(fmt, n, k, config, matrix, dev):
 
 def test_graph_replays_match_eager(dev):
     print("graph capture", flush=True)
-    # dense, vector path: Q8_0, one token
+    # dense, vector path: Q8_0, one token (batched)
     n1, k1 = 6144, 2560
     w1 = _packed(q.Q8_0, n1, k1, 90, 0, dev)
     x1 = _bf16(wl.x_bf16_bits((1, k1), wl.rng_for(90, 0, "x")), dev)
@@ -76,6 +76,19 @@ def test_graph_replays_match_eager(dev):
     # many-token product: 40 tokens on the matrix cores
     x5 = _bf16(wl.x_bf16_bits((40, k2), wl.rng_for(90, 6, "x")), dev)
     y5 = torch.empty((40, n2), device=dev)
+    # one-batch kernels: Q4_0 down-like 2560 x 9728 (19 steps per wave), and the o-like Q8_0
+    # 2560 x 4096 with a residual added in place (the fused call's one-batch form)
+    n6, k6 = 2560, 9728
+    w6 = _packed(q.Q4_0, n6, k6, 90, 7, dev)
+    x6 = _bf16(wl.x_bf16_bits((1, k6), wl.rng_for(90, 7, "x")), dev)
+    y6 = torch.empty((1, n6), device=dev)
+    assert q.dense_path(q.Q4_0, n6, k6, q.X_BF16, 1) == q.PATH_VALU_ONE
+    n7, k7 = 2560, 4096
+    w7 = _packed(q.Q8_0, n7, k7, 90, 8, dev)
+    x7 = _bf16(wl.x_bf16_bits((1, k7), wl.rng_for(90, 8, "x")), dev)
+    res7 = torch.from_numpy(wl.x_f32((1, n7), wl.rng_for(90, 8, "res"))).to(dev)
+    y7 = torch.empty((1, n7), device=dev)
+    assert q.dense_path(q.Q8_0, n7, k7, q.X_BF16, 1) == q.PATH_VALU_ONE
 
     def step():
         q.qgemv(q.Q8_0, w1, n1, k1, x1, y=y1)
@@ -89,8 +102,11 @@ def test_graph_replays_match_eager(dev):
         yr.copy_(res)
         q.moe_qgemv_topk_fused(fmt, de, E, dn, dk, ids, gw, hd, q.MOE_DOWN_COMBINE, residual=yr, y=yr)
         q.qgemm(q.Q4_0, w2, n2, k2, x5, y=y5)
+        q.qgemv(q.Q4_0, w6, n6, k6, x6, y=y6)
+        y7.copy_(res7)
+        q.qgemv_fused(q.Q8_0, w7, n7, k7, x7, residual=y7, y=y7)
 
-    outs = (y1, y2, ids, gw, yg, yd, y3, ya, yr, y5)
+    outs = (y1, y2, ids, gw, yg, yd, y3, ya, yr, y5, y6, y7)
 
     def eager():
         step()
