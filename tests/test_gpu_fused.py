@@ -188,6 +188,7 @@ FULL = [
     ("down", q.Q8_0, 2560, 9728, 1, False, NONE, True, False),
     ("gate_up_q4", q.Q4_0, 19456, 2560, 1, True, SWIGLU, False, True),
     ("gate_up_q4_m8", q.Q4_0, 24576, 4096, 8, True, SWIGLU, False, True),
+    ("o_norm_res_bf16", q.Q8_0, 2560, 4096, 1, True, NONE, True, True),
 ]
 
 
