@@ -29,18 +29,15 @@ __global__ void k_dequant(LayoutArgs a, const uint8_t *__restrict__ packed, floa
                 for (int p = 0; p < 4; ++p) out[4 * i + p] = d * i8_at(c[i], p);
         } else if (a.fmt == QG_Q4_0) {
             uint32_t s = packed[so] | (packed[so + 1] << 8);
-            float d = f16_bits_to_f32(s);
+            float d = q4_scale(s);
             uint32_t c[4] = {c0.x, c0.y, c0.z, c0.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i) {
+                float v[8];
+                q4_unpack8(c[i], v);
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    uint32_t v = __builtin_bit_cast(uint32_t, q4_pair(c[i], kk));
-                    float lo = __builtin_bit_cast(float, v << 16) - 136.0f;
-                    float hi = __builtin_bit_cast(float, v & 0xFFFF0000u) - 136.0f;
-                    out[8 * i + 2 * kk] = d * lo;
-                    out[8 * i + 2 * kk + 1] = d * hi;
-                }
+                for (int e = 0; e < 8; ++e) out[8 * i + e] = d * v[e];
+            }
         } else {
             float sc = e8m0_to_f32(packed[so]);
             uint32_t c[4] = {c0.x, c0.y, c0.z, c0.w};
@@ -190,7 +187,7 @@ Plan make_plan(const Layout &lo, int M, bool dot, int maxslots_lds)
     g.stb = lo.stb;
     g.soff = lo.soff;
     // activation window: as many steps as fit XBUDGET (at least one)
-    const size_t per_block = (size_t)maxslots_lds * x_quads(lo.fmt, dot) * 16 + (x_aux(lo.fmt) ? (size_t)maxslots_lds * 4 : 0);
+    const size_t per_block = (size_t)maxslots_lds * x_quads(lo.fmt, dot) * 16;
     int64_t sw_max = (int64_t)(XBUDGET / per_block) / lo.L;
     if (sw_max < 1) sw_max = 1;
     // split-K factor: more waves per tile when tiles are few; never more than
@@ -405,7 +402,7 @@ int chain_link_plan(int fmt, int xt, int m, int P, const qg_chain_link_t &in, Ch
     g.SW = (int32_t)sw;
     g.nwin = 1;
     g.wblk = (int32_t)(sw * lo.L);
-    const size_t b = chain_lds_bytes(m, dot, fmt, g.wblk, g.tpi * g.R);
+    const size_t b = chain_lds_bytes(m, dot, g.wblk, g.tpi * g.R);
     if (b > 150 * 1024) return QG_EUNSUPPORTED;
     *lds = b;
     out->x = in.x;

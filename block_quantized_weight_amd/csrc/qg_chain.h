@@ -81,27 +81,25 @@ template <int FMT, bool XBF16, bool DOT, int M> struct ChainBatch {
                                                                    : 4;
 };
 
-// LDS carve-up of one link: staged activations, Q4_0 block sums, split-K
-// partials, and a double-buffered block of finished rows for the control wave.
-template <int M, bool DOT, int FMT>
+// LDS carve-up of one link: staged activations, split-K partials, and a
+// double-buffered block of finished rows for the control wave.
+template <int M, bool DOT>
 struct ChainLds {
     uint4 *xs;
-    float *corr, *red, *out;
+    float *red, *out;
     __device__ ChainLds(uint8_t *smem, const Geom &g)
     {
         constexpr int QPB = DOT ? 4 : 8;
         xs = (uint4 *)smem;
-        corr = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
-        red = corr + (FMT == QG_Q4_0 ? M * g.wblk : 0);
+        red = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
         out = red + CWAVES * M * 64;
     }
 };
 
-inline size_t chain_lds_bytes(int M, bool dot, int fmt, int wblk, int rows_per_pass)
+inline size_t chain_lds_bytes(int M, bool dot, int wblk, int rows_per_pass)
 {
     const int QPB = dot ? 4 : 8;
-    return (size_t)M * QPB * wblk * 16 + (fmt == QG_Q4_0 ? (size_t)M * wblk * 4 : 0) + (size_t)CWAVES * M * 64 * 4 +
-           (size_t)2 * M * rows_per_pass * 4;
+    return (size_t)M * QPB * wblk * 16 + (size_t)CWAVES * M * 64 * 4 + (size_t)2 * M * rows_per_pass * 4;
 }
 
 // ------------------------------------------------------------ control wave
@@ -137,7 +135,7 @@ __device__ __forceinline__ void chain_publish(uint32_t value)
 // Stages x (M tokens) of one link into LDS with the 64 lanes of the control
 // wave; each lane issues the loads of CH blocks before writing any of them.
 template <int M, int FMT, bool XBF16, bool DOT>
-__device__ __forceinline__ void chain_stage(const Geom &g, const void *x, uint4 *xs, float *corr)
+__device__ __forceinline__ void chain_stage(const Geom &g, const void *x, uint4 *xs)
 {
     constexpr int QPB = DOT ? 4 : 8;
     constexpr int CH = XBF16 ? 2 : 1;       // blocks per lane in flight (fp32 blocks are twice the registers)
@@ -163,42 +161,13 @@ __device__ __forceinline__ void chain_stage(const Geom &g, const void *x, uint4 
             const int t = idx / g.wblk, bl = idx - t * g.wblk;
             const bool ok = bl < g.nb;
             uint4 q[8];
-            float sum = 0.0f;
-            const uint32_t *rw = (const uint32_t *)raw[c];
-            if (XBF16) {
-                if (DOT) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) q[i] = raw[c][i];
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const uint32_t a0 = rw[2 * i], a1 = rw[2 * i + 1];
-                        q[i] = make_uint4(a0 << 16, a0 & 0xFFFF0000u, a1 << 16, a1 & 0xFFFF0000u);
-                    }
-                }
-                if (FMT == QG_Q4_0) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        sum += __builtin_bit_cast(float, rw[i] << 16);
-                        sum += __builtin_bit_cast(float, rw[i] & 0xFFFF0000u);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) q[i] = raw[c][i];
-                if (FMT == QG_Q4_0) {
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) sum += __builtin_bit_cast(float, rw[i]);
-                }
-            }
+            stage_block<XBF16, DOT>(raw[c], q);
             if (!ok) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) q[i] = make_uint4(0, 0, 0, 0);
-                sum = 0.0f;
             }
 #pragma unroll
             for (int i = 0; i < QPB; ++i) xs[(t * QPB + i) * g.wblk + bl] = q[i];
-            if (FMT == QG_Q4_0) corr[t * g.wblk + bl] = (DOT ? 136.0f : 8.0f) * sum;
         }
     }
 }
@@ -258,7 +227,7 @@ __device__ __forceinline__ bool next_work(const ChainLink *links, int nlinks, in
 // computing.  Returns true if the next pass's first batch ended up in `B`.
 template <typename E, int M>
 __device__ __forceinline__ bool chain_pass_loop(const Geom &g, const PassWork &w, const PassWork &nx, int slot,
-                                                const uint4 *xs, const float *corr, float acc[M],
+                                                const uint4 *xs, float acc[M],
                                                 typename E::Regs &A, typename E::Regs &B)
 {
     constexpr int U = E::U;
@@ -272,7 +241,7 @@ __device__ __forceinline__ bool chain_pass_loop(const Geom &g, const PassWork &w
             E::load(g, more ? w.ct : nx.ct, more ? w.st : nx.st, threadIdx.x & 63,
                     more ? w.jf + (b + 1) * U * w.KS : nx.jf, c, more ? w.KS : nx.KS, B);
         }
-        E::compute(g, A, min(w.nsteps - b * U, U), w.jf + b * U * w.KS, w.KS, slot, 0, xs, corr, acc);
+        E::compute(g, A, min(w.nsteps - b * U, U), w.jf + b * U * w.KS, w.KS, slot, 0, xs, acc);
         if (++b >= nb) return true;
         {
             const bool more = b + 1 < nb;
@@ -280,7 +249,7 @@ __device__ __forceinline__ bool chain_pass_loop(const Geom &g, const PassWork &w
             E::load(g, more ? w.ct : nx.ct, more ? w.st : nx.st, threadIdx.x & 63,
                     more ? w.jf + (b + 1) * U * w.KS : nx.jf, c, more ? w.KS : nx.KS, A);
         }
-        E::compute(g, B, min(w.nsteps - b * U, U), w.jf + b * U * w.KS, w.KS, slot, 0, xs, corr, acc);
+        E::compute(g, B, min(w.nsteps - b * U, U), w.jf + b * U * w.KS, w.KS, slot, 0, xs, acc);
         if (++b >= nb) return false;
     }
 }
@@ -289,7 +258,7 @@ template <int FMT, bool XBF16, bool DOT, int M>
 __global__ __launch_bounds__(CTPB) void k_chain(const ChainLink *__restrict__ links, int nlinks)
 {
     using E = Engine<FMT, XBF16, DOT, M, ChainBatch<FMT, XBF16, DOT, M>::U>;
-    using LdsT = ChainLds<M, DOT, FMT>;
+    using LdsT = ChainLds<M, DOT>;
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ uint32_t s_base;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -317,7 +286,7 @@ __global__ __launch_bounds__(CTPB) void k_chain(const ChainLink *__restrict__ li
 
         if (control) {
             if (i > 0) chain_poll(base + (uint32_t)i);   // product i-1 complete everywhere
-            chain_stage<M, FMT, XBF16, DOT>(g, links[i].x, lds.xs, lds.corr);
+            chain_stage<M, FMT, XBF16, DOT>(g, links[i].x, lds.xs);
         }
         __syncthreads();                                   // activations of link i staged
 
@@ -336,8 +305,8 @@ __global__ __launch_bounds__(CTPB) void k_chain(const ChainLink *__restrict__ li
                         nx = w;             // nothing left: repeat this pass's first step
                         nx.nsteps = 1;
                     }
-                    const bool flip = phase ? chain_pass_loop<E, M>(g, w, nx, slot, lds.xs, lds.corr, acc, rb, ra)
-                                            : chain_pass_loop<E, M>(g, w, nx, slot, lds.xs, lds.corr, acc, ra, rb);
+                    const bool flip = phase ? chain_pass_loop<E, M>(g, w, nx, slot, lds.xs, acc, rb, ra)
+                                            : chain_pass_loop<E, M>(g, w, nx, slot, lds.xs, acc, ra, rb);
                     if (flip) phase = !phase;
                 }
                 if (g.KS > 1) {

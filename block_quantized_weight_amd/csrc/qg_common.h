@@ -18,11 +18,15 @@
 //    inner product uses (fp32 for int8 codes, bf16 pairs for 4-bit codes),
 //    in a quad-major order that makes every ds_read_b128 conflict-free.
 //  * Inner products: int8 codes go through one sign-extending byte convert
-//    and one fp32 FMA per weight; Q4_0 nibbles are turned into bf16 (128+q)
-//    with one and-or per pair and fed to v_dot2c_f32_bf16, the 136*sum(x)
-//    offset being removed per block; E2M1 nibbles are converted two at a time
-//    by the gfx950 scaled FP4->bf16 convert and also fed to the bf16 dot.
-//    Accumulation is fp32; the block scale is applied once per block.
+//    and one fp32 FMA per weight; Q4_0 codes are stored as the 4-bit two's
+//    complement of q-8 and each becomes the exact fp32 (q-8)/16 through one
+//    v_cvt_off_f32_i4 (byte-selected by SDWA), then bf16 pairs for
+//    v_dot2c_f32_bf16 (or fp32 FMAs with fp32 activations); E2M1 nibbles are
+//    converted two at a time by the gfx950 scaled FP4->bf16 convert and also
+//    fed to the bf16 dot.  Every weight enters the dot product as its exact
+//    value (times a power of two), so the rounding error of a row is bounded
+//    by its sum of |w * x|.  Accumulation is fp32; the block scale is applied
+//    once per block.
 //  * Split-K inside a workgroup (KS waves per tile) is reduced through LDS in
 //    a fixed order, then across the L lanes of a row by a xor butterfly.  No
 //    atomics: results are bitwise reproducible.
@@ -59,10 +63,8 @@ struct Layout {
 };
 
 // Staged form of one block of 32 activations in LDS: x_quads() 16-byte quads
-// (fp32, or bf16 pairs for the bf16 dot) plus, for Q4_0, one float per block
-// (the offset correction).
+// (fp32, or bf16 pairs for the bf16 dot).
 __host__ __device__ constexpr int x_quads(int fmt, bool dot) { return dot ? 4 : 8; }
-__host__ __device__ constexpr bool x_aux(int fmt) { return fmt == QG_Q4_0; }
 
 inline int block_bytes(int fmt) { return fmt == QG_Q8_0 ? 34 : fmt == QG_Q4_0 ? 18 : 17; }
 
@@ -119,8 +121,8 @@ inline Layout make_layout(int fmt, int64_t n, int64_t k)
 // ------------------------------------------------- per-block code permutation
 // Canonical block -> packed codes (P*16 bytes) and scale; and back.
 //  Q8_0 : part 0 = codes 0..15, part 1 = codes 16..31 (no permutation).
-//  Q4_0 : packed dword i, bits [4k,4k+4) = q[8i+2k], bits [16+4k,..) = q[8i+2k+1],
-//         so (dword >> 4k) & 0x000F000F holds the pair (8i+2k, 8i+2k+1).
+//  Q4_0 : packed byte B = t[2B] | t[2B+1] << 4 with t = q ^ 8, the 4-bit two's
+//         complement of the signed weight q - 8 (one byte = one adjacent pair).
 //  MXFP4: packed byte B = q[2B] | q[2B+1] << 4 (one byte = one adjacent pair).
 __host__ __device__ inline void nibbles_from_canon(const uint8_t *body, uint8_t q[32])
 {
@@ -147,13 +149,7 @@ __host__ __device__ inline void canon_to_packed(int fmt, const uint8_t *blk, uin
     if (fmt == QG_Q4_0) {
         *scale = (uint16_t)(blk[0] | (blk[1] << 8));
         nibbles_from_canon(blk + 2, q);
-        for (int i = 0; i < 4; ++i) {
-            const uint8_t *e = q + 8 * i;
-            codes[4 * i + 0] = (uint8_t)(e[0] | (e[2] << 4));
-            codes[4 * i + 1] = (uint8_t)(e[4] | (e[6] << 4));
-            codes[4 * i + 2] = (uint8_t)(e[1] | (e[3] << 4));
-            codes[4 * i + 3] = (uint8_t)(e[5] | (e[7] << 4));
-        }
+        for (int b = 0; b < 16; ++b) codes[b] = (uint8_t)((q[2 * b] ^ 8) | ((q[2 * b + 1] ^ 8) << 4));
         return;
     }
     *scale = blk[0];
@@ -173,12 +169,9 @@ __host__ __device__ inline void packed_to_canon(int fmt, const uint8_t *codes, u
     if (fmt == QG_Q4_0) {
         blk[0] = (uint8_t)(scale & 0xFF);
         blk[1] = (uint8_t)(scale >> 8);
-        for (int i = 0; i < 4; ++i) {
-            uint8_t *e = q + 8 * i;
-            e[0] = codes[4 * i + 0] & 15; e[2] = codes[4 * i + 0] >> 4;
-            e[4] = codes[4 * i + 1] & 15; e[6] = codes[4 * i + 1] >> 4;
-            e[1] = codes[4 * i + 2] & 15; e[3] = codes[4 * i + 2] >> 4;
-            e[5] = codes[4 * i + 3] & 15; e[7] = codes[4 * i + 3] >> 4;
+        for (int b = 0; b < 16; ++b) {
+            q[2 * b] = (codes[b] & 15) ^ 8;
+            q[2 * b + 1] = (codes[b] >> 4) ^ 8;
         }
         nibbles_to_canon(q, blk + 2);
         return;
@@ -274,12 +267,39 @@ __device__ __forceinline__ float i8_at(uint32_t w, int p)
     return (float)(int8_t)(w >> (8 * p));   // v_cvt_f32_i32 with a sign-extended byte select
 }
 
-// Q4_0 pair k of a packed dword as bf16 (128+q_lo, 128+q_hi).
-__device__ __forceinline__ bf16x2_t q4_pair(uint32_t w, int kk)
+// The eight Q4_0 weights of a packed dword, in element order, as the exact
+// fp32 values (q - 8) / 16.  Byte b holds t = q ^ 8 of elements 2b (low
+// nibble) and 2b + 1 (high nibble); v_cvt_off_f32_i4 reads bits [3:0] of its
+// operand as a signed 4-bit integer s and returns s / 16 exactly (the CDNA3
+// ISA's table for it runs from -0.5 for 1000b to 0.4375 for 0111b).  SDWA
+// selects the byte, so the dword costs one shift and eight converts.  The
+// block scale is applied as 16 * d.
+__device__ __forceinline__ void q4_unpack8(uint32_t w, float (&v)[8])
 {
-    uint32_t v = ((w >> (4 * kk)) & 0x000F000Fu) | 0x43004300u;
-    return __builtin_bit_cast(bf16x2_t, v);
+    uint32_t h;
+    asm("v_lshrrev_b32 %8, 4, %9\n\t"
+        "v_cvt_off_f32_i4_e32 %0, %9\n\t"
+        "v_cvt_off_f32_i4_e32 %1, %8\n\t"
+        "v_cvt_off_f32_i4_sdwa %2, %9 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1\n\t"
+        "v_cvt_off_f32_i4_sdwa %3, %8 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1\n\t"
+        "v_cvt_off_f32_i4_sdwa %4, %9 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+        "v_cvt_off_f32_i4_sdwa %5, %8 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+        "v_cvt_off_f32_i4_sdwa %6, %9 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3\n\t"
+        "v_cvt_off_f32_i4_sdwa %7, %8 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+          "=&v"(h)
+        : "v"(w));
 }
+
+// Two exact fp32 values (at most 8 significant bits) as a bf16 pair.
+__device__ __forceinline__ bf16x2_t pk_bf16(float lo, float hi)
+{
+    const f32x2_t v = {lo, hi};
+    return __builtin_convertvector(v, bf16x2_t);
+}
+
+// Q4_0 block scale as applied to the (q - 8) / 16 values.
+__device__ __forceinline__ float q4_scale(uint32_t bits) { return 16.0f * f16_bits_to_f32(bits); }
 
 // Global-memory accessors.  Pointers that reach a kernel through memory (not
 // as kernel arguments) are generic; casting them to the global address space
@@ -338,39 +358,26 @@ __device__ __forceinline__ f32x2_t fp4_pair_f32(uint32_t w)
 }
 
 // Staged form of one block of 32 activations (raw: 4 quads of bf16 or 8
-// quads of fp32, in element order): q[0 .. x_quads) and the per-block float.
-template <int FMT, bool XBF16, bool DOT>
-__device__ __forceinline__ float stage_block(const uint4 (&raw)[8], uint4 (&q)[8])
+// quads of fp32, in element order): q[0 .. x_quads).
+template <bool XBF16, bool DOT>
+__device__ __forceinline__ void stage_block(const uint4 *raw, uint4 (&q)[8])
 {
-    const uint32_t *rw = (const uint32_t *)raw;
-    float sum = 0.0f;
     if (XBF16) {
         if (DOT) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) q[i] = raw[i];
         } else {
+            const uint32_t *rw = (const uint32_t *)raw;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const uint32_t a0 = rw[2 * i], a1 = rw[2 * i + 1];
                 q[i] = make_uint4(a0 << 16, a0 & 0xFFFF0000u, a1 << 16, a1 & 0xFFFF0000u);
             }
         }
-        if (FMT == QG_Q4_0) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                sum += __builtin_bit_cast(float, rw[i] << 16);
-                sum += __builtin_bit_cast(float, rw[i] & 0xFFFF0000u);
-            }
-        }
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) q[i] = raw[i];
-        if (FMT == QG_Q4_0) {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) sum += __builtin_bit_cast(float, rw[i]);
-        }
     }
-    return FMT == QG_Q4_0 ? (DOT ? 136.0f : 8.0f) * sum : 0.0f;
 }
 
 // ------------------------------------------------------------- GEMV engine
@@ -395,10 +402,9 @@ struct Slots {
 
 template <bool XBF16, bool DOT>
 struct XStage {
-    // Stages window w of M slots: xs[(t*QPB + q)*wblk + bl] (16 B quads) and,
-    // for Q4_0, aux[t*wblk + bl] (the per-block correction of stage_block).
+    // Stages window w of M slots: xs[(t*QPB + q)*wblk + bl] (16 B quads).
     template <int M, int FMT>
-    static __device__ __forceinline__ void run(const Geom &g, const void *x, const Slots &sl, int w, uint4 *xs, float *aux)
+    static __device__ __forceinline__ void run(const Geom &g, const void *x, const Slots &sl, int w, uint4 *xs)
     {
         constexpr int QPB = x_quads(FMT, DOT);
         const int b0 = w * g.SW * g.L;
@@ -407,7 +413,6 @@ struct XStage {
             const int t = idx / g.wblk, bl = idx - t * g.wblk, b = b0 + bl;
             const int64_t xo = (int64_t)sl.xrow[t] * g.k;
             uint4 raw[8], q[8];
-            float a = 0.0f;
             if (b < g.nb) {
                 if (XBF16) {
                     const uint4 *src = (const uint4 *)((const uint16_t *)x + xo + (int64_t)b * QK);
@@ -418,14 +423,13 @@ struct XStage {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) raw[i] = ld_global16(src + i);
                 }
-                a = stage_block<FMT, XBF16, DOT>(raw, q);
+                stage_block<XBF16, DOT>(raw, q);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) q[i] = make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < QPB; ++i) xs[(t * QPB + i) * g.wblk + bl] = q[i];
-            if (x_aux(FMT)) aux[t * g.wblk + bl] = a;
         }
     }
 };
@@ -474,8 +478,8 @@ struct Engine {
     // Slot t reads staged activation row xm(t) (the identity for the dense
     // product); slots t >= xm.count() are skipped.
     template <typename XMap = IdMap>
-    static __device__ __forceinline__ void step(const Geom &g, const uint4 *c, uint32_t sbits, const uint4 *xs,
-                                                const float *corr, int bl, float acc[M], const XMap &xm = XMap())
+    static __device__ __forceinline__ void step(const Geom &g, const uint4 *c, uint32_t sbits, const uint4 *xs, int bl,
+                                                float acc[M], const XMap &xm = XMap())
     {
         if (FMT == QG_Q8_0) {
             const float d = f16_bits_to_f32(sbits);
@@ -495,49 +499,41 @@ struct Engine {
                 acc[t] = __builtin_fmaf(d, s, acc[t]);
             }
         } else if (FMT == QG_Q4_0) {
-            const float d = f16_bits_to_f32(sbits);
+            const float d = q4_scale(sbits);
             const uint32_t cw[4] = {c[0].x, c[0].y, c[0].z, c[0].w};
+            float v[4][8];          // v[i][e]: element 8i + e, (q - 8) / 16
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q4_unpack8(cw[i], v[i]);
             if (DOT) {
-                bf16x2_t pr[4][4];
+                bf16x2_t pr[16];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) pr[i][kk] = q4_pair(cw[i], kk);
+                for (int p = 0; p < 16; ++p) pr[p] = pk_bf16(v[p >> 2][2 * (p & 3)], v[p >> 2][2 * (p & 3) + 1]);
 #pragma unroll
                 for (int t = 0; t < M; ++t) {
                     if (t >= xm.count()) break;
-                    float s = -corr[xm(t) * g.wblk + bl];
+                    float s = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const uint4 xq = xs[(xm(t) * 4 + i) * g.wblk + bl];
-                        s = dot2(pr[i][0], u32_as_bf16x2(xq.x), s);
-                        s = dot2(pr[i][1], u32_as_bf16x2(xq.y), s);
-                        s = dot2(pr[i][2], u32_as_bf16x2(xq.z), s);
-                        s = dot2(pr[i][3], u32_as_bf16x2(xq.w), s);
+                        s = dot2(pr[4 * i + 0], u32_as_bf16x2(xq.x), s);
+                        s = dot2(pr[4 * i + 1], u32_as_bf16x2(xq.y), s);
+                        s = dot2(pr[4 * i + 2], u32_as_bf16x2(xq.z), s);
+                        s = dot2(pr[4 * i + 3], u32_as_bf16x2(xq.w), s);
                     }
                     acc[t] = __builtin_fmaf(d, s, acc[t]);
                 }
             } else {
-                // fp32 activations: quad 2i holds elements 8i..8i+3 (nibble bits 0,16,4,20),
-                // quad 2i+1 holds 8i+4..8i+7 (bits 8,24,12,28).
-                float v[32];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int sh[8] = {0, 16, 4, 20, 8, 24, 12, 28};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[8 * i + e] = (float)((cw[i] >> sh[e]) & 15u);
-                }
 #pragma unroll
                 for (int t = 0; t < M; ++t) {
                     if (t >= xm.count()) break;
-                    float s = -corr[xm(t) * g.wblk + bl];
+                    float s = 0.0f;
 #pragma unroll
                     for (int qd = 0; qd < 8; ++qd) {
                         const float4 xq = __builtin_bit_cast(float4, xs[(xm(t) * 8 + qd) * g.wblk + bl]);
-                        s = __builtin_fmaf(v[4 * qd + 0], xq.x, s);
-                        s = __builtin_fmaf(v[4 * qd + 1], xq.y, s);
-                        s = __builtin_fmaf(v[4 * qd + 2], xq.z, s);
-                        s = __builtin_fmaf(v[4 * qd + 3], xq.w, s);
+                        s = __builtin_fmaf(v[qd >> 1][4 * (qd & 1) + 0], xq.x, s);
+                        s = __builtin_fmaf(v[qd >> 1][4 * (qd & 1) + 1], xq.y, s);
+                        s = __builtin_fmaf(v[qd >> 1][4 * (qd & 1) + 2], xq.z, s);
+                        s = __builtin_fmaf(v[qd >> 1][4 * (qd & 1) + 3], xq.w, s);
                     }
                     acc[t] = __builtin_fmaf(d, s, acc[t]);
                 }
@@ -602,7 +598,7 @@ struct Engine {
 
     template <typename XMap = IdMap>
     static __device__ __forceinline__ void compute(const Geom &g, const Regs &r, int cnt, int jfirst, int KS,
-                                                   int slot, int b0, const uint4 *xs, const float *corr, float acc[M],
+                                                   int slot, int b0, const uint4 *xs, float acc[M],
                                                    const XMap &xm = XMap())
     {
 #pragma unroll
@@ -610,7 +606,7 @@ struct Engine {
             if (u < cnt) {
                 const int j = jfirst + u * KS;
                 const int bl = j * g.L + slot - b0;
-                step(g, r.c[u], r.s[u], xs, corr, bl, acc, xm);
+                step(g, r.c[u], r.s[u], xs, bl, acc, xm);
             }
         }
     }
@@ -619,24 +615,24 @@ struct Engine {
     // whole workgroup calls it together (it contains barriers when staging).
     // Returns the per-lane partial sums (before the KS and L reductions).
     static __device__ __forceinline__ void pass(const Geom &g, const void *x, const Slots &sl, int tile, bool &staged,
-                                                uint4 *xs, float *corr, float acc[M])
+                                                uint4 *xs, float acc[M])
     {
         XStage<XBF16, DOT> st;
-        pass_st(g, x, sl, tile, staged, xs, corr, acc, st);
+        pass_st(g, x, sl, tile, staged, xs, acc, st);
     }
 
     // The same with a given stager: an object whose run<M, FMT>(g, x, sl, w,
-    // xs, corr) fills window w's staged activations in this engine's form; the
+    // xs) fills window w's staged activations in this engine's form; the
     // whole workgroup calls it between two barriers.
     template <class ST>
     static __device__ __forceinline__ void pass_st(const Geom &g, const void *x, const Slots &sl, int tile, bool &staged,
-                                                   uint4 *xs, float *corr, float acc[M], ST &stg)
+                                                   uint4 *xs, float acc[M], ST &stg)
     {
         const bool active = tile < g.tiles;
         // inactive waves load (and ignore) tile 0, step 0, so that loads stay unconditional
         const int tl = active ? tile : 0;
         pass_core(g, x, sl, g.w + (int64_t)tl * g.ctb, g.w + g.soff + (int64_t)tl * g.stb, threadIdx.x & 63, active,
-                  staged, xs, corr, acc, stg);
+                  staged, xs, acc, stg);
     }
 
     // The pass with the lane's own tile bases (ct, st) and record lane rl:
@@ -646,7 +642,7 @@ struct Engine {
     template <class ST>
     static __device__ __forceinline__ void pass_core(const Geom &g, const void *x, const Slots &sl, const uint8_t *ct,
                                                      const uint8_t *st, int rl, bool active, bool &staged, uint4 *xs,
-                                                     float *corr, float acc[M], ST &stg)
+                                                     float acc[M], ST &stg)
     {
         const int lane = rl, wave = threadIdx.x >> 6;
         const int KS = g.KS, kpart = wave & (KS - 1);
@@ -663,7 +659,7 @@ struct Engine {
             load(g, ct, st, lane, nsteps > 0 ? jf : 0, max(1, min(nsteps, U)), KS, ra);
             if (g.nwin > 1 || !staged) {
                 __syncthreads();
-                stg.template run<M, FMT>(g, x, sl, w, xs, corr);
+                stg.template run<M, FMT>(g, x, sl, w, xs);
                 __syncthreads();
                 staged = true;
             }
@@ -673,13 +669,13 @@ struct Engine {
                 const int cA = min(nsteps - done, U);
                 const int rB = nsteps - done - cA;
                 load(g, ct, st, lane, rB > 0 ? jf + (done + cA) * KS : jlast, rB > 0 ? min(rB, U) : 1, KS, rb);
-                compute(g, ra, cA, jf + done * KS, KS, slot, b0, xs, corr, acc);
+                compute(g, ra, cA, jf + done * KS, KS, slot, b0, xs, acc);
                 done += cA;
                 if (done >= nsteps) break;
                 const int cB = min(nsteps - done, U);
                 const int rA = nsteps - done - cB;
                 load(g, ct, st, lane, rA > 0 ? jf + (done + cB) * KS : jlast, rA > 0 ? min(rA, U) : 1, KS, ra);
-                compute(g, rb, cB, jf + done * KS, KS, slot, b0, xs, corr, acc);
+                compute(g, rb, cB, jf + done * KS, KS, slot, b0, xs, acc);
                 done += cB;
             }
         }
@@ -714,7 +710,6 @@ __device__ __forceinline__ void reduce_partials(const Geom &g, float *red, float
 inline __host__ __device__ size_t lds_bytes(int M, bool dot, int fmt, int wblk)
 {
     size_t b = (size_t)M * x_quads(fmt, dot) * wblk * 16;
-    if (x_aux(fmt)) b += (size_t)M * wblk * 4;
     b += (size_t)WAVES * M * 64 * 4;
     return b;
 }
@@ -725,8 +720,7 @@ __global__ __launch_bounds__(TPB) void k_dense(Geom g, const void *__restrict__ 
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int QPB = x_quads(FMT, DOT);
     uint4 *xs = (uint4 *)smem;
-    float *corr = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
-    float *red = corr + (x_aux(FMT) ? M * g.wblk : 0);
+    float *red = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
     __shared__ int32_t s_rows[QG_MAX_M];
     if (threadIdx.x < QG_MAX_M) s_rows[threadIdx.x] = threadIdx.x;   // read only after the staging barrier
     Slots sl{s_rows, s_rows};
@@ -737,7 +731,7 @@ __global__ __launch_bounds__(TPB) void k_dense(Geom g, const void *__restrict__ 
     for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {
         const int tile = grp * g.tpi + tsub;
         float acc[M];
-        Engine<FMT, XBF16, DOT, M>::pass(g, x, sl, tile, staged, xs, corr, acc);
+        Engine<FMT, XBF16, DOT, M>::pass(g, x, sl, tile, staged, xs, acc);
         reduce_partials<M>(g, red, acc);
         const int64_t row = (int64_t)tile * g.R + rsub;
         if (kpart == 0 && tile < g.tiles && row < g.n) {
@@ -782,8 +776,7 @@ __device__ __forceinline__ void dense_one_pass(const Geom &g, const void *__rest
     constexpr int QPB = x_quads(FMT, DOT);
     constexpr int XQ = XBF16 ? 4 : 8;       // 16-byte loads per activation block
     uint4 *xs = (uint4 *)smem;
-    float *corr = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
-    float *red = corr + (x_aux(FMT) ? M * g.wblk : 0);
+    float *red = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tsub = wave >> g.ksh, kpart = wave & (g.KS - 1);
     const int slot = lane & (g.L - 1);
@@ -821,23 +814,21 @@ __device__ __forceinline__ void dense_one_pass(const Geom &g, const void *__rest
         if (idx < total) {
             const int t = idx / g.wblk, bl = idx - t * g.wblk;
             uint4 q[8];
-            float a = 0.0f;
             if (bl < g.nb) {
-                a = stage_block<FMT, XBF16, DOT>(raw[r], q);
+                stage_block<XBF16, DOT>(raw[r], q);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) q[i] = make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < QPB; ++i) xs[(t * QPB + i) * g.wblk + bl] = q[i];
-            if (x_aux(FMT)) corr[t * g.wblk + bl] = a;
         }
     }
     __syncthreads();
 
 #pragma unroll
     for (int t = 0; t < M; ++t) acc[t] = 0.0f;
-    E::compute(g, rw, nsteps, kpart, g.KS, slot, 0, xs, corr, acc);
+    E::compute(g, rw, nsteps, kpart, g.KS, slot, 0, xs, acc);
     reduce_partials<M>(g, red, acc);
 }
 
@@ -913,7 +904,7 @@ struct MoeArgs {
 // Runs the dense passes of this workgroup over expert `e` for `cnt` slots
 // (1 <= cnt <= 8), dispatched to the engine instantiated for that count.
 template <int FMT, bool XBF16, bool DOT, int M>
-__device__ __forceinline__ void moe_tiles(Geom g, const void *x, const Slots sl, uint4 *xs, float *corr, float *red, int grp,
+__device__ __forceinline__ void moe_tiles(Geom g, const void *x, const Slots sl, uint4 *xs, float *red, int grp,
                           float *part_out /* [M][tpi*R] or null */, float *y)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -922,7 +913,7 @@ __device__ __forceinline__ void moe_tiles(Geom g, const void *x, const Slots sl,
     bool staged = false;
     const int tile = grp * g.tpi + tsub;
     float acc[M];
-    Engine<FMT, XBF16, DOT, M>::pass(g, x, sl, tile, staged, xs, corr, acc);
+    Engine<FMT, XBF16, DOT, M>::pass(g, x, sl, tile, staged, xs, acc);
     reduce_partials<M>(g, red, acc);
     const int64_t row = (int64_t)tile * g.R + rsub;
     if (kpart == 0 && tile < g.tiles && row < g.n) {
@@ -940,18 +931,18 @@ __device__ __forceinline__ void moe_tiles(Geom g, const void *x, const Slots sl,
 }
 
 template <int FMT, bool XBF16, bool DOT>
-__device__ __forceinline__ void moe_dispatch(int cnt, Geom g, const void *x, const Slots sl, uint4 *xs, float *corr, float *red,
+__device__ __forceinline__ void moe_dispatch(int cnt, Geom g, const void *x, const Slots sl, uint4 *xs, float *red,
                              int grp, float *part_out, float *y)
 {
     switch (cnt) {
-    case 1: moe_tiles<FMT, XBF16, DOT, 1>(g, x, sl, xs, corr, red, grp, part_out, y); break;
-    case 2: moe_tiles<FMT, XBF16, DOT, 2>(g, x, sl, xs, corr, red, grp, part_out, y); break;
-    case 3: moe_tiles<FMT, XBF16, DOT, 3>(g, x, sl, xs, corr, red, grp, part_out, y); break;
-    case 4: moe_tiles<FMT, XBF16, DOT, 4>(g, x, sl, xs, corr, red, grp, part_out, y); break;
-    case 5: moe_tiles<FMT, XBF16, DOT, 5>(g, x, sl, xs, corr, red, grp, part_out, y); break;
-    case 6: moe_tiles<FMT, XBF16, DOT, 6>(g, x, sl, xs, corr, red, grp, part_out, y); break;
-    case 7: moe_tiles<FMT, XBF16, DOT, 7>(g, x, sl, xs, corr, red, grp, part_out, y); break;
-    default: moe_tiles<FMT, XBF16, DOT, 8>(g, x, sl, xs, corr, red, grp, part_out, y); break;
+    case 1: moe_tiles<FMT, XBF16, DOT, 1>(g, x, sl, xs, red, grp, part_out, y); break;
+    case 2: moe_tiles<FMT, XBF16, DOT, 2>(g, x, sl, xs, red, grp, part_out, y); break;
+    case 3: moe_tiles<FMT, XBF16, DOT, 3>(g, x, sl, xs, red, grp, part_out, y); break;
+    case 4: moe_tiles<FMT, XBF16, DOT, 4>(g, x, sl, xs, red, grp, part_out, y); break;
+    case 5: moe_tiles<FMT, XBF16, DOT, 5>(g, x, sl, xs, red, grp, part_out, y); break;
+    case 6: moe_tiles<FMT, XBF16, DOT, 6>(g, x, sl, xs, red, grp, part_out, y); break;
+    case 7: moe_tiles<FMT, XBF16, DOT, 7>(g, x, sl, xs, red, grp, part_out, y); break;
+    default: moe_tiles<FMT, XBF16, DOT, 8>(g, x, sl, xs, red, grp, part_out, y); break;
     }
 }
 
@@ -975,8 +966,7 @@ __global__ __launch_bounds__(TPB) void k_moe_gate_up(Geom g, MoeArgs a, const vo
     const int nsl = s_nsl;
     constexpr int QPB = x_quads(FMT, DOT);
     uint4 *xs = (uint4 *)smem;
-    float *corr = (float *)(smem + (size_t)QG_MAX_M * QPB * g.wblk * 16);
-    float *red = corr + (x_aux(FMT) ? QG_MAX_M * g.wblk : 0);
+    float *red = (float *)(smem + (size_t)QG_MAX_M * QPB * g.wblk * 16);
     Geom ge = g;
     ge.w = a.experts + (int64_t)e * a.expert_bytes;
     for (int c0 = 0; c0 < nsl; c0 += QG_MAX_M) {
@@ -990,7 +980,7 @@ __global__ __launch_bounds__(TPB) void k_moe_gate_up(Geom g, MoeArgs a, const vo
         Slots sl{s_xrow, s_yrow};
         for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {
             __syncthreads();
-            moe_dispatch<FMT, XBF16, DOT>(cnt, ge, x, sl, xs, corr, red, grp, nullptr, y);
+            moe_dispatch<FMT, XBF16, DOT>(cnt, ge, x, sl, xs, red, grp, nullptr, y);
         }
     }
 }
@@ -1012,8 +1002,7 @@ __global__ __launch_bounds__(TPB) void k_moe_down(Geom g, MoeArgs a, const void 
     distinct_experts(a.ids, nslots, a.n_experts, s_ids, s_list, &s_count);
     constexpr int QPB = x_quads(FMT, DOT);
     uint4 *xs = (uint4 *)smem;
-    float *corr = (float *)(smem + (size_t)QG_MAX_M * QPB * g.wblk * 16);
-    float *red = corr + (x_aux(FMT) ? QG_MAX_M * g.wblk : 0);
+    float *red = (float *)(smem + (size_t)QG_MAX_M * QPB * g.wblk * 16);
     float *part = red + WAVES * QG_MAX_M * 64;           // [nslots][tpi*R]
     const int rows_pg = g.tpi * g.R;
     for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {
@@ -1038,7 +1027,7 @@ __global__ __launch_bounds__(TPB) void k_moe_down(Geom g, MoeArgs a, const void 
                 __syncthreads();
                 // partial results land in a staging area, then move to part[slot]
                 float *tmp = part + nslots * rows_pg;    // [8][rows_pg]
-                moe_dispatch<FMT, XBF16, DOT>(cnt, ge, x, sl, xs, corr, red, grp, tmp, nullptr);
+                moe_dispatch<FMT, XBF16, DOT>(cnt, ge, x, sl, xs, red, grp, tmp, nullptr);
                 __syncthreads();
                 for (int i = threadIdx.x; i < cnt * rows_pg; i += TPB) {
                     const int t = i / rows_pg, rl = i - t * rows_pg;

@@ -117,16 +117,14 @@ struct NormStage {
     }
 
     template <int M, int FMT>
-    __device__ __forceinline__ void run(const Geom &g, const void *x, const Slots &sl, int w, uint4 *xs, float *aux)
+    __device__ __forceinline__ void run(const Geom &g, const void *x, const Slots &sl, int w, uint4 *xs)
     {
         const bool sums_here = g.nwin == 1;
         if (!sums_here && !have) rms_pass<M>(g, x, sl);
         have = true;
         constexpr int QPB = x_quads(FMT, false);
         const int b0 = w * g.SW * g.L;
-        // one half block (16 activations) per thread and iteration; the two
-        // halves of a block are adjacent lanes (total is even, so a pair is
-        // always active together)
+        // one half block (16 activations) per thread and iteration
         const int total = 2 * M * g.wblk;
         float ss[M];
 #pragma unroll
@@ -136,7 +134,7 @@ struct NormStage {
             const int t = item / g.wblk, bl = item - t * g.wblk, b = b0 + bl;
             const int64_t xo = (int64_t)sl.xrow[t] * g.k + (int64_t)b * QK + half * 16;
             uint4 *dst = xs + (t * QPB + half * 4) * g.wblk + bl;
-            float sq = 0.0f, sum = 0.0f;
+            float sq = 0.0f;
             if (b < g.nb) {
                 uint4 raw[4];
                 if (XBF16) {
@@ -164,18 +162,12 @@ struct NormStage {
                     sq = fmaf(x3, x3, sq);
                     const float p0 = x0 * __builtin_bit_cast(float, gv.x), p1 = x1 * __builtin_bit_cast(float, gv.y);
                     const float p2 = x2 * __builtin_bit_cast(float, gv.z), p3 = x3 * __builtin_bit_cast(float, gv.w);
-                    if (FMT == QG_Q4_0) sum += (p0 + p1) + (p2 + p3);
                     dst[i * g.wblk] = make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
                                                  __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dst[i * g.wblk] = make_uint4(0, 0, 0, 0);
-            }
-            if (x_aux(FMT)) {
-                // the Q4_0 zero point of the whole block (as in stage_block): halves in order
-                const float other = __shfl_xor(sum, 1, 64);
-                if (half == 0) aux[t * g.wblk + bl] = 8.0f * (sum + other);
             }
 #pragma unroll
             for (int tt = 0; tt < M; ++tt) ss[tt] += tt == t ? sq : 0.0f;
@@ -188,9 +180,9 @@ struct NormStage {
 template <bool XBF16, bool DOT>
 struct PlainStage {
     template <int M, int FMT>
-    __device__ __forceinline__ void run(const Geom &g, const void *x, const Slots &sl, int w, uint4 *xs, float *aux)
+    __device__ __forceinline__ void run(const Geom &g, const void *x, const Slots &sl, int w, uint4 *xs)
     {
-        XStage<XBF16, DOT>::template run<M, FMT>(g, x, sl, w, xs, aux);
+        XStage<XBF16, DOT>::template run<M, FMT>(g, x, sl, w, xs);
     }
 };
 
@@ -220,8 +212,7 @@ __global__ __launch_bounds__(TPB) void k_dense_ep(Geom g, EpiArgs e, const void 
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int QPB = x_quads(FMT, DOT);
     uint4 *xs = (uint4 *)smem;
-    float *corr = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
-    float *red = corr + (x_aux(FMT) ? M * g.wblk : 0);
+    float *red = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
     __shared__ int32_t s_rows[QG_MAX_M];
     __shared__ float s_part[WAVES * QG_MAX_M];
     if (threadIdx.x < QG_MAX_M) s_rows[threadIdx.x] = threadIdx.x;   // read only after the first barrier
@@ -240,7 +231,7 @@ __global__ __launch_bounds__(TPB) void k_dense_ep(Geom g, EpiArgs e, const void 
     for (int grp = blockIdx.x; grp < g.ngroups; grp += gridDim.x) {
         const int tile = grp * g.tpi + tsub;
         float acc[M];
-        Engine<FMT, XBF16, DOT, M>::pass_st(g, x, sl, tile, staged, xs, corr, acc, st);
+        Engine<FMT, XBF16, DOT, M>::pass_st(g, x, sl, tile, staged, xs, acc, st);
         reduce_partials<M>(g, red, acc);
         const int64_t row = (int64_t)tile * g.R + rsub;
         if (kpart == 0 && tile < g.tiles && row < e.n_out) {
@@ -285,8 +276,7 @@ __global__ __launch_bounds__(TPB) void k_dense_glu_lanes(Geom g, EpiArgs e, cons
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int QPB = x_quads(FMT, DOT);
     uint4 *xs = (uint4 *)smem;
-    float *corr = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
-    float *red = corr + (x_aux(FMT) ? M * g.wblk : 0);
+    float *red = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
     __shared__ int32_t s_rows[QG_MAX_M];
     __shared__ float s_part[WAVES * QG_MAX_M];
     if (threadIdx.x < QG_MAX_M) s_rows[threadIdx.x] = threadIdx.x;   // read only after the first barrier
@@ -311,7 +301,7 @@ __global__ __launch_bounds__(TPB) void k_dense_glu_lanes(Geom g, EpiArgs e, cons
         const int rl = 32 * h + (lane & 31);
         float acc[M];
         Engine<FMT, XBF16, DOT, M>::pass_core(g, x, sl, g.w + (int64_t)tile * g.ctb, g.w + g.soff + (int64_t)tile * g.stb,
-                                              rl, active, staged, xs, corr, acc, st);
+                                              rl, active, staged, xs, acc, st);
         reduce_partials<M>(g, red, acc);
         float up[M];
 #pragma unroll
@@ -345,8 +335,7 @@ __global__ __launch_bounds__(64 * GLU_WAVES) void k_dense_glu(Geom g, EpiArgs e,
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int QPB = x_quads(FMT, DOT);
     uint4 *xs = (uint4 *)smem;
-    float *corr = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
-    float *red = corr + (x_aux(FMT) ? M * g.wblk : 0);
+    float *red = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
     __shared__ int32_t s_rows[QG_MAX_M];
     __shared__ float s_part[GLU_WAVES * QG_MAX_M];
     __shared__ float s_up[GLU_WAVES / 2][QG_MAX_M][64];
@@ -371,7 +360,7 @@ __global__ __launch_bounds__(64 * GLU_WAVES) void k_dense_glu(Geom g, EpiArgs e,
         const bool active = pair < e.half_tiles;
         const int tile = active ? (up ? pair + e.half_tiles : pair) : g.tiles;
         float acc[M];
-        Engine<FMT, XBF16, DOT, M>::pass_st(g, x, sl, tile, staged, xs, corr, acc, st);
+        Engine<FMT, XBF16, DOT, M>::pass_st(g, x, sl, tile, staged, xs, acc, st);
         reduce_partials<M>(g, red, acc);
         if (up && kpart == 0 && active) {
 #pragma unroll

@@ -9,12 +9,11 @@
 //   A (16 x 32)  the tokens' activations of that block (A row = token, rows
 //                past M are zero), bf16 exactly as given;
 //   B (32 x 16)  the 16 rows' codes, converted to bf16 in registers (exact:
-//                Q4_0 as 128+q, E2M1 values, int8 codes);
-//   C            for Q4_0, -136 * (sum of the block's activations) per token,
-//                itself one MFMA of A with a constant B of -136 (exact
-//                products, fp32 sums), computed once per block; else zero;
+//                Q4_0 as (q-8)/16, E2M1 values, int8 codes);
+//   C            zero;
 //   D[t][r]      the block's dot product for token t and row r before the
-//                block scale, which is applied in fp32: acc += d * D.
+//                block scale, which is applied in fp32: acc += d * D (16 d
+//                for Q4_0).
 // The sum over k inside the instruction is order-free, so any assignment of
 // the 32 k values to operand slots works as long as A and B agree: lane l of
 // both holds 8 consecutive k (octet l/16 of the block), A for token l%16 and
@@ -146,8 +145,10 @@ struct MEngine {
     {
         uint32_t q[4];
         if (FMT == QG_Q4_0) {
+            float v[8];
+            q4_unpack8(c[0], v);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) q[kk] = ((c[0] >> (4 * kk)) & 0x000F000Fu) | 0x43004300u;
+            for (int kk = 0; kk < 4; ++kk) q[kk] = __builtin_bit_cast(uint32_t, pk_bf16(v[2 * kk], v[2 * kk + 1]));
         } else if (FMT == QG_MXFP4) {
             q[0] = __builtin_bit_cast(uint32_t, fp4_pair_bf16<0>(c[0]));
             q[1] = __builtin_bit_cast(uint32_t, fp4_pair_bf16<1>(c[0]));
@@ -170,7 +171,7 @@ struct MEngine {
 
     static __device__ __forceinline__ float scale(uint32_t bits)
     {
-        return FMT == QG_MXFP4 ? e8m0_to_f32(bits) : f16_bits_to_f32(bits);
+        return FMT == QG_MXFP4 ? e8m0_to_f32(bits) : FMT == QG_Q4_0 ? q4_scale(bits) : f16_bits_to_f32(bits);
     }
 
     // The MFMAs of one step (block index jL + s of every row of the unit)
@@ -216,11 +217,7 @@ struct MEngine {
                 uint4 av = xs[(bl * mp + min(tok, mp - 1)) * 4 + oct];
                 if (tok >= mp) av = make_uint4(0, 0, 0, 0);
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
-                f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
-                if (FMT == QG_Q4_0) {
-                    const bf16x8_t k136 = __builtin_bit_cast(bf16x8_t, make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));
-                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, k136, c, 0, 0, 0);    // -136 * sum(x), every row
-                }
+                const f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int G = 0; G < Sh::RG; ++G) {
                     const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[G], c, 0, 0, 0);

@@ -101,7 +101,7 @@ struct ItemWork {
 // other buffer before computing.  Returns true if nx's first batch is in B.
 template <typename E, int MS, typename XMap>
 __device__ __forceinline__ bool stream_item(const Geom &g, const ItemWork &w, const ItemWork &nx, int slot,
-                                            const uint4 *xs, const float *corr, float acc[MS], const XMap &xm,
+                                            const uint4 *xs, float acc[MS], const XMap &xm,
                                             typename E::Regs &A, typename E::Regs &B)
 {
     constexpr int U = E::U;
@@ -116,7 +116,7 @@ __device__ __forceinline__ bool stream_item(const Geom &g, const ItemWork &w, co
             E::load(g, more ? w.ct : nx.ct, more ? w.st : nx.st, lane, more ? w.jf + (b + 1) * U * w.KS : nx.jf, c,
                     w.KS, B);
         }
-        E::compute(g, A, min(w.nsteps - b * U, U), w.jf + b * U * w.KS, w.KS, slot, 0, xs, corr, acc, xm);
+        E::compute(g, A, min(w.nsteps - b * U, U), w.jf + b * U * w.KS, w.KS, slot, 0, xs, acc, xm);
         if (++b >= nb) return true;
         {
             const bool more = b + 1 < nb;
@@ -124,18 +124,17 @@ __device__ __forceinline__ bool stream_item(const Geom &g, const ItemWork &w, co
             E::load(g, more ? w.ct : nx.ct, more ? w.st : nx.st, lane, more ? w.jf + (b + 1) * U * w.KS : nx.jf, c,
                     w.KS, A);
         }
-        E::compute(g, B, min(w.nsteps - b * U, U), w.jf + b * U * w.KS, w.KS, slot, 0, xs, corr, acc, xm);
+        E::compute(g, B, min(w.nsteps - b * U, U), w.jf + b * U * w.KS, w.KS, slot, 0, xs, acc, xm);
         if (++b >= nb) return false;
     }
 }
 
-// Dynamic LDS: staged rows, Q4_0 corrections, then down-combine's split
-// partials or, with the gate, the per-slot row totals of the tile pairs.
+// Dynamic LDS: staged rows, then down-combine's split partials or, with the
+// gate, the per-slot row totals of the tile pairs.
 inline __host__ __device__ size_t moe_stream_lds(int fmt, bool dot, int nrows, int wblk, int mode, int glu_slots = 0,
                                                  int rows_per_tile = 0)
 {
     size_t b = (size_t)nrows * x_quads(fmt, dot) * wblk * 16;
-    if (x_aux(fmt)) b += (size_t)nrows * wblk * 4;
     if (mode == QG_MOE_DOWN_COMBINE) b += (size_t)WAVES * QG_MAX_M * 64 * 4;
     if (glu_slots) b += (size_t)WAVES * glu_slots * rows_per_tile * 4;
     return b;
@@ -158,8 +157,7 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
     const int nslots = a.m * a.top_k;
     const int nrows = MODE == QG_MOE_GATE_UP ? a.m : nslots;
     uint4 *xs = (uint4 *)smem;
-    float *corr = (float *)(smem + (size_t)nrows * QPB * g.wblk * 16);
-    float *red = corr + (x_aux(FMT) ? nrows * g.wblk : 0);
+    float *red = (float *)(smem + (size_t)nrows * QPB * g.wblk * 16);
     float *res = red;               // GLU: [2][PP][nslots][R] row totals (gate_up has no down partials)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int IS = a.isplit;
@@ -227,7 +225,6 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
     auto stage_unit = [&](int idx, const uint4 (&raw)[8]) {
         const int r = idx / g.wblk, bl = idx - r * g.wblk;
         uint4 q[8];
-        float av = 0.0f;
         if (bl < g.nb) {
             if constexpr (NORM) {
                 // x (exact in fp32) times gamma, in the fp32 form; x^2 summed per row
@@ -260,9 +257,9 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
                 }
 #pragma unroll
                 for (int t = 0; t < QG_MAX_M; ++t) ss[t] += t == r ? sq : 0.0f;
-                av = stage_block<FMT, false, false>(xf, q);
+                stage_block<false, false>(xf, q);
             } else {
-                av = stage_block<FMT, XBF16, DOT>(raw, q);
+                stage_block<XBF16, DOT>(raw, q);
             }
         } else {
 #pragma unroll
@@ -270,7 +267,6 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
         }
 #pragma unroll
         for (int i = 0; i < QPB; ++i) xs[(r * QPB + i) * g.wblk + bl] = q[i];
-        if (x_aux(FMT)) corr[r * g.wblk + bl] = av;
     };
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
@@ -311,8 +307,8 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
             } else {
                 nx.nsteps = 1;      // nothing follows: repeat this item's first step
             }
-            const bool flip = in_a ? stream_item<E, MS>(g, w, nx, slot, xs, corr, acc, sm, ra, rb)
-                                   : stream_item<E, MS>(g, w, nx, slot, xs, corr, acc, sm, rb, ra);
+            const bool flip = in_a ? stream_item<E, MS>(g, w, nx, slot, xs, acc, sm, ra, rb)
+                                   : stream_item<E, MS>(g, w, nx, slot, xs, acc, sm, rb, ra);
             if (flip) in_a = !in_a;
         }
         if (MODE == QG_MOE_GATE_UP) {

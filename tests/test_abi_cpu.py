@@ -95,15 +95,19 @@ def test_packed_record_placement(fmt):
         # the scale travels unchanged
         so = lo["scale_offset"] + t * lo["scale_tile_bytes"] + j * 64 * sb + lane * sb
         assert bytes(p[so:so + sb]) == bytes(c[row, blk, :sb])
-        # the code bytes are a permutation of the block's code nibbles/bytes
+        # the code bytes: Q8_0 as stored; the 4-bit formats with byte B holding
+        # elements 2B (low nibble) and 2B+1 (high nibble), Q4_0 nibbles as q ^ 8
         co = t * lo["code_tile_bytes"] + j * P * 1024 + lane * 16
         got = np.concatenate([p[co + h * 1024: co + h * 1024 + 16] for h in range(P)])
         body = c[row, blk, sb:]
         if fmt == q.Q8_0:
             assert np.array_equal(got, body)
         else:
-            nib = lambda a: sorted(list(a & 15) + list(a >> 4))
-            assert nib(got) == nib(body)
+            codes = np.concatenate([body & 15, body >> 4])          # element order
+            if fmt == q.Q4_0:
+                codes = codes ^ 8
+            want = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+            assert np.array_equal(got, want)
 
 
 def test_padding_bytes_are_zero():

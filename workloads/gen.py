@@ -82,6 +82,24 @@ def q4_0_blocks(n, k, rng_codes, rng_scales, d_lo=1e-3, d_hi=1e-2):
     return encode_q4_0(q, _fp16_bits_uniform(rng_scales, (n, nb), d_lo, d_hi))
 
 
+def q4_0_zero_heavy_blocks(n, k, rng_codes, rng_scales, d_lo=1e-3, d_hi=1e-2):
+    """Q4_0 rows dominated by code 8 (weight zero), with non-zero scales:
+    row r % 4 == 0 all code 8; 1 one code other than 8, anywhere in the row;
+    2 mostly 8 (each code drawn from 0..15 with probability 1/16); 3 uniform."""
+    nb = k // QK
+    q = np.full((n, nb, QK), 8, dtype=np.uint8)
+    kind = np.arange(n) % 4
+    others = np.array([c for c in range(16) if c != 8], dtype=np.uint8)
+    for r in np.nonzero(kind == 1)[0]:
+        pos = rng_codes.integers(0, nb * QK)
+        q[r].reshape(-1)[pos] = others[rng_codes.integers(0, len(others))]
+    few = (kind == 2)[:, None, None] & (rng_codes.random((n, nb, QK)) < 1.0 / 16)
+    q[few] = rng_codes.integers(0, 16, size=int(few.sum()), dtype=np.uint8)
+    full = kind == 3
+    q[full] = rng_codes.integers(0, 16, size=(int(full.sum()), nb, QK), dtype=np.uint8)
+    return encode_q4_0(q, _fp16_bits_uniform(rng_scales, (n, nb), d_lo, d_hi))
+
+
 def mxfp4_blocks(n, k, rng_codes, rng_scales, e_lo=-8, e_hi=-2):
     nb = k // QK
     c = rng_codes.integers(0, 16, size=(n, nb, QK), dtype=np.uint8)
@@ -114,6 +132,13 @@ def x_f32(shape, rng):
 
 def x_bf16_bits(shape, rng):
     return f32_to_bf16_bits_rne(x_f32(shape, rng))
+
+
+def x_mixed_f32(shape, rng, decades=3.0):
+    """N(0,1) times 10^U(-decades, decades): magnitudes spread over
+    2 * decades decades inside every block."""
+    x = rng.standard_normal(size=shape) * 10.0 ** rng.uniform(-decades, decades, size=shape)
+    return x.astype(np.float32)
 
 
 def norm_weight_f32(k, rng, lo=0.25, hi=2.0):
