@@ -31,6 +31,7 @@ import workloads as wl  # noqa: E402
 METRIC = "achieved HBM GB/s (% of peak) for M=1 quant GEMV; equiv. decode tok/s"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q8_0_sweep_m1_traffic.md")
+TRACE_FILE = os.path.join(ROOT, "profiles", "q8_0_sweep_m1_kernel_trace.md")
 
 
 def parse():
@@ -46,12 +47,12 @@ def parse():
     ap.add_argument("--no-events", action="store_true", help="skip the roofline / per-shape timing pass")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", choices=["c2", "c2f", "c0", "c1", "c3", "c4", "gemm"], default="c2",
+    ap.add_argument("--workload", choices=["c2", "c2f", "c0", "c1", "c3", "c4", "gemm", "stream"], default="c2",
                     help="c2: the full Q8_0 decode sweep (the headline line); c2f: the same sweep with the decode "
                          "step's neighbours fused in (RMSNorm, SwiGLU, residual; qgemv_fused) next to the plain "
                          "sweep; c0/c1/c3/c4: the other workloads, each timed over >= 1 GiB of distinct weight "
                          "copies so the device-side cache cannot serve repeated reads; gemm: qgemm on the c3 "
-                         "matrices at 16..128 tokens")
+                         "matrices at 16..128 tokens; stream: the read-only streaming ceiling over a 4 GiB buffer")
     ap.add_argument("--tokens", default="16,32,64,128",
                     help="gemm workload: the token counts to run (comma-separated, 1..128)")
     ap.add_argument("--quiet", action="store_true")
@@ -93,13 +94,13 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16
 
 def mfma_issued(fmt, n, k):
     """MFMA instructions one matrix-core launch issues: per 16-row unit and
-    step, one per (row group, block), plus one per block for Q4_0's offset."""
+    step, one per (row group, block)."""
     import block_quantized_weight_amd as q
     lo = q.layout(fmt, n, k)
     L, S, tiles = lo["lanes_per_row"], lo["steps"], lo["tiles"]
     tpw = L // 4 if L >= 8 else 1
     units = -(-tiles // tpw)
-    per_step = (L if L >= 4 else 4) + (L if fmt == q.Q4_0 else 0)
+    per_step = L if L >= 4 else 4
     return units * S * per_step
 
 
@@ -179,7 +180,7 @@ def run_other(args):
                      "weight_copies": reps}
             if issued_flop:
                 # matrix-core work of the set: algorithmic 2*m*n*k against the bf16 dense peak,
-                # and what the MFMAs issue (16 token rows per instruction, plus Q4_0's offset MFMA)
+                # and what the MFMAs issue (16 token rows per instruction)
                 extra["mfma"] = {"useful_tflops": round(useful_flop / us / 1e6, 2),
                                  "issued_tflops": round(issued_flop / us / 1e6, 2),
                                  "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
@@ -230,7 +231,25 @@ def run_other(args):
                            "frac": round(flop / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 5)},
                   "as_cobatches_of_8": {"us": round(us8, 3), "tokens_per_s": round(m * 1e6 / us8, 1)}})
 
-    if args.workload == "gemm":
+    if args.workload == "stream":
+        # the achievable read rate: every byte of a 4 GiB buffer (16x the device cache) read once per pass
+        nbytes = 4 << 30
+        buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        sink = torch.empty(q.STREAM_SINK, dtype=torch.int32, device=dev)
+        for _ in range(max(1, args.warmup)):
+            q.read_stream(buf, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, args.steps)
+        e0.record()
+        for _ in range(reps):
+            q.read_stream(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        emit("read-only stream, 4 GiB buffer, 16-byte nontemporal loads (qg_read_stream)", nbytes / us / 1e3, us,
+             {"bytes_per_pass": nbytes, "passes": reps})
+    elif args.workload == "gemm":
         gemm_case(3, [("qkv", 6144, 4096, 0), ("gate_up", 24576, 4096, 1), ("down", 4096, 12288, 2)],
                   [int(t) for t in args.tokens.split(",")],
                   "q4_0 qgemm, 8b-like: qkv 6144x4096 + gate_up 24576x4096 + down 4096x12288")
@@ -332,16 +351,29 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """Measured HBM bytes per launch for the current kernel sources, or None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def recorded_profile(path, key):
+    """A figure recorded in a committed rocprofv3 summary for the current
+    kernel sources (its source_digest line must match), or None."""
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m_src = re.search(r"source_digest:\s*([0-9a-f]+)", text)
-    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_val = re.search(key + r":\s*([0-9.eE+]+)", text)
     if not m_src or not m_val or m_src.group(1) != source_digest():
         return None
     return float(m_val.group(1))
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def run_fused_sweep(args, torch, q, dev, shapes, wviews, xs, ys, fmt, config):
@@ -560,6 +592,21 @@ def main():
     if chain is not None and q.chain_error() != 0:
         raise RuntimeError("a chain barrier timed out: the timed run is invalid")
 
+    # the same 145 launches issued one by one from the host (no graph), for comparison
+    eager_us = None
+    if args.mode != "eager" and not args.no_events:
+        for _ in range(2):
+            step_launches()
+        torch.cuda.synchronize()
+        reps = max(3, args.steps // 3)
+        e0.record(stream)
+        for _ in range(reps):
+            step_launches()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_us = e0.elapsed_time(e1) * 1e3 / reps
+        log(args, f"eager launches: {eager_us:.1f} us/step")
+
     # ---- roofline of the GEMV kernel.  Every launch of the step is the vector
     # GEMV (Q8_0, bf16 x, M=1: o in its one-batch form k_dense_one, the other
     # shapes in k_dense); its mean launch duration is the graph step time over
@@ -573,12 +620,24 @@ def main():
         mean_dur = ms_step * 1e-3 / len(shapes)
         mean_bytes = step_bytes / len(shapes)
         achieved = mean_bytes / mean_dur / 1e9
-        traffic = recorded_traffic()
+        traffic = recorded_profile(TRAFFIC_FILE, "hbm_bytes_per_launch")
+        trace_us = recorded_profile(TRACE_FILE, "mean_gemv_us")
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else round(traffic),
-                "kernel": "qg::k_dense / k_dense_one<Q8_0, bf16 x, M=1>",
-                "bytes_per_launch": round(mean_bytes), "mean_launch_us": round(mean_dur * 1e6, 3)}
+                "kernel": "qg::k_dense / k_dense_one<Q8_0, bf16 x, M=1>" if args.mode != "chain"
+                          else "qg::k_chain<Q8_0, bf16 x, M=1>",
+                "bytes_per_launch": round(mean_bytes), "mean_launch_us": round(mean_dur * 1e6, 3),
+                "basis": {
+                    "achieved": "algorithmic bytes per product / (timed region on the launch stream, HIP events, "
+                                "/ products per step); includes the gaps between graph nodes" if args.mode != "chain"
+                                else "algorithmic bytes per product / (timed region / products per step) of the "
+                                     "one persistent launch",
+                    "traffic": "rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, scaled by a device copy of known "
+                               "size, recorded in " + os.path.relpath(TRAFFIC_FILE, ROOT) +
+                               " for these kernel sources (null if the sources changed since)",
+                    "trace_mean_gemv_us": trace_us,
+                    "trace_source": os.path.relpath(TRACE_FILE, ROOT)}}
         groups = {}
         for i, (_, name, n, k) in enumerate(shapes):
             groups.setdefault(name.split(".")[-1], []).append(i)
@@ -590,7 +649,8 @@ def main():
             us = graph_time(torch, launches, 5) / len(idx)
             _, _, n, k = shapes[idx[0]]
             per_shape[key] = {"n": n, "k": k, "bytes": alg[idx[0]], "us": round(us, 3),
-                              "gbs": round(alg[idx[0]] / us / 1e3, 1)}
+                              "gbs": round(alg[idx[0]] / us / 1e3, 1), "launches": len(idx)}
+        roof["basis"]["per_shape_sum_us"] = round(sum(v["us"] * v["launches"] for v in per_shape.values()), 1)
         log(args, f"roofline {roof}; per shape {per_shape}")
 
     if args.calib_copy_mib:
@@ -621,10 +681,29 @@ def main():
             yg = ys[idx].cpu().numpy()
             yg = yg if rows is None else yg[:, rows]
             worst = max(worst, oracle.max_rel_err(yg, yref, l1))
-        cpu = {"value": round(bytes_cpu / t_cpu / 1e9, 4), "unit": "GB/s", "cores": oracle.threads(),
+        cores = oracle.threads()
+        # one core: the oracle on the Q8_0 2048x2048 (fp32 x) and Q4_0 2560x9728 (bf16 x) workloads
+        one = {}
+        oracle.set_threads(1)
+        try:
+            for name, cfg, f, n, k, xt in (("q8_0 2048x2048 fp32 x", 0, q.Q8_0, 2048, 2048, oracle.X_F32),
+                                           ("q4_0 2560x9728 bf16 x", 1, q.Q4_0, 2560, 9728, oracle.X_BF16)):
+                canon = wl.blocks_for(f, n, k, config=cfg, matrix=0 if cfg == 0 else 1)
+                rng = wl.rng_for(cfg, 0 if cfg == 0 else 1, "x")
+                xv = wl.x_f32((1, k), rng) if xt == oracle.X_F32 else wl.x_bf16_bits((1, k), rng)
+                t1 = time.perf_counter()
+                oracle.gemv(f, canon, n, k, xv, xt)
+                dt = time.perf_counter() - t1
+                b = n * (k // 32) * wl.BLOCK_BYTES[f] + k * (4 if xt == oracle.X_F32 else 2) + 4 * n
+                one[name] = {"s": round(dt, 4), "gbs": round(b / dt / 1e9, 4)}
+        finally:
+            oracle.set_threads(cores)
+        cpu = {"value": round(bytes_cpu / t_cpu / 1e9, 4), "unit": "GB/s", "cores": cores,
                "kind": "oracle",
                "sample": "layers 0-9 (qkv, o, gate_up, down) in full + every 9th LM-head row; "
                          f"{bytes_cpu / 1e6:.1f} MB of the sweep's algorithmic bytes, {t_cpu:.1f} s wall",
+               "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
+               "one_core": one,
                "gpu_vs_oracle_max_rel_err": worst}
         log(args, f"cpu oracle: {cpu}")
 
@@ -639,6 +718,7 @@ def main():
         "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "equiv_decode_tok_s": round(1e3 / ms_step, 1),
         "roofline": roof,
+        "eager_us_per_step": None if eager_us is None else round(eager_us, 1),
         "per_shape": per_shape or None,
         "cpu_baseline": cpu,
     }

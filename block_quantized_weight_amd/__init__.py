@@ -36,6 +36,7 @@ SIGNATURES = {
     "qg_unpack": (_i, [_i, _vp, _i64, _i64, _vp, _vp]),
     "qg_dequant_f32": (_i, [_i, _vp, _i64, _i64, _vp, _vp]),
     "qg_dense_path": (_i, [_i, _i64, _i64, _i, _i64]),
+    "qg_read_stream": (_i, [_vp, _i64, _vp, _vp]),
     "qgemv_q8_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_q4_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_mxfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
@@ -202,6 +203,20 @@ def dequant_f32(fmt, packed, n, k, out=None, stream=None):
     _check("qg_dequant_f32", lib().qg_dequant_f32(fmt, _dev_ptr(packed, "packed"), n, k, _dev_ptr(out, "out"),
                                                   _stream(stream)))
     return out
+
+
+STREAM_SINK = 16384
+
+
+def read_stream(buf, sink=None, stream=None):
+    """Reads every byte of the device tensor buf once (measurement aid: the
+    achievable HBM read rate); returns the sink (uint32 [STREAM_SINK])."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(STREAM_SINK, dtype=torch.int32, device=buf.device)
+    _check("qg_read_stream", lib().qg_read_stream(_dev_ptr(buf, "buf"), buf.numel() * buf.element_size(),
+                                                  _dev_ptr(sink, "sink"), _stream(stream)))
+    return sink
 
 
 _GEMV = {Q8_0: "qgemv_q8_0", Q4_0: "qgemv_q4_0", MXFP4: "qgemv_mxfp4"}

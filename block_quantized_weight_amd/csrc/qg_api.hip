@@ -71,6 +71,37 @@ __global__ void k_unpack(LayoutArgs a, const uint8_t *__restrict__ packed, uint8
         unpack_record(a, packed, canon, r);
 }
 
+// ------------------------------------------------------- streaming ceiling
+// Read-only probe of the device's achievable HBM read rate, the ceiling the
+// GEMV kernels are measured against (decode is bound by memory bandwidth:
+// imp README, "Known limitations").  Every 16-byte chunk of the buffer is
+// loaded once, nontemporally, with the GEMV's access shape (a wavefront load
+// instruction reads 1 KiB of consecutive bytes); each wave XOR-folds what it
+// read into one word of the sink so no load can be dropped.
+constexpr int STREAM_WGS = QG_STREAM_SINK / WAVES;   // one sink word per wave
+constexpr int STREAM_U = 4;                          // loads in flight per lane
+
+__global__ __launch_bounds__(TPB) void k_read_stream(const uint8_t *__restrict__ p, int64_t n16,
+                                                     uint32_t *__restrict__ sink)
+{
+    uint32_t acc = 0;
+    const int64_t nthr = (int64_t)gridDim.x * TPB;
+    int64_t i = (int64_t)blockIdx.x * TPB + threadIdx.x;
+    for (; i + (STREAM_U - 1) * nthr < n16; i += STREAM_U * nthr) {
+        uint4 v[STREAM_U];
+#pragma unroll
+        for (int u = 0; u < STREAM_U; ++u) v[u] = ld_stream16(p + (i + u * nthr) * 16);
+#pragma unroll
+        for (int u = 0; u < STREAM_U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += nthr) {
+        const uint4 v = ld_stream16(p + i * 16);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+    if ((threadIdx.x & 63) == 0) sink[blockIdx.x * WAVES + (threadIdx.x >> 6)] = acc;
+}
+
 // ----------------------------------------------------------------- router
 // Top-k routing on the device, one wavefront per token.  Each logit becomes a
 // 64-bit key: the float's bits in an order-preserving unsigned form (NaN taken
@@ -162,6 +193,12 @@ __global__ __launch_bounds__(64) void k_router(const float *__restrict__ logits,
 hipStream_t as_stream(void *s) { return (hipStream_t)s; }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Packed weights start on a 256-byte boundary, so every tile, every 1 KiB
+// wavefront load of codes and every expert (whose sizes are multiples of 256
+// bytes) starts on a whole cache line: a 16-byte-aligned base would split each
+// 1 KiB load over nine 128-byte lines instead of eight.
+constexpr uintptr_t W_ALIGN = 256;
 
 int check_shape(int fmt, int64_t n, int64_t k)
 {
@@ -330,7 +367,7 @@ int dense(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
     if (!w || !x || !y) return QG_EINVAL;
     if (xt != QG_F32 && xt != QG_BF16) return QG_EINVAL;
     if (m < 1 || m > QG_MAX_M) return QG_EINVAL;
-    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
+    if (!aligned(w, W_ALIGN) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
     const Layout lo = make_layout(fmt, n, k);
     if (mfma_fits(lo, xt, m)) {
         MPlan p = make_mplan(lo, (int)m);
@@ -365,14 +402,17 @@ int grid_for(int64_t items, int block)
     return (int)g;
 }
 
-// Chain plan of one link: the layout, KS for CWAVES waves sized from the
-// tiles each workgroup owns, one activation window (the whole x in LDS).
-int chain_link_plan(int fmt, int xt, int m, int P, const qg_chain_link_t &in, ChainLink *out, size_t *lds)
+// Chain plan of one link: the layout with one activation window over the
+// whole K, and the most tiles any of the P workgroups owns.  The LDS the link
+// needs (staged x, partial sums, finished rows) is returned in *xs, *part and
+// *out bytes.
+int chain_link_plan(int fmt, int xt, int m, int P, const qg_chain_link_t &in, ChainLink *out, size_t *xs,
+                    size_t *part, size_t *outb)
 {
     int st = check_shape(fmt, in.n, in.k);
     if (st) return st;
     if (!in.w_packed || !in.x || !in.y) return QG_EINVAL;
-    if (!aligned(in.w_packed, 16) || !aligned(in.x, 16) || !aligned(in.y, 4)) return QG_EALIGN;
+    if (!aligned(in.w_packed, W_ALIGN) || !aligned(in.x, 16) || !aligned(in.y, 4)) return QG_EALIGN;
     const Layout lo = make_layout(fmt, in.n, in.k);
     const bool dot = uses_dot(fmt, xt);
     Geom &g = out->g;
@@ -389,24 +429,22 @@ int chain_link_plan(int fmt, int xt, int m, int P, const qg_chain_link_t &in, Ch
     g.ctb = lo.ctb;
     g.stb = lo.stb;
     g.soff = lo.soff;
-    const int64_t tpw = (lo.tiles + P - 1) / P;               // tiles per workgroup (max)
-    int tp2 = 1;
-    while (tp2 < tpw && tp2 < CWAVES) tp2 <<= 1;
-    int KS = CWAVES / tp2;
-    while (KS > 1 && KS > lo.S) KS >>= 1;
-    g.KS = KS;
-    g.ksh = ilog2(KS);
-    g.tpi = CWAVES / KS;
+    g.KS = 1;
+    g.ksh = 0;
+    g.tpi = 1;
     g.ngroups = 0;
-    const int64_t sw = ((lo.S + KS - 1) / KS) * KS;
-    g.SW = (int32_t)sw;
+    g.SW = (int32_t)lo.S;
     g.nwin = 1;
-    g.wblk = (int32_t)(sw * lo.L);
-    const size_t b = chain_lds_bytes(m, dot, g.wblk, g.tpi * g.R);
-    if (b > 150 * 1024) return QG_EUNSUPPORTED;
-    *lds = b;
+    g.wblk = (int32_t)(lo.S * lo.L);
+    // items of a workgroup are counted in int: tiles * S per workgroup
+    const int64_t tmax = (lo.tiles + P - 1) / P;
+    if (tmax * lo.S > 0x3FFFFFFF) return QG_EUNSUPPORTED;
+    out->tmax = (int32_t)tmax;
     out->x = in.x;
     out->y = in.y;
+    *xs = chain_xs_bytes(m, dot, g.wblk);
+    *part = chain_part_bytes(m, (int)tmax);
+    *outb = chain_out_bytes(m, (int)tmax, lo.R);
     return QG_OK;
 }
 
@@ -496,7 +534,7 @@ int qg_pack(int fmt, const void *canon, int64_t n, int64_t k, void *packed, void
     int st = check_shape(fmt, n, k);
     if (st) return st;
     if (!canon || !packed) return QG_EINVAL;
-    if (!aligned(packed, 16)) return QG_EALIGN;
+    if (!aligned(packed, W_ALIGN)) return QG_EALIGN;
     const Layout lo = make_layout(fmt, n, k);
     const int64_t nrec = nrecords(lo);
     hipLaunchKernelGGL(k_pack, dim3(grid_for(nrec, 256)), dim3(256), 0, as_stream(stream), layout_args(lo),
@@ -509,7 +547,7 @@ int qg_unpack(int fmt, const void *packed, int64_t n, int64_t k, void *canon, vo
     int st = check_shape(fmt, n, k);
     if (st) return st;
     if (!canon || !packed) return QG_EINVAL;
-    if (!aligned(packed, 16)) return QG_EALIGN;
+    if (!aligned(packed, W_ALIGN)) return QG_EALIGN;
     const Layout lo = make_layout(fmt, n, k);
     const int64_t nrec = nrecords(lo);
     hipLaunchKernelGGL(k_unpack, dim3(grid_for(nrec, 256)), dim3(256), 0, as_stream(stream), layout_args(lo),
@@ -522,11 +560,20 @@ int qg_dequant_f32(int fmt, const void *w_packed, int64_t n, int64_t k, float *w
     int st = check_shape(fmt, n, k);
     if (st) return st;
     if (!w_packed || !w) return QG_EINVAL;
-    if (!aligned(w_packed, 16) || !aligned(w, 4)) return QG_EALIGN;
+    if (!aligned(w_packed, W_ALIGN) || !aligned(w, 4)) return QG_EALIGN;
     const Layout lo = make_layout(fmt, n, k);
     const int64_t nrec = nrecords(lo);
     hipLaunchKernelGGL(k_dequant, dim3(grid_for(nrec, 256)), dim3(256), 0, as_stream(stream), layout_args(lo),
                        (const uint8_t *)w_packed, w, k, nrec);
+    return launch_status();
+}
+
+int qg_read_stream(const void *buf, int64_t bytes, uint32_t *sink, void *stream)
+{
+    if (!buf || !sink || bytes <= 0 || (bytes % 16) != 0) return QG_EINVAL;
+    if (!aligned(buf, W_ALIGN) || !aligned(sink, 4)) return QG_EALIGN;
+    hipLaunchKernelGGL(k_read_stream, dim3(STREAM_WGS), dim3(TPB), 0, as_stream(stream), (const uint8_t *)buf,
+                       bytes / 16, sink);
     return launch_status();
 }
 
@@ -581,7 +628,7 @@ int qgemm(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
     if (!w || !x || !y) return QG_EINVAL;
     if (xt != QG_F32 && xt != QG_BF16) return QG_EINVAL;
     if (m < 1 || m > QG_MAX_GEMM_M) return QG_EINVAL;
-    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
+    if (!aligned(w, W_ALIGN) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
     const Layout lo = make_layout(fmt, n, k);
     if (gemm_fits(lo, xt)) {
         // one launch: grid.y = passes of TG token groups of 16, LDS planned for one pass
@@ -628,7 +675,7 @@ int qgemv_fused(int fmt, const void *w, int64_t n, int64_t k, const void *x, int
     if (m < 1 || m > QG_MAX_M) return QG_EINVAL;
     if (norm_weight && !(norm_eps >= 0.0f && norm_eps <= 3.4e38f)) return QG_EINVAL;    // rejects NaN too
     if (act == QG_ACT_SWIGLU && (n % 2) != 0) return QG_EINVAL;
-    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, yt == QG_F32 ? 4 : 2)) return QG_EALIGN;
+    if (!aligned(w, W_ALIGN) || !aligned(x, 16) || !aligned(y, yt == QG_F32 ? 4 : 2)) return QG_EALIGN;
     if ((norm_weight && !aligned(norm_weight, 16)) || (residual && !aligned(residual, 4))) return QG_EALIGN;
     const int64_t n_out = act == QG_ACT_SWIGLU ? n / 2 : n;
     if (residual && !(yt == QG_F32 && (const void *)residual == y) &&
@@ -696,7 +743,7 @@ static int moe_impl(int fmt, const void *w_experts, int64_t n_experts, int64_t n
     if (act == QG_ACT_SWIGLU && (n % 2) != 0) return QG_EINVAL;
     if (m < 1 || m > QG_MAX_M || n_experts < 1 || top_k < 1 || top_k > n_experts) return QG_EINVAL;
     if (m * top_k > 64 || n_experts > 65536) return QG_EUNSUPPORTED;
-    if (!aligned(w_experts, 16) || !aligned(x, 16) || !aligned(y, yt == QG_F32 ? 4 : 2) || !aligned(topk_ids, 4) ||
+    if (!aligned(w_experts, W_ALIGN) || !aligned(x, 16) || !aligned(y, yt == QG_F32 ? 4 : 2) || !aligned(topk_ids, 4) ||
         (topk_w && !aligned(topk_w, 4)) || (norm_weight && !aligned(norm_weight, 16)) ||
         (residual && !aligned(residual, 4)))
         return QG_EALIGN;
@@ -842,17 +889,30 @@ int qg_chain_plan(int fmt, int xt, int64_t m, const qg_chain_link_t *links, int6
     ChainHdr *h = (ChainHdr *)plan;
     ChainLink *L = (ChainLink *)((uint8_t *)plan + sizeof(ChainHdr) + 16);
     int P = cus < CHAIN_MAX_WG ? cus : CHAIN_MAX_WG;
-    size_t lds = 0;
+    size_t xs = 0, part = 0, outb = 0;
     for (int64_t i = 0; i < count; ++i) {
-        size_t b = 0;
-        int st = chain_link_plan(fmt, xt, (int)m, P, links[i], &L[i], &b);
+        size_t a = 0, b = 0, c = 0;
+        int st = chain_link_plan(fmt, xt, (int)m, P, links[i], &L[i], &a, &b, &c);
         if (st) return st;
-        if (b > lds) lds = b;
+        xs = a > xs ? a : xs;
+        part = b > part ? b : part;
+        outb = c > outb ? c : outb;
     }
+    // LDS: staged x of the widest link, then partial sums, then finished rows
+    const size_t lds = xs + part + outb;
+    if (lds > CHAIN_LDS_MAX) return QG_EUNSUPPORTED;
     const void *fn = chain_kernel(fmt, xt, (int)m);
     if (allow_lds(fn, lds) != hipSuccess) return QG_EHIP;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, CTPB, lds) != hipSuccess) return QG_EHIP;
     if (occ < 1) return QG_EUNSUPPORTED;
+    // The grid barriers need every workgroup resident at once.  A kernel that
+    // spills registers to scratch may have its waves held back until scratch
+    // memory is free (the runtime sizes scratch for fewer waves than a full
+    // device), which would leave the barrier waiting for workgroups that
+    // cannot start; such a variant is refused.
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, fn) != hipSuccess) return QG_EHIP;
+    if (fa.localSizeBytes > 0) return QG_EUNSUPPORTED;
     memset(h, 0, sizeof(*h));
     h->magic = CHAIN_MAGIC;
     h->fmt = fmt;
@@ -861,6 +921,8 @@ int qg_chain_plan(int fmt, int xt, int64_t m, const qg_chain_link_t *links, int6
     h->count = (int32_t)count;
     h->grid = P;
     h->lds = (int64_t)lds;
+    h->part_off = (int64_t)xs;
+    h->out_off = (int64_t)(xs + part);
     return QG_OK;
 }
 
@@ -874,7 +936,8 @@ int qgemv_chain(const void *plan_host, const void *plan_device, void *stream)
     int nlinks = h->count;
     const void *fn = chain_kernel(h->fmt, h->xt, h->m);
     if (allow_lds(fn, (size_t)h->lds) != hipSuccess) return QG_EHIP;
-    void *args[] = {(void *)&links, (void *)&nlinks};
+    int part_off = (int)h->part_off, out_off = (int)h->out_off;
+    void *args[] = {(void *)&links, (void *)&nlinks, (void *)&part_off, (void *)&out_off};
     hipError_t e = hipLaunchCooperativeKernel(fn, dim3(h->grid), dim3(CTPB), args, (unsigned)h->lds,
                                               as_stream(stream));
     return e == hipSuccess ? launch_status() : QG_EHIP;

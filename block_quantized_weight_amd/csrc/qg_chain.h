@@ -1,37 +1,50 @@
 // qg_chain.h -- a chain of dense GEMVs run by one persistent kernel.
 //
 // A decode step streams its weight matrices one after another, each product
-// depending on the previous one; with one kernel per product every matrix
-// pays a launch, a ramp-up and a drain of a few microseconds, which at
-// 1.4-7 us of traffic per matrix costs more than half the bandwidth.  Imparo
-// answers the same problem on Metal with one persistent dispatch per decode
-// layer and a grid barrier in place of each dispatch boundary (Imparo README,
+// depending on the previous one.  With one kernel per product every matrix
+// pays a launch, a ramp-up of its memory stream and a drain: at 1.4-7 us of
+// traffic per matrix that costs more than half the bandwidth.  Imparo answers
+// the same problem on Metal with one persistent dispatch per decode layer and
+// a grid barrier in place of each dispatch boundary (Imparo README,
 // "Megakernel Decode").  Here one cooperative kernel walks the whole chain,
-// one workgroup per compute unit:
+// one workgroup per compute unit, and the weight stream does not stop at the
+// barriers:
 //
-//  * every workgroup owns a balanced range of tiles of every link;
-//  * product i+1 starts on a workgroup only after all workgroups finished
-//    product i (grid barrier on per-workgroup epoch flags; each wait is
-//    bounded and records a timeout instead of hanging);
-//  * eight compute wavefronts only stream weights and compute.  Each keeps
-//    its next batch of weights in flight at all times, across passes and
-//    across link boundaries (weights do not depend on the barrier);
-//  * one control wavefront does everything that must wait on memory it
-//    wrote or read across the device: it polls the barrier, stages the
-//    activations into LDS, writes the outputs and publishes completion.  On
-//    gfx9 one counter tracks all of a wave's vector loads and stores in
-//    order, so these waits in a compute wave would also wait for the weight
-//    batches it has in flight.
+//  * Work split.  Workgroup g owns tiles [g T / P, (g+1) T / P) of a link
+//    (T tiles, P workgroups).  Its tiles' (tile, step) items, tile-major, are
+//    cut into CW equal contiguous ranges, one per compute wave, so every wave
+//    streams the same number of 16-byte records whatever the shape.  A wave
+//    keeps one partial sum per tile it touches and leaves it in LDS; after a
+//    workgroup barrier each tile's partials are added in wave order and across
+//    the tile's L lanes of a row (a fixed order: bitwise reproducible).
+//  * Weight prefetch.  A compute wave reads its items in batches of U, two
+//    batches in flight ahead of the arithmetic, across link boundaries: weights
+//    do not depend on the barrier, so while a workgroup waits for the others
+//    its next product's first batches are already on their way from HBM.
+//  * Barrier.  One control wave per workgroup writes the link's rows with
+//    device-scope stores, waits for them, publishes the workgroup's epoch flag,
+//    polls all workgroups' flags, and stages the next link's activations with
+//    device-scope loads.  Device scope (the sc1 cache policy) makes those
+//    accesses coherent across the MI355X's eight XCDs without writing back or
+//    invalidating a whole L2, which is what an agent-scope fence does.  The
+//    compute waves touch no barrier memory, so their waits on the memory
+//    counter never include a barrier round trip, and the control wave has no
+//    weight loads of its own to wait behind.
+//  * Every barrier wait is bounded by a wall-clock limit (the 100 MHz
+//    real-time counter): a wait that gives up records a timeout, and the
+//    workgroup's rows of the links it computes afterwards are written as NaN,
+//    so the kernel always finishes and a stale result cannot pass a check.
 #pragma once
 #include "qg_common.h"
 
 namespace qg {
 
-constexpr int CWAVES = 8;                 // compute wavefronts per workgroup
-constexpr int CTPB = 64 * (CWAVES + 1);   // + one control wavefront
-constexpr int CHAIN_MAX_WG = 1024;        // flag slots
-constexpr uint32_t CHAIN_MAGIC = 0x51474332u;
-constexpr long CHAIN_SPIN_LIMIT = 400000;
+constexpr int CW = 7;                      // compute wavefronts per workgroup
+constexpr int CTPB = 64 * (CW + 1);        // + one control wavefront
+constexpr int CHAIN_MAX_WG = 256;          // flag slots (workgroups of a chain launch at most)
+constexpr uint32_t CHAIN_MAGIC = 0x51474333u;
+constexpr uint64_t CHAIN_WAIT_TICKS = 2000000;   // 20 ms of the 100 MHz real-time counter
+constexpr size_t CHAIN_LDS_MAX = 150 * 1024;
 
 // Device-resident barrier state.  Flags only grow: a launch reads the epoch
 // base from qg_chain_gen, workgroup g publishes base + i + 1 after link i, and
@@ -56,113 +69,141 @@ inline int chain_error_read(bool clear)
     return (int)v;
 }
 
+// One link of the plan (device copy): the layout of its packed matrix (one
+// activation window over the whole K: g.wblk = S * L), its activations and
+// outputs, and the most tiles any workgroup owns.
 struct ChainLink {
-    Geom g;              // layout of the link; KS / tpi chosen for CWAVES waves
+    Geom g;
     const void *x;
     float *y;
+    int32_t tmax;
 };
 
+// LDS carve-up for M tokens: staged activations (the widest link's), the
+// compute waves' partial sums [tile][wave][token][lane], then the finished
+// rows [token][tmax * R].
 struct ChainHdr {
     uint32_t magic;
     int32_t fmt, xt, m, count, grid;
-    int64_t lds;
+    int64_t lds, part_off, out_off;
 };
 
-// Steps per weight batch.  Two batches stay live across a whole pass (one in
-// flight, one computing) beside the control wave's staging registers, so the
-// wider compute variants (fp32 activations, more than 4 tokens) take smaller
-// batches to stay within the 168 registers this launch shape allows without
-// spilling (Q4_0 with fp32 activations and one token spills even at 2).
-template <int FMT, bool XBF16, bool DOT, int M> struct ChainBatch {
-    static constexpr int U = !XBF16 && FMT == QG_Q4_0 && M == 1 ? 1
-                             : !XBF16 || (FMT == QG_Q8_0 && M > 4) ? 2
-                             : FMT == QG_Q8_0                      ? 4
-                             : DOT                                 ? (M > 4 ? 4 : 8)
-                                                                   : 4;
-};
+inline size_t chain_xs_bytes(int M, bool dot, int wblk) { return (size_t)M * (dot ? 4 : 8) * wblk * 16; }
+inline size_t chain_part_bytes(int M, int tmax) { return (size_t)tmax * CW * M * 64 * 4; }
+inline size_t chain_out_bytes(int M, int tmax, int R) { return (size_t)M * tmax * R * 4; }
 
-// LDS carve-up of one link: staged activations, split-K partials, and a
-// double-buffered block of finished rows for the control wave.
-template <int M, bool DOT>
-struct ChainLds {
-    uint4 *xs;
-    float *red, *out;
-    __device__ ChainLds(uint8_t *smem, const Geom &g)
-    {
-        constexpr int QPB = DOT ? 4 : 8;
-        xs = (uint4 *)smem;
-        red = (float *)(smem + (size_t)M * QPB * g.wblk * 16);
-        out = red + CWAVES * M * 64;
-    }
-};
+// Items per weight batch: 6 Q8_0 records (2 KiB each per wave) or 12 4-bit
+// ones (1 KiB), two batches in flight: 24 KiB per wave, 168 KiB per compute
+// unit, enough to cover a barrier and the staging after it at the per-unit
+// share of the HBM bandwidth.  4-bit co-batches of 4 or more tokens take 8
+// (their wider arithmetic would otherwise spill registers).
+template <int FMT, int M> struct ChainBatch { static constexpr int U = FMT == QG_Q8_0 ? 6 : M <= 3 ? 12 : 8; };
 
-inline size_t chain_lds_bytes(int M, bool dot, int wblk, int rows_per_pass)
+__device__ __forceinline__ void wg_tiles(int tiles, int grp, int P, int &t0, int &t1)
 {
-    const int QPB = dot ? 4 : 8;
-    return (size_t)M * QPB * wblk * 16 + (size_t)CWAVES * M * 64 * 4 + (size_t)2 * M * rows_per_pass * 4;
+    t0 = (int)((int64_t)grp * tiles / P);
+    t1 = (int)((int64_t)(grp + 1) * tiles / P);
+}
+
+// Items [lo, hi) of compute wave w among I items of its workgroup.
+__device__ __forceinline__ void wave_items(int I, int w, int &lo, int &hi)
+{
+    lo = (int)((int64_t)w * I / CW);
+    hi = (int)((int64_t)(w + 1) * I / CW);
+}
+
+// Device-scope (sc1) accesses: coherent across the XCDs without L2 fences.
+__device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_dev_f32(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_dev_u32(uint32_t *p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until every vector memory access this wave issued has completed
+// (loads returned, stores acknowledged at their scope).  The signal fences
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wait_vmem()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0), expcnt(7), lgkmcnt(15)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // ------------------------------------------------------------ control wave
-// Wait until every workgroup published at least `target`.
-__device__ __forceinline__ void chain_poll(uint32_t target)
+// Waits until every workgroup published at least `target`.  Returns false if
+// the wait gave up (the timeout is recorded in qg_chain_err).
+__device__ __forceinline__ bool chain_poll(uint32_t target)
 {
     const int lane = threadIdx.x & 63;
     const int P = gridDim.x;
-    long spins = 0;
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + CHAIN_WAIT_TICKS;
+    constexpr int NF = CHAIN_MAX_WG / 64;   // flags per lane, all loaded in one round trip
     while (true) {
+        uint32_t f[NF];
+#pragma unroll
+        for (int r = 0; r < NF; ++r) f[r] = lane + 64 * r < P ? ld_dev_u32(&qg_chain_flags[lane + 64 * r]) : target;
         bool ok = true;
-        for (int q = lane; q < P; q += 64) {
-            const uint32_t f = __hip_atomic_load(&qg_chain_flags[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ok = ok && (int32_t)(f - target) >= 0;
+#pragma unroll
+        for (int r = 0; r < NF; ++r) ok &= (int32_t)(f[r] - target) >= 0;
+        if (__all(ok)) return true;
+        if (__builtin_amdgcn_s_memrealtime() > t_end) {
+            if (lane == 0) st_dev_u32(&qg_chain_err, 1u);
+            return false;
         }
-        if (__all(ok)) break;
-        if (++spins > CHAIN_SPIN_LIMIT) {
-            if (lane == 0) __hip_atomic_store(&qg_chain_err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-__device__ __forceinline__ void chain_publish(uint32_t value)
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if ((threadIdx.x & 63) == 0)
-        __hip_atomic_store(&qg_chain_flags[blockIdx.x], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Stages x (M tokens) of one link into LDS with the 64 lanes of the control
-// wave; each lane issues the loads of CH blocks before writing any of them.
-template <int M, int FMT, bool XBF16, bool DOT>
+// Stages x (M tokens) of one link into LDS in the engine's form, with the 64
+// lanes of the control wave: each lane issues the device-scope loads of up to
+// CH blocks before writing any of them (one memory round trip per 64 * CH
+// blocks).
+template <int M, bool XBF16, bool DOT>
 __device__ __forceinline__ void chain_stage(const Geom &g, const void *x, uint4 *xs)
 {
     constexpr int QPB = DOT ? 4 : 8;
-    constexpr int CH = XBF16 ? 2 : 1;       // blocks per lane in flight (fp32 blocks are twice the registers)
-    constexpr int NLD = XBF16 ? 4 : 8;       // 16-byte loads per block
+    constexpr int NW = XBF16 ? 8 : 16;      // 8-byte loads per block
+    constexpr int CH = XBF16 ? 5 : 3;       // blocks per lane per round
     const int lane = threadIdx.x & 63;
     const int total = M * g.wblk;
     for (int base = 0; base < total; base += 64 * CH) {
-        uint4 raw[CH][NLD];
+        uint64_t raw[CH][NW];
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int idx = base + c * 64 + lane;
             const int t = idx / g.wblk, b = idx - t * g.wblk;
             const bool ok = idx < total && b < g.nb;
-            const uint8_t *src = (const uint8_t *)x +
-                                 ((int64_t)(ok ? t : 0) * g.k + (int64_t)(ok ? b : 0) * QK) * (XBF16 ? 2 : 4);
+            const uint64_t *src = (const uint64_t *)((const uint8_t *)x +
+                                                     ((int64_t)(ok ? t : 0) * g.k + (int64_t)(ok ? b : 0) * QK) *
+                                                         (XBF16 ? 2 : 4));
 #pragma unroll
-            for (int i = 0; i < NLD; ++i) raw[c][i] = ld_global16(src + 16 * i);
+            for (int i = 0; i < NW; ++i) raw[c][i] = ld_dev_u64(src + i);
         }
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int idx = base + c * 64 + lane;
             if (idx >= total) continue;
             const int t = idx / g.wblk, bl = idx - t * g.wblk;
-            const bool ok = bl < g.nb;
-            uint4 q[8];
-            stage_block<XBF16, DOT>(raw[c], q);
-            if (!ok) {
+            uint4 r8[8], q[8];
+#pragma unroll
+            for (int i = 0; i < NW / 2; ++i)
+                r8[i] = make_uint4((uint32_t)raw[c][2 * i], (uint32_t)(raw[c][2 * i] >> 32), (uint32_t)raw[c][2 * i + 1],
+                                   (uint32_t)(raw[c][2 * i + 1] >> 32));
+            stage_block<XBF16, DOT>(r8, q);
+            if (bl >= g.nb) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) q[i] = make_uint4(0, 0, 0, 0);
             }
@@ -173,182 +214,254 @@ __device__ __forceinline__ void chain_stage(const Geom &g, const void *x, uint4 
 }
 
 // ------------------------------------------------------------ compute waves
-// Work of a compute wave inside one pass of one link.
-struct PassWork {
-    const uint8_t *ct, *st;   // code / scale base of the wave's tile (a valid tile even when idle)
-    int jf, nsteps, tile, KS;
+// Position of a compute wave in its stream of items: link `li`, the next item
+// `q` of its range [q, qe) of that link, and that item's tile (local to the
+// workgroup) `tl` and step `j`.  Wave-uniform: kept in scalar registers.
+struct ChainCursor {
+    int li, q, qe, tl, j;
 };
 
-__device__ __forceinline__ void wg_tiles(const Geom &g, int grp, int P, int64_t &t0, int64_t &t1)
-{
-    t0 = (int64_t)grp * g.tiles / P;
-    t1 = (int64_t)(grp + 1) * g.tiles / P;
-}
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-__device__ __forceinline__ PassWork pass_work(const Geom &g, int64_t t0, int64_t t1, int p)
+// The cursor at the first item, at or after link `li`, of a link in which
+// this wave has items (li = nlinks at the end).
+__device__ __forceinline__ ChainCursor cursor_at(const ChainLink *links, int nlinks, int grp, int P, int w, int li)
 {
-    const int wave = threadIdx.x >> 6;
-    const int tsub = wave >> g.ksh, kpart = wave & (g.KS - 1);
-    PassWork w;
-    const int64_t tile = t0 + (int64_t)p * g.tpi + tsub;
-    const bool active = tile < t1;
-    const int64_t tl = active ? tile : (t0 < g.tiles ? t0 : 0);
-    w.tile = (int)tile;
-    w.ct = g.w + tl * g.ctb;
-    w.st = g.w + g.soff + tl * g.stb;
-    w.jf = kpart;
-    w.KS = g.KS;
-    w.nsteps = (active && kpart < g.S) ? (g.S - kpart + g.KS - 1) / g.KS : 0;
-    return w;
-}
-
-// The first pass after (i, p) in which this wave has work; false at the end.
-__device__ __forceinline__ bool next_work(const ChainLink *links, int nlinks, int grp, int P, int i, int p,
-                                          PassWork &out)
-{
-    while (true) {
-        Geom g = links[i].g;
-        int64_t t0, t1;
-        wg_tiles(g, grp, P, t0, t1);
-        const int npass = (int)((t1 - t0 + g.tpi - 1) / g.tpi);
-        if (++p >= npass) {
-            if (++i >= nlinks) return false;
-            p = -1;
-            continue;
+    ChainCursor c{nlinks, 0, 0, 0, 0};
+    for (; li < nlinks; ++li) {
+        const int tiles = links[li].g.tiles, S = links[li].g.S;
+        int t0, t1, lo, hi;
+        wg_tiles(tiles, grp, P, t0, t1);
+        wave_items((t1 - t0) * S, w, lo, hi);
+        if (lo < hi) {
+            c.li = li;
+            c.q = lo;
+            c.qe = hi;
+            c.tl = lo / S;
+            c.j = lo - c.tl * S;
+            break;
         }
-        out = pass_work(g, t0, t1, p);
-        if (out.nsteps > 0) return true;
     }
+    c.li = uni(c.li);
+    c.q = uni(c.q);
+    c.qe = uni(c.qe);
+    c.tl = uni(c.tl);
+    c.j = uni(c.j);
+    return c;
 }
 
-// Streams the wave's batches of one pass: `A` holds the first batch (already
-// in flight); each step loads the following batch -- or the first batch of
-// the wave's next working pass (`nx`) -- into the other buffer before
-// computing.  Returns true if the next pass's first batch ended up in `B`.
-template <typename E, int M>
-__device__ __forceinline__ bool chain_pass_loop(const Geom &g, const PassWork &w, const PassWork &nx, int slot,
-                                                const uint4 *xs, float acc[M],
-                                                typename E::Regs &A, typename E::Regs &B)
+// A batch of up to U items of one link, in registers.
+template <int FMT, int U>
+struct ChainRegs {
+    static constexpr int P = FMT == QG_Q8_0 ? 2 : 1;
+    uint4 c[U][P];
+    uint32_t s[U];
+    int li, cnt, tl0, j0;          // link, items, first item's local tile and step
+};
+
+// Issues the loads of the next batch at the cursor and returns the cursor
+// after it.  Every call issues U items' worth of loads (items past the batch
+// repeat its last one, a cache hit), so the compiler's memory-counter waits
+// stay exact; past the end of the stream it re-reads a valid record that is
+// never used.  Addresses are a scalar base per item plus the lane's offset.
+template <int FMT, int U>
+__device__ __forceinline__ ChainCursor chain_issue(const ChainLink *links, int nlinks, int grp, int P, int w,
+                                                   const ChainCursor c, ChainRegs<FMT, U> &b)
 {
-    constexpr int U = E::U;
-    const int nb = (w.nsteps + U - 1) / U;
-    const int ncnt = max(1, min(nx.nsteps, U));
-    int b = 0;
-    while (true) {
-        {
-            const bool more = b + 1 < nb;
-            const int c = more ? min(w.nsteps - (b + 1) * U, U) : ncnt;
-            E::load(g, more ? w.ct : nx.ct, more ? w.st : nx.st, threadIdx.x & 63,
-                    more ? w.jf + (b + 1) * U * w.KS : nx.jf, c, more ? w.KS : nx.KS, B);
+    constexpr int PP = ChainRegs<FMT, U>::P;
+    constexpr int SB = FMT == QG_MXFP4 ? 1 : 2;
+    const int lane = threadIdx.x & 63;
+    const bool live = c.li < nlinks;
+    const Geom &g = links[live ? c.li : nlinks - 1].g;
+    const int S = g.S;
+    int t0, t1;
+    wg_tiles(g.tiles, grp, P, t0, t1);
+    const int cnt = live ? min(U, c.qe - c.q) : 0;
+    b.li = c.li;
+    b.cnt = cnt;
+    b.tl0 = c.tl;
+    b.j0 = c.j;
+    int tl = c.tl, j = c.j;
+    const uint32_t coff = (uint32_t)lane * 16, soff = (uint32_t)lane * SB;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int tile = live ? t0 + tl : 0;
+        const int jj = live ? j : 0;
+        const uint8_t *cb = g.w + (int64_t)tile * g.ctb + (int64_t)jj * (PP * 1024);
+        const uint8_t *sb = g.w + g.soff + (int64_t)tile * g.stb + (int64_t)jj * 64 * SB;
+#pragma unroll
+        for (int h = 0; h < PP; ++h) b.c[u][h] = ld_stream16(cb + h * 1024 + coff);
+        if (FMT == QG_MXFP4)
+            b.s[u] = ld_stream_u8(sb + soff);
+        else
+            b.s[u] = ld_stream_u16((const uint16_t *)(sb + soff));
+        if (u + 1 < cnt && ++j == S) {       // position of the batch's next item
+            j = 0;
+            ++tl;
         }
-        E::compute(g, A, min(w.nsteps - b * U, U), w.jf + b * U * w.KS, w.KS, slot, 0, xs, acc);
-        if (++b >= nb) return true;
-        {
-            const bool more = b + 1 < nb;
-            const int c = more ? min(w.nsteps - (b + 1) * U, U) : ncnt;
-            E::load(g, more ? w.ct : nx.ct, more ? w.st : nx.st, threadIdx.x & 63,
-                    more ? w.jf + (b + 1) * U * w.KS : nx.jf, c, more ? w.KS : nx.KS, A);
+    }
+    if (!live) return c;
+    if (c.q + cnt >= c.qe) return cursor_at(links, nlinks, grp, P, w, c.li + 1);
+    if (++j == S) {                          // the item after the batch's last one
+        j = 0;
+        ++tl;
+    }
+    return ChainCursor{c.li, uni(c.q + cnt), c.qe, uni(tl), uni(j)};
+}
+
+// This wave's partial sums: the tile being summed (-1: none) and its values.
+template <int M>
+struct ChainAcc {
+    int tl;
+    float a[M];
+};
+
+template <int M>
+__device__ __forceinline__ void acc_flush(ChainAcc<M> &acc, float *part, int w)
+{
+    const int lane = threadIdx.x & 63;
+    if (acc.tl >= 0) {
+#pragma unroll
+        for (int t = 0; t < M; ++t) part[((acc.tl * CW + w) * M + t) * 64 + lane] = acc.a[t];
+    }
+#pragma unroll
+    for (int t = 0; t < M; ++t) acc.a[t] = 0.0f;
+}
+
+// Adds the batch's items (all of one link) into the accumulators, flushing a
+// tile's partials to LDS when an item starts another tile.
+template <int FMT, bool XBF16, bool DOT, int M, int U>
+__device__ __forceinline__ void chain_compute(const Geom &g, const ChainRegs<FMT, U> &b, const uint4 *xs,
+                                              float *part, int w, ChainAcc<M> &acc)
+{
+    using E = Engine<FMT, XBF16, DOT, M, U>;
+    const int slot = (threadIdx.x & 63) & (g.L - 1);
+    int tl = b.tl0, j = b.j0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (u < b.cnt) {
+            if (tl != acc.tl) {
+                acc_flush<M>(acc, part, w);
+                acc.tl = tl;
+            }
+            E::step(g, b.c[u], b.s[u], xs, j * g.L + slot, acc.a);
+            // one item at a time: the scheduler may not hoist the next item's
+            // activation reads (32 registers each) above this one's arithmetic
+            __builtin_amdgcn_sched_barrier(0);
+            if (++j == g.S) {
+                j = 0;
+                ++tl;
+            }
         }
-        E::compute(g, B, min(w.nsteps - b * U, U), w.jf + b * U * w.KS, w.KS, slot, 0, xs, acc);
-        if (++b >= nb) return false;
     }
 }
 
 template <int FMT, bool XBF16, bool DOT, int M>
-__global__ __launch_bounds__(CTPB) void k_chain(const ChainLink *__restrict__ links, int nlinks)
+__global__ __launch_bounds__(CTPB) void k_chain(const ChainLink *__restrict__ links, int nlinks, int part_off,
+                                                int out_off)
 {
-    using E = Engine<FMT, XBF16, DOT, M, ChainBatch<FMT, XBF16, DOT, M>::U>;
-    using LdsT = ChainLds<M, DOT>;
+    constexpr int U = ChainBatch<FMT, M>::U;
+    using BR = ChainRegs<FMT, U>;
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ uint32_t s_base;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const bool control = wave == CWAVES;
+    // the wave index is uniform over the wave: keep it (and the whole item
+    // cursor derived from it) in scalar registers
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int P = gridDim.x, grp = blockIdx.x;
-    if (threadIdx.x == 0) s_base = __hip_atomic_load(&qg_chain_gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint4 *xs = (uint4 *)smem;
+    float *part = (float *)(smem + part_off);
+    float *out = (float *)(smem + out_off);
+    if (threadIdx.x == 0) s_base = ld_dev_u32(&qg_chain_gen);
     __syncthreads();
     const uint32_t base = s_base;
 
-    typename E::Regs ra, rb;
-    bool phase = false;             // false: the next working pass's first batch is in ra
-    if (!control) {
-        PassWork first;
-        if (next_work(links, nlinks, grp, P, 0, -1, first))
-            E::load(links[0].g, first.ct, first.st, lane, first.jf, max(1, min(first.nsteps, E::U)), first.KS, ra);
+    if (wave == CW) {
+        // ---------------------------------------------------- control wave
+        chain_stage<M, XBF16, DOT>(links[0].g, links[0].x, xs);
+        bool stale = false;                  // a barrier wait gave up: rows from here on are NaN
+        for (int i = 0; i < nlinks; ++i) {
+            const Geom &g = links[i].g;
+            const int ostride = links[i].tmax * g.R;
+            __syncthreads();                 // #1 activations of link i staged
+            __syncthreads();                 // #2 partial sums in LDS
+            __syncthreads();                 // #3 finished rows in LDS
+            int t0, t1;
+            wg_tiles(g.tiles, grp, P, t0, t1);
+            const int r0 = t0 * g.R, nr = min(t1 * g.R, g.n) - r0;
+            for (int idx = lane; idx < M * nr; idx += 64) {
+                const int t = idx / nr, r = idx - t * nr;
+                st_dev_f32(links[i].y + (int64_t)t * g.n + r0 + r, stale ? __builtin_nanf("") : out[t * ostride + r]);
+            }
+            wait_vmem();                     // this workgroup's rows of link i are visible device-wide
+            if (lane == 0) st_dev_u32(&qg_chain_flags[grp], base + (uint32_t)i + 1);
+            if (i + 1 < nlinks) {
+                if (!chain_poll(base + (uint32_t)i + 1)) stale = true;    // link i complete everywhere
+                chain_stage<M, XBF16, DOT>(links[i + 1].g, links[i + 1].x, xs);
+            }
+        }
+        if (grp == 0) {
+            chain_poll(base + (uint32_t)nlinks);
+            if (lane == 0) st_dev_u32(&qg_chain_gen, base + (uint32_t)nlinks);
+        }
+        return;
     }
 
+    // -------------------------------------------------------- compute waves
+    ChainCursor cur = cursor_at(links, nlinks, grp, P, wave, 0);
+    BR ra, rb;
+    cur = chain_issue<FMT, U>(links, nlinks, grp, P, wave, cur, ra);
+    cur = chain_issue<FMT, U>(links, nlinks, grp, P, wave, cur, rb);
+    bool a_first = true;                     // the older batch in flight is ra
     for (int i = 0; i < nlinks; ++i) {
-        const Geom g = links[i].g;
-        int64_t t0, t1;
-        wg_tiles(g, grp, P, t0, t1);
-        const int npass = (int)((t1 - t0 + g.tpi - 1) / g.tpi);
-        const int rows_pp = g.tpi * g.R;
-        LdsT lds(smem, g);
-
-        if (control) {
-            if (i > 0) chain_poll(base + (uint32_t)i);   // product i-1 complete everywhere
-            chain_stage<M, FMT, XBF16, DOT>(g, links[i].x, lds.xs);
+        const Geom &g = links[i].g;
+        ChainAcc<M> acc;
+        acc.tl = -1;
+#pragma unroll
+        for (int t = 0; t < M; ++t) acc.a[t] = 0.0f;
+        __syncthreads();                     // #1 activations of link i staged
+        // this wave's batches of link i, oldest first; a computed buffer is
+        // refilled with the next batch of the stream before the other is used
+        while (true) {
+            if (a_first) {
+                if (ra.li != i) break;
+                chain_compute<FMT, XBF16, DOT, M, U>(g, ra, xs, part, wave, acc);
+                cur = chain_issue<FMT, U>(links, nlinks, grp, P, wave, cur, ra);
+            } else {
+                if (rb.li != i) break;
+                chain_compute<FMT, XBF16, DOT, M, U>(g, rb, xs, part, wave, acc);
+                cur = chain_issue<FMT, U>(links, nlinks, grp, P, wave, cur, rb);
+            }
+            a_first = !a_first;
         }
-        __syncthreads();                                   // activations of link i staged
-
-        const int tsub = wave >> g.ksh, kpart = wave & (g.KS - 1);
-        const int rsub = lane >> g.lsh, slot = lane & (g.L - 1);
-        for (int p = 0; p < npass; ++p) {
-            float *outp = lds.out + (p & 1) * M * rows_pp;
-            float acc[M];
+        acc_flush<M>(acc, part, wave);
+        __syncthreads();                     // #2 partial sums in LDS
+        // each local tile: the partials of the waves that touched it, in wave
+        // order, then the L lanes of each row
+        int t0, t1;
+        wg_tiles(g.tiles, grp, P, t0, t1);
+        const int nt = t1 - t0, I = nt * g.S, ostride = links[i].tmax * g.R;
+        for (int tl = wave; tl < nt; tl += CW) {
+            float v[M];
 #pragma unroll
-            for (int t = 0; t < M; ++t) acc[t] = 0.0f;
-            if (!control) {
-                const PassWork w = pass_work(g, t0, t1, p);
-                if (w.nsteps > 0) {
-                    PassWork nx;
-                    if (!next_work(links, nlinks, grp, P, i, p, nx)) {
-                        nx = w;             // nothing left: repeat this pass's first step
-                        nx.nsteps = 1;
-                    }
-                    const bool flip = phase ? chain_pass_loop<E, M>(g, w, nx, slot, lds.xs, acc, rb, ra)
-                                            : chain_pass_loop<E, M>(g, w, nx, slot, lds.xs, acc, ra, rb);
-                    if (flip) phase = !phase;
-                }
-                if (g.KS > 1) {
+            for (int t = 0; t < M; ++t) v[t] = 0.0f;
+            for (int w = 0; w < CW; ++w) {
+                int lo, hi;
+                wave_items(I, w, lo, hi);
+                if (lo < hi && lo < (tl + 1) * g.S && hi > tl * g.S) {      // wave w touched tile tl
 #pragma unroll
-                    for (int t = 0; t < M; ++t) lds.red[(wave * M + t) * 64 + lane] = acc[t];
+                    for (int t = 0; t < M; ++t) v[t] += part[((tl * CW + w) * M + t) * 64 + lane];
                 }
             }
-            if (g.KS > 1) __syncthreads();                // split-K partials in LDS
-            if (!control) {
-                if (g.KS > 1 && kpart == 0) {
-                    for (int qq = 1; qq < g.KS; ++qq)
+            for (int off = 1; off < g.L; off <<= 1) {
 #pragma unroll
-                        for (int t = 0; t < M; ++t) acc[t] += lds.red[((wave + qq) * M + t) * 64 + lane];
-                }
-                for (int off = 1; off < g.L; off <<= 1) {
-#pragma unroll
-                    for (int t = 0; t < M; ++t) acc[t] += __shfl_xor(acc[t], off, 64);
-                }
-                if (kpart == 0) {
-#pragma unroll
-                    for (int t = 0; t < M; ++t)
-                        if ((t & (g.L - 1)) == slot) outp[t * rows_pp + tsub * g.R + rsub] = acc[t];
-                }
+                for (int t = 0; t < M; ++t) v[t] += __shfl_xor(v[t], off, 64);
             }
-            __syncthreads();                               // rows of pass p in LDS
-            if (control) {
-                const int64_t row0 = (t0 + (int64_t)p * g.tpi) * g.R;
-                const int64_t rend = t1 * g.R < g.n ? t1 * g.R : g.n;
-                for (int idx = lane; idx < M * rows_pp; idx += 64) {
-                    const int t = idx / rows_pp, rl = idx - t * rows_pp;
-                    const int64_t row = row0 + rl;
-                    if (row < rend) st_global_f32(links[i].y + (int64_t)t * g.n + row, outp[idx]);
-                }
+            if ((lane & (g.L - 1)) == 0) {
+#pragma unroll
+                for (int t = 0; t < M; ++t) out[t * ostride + tl * g.R + (lane >> g.lsh)] = v[t];
             }
         }
-        if (control) chain_publish(base + (uint32_t)i + 1);
-    }
-    // final barrier, then workgroup 0 moves the epoch base for the next launch
-    if (control && grp == 0) {
-        chain_poll(base + (uint32_t)nlinks);
-        if (lane == 0)
-            __hip_atomic_store(&qg_chain_gen, base + (uint32_t)nlinks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();                     // #3 finished rows in LDS
     }
 }
 

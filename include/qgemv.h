@@ -32,7 +32,14 @@
  * R = 64/L rows, each wavefront load instruction reads 1 KiB of codes that is
  * contiguous in memory; scales are a separate stream.  The layout depends only
  * on (fmt, n, k); qg_layout reports it, qg_packed_bytes its size.  Packing is
- * bit-exact: qg_unpack(qg_pack(B)) == B byte for byte.
+ * bit-exact: qg_unpack(qg_pack(B)) == B byte for byte.  Keeping a private
+ * kernel layout beside the canonical file format follows Imparo, which
+ * converts its GateUp weights into a layout of its own at load time (Imparo
+ * README, opening release notes); the canonical blocks stay the interchange
+ * form, as GGUF is for both engines (imp README, "What is imp").
+ * Packed weight pointers (w_packed, w_experts, qg_pack's output, qg_unpack's
+ * input) must be 256-byte aligned: every 1 KiB load then covers whole cache
+ * lines.
  *
  * Conventions for every entry point below:
  *  - Pointers named as device memory are device memory owned by the caller
@@ -113,39 +120,49 @@ typedef struct {
 /* Human-readable name of a status code (static string). */
 const char *qg_status_str(int status);
 
-/* Size in bytes of the packed form of an n x k matrix, or -1 if (fmt, n, k) is invalid. */
+/* Size in bytes of the packed form of an n x k matrix (a multiple of 256), or
+ * -1 if (fmt, n, k) is invalid.  Part of the load-time layout described above
+ * (Imparo README, opening release notes: a private weight layout made at load). */
 int64_t qg_packed_bytes(int fmt, int64_t n, int64_t k);
 
-/* Fills *out with the packed layout of an n x k matrix.  out: host memory. */
+/* Fills *out with the packed layout of an n x k matrix.  out: host memory.
+ * Returns QG_EINVAL (null out, bad shape) or QG_EUNSUPPORTED (n or k above
+ * 2^31 - 1); nothing is written then. */
 int qg_layout(int fmt, int64_t n, int64_t k, qg_layout_t *out);
 
 /*
- * Canonical -> packed (and back) on the host.  canon: host memory,
- * n * (k/32) canonical blocks.  packed: host memory, qg_packed_bytes bytes;
- * every padding byte of the packed form is written as zero.
+ * Canonical -> packed (and back) on the host: the load-time conversion into
+ * the kernels' private layout (Imparo README, opening release notes).
+ * canon: host memory, n * (k/32) canonical blocks.  packed: host memory,
+ * qg_packed_bytes bytes; every padding byte of the packed form is written as
+ * zero.  Unpacking restores the canonical bytes exactly.  Synchronous; status
+ * QG_EINVAL for null pointers or a bad shape.
  */
 int qg_pack_host(int fmt, const void *canon, int64_t n, int64_t k, void *packed);
 int qg_unpack_host(int fmt, const void *packed, int64_t n, int64_t k, void *canon);
 
 /*
- * The same transforms on the device.  canon, packed: device memory; packed
- * must be 16-byte aligned (256 recommended).  Bit-identical to the host
- * versions.
+ * The same transforms on the device, enqueued on `stream`.  canon, packed:
+ * device memory owned by the caller; packed must be 256-byte aligned
+ * (QG_EALIGN otherwise).  Bit-identical to the host versions.
  */
 int qg_pack(int fmt, const void *canon, int64_t n, int64_t k, void *packed, void *stream);
 int qg_unpack(int fmt, const void *packed, int64_t n, int64_t k, void *canon, void *stream);
 
 /*
- * Test aid: decodes a packed matrix to fp32 w[n][k] (device memory, row-major)
- * through the same unpack steps the GEMV kernels use.  Every decoded weight
- * is exact in fp32 when it is finite, so the result is comparable bit for bit.
+ * Test aid: decodes a packed matrix to fp32 w[n][k] (device memory, row-major,
+ * 4-byte aligned) through the same unpack steps the GEMV kernels use, so the
+ * block definitions above (the Q8_0 / Q4_0 rows of the imp README "Features"
+ * table and the MXFP4 format of the imp release notes v0.6) can be checked
+ * weight by weight.  Every decoded weight is exact in fp32 when it is finite,
+ * so the result is comparable bit for bit.  w_packed: 256-byte aligned.
  */
 int qg_dequant_f32(int fmt, const void *w_packed, int64_t n, int64_t k, float *w, void *stream);
 
 /*
  * Dense product for a co-batch of m tokens (1 <= m <= 8):
  *     y[t][i] = sum_c W[i][c] * x[t][c]        t < m, i < n
- * w_packed: device, packed layout of (fmt, n, k), 16-byte aligned (256 recommended).
+ * w_packed: device, packed layout of (fmt, n, k), 256-byte aligned.
  * x: device, [m][k] row-major, fp32 or bf16 (xt), 16-byte aligned.
  * y: device, fp32 [m][n] row-major, 4-byte aligned, overwritten.
  * Accumulation is fp32; x is used exactly (bf16 -> fp32 is exact).
@@ -164,6 +181,19 @@ int qgemv_q4_0(const void *w_packed, int64_t n, int64_t k, const void *x, int xt
                float *y, void *stream);
 int qgemv_mxfp4(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
                 float *y, void *stream);
+
+/*
+ * Measurement aid: reads every byte of buf once (16-byte nontemporal loads,
+ * 1 KiB per wavefront load instruction, the GEMV kernels' access shape) and
+ * XOR-folds it into sink, one word per wavefront.  Timing it over a buffer
+ * far larger than the device caches gives the achievable HBM read rate that
+ * the products' bandwidth is compared with (decode is bound by memory
+ * bandwidth: imp README, "Known limitations").  buf: device, 256-byte
+ * aligned, bytes a positive multiple of 16.  sink: device uint32
+ * [QG_STREAM_SINK], overwritten.
+ */
+#define QG_STREAM_SINK 16384
+int qg_read_stream(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
 
 /*
  * Which kernel family a dense call with these arguments runs: QG_PATH_VALU,
@@ -219,7 +249,7 @@ int qgemv_fused(int fmt, const void *w_packed, int64_t n, int64_t k, const void 
 /*
  * Top-k expert product.  w_experts: device, n_experts packed matrices of
  * identical shape (fmt, n, k) back to back, expert e at byte offset
- * e * qg_packed_bytes(fmt, n, k) (a multiple of 256); 16-byte aligned.
+ * e * qg_packed_bytes(fmt, n, k) (a multiple of 256); 256-byte aligned.
  * topk_ids: device int32 [m][top_k]; topk_w: device fp32 [m][top_k].
  * Ids should be distinct within a token (repeated ids still follow the
  * formulas below); an id outside [0, n_experts) contributes nothing.
@@ -295,8 +325,12 @@ int moe_router_topk(const float *logits, int64_t m, int64_t n_experts, int64_t t
  * compute unit and is launched cooperatively.  Barrier state lives in static
  * device memory: chains launched concurrently on one device (different
  * streams) race and must not overlap.  A barrier that waits too long ends its
- * wait and records a timeout, so the kernel always finishes; qg_chain_error
- * reports it.
+ * wait and records a timeout, so the kernel always finishes; the rows a
+ * workgroup computes after such a wait are written as NaN (their activations
+ * may be stale), and qg_chain_error reports it.  qg_chain_plan refuses
+ * (QG_EUNSUPPORTED) a kernel variant that would need scratch memory: the
+ * runtime may hold back waves that need scratch, so not every workgroup could
+ * be resident for the barriers.
  */
 typedef struct {
     const void *w_packed;   /* device, packed (fmt, n, k) */

@@ -47,6 +47,7 @@ def lib():
         i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
         for name, rt, args in [
             ("orc_threads", ctypes.c_int, []),
+            ("orc_set_threads", None, [ctypes.c_int]),
             ("orc_fp16", ctypes.c_double, [ctypes.c_uint16]),
             ("orc_bf16", ctypes.c_double, [ctypes.c_uint16]),
             ("orc_e8m0", ctypes.c_double, [ctypes.c_uint8]),
@@ -70,6 +71,12 @@ def _ptr(a):
 def threads():
     """OpenMP threads the oracle's parallel loops use."""
     return lib().orc_threads()
+
+
+def set_threads(n):
+    """Threads for the oracle's parallel loops (for timing; results do not
+    depend on it: each row is summed by one thread, in index order)."""
+    lib().orc_set_threads(int(n))
 
 
 def fp16(h):

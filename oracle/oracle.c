@@ -45,6 +45,17 @@ int orc_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the threads of the oracle's parallel loops (timing legs only: results
+ * do not depend on it, every row is summed by one thread in index order). */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
 enum { ORC_X_F32 = 0, ORC_X_BF16 = 1 };
 enum { ORC_MOE_GATE_UP = 0, ORC_MOE_DOWN = 1 };
 

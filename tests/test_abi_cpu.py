@@ -145,6 +145,14 @@ def test_gemv_argument_validation():
     assert L.qgemv_mxfp4(a, 64, 64, a, 5, 1, a, None) == q.QG_EINVAL           # bad xt
     assert L.qgemv_mxfp4(a, -1, 64, a, q.X_BF16, 1, a, None) == q.QG_EINVAL    # n <= 0
     assert L.qgemv_q8_0(ODD, 64, 64, a, q.X_F32, 1, a, None) == q.QG_EALIGN    # w not 16-aligned
+    # packed weights must start on a 256-byte boundary (whole cache lines per 1 KiB wave load)
+    W16 = ctypes.c_void_p(0x100000 + 16)
+    for f in (L.qgemv_q8_0, L.qgemv_q4_0, L.qgemv_mxfp4):
+        assert f(W16, 64, 64, a, q.X_F32, 1, a, None) == q.QG_EALIGN
+        assert f(ctypes.c_void_p(0x100000 + 128), 64, 64, a, q.X_F32, 1, a, None) == q.QG_EALIGN
+    assert L.qgemm(q.Q4_0, W16, 256, 512, a, q.X_BF16, 16, a, None) == q.QG_EALIGN
+    assert L.qgemv_fused(q.Q8_0, W16, 64, 64, a, q.X_F32, 1, None, ctypes.c_float(0.0), 0, None, a, q.X_F32,
+                         None) == q.QG_EALIGN
     assert L.qgemv_q8_0(a, 64, 64, ODD, q.X_F32, 1, a, None) == q.QG_EALIGN    # x not 16-aligned
     assert L.qgemv_q8_0(a, 64, 64, a, q.X_F32, 1, ODD, None) == q.QG_EALIGN    # y not 4-aligned
 
@@ -159,6 +167,8 @@ def test_moe_argument_validation():
     assert f(q.MXFP4, a, 32, 64, 64, a, a, 9, 4, a, q.X_BF16, 0, a, None) == q.QG_EINVAL      # m > 8
     assert f(q.MXFP4, a, 100, 64, 64, a, a, 8, 9, a, q.X_BF16, 0, a, None) == q.QG_EUNSUPPORTED  # m*top_k
     assert f(q.MXFP4, ODD, 32, 64, 64, a, a, 1, 4, a, q.X_BF16, 0, a, None) == q.QG_EALIGN
+    assert f(q.MXFP4, ctypes.c_void_p(0x100000 + 64), 32, 64, 64, a, a, 1, 4, a, q.X_BF16, 0, a,
+             None) == q.QG_EALIGN                     # experts 16- but not 256-aligned
     assert f(q.MXFP4, a, 32, 64, 64, ODD, a, 1, 4, a, q.X_BF16, 0, a, None) == q.QG_EALIGN
 
 
@@ -167,6 +177,8 @@ def test_pack_and_dequant_validation():
     a = ctypes.c_void_p(0x100000)
     assert L.qg_pack(q.Q8_0, a, 4, 40, a, None) == q.QG_EINVAL
     assert L.qg_pack(q.Q8_0, a, 4, 64, ODD, None) == q.QG_EALIGN
+    assert L.qg_pack(q.Q8_0, a, 4, 64, ctypes.c_void_p(0x100000 + 32), None) == q.QG_EALIGN
+    assert L.qg_unpack(q.Q8_0, ctypes.c_void_p(0x100000 + 32), 4, 64, a, None) == q.QG_EALIGN
     assert L.qg_unpack(q.Q8_0, BAD, 4, 64, a, None) == q.QG_EINVAL
     assert L.qg_dequant_f32(q.Q8_0, a, 4, 64, ODD, None) == q.QG_EALIGN
     assert L.qg_pack_host(q.Q8_0, None, 4, 64, None) == q.QG_EINVAL

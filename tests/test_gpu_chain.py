@@ -117,3 +117,33 @@ def test_chain_matches_single_launch_results(dev):
         d = (ys.double() - y.double()).abs().cpu().numpy()
         assert np.max(d / l1) <= 2 * TOL
     assert q.chain_error() == 0
+
+
+@pytest.mark.parametrize("fmt", [q.Q8_0, q.Q4_0])
+def test_chain_dependent_links(dev, fmt):
+    """Link i+1 reads link i's output as its activations (fp32), as consecutive
+    projections of a decode step do.  Each link is checked against the oracle
+    applied to the activations it was given (the previous link's output, read
+    back), so a workgroup that read a stale activation vector fails.  The chain
+    runs twice with different inputs, so stale values would differ."""
+    shapes = [(2048, 1024), (1536, 2048), (4096, 1536), (1024, 4096), (3072, 1024), (640, 3072)]
+    say(f"chain dependent links fmt={fmt}")
+    canons, ws, ys = [], [], []
+    for j, (n, k) in enumerate(shapes):
+        canon = wl.blocks_for(fmt, n, k, config=83, matrix=j)
+        canons.append(canon)
+        ws.append(q.pack(fmt, torch.from_numpy(canon.reshape(-1)).to(dev), n, k))
+        ys.append(torch.full((1, n), float("nan"), device=dev))
+    x0 = torch.empty((1, shapes[0][1]), dtype=torch.float32, device=dev)
+    xs = [x0] + ys[:-1]
+    ch = q.Chain(fmt, [(w, n, k, x, y) for w, (n, k), x, y in zip(ws, shapes, xs, ys)])
+    for run in range(2):
+        x0.copy_(torch.from_numpy(wl.x_f32((1, shapes[0][1]), wl.rng_for(83, 100 + run, "x"))))
+        ch.run()
+        torch.cuda.synchronize()
+        assert q.chain_error() == 0
+        for j, (n, k) in enumerate(shapes):
+            xin = xs[j].cpu().numpy()
+            ref, l1 = oracle.gemv(fmt, canons[j], n, k, xin, oracle.X_F32)
+            err = oracle.max_rel_err(ys[j].cpu().numpy(), ref, l1)
+            assert err <= TOL, (run, j, err)
