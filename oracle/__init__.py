@@ -19,11 +19,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-Q8_0, Q4_0, MXFP4 = 0, 1, 2
+Q8_0, Q4_0, MXFP4, NVFP4 = 0, 1, 2, 3
 X_F32, X_BF16 = 0, 1
 MOE_GATE_UP, MOE_DOWN = 0, 1
 ACT_NONE, ACT_SWIGLU = 0, 1
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17, NVFP4: 9}      # NVFP4: per 16 weights
 
 
 def build(force=False):
@@ -52,6 +52,11 @@ def lib():
             ("orc_bf16", ctypes.c_double, [ctypes.c_uint16]),
             ("orc_e8m0", ctypes.c_double, [ctypes.c_uint8]),
             ("orc_e2m1", ctypes.c_double, [ctypes.c_uint8]),
+            ("orc_e4m3", ctypes.c_double, [ctypes.c_uint8]),
+            ("orc_e4m3_round", ctypes.c_uint8, [ctypes.c_float]),
+            ("orc_e2m1_round", ctypes.c_uint8, [ctypes.c_float]),
+            ("orc_tensor_bytes", i64, [ctypes.c_int, i64, i64]),
+            ("orc_nvfp4_quantize", ctypes.c_int, [vp, i64, i64, vp]),
             ("orc_decode", ctypes.c_int, [ctypes.c_int, vp, i64, i64, dp]),
             ("orc_gemv", ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, ctypes.c_int, i64,
                                         vp, i64, dp, dp]),
@@ -95,9 +100,44 @@ def e2m1(c):
     return lib().orc_e2m1(int(c))
 
 
+def e4m3(b):
+    """OCP FP8 E4M3 byte -> value (fp64)."""
+    return lib().orc_e4m3(int(b))
+
+
+def e4m3_round(v):
+    """Non-negative fp32 v -> the nearest E4M3 code (ties to even, saturating at 448)."""
+    return int(lib().orc_e4m3_round(float(np.float32(v))))
+
+
+def e2m1_round(r):
+    """fp32 r -> the nearest E2M1 code (ties to even, saturating at +-6; +0 for zero)."""
+    return int(lib().orc_e2m1_round(float(np.float32(r))))
+
+
+def nvfp4_quantize(w):
+    """fp32 weights [n, k] -> one canonical NVFP4 tensor (uint8), by the
+    quantizer of oracle.c (fp32 arithmetic in the order written there)."""
+    wa = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = wa.shape
+    out = np.empty(tensor_bytes(NVFP4, n, k), dtype=np.uint8)
+    if lib().orc_nvfp4_quantize(_ptr(wa), n, k, _ptr(out)) != 0:
+        raise ValueError("orc_nvfp4_quantize rejected its arguments")
+    return out
+
+
+def tensor_bytes(fmt, n, k):
+    """Bytes of one canonical n x k tensor (NVFP4: its blocks of 16 weights,
+    then the fp32 tensor scale)."""
+    v = lib().orc_tensor_bytes(fmt, n, k)
+    if v < 0:
+        raise ValueError("bad format or shape")
+    return v
+
+
 def _blocks(fmt, blocks, n, k):
-    b = np.ascontiguousarray(blocks, dtype=np.uint8)
-    if b.size != n * (k // 32) * BLOCK_BYTES[fmt]:
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1)
+    if b.size != tensor_bytes(fmt, n, k):
         raise ValueError("block array size does not match n, k")
     return b
 
@@ -136,8 +176,8 @@ def gemv(fmt, blocks, n, k, x, xt, rows=None):
 
 def moe(fmt, experts, n_experts, n, k, ids, g, x, xt, mode, rows=None):
     """GATE_UP: y, l1 [m, top_k, nrows]; DOWN: y, l1 [m, nrows]."""
-    e = np.ascontiguousarray(experts, dtype=np.uint8)
-    if e.size != n_experts * n * (k // 32) * BLOCK_BYTES[fmt]:
+    e = np.ascontiguousarray(experts, dtype=np.uint8).reshape(-1)
+    if e.size != n_experts * tensor_bytes(fmt, n, k):
         raise ValueError("expert array size does not match")
     ida = np.ascontiguousarray(ids, dtype=np.int32)
     m, top_k = ida.shape
@@ -246,9 +286,11 @@ def rmsnorm(x, gamma, eps):
 
 def _row_weights(fmt, blocks, n, k, rows):
     """Decoded weights of the given rows, float64 [len(rows), k]."""
-    b = _blocks(fmt, blocks, n, k).reshape(n, -1)
-    sub = np.ascontiguousarray(b[np.asarray(rows, dtype=np.int64)])
-    return decode(fmt, sub.reshape(-1), len(rows), k)
+    b = _blocks(fmt, blocks, n, k)
+    tail = b[n * (k // 16) * 9:] if fmt == NVFP4 else b[:0]      # the NVFP4 tensor scale
+    body = b[:b.size - tail.size].reshape(n, -1)
+    sub = np.ascontiguousarray(body[np.asarray(rows, dtype=np.int64)])
+    return decode(fmt, np.concatenate([sub.reshape(-1), tail]), len(rows), k)
 
 
 def dense_fused(fmt, blocks, n, k, x, xt, norm_weight=None, eps=0.0, act=ACT_NONE, residual=None, rows=None):
@@ -313,8 +355,7 @@ def moe_fused(fmt, experts, n_experts, n, k, ids, g, x, xt, mode, norm_weight=No
     in dense_fused, for down the sum over slots of |g| * row L1."""
     ida = np.asarray(ids, dtype=np.int64)
     m, top_k = ida.shape
-    bb = BLOCK_BYTES[fmt]
-    per = n * (k // 32) * bb
+    per = tensor_bytes(fmt, n, k)
     e_all = np.ascontiguousarray(experts, dtype=np.uint8)
     if e_all.size != n_experts * per:
         raise ValueError("expert array size does not match")

@@ -24,6 +24,26 @@
  *     1, 1 mantissa bit, exponent field 0 subnormal, no inf/NaN codes.
  *   - UE8M0 is an unsigned 8-bit biased exponent (bias 127), value 2^(E-127);
  *     E = 255 is read as NaN.
+ *   - NVFP4 is the 4-bit format of imp's decode cache and sm_120a GEMV (imp
+ *     README, "Why this exists" and the "Features" table's sm_120a row: FP4
+ *     values with packed E2M1 and E4M3 conversions); the pages name it but do
+ *     not define it.  Its public definition: blocks of 16 E2M1 values, one
+ *     FP8 E4M3 scale per block, and one fp32 scale per tensor;
+ *     w = E2M1(c) * E4M3(s) * s_tensor.  E4M3 here is the OCP FP8 E4M3 format:
+ *     1 sign, 4 exponent bits (bias 7), 3 mantissa bits, exponent field 0
+ *     subnormal, S.1111.111 NaN, no infinities (largest finite 448).
+ *     Canonical byte layout (a reading): per 16 weights, the E4M3 scale byte
+ *     then 8 code bytes, byte j holding element j in its low nibble and
+ *     element j+8 in its high nibble; a tensor is its n * (k/16) blocks
+ *     row-major followed by the fp32 tensor scale, little-endian.
+ *   - The NVFP4 quantizer (imp's load-time "decode cache" from Q8_0: imp
+ *     README, "Why this exists") follows the same public recipe: the tensor
+ *     scale maps the tensor's largest magnitude to 6 * 448, each block scale is
+ *     the block's largest magnitude over 6 in units of the tensor scale,
+ *     rounded to E4M3, and each value is rounded to E2M1 in units of the
+ *     decoded block scale; roundings are to nearest, ties to the even code,
+ *     saturating at the largest finite value.  Its arithmetic is fp32, in the
+ *     order written in orc_nvfp4_quantize.
  * Parity pins for every function live in tests/test_oracle.py.
  */
 #include <math.h>
@@ -34,7 +54,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_Q8_0 = 0, ORC_Q4_0 = 1, ORC_MXFP4 = 2 };
+enum { ORC_Q8_0 = 0, ORC_Q4_0 = 1, ORC_MXFP4 = 2, ORC_NVFP4 = 3 };
 
 /* Threads an OpenMP region of the oracle uses (1 without OpenMP). */
 int orc_threads(void)
@@ -103,9 +123,44 @@ double orc_e2m1(uint8_t c)
     return s ? -mag : mag;
 }
 
+/* OCP FP8 E4M3 s: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0;
+ * exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinity. */
+double orc_e4m3(uint8_t b)
+{
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);
+    else
+        mag = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* Bytes of one canonical block (32 weights; 16 for NVFP4). */
 static int block_bytes(int fmt)
 {
-    return fmt == ORC_Q8_0 ? 34 : fmt == ORC_Q4_0 ? 18 : fmt == ORC_MXFP4 ? 17 : 0;
+    return fmt == ORC_Q8_0 ? 34 : fmt == ORC_Q4_0 ? 18 : fmt == ORC_MXFP4 ? 17 : fmt == ORC_NVFP4 ? 9 : 0;
+}
+
+static int block_len(int fmt) { return fmt == ORC_NVFP4 ? 16 : 32; }
+
+/* Bytes of one canonical n x k tensor (NVFP4: blocks, then the fp32 tensor scale). */
+int64_t orc_tensor_bytes(int fmt, int64_t n, int64_t k)
+{
+    if (block_bytes(fmt) == 0 || n <= 0 || k <= 0 || (k % 32) != 0)
+        return -1;
+    return n * (k / block_len(fmt)) * (int64_t)block_bytes(fmt) + (fmt == ORC_NVFP4 ? 4 : 0);
+}
+
+/* The fp32 tensor scale stored after an NVFP4 tensor's blocks. */
+static double nvfp4_tensor_scale(const uint8_t *blocks, int64_t n, int64_t k)
+{
+    const uint8_t *p = blocks + n * (k / 16) * 9;
+    union { uint32_t u; float f; } v;
+    v.u = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+    return (double)v.f;
 }
 
 /* Weight i (0..31) of one canonical block. */
@@ -120,6 +175,11 @@ static double block_weight(int fmt, const uint8_t *blk, int i)
         uint8_t byte = blk[2 + (i & 15)];
         int q = (i < 16) ? (byte & 15) : (byte >> 4);
         return d * (double)(q - 8);
+    }
+    if (fmt == ORC_NVFP4) {                      /* i in 0..15; the tensor scale is applied by the caller */
+        uint8_t byte = blk[1 + (i & 7)];
+        uint8_t c = (i < 8) ? (byte & 15) : (byte >> 4);
+        return orc_e2m1(c) * orc_e4m3(blk[0]);
     }
     /* MXFP4 */
     {
@@ -137,12 +197,19 @@ static double act(const void *x, int xt, int64_t idx)
     return orc_bf16(((const uint16_t *)x)[idx]);
 }
 
-/* Element (r, c) of an n x k matrix of canonical blocks. */
-static double weight_at(int fmt, const uint8_t *blocks, int64_t k, int64_t r, int64_t c)
+/* Element (r, c) of an n x k matrix of canonical blocks (ts: the NVFP4 tensor
+ * scale, 1 for the other formats). */
+static double weight_at(int fmt, const uint8_t *blocks, int64_t k, int64_t r, int64_t c, double ts)
 {
-    int64_t nb = k / 32;
-    const uint8_t *blk = blocks + (r * nb + c / 32) * (int64_t)block_bytes(fmt);
-    return block_weight(fmt, blk, (int)(c % 32));
+    const int bl = block_len(fmt);
+    int64_t nb = k / bl;
+    const uint8_t *blk = blocks + (r * nb + c / bl) * (int64_t)block_bytes(fmt);
+    return block_weight(fmt, blk, (int)(c % bl)) * ts;
+}
+
+static double tensor_scale(int fmt, const uint8_t *blocks, int64_t n, int64_t k)
+{
+    return fmt == ORC_NVFP4 ? nvfp4_tensor_scale(blocks, n, k) : 1.0;
 }
 
 static int check(int fmt, int64_t n, int64_t k, int xt)
@@ -159,10 +226,11 @@ int orc_decode(int fmt, const uint8_t *blocks, int64_t n, int64_t k, double *w)
 {
     if (check(fmt, n, k, ORC_X_F32))
         return 1;
+    const double ts = tensor_scale(fmt, blocks, n, k);
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < n; ++r)
         for (int64_t c = 0; c < k; ++c)
-            w[r * k + c] = weight_at(fmt, blocks, k, r, c);
+            w[r * k + c] = weight_at(fmt, blocks, k, r, c, ts);
     return 0;
 }
 
@@ -181,13 +249,14 @@ int orc_gemv(int fmt, const uint8_t *blocks, int64_t n, int64_t k,
     for (int64_t i = 0; i < nrows; ++i)
         if (rows && (rows[i] < 0 || rows[i] >= n))
             return 1;
+    const double ts = tensor_scale(fmt, blocks, n, k);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < nrows; ++i) {
         int64_t r = rows ? rows[i] : i;
         for (int64_t t = 0; t < m; ++t) {
             double s = 0.0, a = 0.0;
             for (int64_t c = 0; c < k; ++c) {
-                double p = weight_at(fmt, blocks, k, r, c) * act(x, xt, t * k + c);
+                double p = weight_at(fmt, blocks, k, r, c, ts) * act(x, xt, t * k + c);
                 s += p;
                 a += fabs(p);
             }
@@ -223,7 +292,7 @@ int orc_moe(int fmt, const uint8_t *experts, int64_t n_experts, int64_t n, int64
     for (int64_t i = 0; i < nrows; ++i)
         if (rows && (rows[i] < 0 || rows[i] >= n))
             return 1;
-    int64_t mat_bytes = n * (k / 32) * (int64_t)block_bytes(fmt);
+    int64_t mat_bytes = orc_tensor_bytes(fmt, n, k);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < nrows; ++i) {
         int64_t r = rows ? rows[i] : i;
@@ -231,10 +300,11 @@ int orc_moe(int fmt, const uint8_t *experts, int64_t n_experts, int64_t n, int64
             double ys = 0.0, ya = 0.0;
             for (int64_t j = 0; j < top_k; ++j) {
                 const uint8_t *W = experts + (int64_t)ids[t * top_k + j] * mat_bytes;
+                const double ts = tensor_scale(fmt, W, n, k);
                 int64_t xoff = (mode == ORC_MOE_GATE_UP) ? t * k : (t * top_k + j) * k;
                 double s = 0.0, a = 0.0;
                 for (int64_t c = 0; c < k; ++c) {
-                    double p = weight_at(fmt, W, k, r, c) * act(x, xt, xoff + c);
+                    double p = weight_at(fmt, W, k, r, c, ts) * act(x, xt, xoff + c);
                     s += p;
                     a += fabs(p);
                 }
@@ -253,5 +323,91 @@ int orc_moe(int fmt, const uint8_t *experts, int64_t n_experts, int64_t n, int64
             }
         }
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------ NVFP4 quantizer */
+/* Round v >= 0 to the nearest non-negative finite E4M3 value (ties to the even
+ * code), saturating at 448: the code, by searching every candidate. */
+uint8_t orc_e4m3_round(float v)
+{
+    if (v >= 448.0f)
+        return 0x7E;
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double d = fabs(orc_e4m3((uint8_t)c) - (double)v);
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return (uint8_t)best;
+}
+
+/* Round r to the nearest E2M1 value (ties to the even code, saturating at +-6):
+ * the 4-bit code, with the sign bit only on a non-zero magnitude. */
+uint8_t orc_e2m1_round(float r)
+{
+    double a = fabs((double)r);
+    if (a >= 6.0)
+        return (uint8_t)(r < 0 ? 15 : 7);
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c <= 7; ++c) {
+        double d = fabs(orc_e2m1((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            bd = d;
+            best = c;
+        }
+    }
+    if (best != 0 && r < 0)
+        best |= 8;
+    return (uint8_t)best;
+}
+
+/* fp32 weights w[n][k] -> one canonical NVFP4 tensor (orc_tensor_bytes bytes).
+ * fp32 arithmetic, in this order:
+ *   A   = max |w| over the tensor;  s_t = A / 2688 (6 * 448), or 1 if A = 0
+ *   per block of 16:  a = max |w|;  s8 = E4M3 rounding of (a / 6) / s_t
+ *                     S = E4M3(s8) * s_t
+ *                     code = 0 where S = 0, else E2M1 rounding of w / S */
+int orc_nvfp4_quantize(const float *w, int64_t n, int64_t k, uint8_t *out)
+{
+    if (n <= 0 || k <= 0 || (k % 32) != 0)
+        return 1;
+    float A = 0.0f;
+    for (int64_t i = 0; i < n * k; ++i)
+        if (fabsf(w[i]) > A)
+            A = fabsf(w[i]);
+    const float st = A > 0.0f ? A / 2688.0f : 1.0f;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t b = 0; b < k / 16; ++b) {
+            const float *wb = w + r * k + b * 16;
+            uint8_t *blk = out + (r * (k / 16) + b) * 9;
+            float a = 0.0f;
+            for (int i = 0; i < 16; ++i)
+                if (fabsf(wb[i]) > a)
+                    a = fabsf(wb[i]);
+            const float u = a / 6.0f;
+            const float v = u / st;
+            const uint8_t s8 = orc_e4m3_round(v);
+            const float S = (float)orc_e4m3(s8) * st;
+            uint8_t code[16];
+            for (int i = 0; i < 16; ++i)
+                code[i] = S == 0.0f ? 0 : orc_e2m1_round(wb[i] / S);
+            blk[0] = s8;
+            for (int j = 0; j < 8; ++j)
+                blk[1 + j] = (uint8_t)(code[j] | (code[j + 8] << 4));
+        }
+    }
+    union { uint32_t u; float f; } t;
+    t.f = st;
+    uint8_t *p = out + n * (k / 16) * 9;
+    p[0] = (uint8_t)t.u;
+    p[1] = (uint8_t)(t.u >> 8);
+    p[2] = (uint8_t)(t.u >> 16);
+    p[3] = (uint8_t)(t.u >> 24);
     return 0;
 }

@@ -8,6 +8,9 @@ oracle consume; little-endian, scale first, one block = 32 weights along K):
   nibble and element j+16 in its high nibble.
 * MXFP4 (17 B): one E8M0 exponent byte, then 16 bytes with the same nibble
   split as Q4_0; each nibble is an FP4 E2M1 code (sign in bit 3).
+* NVFP4 (9 B per 16 weights): one FP8 E4M3 scale byte, then 8 bytes; byte j
+  holds element j in its low nibble and element j+8 in its high nibble (E2M1
+  codes).  A tensor ends with its fp32 scale (4 bytes, little-endian).
 
 A matrix of N rows by K columns is N*(K/32) blocks, row-major.
 
@@ -17,9 +20,17 @@ input of every workload is reproducible on any host.
 import numpy as np
 
 QK = 32
-FMT_Q8_0, FMT_Q4_0, FMT_MXFP4 = 0, 1, 2
-FMT_NAMES = {FMT_Q8_0: "q8_0", FMT_Q4_0: "q4_0", FMT_MXFP4: "mxfp4"}
-BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4_0: 18, FMT_MXFP4: 17}
+FMT_Q8_0, FMT_Q4_0, FMT_MXFP4, FMT_NVFP4 = 0, 1, 2, 3
+FMT_NAMES = {FMT_Q8_0: "q8_0", FMT_Q4_0: "q4_0", FMT_MXFP4: "mxfp4", FMT_NVFP4: "nvfp4"}
+BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4_0: 18, FMT_MXFP4: 17, FMT_NVFP4: 9}   # NVFP4 per 16 weights
+
+
+def canon_bytes(fmt, n, k):
+    """Bytes of one canonical n x k tensor (NVFP4: blocks of 16 weights, then
+    the 4-byte fp32 tensor scale)."""
+    if fmt == FMT_NVFP4:
+        return n * (k // 16) * 9 + 4
+    return n * (k // QK) * BLOCK_BYTES[fmt]
 
 ROLES = {"codes": 0, "scales": 1, "x": 2, "router": 3, "h": 4, "gamma": 5, "res": 6}
 
@@ -107,6 +118,23 @@ def mxfp4_blocks(n, k, rng_codes, rng_scales, e_lo=-8, e_hi=-2):
     return encode_mxfp4(c, e)
 
 
+def nvfp4_tensor(n, k, rng_codes, rng_scales, ts=None):
+    """Canonical NVFP4 tensor: per 16 weights one E4M3 scale byte (uniform
+    over the normal codes 0x20..0x57, values 2^-3 .. 15) then 8 code bytes
+    (byte j = element j | element j+8 << 4, codes uniform 0..15); then the fp32
+    tensor scale (drawn log-uniform in [1e-4, 1e-3] unless given)."""
+    nb = k // 16
+    codes = rng_codes.integers(0, 16, size=(n, nb, 16), dtype=np.uint8)
+    sc = rng_scales.integers(0x20, 0x58, size=(n, nb), dtype=np.uint8)
+    body = np.empty((n, nb, 9), dtype=np.uint8)
+    body[:, :, 0] = sc
+    body[:, :, 1:] = codes[..., :8] | (codes[..., 8:] << 4)
+    if ts is None:
+        ts = float(np.float32(10.0 ** rng_scales.uniform(-4, -3)))
+    tail = np.array([ts], dtype=np.float32).view(np.uint8)
+    return np.concatenate([body.reshape(-1), tail])
+
+
 def blocks_for(fmt, n, k, config, matrix):
     """Canonical blocks of one matrix of a workload, drawn with the workload seeds."""
     rc, rs = rng_for(config, matrix, "codes"), rng_for(config, matrix, "scales")
@@ -116,6 +144,8 @@ def blocks_for(fmt, n, k, config, matrix):
         return q4_0_blocks(n, k, rc, rs)
     if fmt == FMT_MXFP4:
         return mxfp4_blocks(n, k, rc, rs)
+    if fmt == FMT_NVFP4:
+        return nvfp4_tensor(n, k, rc, rs)
     raise ValueError(fmt)
 
 
