@@ -47,12 +47,13 @@ def parse():
     ap.add_argument("--no-events", action="store_true", help="skip the roofline / per-shape timing pass")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", choices=["c2", "c2f", "c0", "c1", "c3", "c4", "gemm", "stream"], default="c2",
+    ap.add_argument("--workload", choices=["c2", "c2f", "c2n", "c0", "c1", "c3", "c4", "gemm", "stream"], default="c2",
                     help="c2: the full Q8_0 decode sweep (the headline line); c2f: the same sweep with the decode "
                          "step's neighbours fused in (RMSNorm, SwiGLU, residual; qgemv_fused) next to the plain "
                          "sweep; c0/c1/c3/c4: the other workloads, each timed over >= 1 GiB of distinct weight "
                          "copies so the device-side cache cannot serve repeated reads; gemm: qgemm on the c3 "
-                         "matrices at 16..128 tokens; stream: the read-only streaming ceiling over a 4 GiB buffer")
+                         "matrices at 16..128 tokens; stream: the read-only streaming ceiling over a 4 GiB buffer; "
+                         "c2n: the c2 sweep through the NVFP4 decode cache (Q8_0 re-quantized at load)")
     ap.add_argument("--tokens", default="16,32,64,128",
                     help="gemm workload: the token counts to run (comma-separated, 1..128)")
     ap.add_argument("--quiet", action="store_true")
@@ -480,13 +481,102 @@ def run_fused_sweep(args, torch, q, dev, shapes, wviews, xs, ys, fmt, config):
     print(json.dumps(out), flush=True)
 
 
+def run_nvfp4_sweep(args, torch, q, dev, shapes, config):
+    """The decode sweep through the NVFP4 decode cache: every Q8_0 matrix of
+    the sweep re-quantized to NVFP4 at load time (qg_requant_q8_0_nvfp4), then
+    the 145 products on the NVFP4 copy (qgemv_nvfp4), one graph.  Reports the
+    NVFP4 bytes streamed, and, on a sample, the product's parity with the
+    oracle of the NVFP4 tensor and its deviation from the Q8_0 product."""
+    import oracle
+    fmt = q.NVFP4
+    offs, total = [], 0
+    for (_, _, n, k) in shapes:
+        offs.append(total)
+        total += q.packed_bytes(fmt, n, k)
+    nvbuf = torch.empty(total, dtype=torch.uint8, device=dev)
+    xs, ys = [], []
+    t0 = time.time()
+    t_req = 0.0
+    def gen(item):
+        j, _, n, k = item
+        return wl.blocks_for(q.Q8_0, n, k, config=config, matrix=j)
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        for base in range(0, len(shapes), 16):
+            chunk = shapes[base:base + 16]
+            for i, blocks in enumerate(ex.map(gen, chunk)):
+                j, _, n, k = chunk[i]
+                idx = base + i
+                canon = torch.from_numpy(blocks.reshape(-1)).to(dev)
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+                q.requant_q8_0_nvfp4(canon, n, k, out=nvbuf[offs[idx]:offs[idx] + q.packed_bytes(fmt, n, k)])
+                torch.cuda.synchronize()
+                t_req += time.perf_counter() - t1
+                del canon
+                xb = wl.x_bf16_bits((1, k), wl.rng_for(config, j, "x"))
+                xs.append(torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16))
+                ys.append(torch.empty((1, n), dtype=torch.float32, device=dev))
+    log(args, f"decode cache built in {time.time() - t0:.1f} s ({t_req * 1e3:.1f} ms of re-quantization kernels)")
+    wv = [nvbuf[offs[i]:offs[i] + q.packed_bytes(fmt, n, k)] for i, (_, _, n, k) in enumerate(shapes)]
+    alg = [n * (k // 32) * 18 + 2 * k + 4 * n for (_, _, n, k) in shapes]
+
+    def sweep(idx=None):
+        for i in range(len(shapes)) if idx is None else idx:
+            _, _, n, k = shapes[i]
+            q.qgemv(fmt, wv[i], n, k, xs[i], y=ys[i])
+
+    us = graph_time(torch, sweep, max(1, args.steps))
+    gbs = sum(alg) / us / 1e3
+    groups = {}
+    for i, (_, name, n, k) in enumerate(shapes):
+        groups.setdefault(name.split(".")[-1], []).append(i)
+    per_shape = {}
+    for key, idx in groups.items():
+        u = graph_time(torch, lambda idx=idx: sweep(idx), 5) / len(idx)
+        _, _, n, k = shapes[idx[0]]
+        per_shape[key] = {"n": n, "k": k, "bytes": alg[idx[0]], "us": round(u, 3), "gbs": round(alg[idx[0]] / u / 1e3, 1)}
+    # sample: layer 0's four matrices in full and every 9th LM-head row
+    sweep()
+    torch.cuda.synchronize()
+    parity, deviation = 0.0, 0.0
+    for i, rows in [(0, None), (1, None), (2, None), (3, None), (144, np.arange(0, 151936, 9))]:
+        j, name, n, k = shapes[i]
+        nv = q.unpack(fmt, wv[i], n, k).cpu().numpy()
+        xb = wl.x_bf16_bits((1, k), wl.rng_for(config, j, "x"))
+        yg = ys[i].cpu().numpy()
+        yg = yg if rows is None else yg[:, rows]
+        ref, l1 = oracle.gemv(oracle.NVFP4, nv, n, k, xb, oracle.X_BF16, rows=rows)
+        parity = max(parity, oracle.max_rel_err(yg, ref, l1))
+        canon8 = wl.blocks_for(q.Q8_0, n, k, config=config, matrix=j)
+        ref8, l18 = oracle.gemv(oracle.Q8_0, canon8, n, k, xb, oracle.X_BF16, rows=rows)
+        deviation = max(deviation, oracle.max_rel_err(yg, ref8, l18))
+    out = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us * 1e-3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "q8_0 full decode sweep through the NVFP4 decode cache (re-quantized at load), M=1: "
+                               "36 x {qkv 6144x2560, o 2560x4096, gate_up 19456x2560, down 2560x9728} + lm_head "
+                               "151936x2560; bf16 x, fp32 y", "launches_per_step": len(shapes),
+                   "bytes_per_step": sum(alg)},
+        "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "equiv_decode_tok_s": round(1e6 / us, 1),
+        "per_shape": per_shape,
+        "requant_ms": round(t_req * 1e3, 2),
+        "parity_max_rel_err_vs_nvfp4_oracle": parity,
+        "deviation_max_rel_err_vs_q8_0_oracle": deviation,
+        "sample": "layer 0 (qkv, o, gate_up, down) in full + every 9th LM-head row",
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the sharded design is described but not run)", file=sys.stderr)
         sys.exit(2)
-    if args.workload not in ("c2", "c2f"):
+    if args.workload not in ("c2", "c2f", "c2n"):
         run_other(args)
         return
 
@@ -502,6 +592,9 @@ def main():
 
     shapes = wl.c2_sweep_shapes()
     fmt, config = q.Q8_0, 2
+    if args.workload == "c2n":
+        run_nvfp4_sweep(args, torch, q, dev, shapes, config)
+        return
     offs, total = [], 0
     for (_, _, n, k) in shapes:
         offs.append(total)

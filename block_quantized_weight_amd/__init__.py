@@ -15,14 +15,19 @@ LIB_PATH = os.path.join(_PKG, "libqgemv.so")
 
 # enums of include/qgemv.h
 QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_EALIGN, QG_EHIP = 0, 1, 2, 3, 4
-Q8_0, Q4_0, MXFP4 = 0, 1, 2
+Q8_0, Q4_0, MXFP4, NVFP4 = 0, 1, 2, 3
 X_F32, X_BF16 = 0, 1
 MOE_GATE_UP, MOE_DOWN_COMBINE = 0, 1
 MAX_M = 8
 MAX_GEMM_M = 128
 PATH_VALU, PATH_MFMA, PATH_VALU_ONE = 0, 1, 2
 ACT_NONE, ACT_SWIGLU = 0, 1
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17, NVFP4: 18}     # canonical bytes per 32 weights
+
+
+def canon_bytes(fmt, n, k):
+    """Bytes of one canonical n x k tensor (NVFP4: its blocks, then the 4-byte tensor scale)."""
+    return n * (k // 32) * BLOCK_BYTES[fmt] + (4 if fmt == NVFP4 else 0)
 
 # exported functions: name -> (restype, argtypes)
 _i, _i64, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
@@ -40,6 +45,8 @@ SIGNATURES = {
     "qgemv_q8_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_q4_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_mxfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
+    "qgemv_nvfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
+    "qg_requant_q8_0_nvfp4": (_i, [_vp, _i64, _i64, _vp, _vp]),
     "qgemm": (_i, [_i, _vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qg_gemm_path": (_i, [_i, _i64, _i64, _i, _i64]),
     "qgemv_fused": (_i, [_i, _vp, _i64, _i64, _vp, _i, _i64, _vp, ctypes.c_float, _i, _vp, _vp, _i, _vp]),
@@ -72,7 +79,7 @@ class Layout(ctypes.Structure):
                 ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("steps", ctypes.c_int64),
                 ("tiles", ctypes.c_int64), ("code_tile_bytes", ctypes.c_int64),
                 ("scale_tile_bytes", ctypes.c_int64), ("scale_offset", ctypes.c_int64),
-                ("packed_bytes", ctypes.c_int64)]
+                ("packed_bytes", ctypes.c_int64), ("tensor_scale_offset", ctypes.c_int64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
@@ -133,7 +140,7 @@ def _np_ptr(a):
 def pack_host(fmt, canon, n, k):
     """Canonical blocks (numpy uint8) -> packed bytes (numpy uint8), on the CPU."""
     c = np.ascontiguousarray(canon, dtype=np.uint8).reshape(-1)
-    if c.size != n * (k // 32) * BLOCK_BYTES.get(fmt, 0):
+    if fmt not in BLOCK_BYTES or c.size != canon_bytes(fmt, n, k):
         raise ValueError("canonical array size does not match (fmt, n, k)")
     out = np.empty(packed_bytes(fmt, n, k), dtype=np.uint8)
     _check("qg_pack_host", lib().qg_pack_host(fmt, _np_ptr(c), n, k, _np_ptr(out)))
@@ -144,7 +151,7 @@ def unpack_host(fmt, packed, n, k):
     p = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1)
     if p.size != packed_bytes(fmt, n, k):
         raise ValueError("packed array size does not match (fmt, n, k)")
-    out = np.zeros(n * (k // 32) * BLOCK_BYTES[fmt], dtype=np.uint8)
+    out = np.zeros(canon_bytes(fmt, n, k), dtype=np.uint8)
     _check("qg_unpack_host", lib().qg_unpack_host(fmt, _np_ptr(p), n, k, _np_ptr(out)))
     return out
 
@@ -190,7 +197,7 @@ def pack(fmt, canon, n, k, out=None, stream=None):
 def unpack(fmt, packed, n, k, out=None, stream=None):
     torch = _torch()
     if out is None:
-        out = torch.zeros(n * (k // 32) * BLOCK_BYTES[fmt], dtype=torch.uint8, device=packed.device)
+        out = torch.zeros(canon_bytes(fmt, n, k), dtype=torch.uint8, device=packed.device)
     _check("qg_unpack", lib().qg_unpack(fmt, _dev_ptr(packed, "packed"), n, k, _dev_ptr(out, "out"),
                                         _stream(stream)))
     return out
@@ -219,7 +226,7 @@ def read_stream(buf, sink=None, stream=None):
     return sink
 
 
-_GEMV = {Q8_0: "qgemv_q8_0", Q4_0: "qgemv_q4_0", MXFP4: "qgemv_mxfp4"}
+_GEMV = {Q8_0: "qgemv_q8_0", Q4_0: "qgemv_q4_0", MXFP4: "qgemv_mxfp4", NVFP4: "qgemv_nvfp4"}
 
 
 def qgemv(fmt, w_packed, n, k, x, y=None, stream=None):
@@ -246,6 +253,21 @@ def qgemv_q4_0(w_packed, n, k, x, y=None, stream=None):
 
 def qgemv_mxfp4(w_packed, n, k, x, y=None, stream=None):
     return qgemv(MXFP4, w_packed, n, k, x, y, stream)
+
+
+def qgemv_nvfp4(w_packed, n, k, x, y=None, stream=None):
+    return qgemv(NVFP4, w_packed, n, k, x, y, stream)
+
+
+def requant_q8_0_nvfp4(canon_q8_0, n, k, out=None, stream=None):
+    """Load-time decode cache: canonical Q8_0 blocks (device uint8) -> packed
+    NVFP4 weights (device uint8) for qgemv_nvfp4."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty(packed_bytes(NVFP4, n, k), dtype=torch.uint8, device=canon_q8_0.device)
+    _check("qg_requant_q8_0_nvfp4", lib().qg_requant_q8_0_nvfp4(_dev_ptr(canon_q8_0, "canon_q8_0"), n, k,
+                                                               _dev_ptr(out, "out"), _stream(stream)))
+    return out
 
 
 def gemm_path(fmt, n, k, xt, m):

@@ -38,6 +38,24 @@ __global__ void k_dequant(LayoutArgs a, const uint8_t *__restrict__ packed, floa
 #pragma unroll
                 for (int e = 0; e < 8; ++e) out[8 * i + e] = d * v[e];
             }
+        } else if (a.fmt == QG_NVFP4) {
+            const float ts = *(const float *)(packed + a.tsoff);
+            const float s0 = e4m3_to_f32(packed[so]), s1 = e4m3_to_f32(packed[so + 1]);
+            uint32_t c[4] = {c0.x, c0.y, c0.z, c0.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bf16x2_t pr[4] = {fp4_pair_bf16<0>(c[i]), fp4_pair_bf16<1>(c[i]), fp4_pair_bf16<2>(c[i]),
+                                  fp4_pair_bf16<3>(c[i])};
+                const float sc = i < 2 ? s0 : s1;
+                // E2M1 * E4M3 is exact in fp32 (at most 6 significant bits), so
+                // each weight is the single rounding of its exact value
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    uint32_t v = __builtin_bit_cast(uint32_t, pr[p]);
+                    out[8 * i + 2 * p] = (sc * __builtin_bit_cast(float, v << 16)) * ts;
+                    out[8 * i + 2 * p + 1] = (sc * __builtin_bit_cast(float, v & 0xFFFF0000u)) * ts;
+                }
+            }
         } else {
             float sc = e8m0_to_f32(packed[so]);
             uint32_t c[4] = {c0.x, c0.y, c0.z, c0.w};
@@ -59,15 +77,17 @@ __global__ void k_dequant(LayoutArgs a, const uint8_t *__restrict__ packed, floa
 
 __global__ void k_pack(LayoutArgs a, const uint8_t *__restrict__ canon, uint8_t *__restrict__ packed, int64_t nrec)
 {
-    const int64_t tid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (tid < a.total - a.end) packed[a.end + tid] = 0;
-    for (int64_t r = tid; r < nrec; r += (int64_t)gridDim.x * blockDim.x)
+    const int64_t tid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x, nthr = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t o = a.end + tid; o < a.total; o += nthr) packed[o] = tail_byte(a, canon, o);
+    for (int64_t r = tid; r < nrec; r += nthr)
         pack_record(a, canon, packed, r);
 }
 
 __global__ void k_unpack(LayoutArgs a, const uint8_t *__restrict__ packed, uint8_t *__restrict__ canon, int64_t nrec)
 {
-    for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < nrec; r += (int64_t)gridDim.x * blockDim.x)
+    const int64_t tid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (a.fmt == QG_NVFP4 && tid < 4) canon[a.cts + tid] = packed[a.tsoff + tid];      // the tensor scale
+    for (int64_t r = tid; r < nrec; r += (int64_t)gridDim.x * blockDim.x)
         unpack_record(a, packed, canon, r);
 }
 
@@ -223,6 +243,7 @@ Plan make_plan(const Layout &lo, int M, bool dot, int maxslots_lds)
     g.ctb = lo.ctb;
     g.stb = lo.stb;
     g.soff = lo.soff;
+    g.tsoff = lo.tsoff;
     // activation window: as many steps as fit XBUDGET (at least one)
     const size_t per_block = (size_t)maxslots_lds * x_quads(lo.fmt, dot) * 16;
     int64_t sw_max = (int64_t)(XBUDGET / per_block) / lo.L;
@@ -274,7 +295,7 @@ struct MPlan {
 // row, and tiles whose per-lane offsets fit in 32 bits.
 bool mfma_fits(const Layout &lo, int xt, int64_t m)
 {
-    if (xt != QG_BF16 || m < mfma_min_m(lo.fmt) || lo.L > MFMA_MAX_L) return false;
+    if (lo.fmt == QG_NVFP4 || xt != QG_BF16 || m < mfma_min_m(lo.fmt) || lo.L > MFMA_MAX_L) return false;
     const int64_t tpw = lo.L >= 8 ? lo.L / 4 : 1;
     return lo.ctb * tpw < ((int64_t)1 << 31) && lo.stb * tpw < ((int64_t)1 << 31);
 }
@@ -383,9 +404,11 @@ int dense(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
     p.g.w = (const uint8_t *)w;
     const int u = one_batch(fmt, xt, p, m);
     dense_fn f = u ? (fmt == QG_Q8_0 ? dense_one_kernel_q8_0(xt, (int)m, u)
-                      : fmt == QG_Q4_0 ? dense_one_kernel_q4_0(xt, (int)m, u) : dense_one_kernel_mxfp4(xt, (int)m, u))
+                      : fmt == QG_Q4_0 ? dense_one_kernel_q4_0(xt, (int)m, u)
+                      : fmt == QG_MXFP4 ? dense_one_kernel_mxfp4(xt, (int)m, u) : dense_one_kernel_nvfp4(xt, (int)m, u))
                    : (fmt == QG_Q8_0 ? dense_kernel_q8_0(xt, (int)m)
-                      : fmt == QG_Q4_0 ? dense_kernel_q4_0(xt, (int)m) : dense_kernel_mxfp4(xt, (int)m));
+                      : fmt == QG_Q4_0 ? dense_kernel_q4_0(xt, (int)m)
+                      : fmt == QG_MXFP4 ? dense_kernel_mxfp4(xt, (int)m) : dense_kernel_nvfp4(xt, (int)m));
     void *args[] = {(void *)&p.g, (void *)&x, (void *)&y};
     if (allow_lds((const void *)f, p.lds) != hipSuccess) return QG_EHIP;
     hipError_t e = hipLaunchKernel((const void *)f, dim3(p.grid), dim3(TPB), args, p.lds, as_stream(stream));
@@ -501,6 +524,7 @@ int qg_layout(int fmt, int64_t n, int64_t k, qg_layout_t *out)
     out->scale_tile_bytes = lo.stb;
     out->scale_offset = lo.soff;
     out->packed_bytes = lo.total;
+    out->tensor_scale_offset = lo.tsoff;
     return QG_OK;
 }
 
@@ -512,7 +536,7 @@ int qg_pack_host(int fmt, const void *canon, int64_t n, int64_t k, void *packed)
     const Layout lo = make_layout(fmt, n, k);
     const LayoutArgs a = layout_args(lo);
     const int64_t nrec = nrecords(lo);
-    memset((uint8_t *)packed + a.end, 0, (size_t)(a.total - a.end));
+    for (int64_t o = a.end; o < a.total; ++o) ((uint8_t *)packed)[o] = tail_byte(a, (const uint8_t *)canon, o);
     for (int64_t r = 0; r < nrec; ++r) pack_record(a, (const uint8_t *)canon, (uint8_t *)packed, r);
     return QG_OK;
 }
@@ -525,6 +549,7 @@ int qg_unpack_host(int fmt, const void *packed, int64_t n, int64_t k, void *cano
     const Layout lo = make_layout(fmt, n, k);
     const LayoutArgs a = layout_args(lo);
     const int64_t nrec = nrecords(lo);
+    if (fmt == QG_NVFP4) memcpy((uint8_t *)canon + a.cts, (const uint8_t *)packed + a.tsoff, 4);
     for (int64_t r = 0; r < nrec; ++r) unpack_record(a, (const uint8_t *)packed, (uint8_t *)canon, r);
     return QG_OK;
 }
@@ -601,6 +626,24 @@ int qgemv_q4_0(const void *w, int64_t n, int64_t k, const void *x, int xt, int64
 int qgemv_mxfp4(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
 {
     return dense(QG_MXFP4, w, n, k, x, xt, m, y, stream);
+}
+
+int qgemv_nvfp4(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
+{
+    return dense(QG_NVFP4, w, n, k, x, xt, m, y, stream);
+}
+
+int qg_requant_q8_0_nvfp4(const void *canon_q8_0, int64_t n, int64_t k, void *nvfp4_packed, void *stream)
+{
+    int st = check_shape(QG_NVFP4, n, k);
+    if (st) return st;
+    if (!canon_q8_0 || !nvfp4_packed) return QG_EINVAL;
+    if (!aligned(nvfp4_packed, W_ALIGN)) return QG_EALIGN;
+    const Layout lo = make_layout(QG_NVFP4, n, k);
+    return launch_requant_nvfp4(lo, (const uint8_t *)canon_q8_0, (uint8_t *)nvfp4_packed, as_stream(stream)) ==
+                   hipSuccess
+               ? QG_OK
+               : QG_EHIP;
 }
 
 // Token groups on the matrix cores: bf16 activations, layouts of at most
@@ -712,10 +755,12 @@ int qgemv_fused(int fmt, const void *w, int64_t n, int64_t k, const void *x, int
     const int u = !norm && glu == 0 ? one_batch(fmt, xt, p, m) : 0;
     dense_ep_fn f = u ? (fmt == QG_Q8_0 ? dense_one_ep_kernel_q8_0(xt, (int)m, u)
                          : fmt == QG_Q4_0 ? dense_one_ep_kernel_q4_0(xt, (int)m, u)
-                                          : dense_one_ep_kernel_mxfp4(xt, (int)m, u))
+                         : fmt == QG_MXFP4 ? dense_one_ep_kernel_mxfp4(xt, (int)m, u)
+                                           : dense_one_ep_kernel_nvfp4(xt, (int)m, u))
                       : fmt == QG_Q8_0 ? dense_ep_kernel_q8_0(xt, (int)m, norm, glu)
                       : fmt == QG_Q4_0 ? dense_ep_kernel_q4_0(xt, (int)m, norm, glu)
-                                       : dense_ep_kernel_mxfp4(xt, (int)m, norm, glu);
+                      : fmt == QG_MXFP4 ? dense_ep_kernel_mxfp4(xt, (int)m, norm, glu)
+                                        : dense_ep_kernel_nvfp4(xt, (int)m, norm, glu);
     void *args[] = {(void *)&p.g, (void *)&e, (void *)&x};
     if (allow_lds((const void *)f, p.lds) != hipSuccess) return QG_EHIP;
     hipError_t err = hipLaunchKernel((const void *)f, dim3(p.grid), dim3(block), args, p.lds, as_stream(stream));
@@ -732,6 +777,7 @@ static int moe_impl(int fmt, const void *w_experts, int64_t n_experts, int64_t n
     int st = check_shape(fmt, n, k);
     if (st) return st;
     if (!w_experts || !topk_ids || !x || !y) return QG_EINVAL;
+    if (fmt == QG_NVFP4) return QG_EUNSUPPORTED;   // per-expert tensor scales: not served by the expert kernels
     if (xt != QG_F32 && xt != QG_BF16) return QG_EINVAL;
     if (yt != QG_F32 && yt != QG_BF16) return QG_EINVAL;
     if (mode != QG_MOE_GATE_UP && mode != QG_MOE_DOWN_COMBINE) return QG_EINVAL;
@@ -882,6 +928,7 @@ int qg_chain_plan(int fmt, int xt, int64_t m, const qg_chain_link_t *links, int6
 {
     if (!valid_fmt(fmt) || (xt != QG_F32 && xt != QG_BF16) || m < 1 || m > QG_MAX_M) return QG_EINVAL;
     if (!links || !plan || count < 1) return QG_EINVAL;
+    if (fmt == QG_NVFP4) return QG_EUNSUPPORTED;
     if (count > (1 << 20)) return QG_EUNSUPPORTED;
     int dev = 0, cus = 0, occ = 0;
     if (hipGetDevice(&dev) != hipSuccess) return QG_EHIP;

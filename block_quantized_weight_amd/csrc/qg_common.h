@@ -59,16 +59,23 @@ constexpr int XBUDGET = 64 * 1024;  // LDS bytes for one window of staged activa
 struct Layout {
     int fmt, L, lsh, R, P, sb;
     int64_t n, k, nb, S, tiles;
-    int64_t ctb, stb, soff, total;
+    int64_t ctb, stb, soff, tsoff, total;   // tsoff: NVFP4 tensor scale (fp32), 0 otherwise
 };
 
 // Staged form of one block of 32 activations in LDS: x_quads() 16-byte quads
 // (fp32, or bf16 pairs for the bf16 dot).
 __host__ __device__ constexpr int x_quads(int fmt, bool dot) { return dot ? 4 : 8; }
 
-inline int block_bytes(int fmt) { return fmt == QG_Q8_0 ? 34 : fmt == QG_Q4_0 ? 18 : 17; }
+// Canonical bytes per 32 weights (NVFP4: two 16-weight blocks of 9 bytes).
+inline int block_bytes(int fmt) { return fmt == QG_Q8_0 ? 34 : fmt == QG_MXFP4 ? 17 : 18; }
 
-inline bool valid_fmt(int fmt) { return fmt == QG_Q8_0 || fmt == QG_Q4_0 || fmt == QG_MXFP4; }
+inline bool valid_fmt(int fmt) { return fmt == QG_Q8_0 || fmt == QG_Q4_0 || fmt == QG_MXFP4 || fmt == QG_NVFP4; }
+
+// Bytes of a canonical n x k tensor (NVFP4: blocks, then its fp32 tensor scale).
+inline int64_t canon_bytes(int fmt, int64_t n, int64_t k)
+{
+    return n * (k / 32) * block_bytes(fmt) + (fmt == QG_NVFP4 ? 4 : 0);
+}
 
 inline int ilog2(int v) { int s = 0; while ((1 << s) < v) ++s; return s; }
 
@@ -115,6 +122,12 @@ inline Layout make_layout(int fmt, int64_t n, int64_t k)
     lo.stb = lo.S * 64 * lo.sb;
     lo.soff = lo.tiles * lo.ctb;
     lo.total = (lo.soff + lo.tiles * lo.stb + 255) / 256 * 256;   // experts stay 256-byte aligned
+    lo.tsoff = 0;
+    if (fmt == QG_NVFP4) {
+        // the fp32 tensor scale in a 256-byte trailer of its own
+        lo.tsoff = lo.total;
+        lo.total += 256;
+    }
     return lo;
 }
 
@@ -124,6 +137,9 @@ inline Layout make_layout(int fmt, int64_t n, int64_t k)
 //  Q4_0 : packed byte B = t[2B] | t[2B+1] << 4 with t = q ^ 8, the 4-bit two's
 //         complement of the signed weight q - 8 (one byte = one adjacent pair).
 //  MXFP4: packed byte B = q[2B] | q[2B+1] << 4 (one byte = one adjacent pair).
+//  NVFP4: the same for the 32 codes of the two 16-weight blocks (elements
+//         0..15 use the first block's scale, 16..31 the second's); the two
+//         E4M3 scale bytes form the 16-bit scale entry (first block low).
 __host__ __device__ inline void nibbles_from_canon(const uint8_t *body, uint8_t q[32])
 {
     for (int j = 0; j < 16; ++j) {
@@ -152,6 +168,18 @@ __host__ __device__ inline void canon_to_packed(int fmt, const uint8_t *blk, uin
         for (int b = 0; b < 16; ++b) codes[b] = (uint8_t)((q[2 * b] ^ 8) | ((q[2 * b + 1] ^ 8) << 4));
         return;
     }
+    if (fmt == QG_NVFP4) {
+        // blk: [s0][8 bytes of block 0][s1][8 bytes of block 1]; byte j of a
+        // block holds its element j (low nibble) and j + 8 (high nibble)
+        *scale = (uint16_t)(blk[0] | (blk[9] << 8));
+        for (int h = 0; h < 2; ++h)
+            for (int j = 0; j < 8; ++j) {
+                q[16 * h + j] = blk[9 * h + 1 + j] & 15;
+                q[16 * h + j + 8] = blk[9 * h + 1 + j] >> 4;
+            }
+        for (int b = 0; b < 16; ++b) codes[b] = (uint8_t)(q[2 * b] | (q[2 * b + 1] << 4));
+        return;
+    }
     *scale = blk[0];
     nibbles_from_canon(blk + 1, q);
     for (int b = 0; b < 16; ++b) codes[b] = (uint8_t)(q[2 * b] | (q[2 * b + 1] << 4));
@@ -176,11 +204,18 @@ __host__ __device__ inline void packed_to_canon(int fmt, const uint8_t *codes, u
         nibbles_to_canon(q, blk + 2);
         return;
     }
-    blk[0] = (uint8_t)scale;
     for (int b = 0; b < 16; ++b) {
         q[2 * b] = codes[b] & 15;
         q[2 * b + 1] = codes[b] >> 4;
     }
+    if (fmt == QG_NVFP4) {
+        blk[0] = (uint8_t)(scale & 0xFF);
+        blk[9] = (uint8_t)(scale >> 8);
+        for (int h = 0; h < 2; ++h)
+            for (int j = 0; j < 8; ++j) blk[9 * h + 1 + j] = (uint8_t)(q[16 * h + j] | (q[16 * h + j + 8] << 4));
+        return;
+    }
+    blk[0] = (uint8_t)scale;
     nibbles_to_canon(q, blk + 1);
 }
 
@@ -188,6 +223,7 @@ __host__ __device__ inline void packed_to_canon(int fmt, const uint8_t *codes, u
 struct LayoutArgs {
     int fmt, L, lsh, R, P, sb, bb;
     int64_t n, nb, S, tiles, ctb, stb, soff, end, total;   // [end, total) is tail padding
+    int64_t tsoff, cts;          // NVFP4: tensor scale offsets, packed and canonical (else 0)
 };
 
 inline LayoutArgs layout_args(const Layout &lo)
@@ -199,7 +235,17 @@ inline LayoutArgs layout_args(const Layout &lo)
     a.ctb = lo.ctb; a.stb = lo.stb; a.soff = lo.soff;
     a.end = lo.soff + lo.tiles * lo.stb;
     a.total = lo.total;
+    a.tsoff = lo.tsoff;
+    a.cts = lo.fmt == QG_NVFP4 ? lo.n * lo.nb * 18 : 0;
     return a;
+}
+
+// Tail padding byte o of the packed form (o in [end, total)): zero, except the
+// NVFP4 tensor scale, which is copied from the canonical tensor.
+__host__ __device__ inline uint8_t tail_byte(const LayoutArgs &a, const uint8_t *canon, int64_t o)
+{
+    if (a.fmt == QG_NVFP4 && o >= a.tsoff && o < a.tsoff + 4) return canon[a.cts + (o - a.tsoff)];
+    return 0;
 }
 
 // One record = (tile, step, lane): its row/block and its byte offsets.
@@ -253,6 +299,16 @@ __host__ __device__ inline void unpack_record(const LayoutArgs &a, const uint8_t
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits)
 {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// OCP FP8 E4M3 -> fp32 (exact): 1 sign, 4 exponent bits (bias 7), 3
+// mantissa bits; exponent field 0 is subnormal (m * 2^-9); S.1111.111 is NaN.
+__host__ __device__ __forceinline__ float e4m3_to_f32(uint32_t b)
+{
+    const uint32_t e = (b >> 3) & 15, m = b & 7;
+    float v = e == 0 ? (float)m * 0x1p-9f : __builtin_bit_cast(float, ((e + 120) << 23) | (m << 20));
+    if (e == 15 && m == 7) v = __builtin_nanf("");
+    return (b & 0x80) ? -v : v;
 }
 
 // UE8M0 -> fp32 2^(E-127): E = 0 is the subnormal 2^-127, E = 255 is NaN.
@@ -389,6 +445,7 @@ struct Geom {
     int32_t n, k, nb;
     int32_t L, lsh, R, S, tiles;
     int64_t ctb, stb, soff;
+    int64_t tsoff;               // NVFP4: byte offset of the fp32 tensor scale
     int32_t KS, ksh, tpi, ngroups;
     int32_t SW, nwin, wblk;      // steps per window, windows, blocks per window
 };
@@ -433,6 +490,15 @@ struct XStage {
         }
     }
 };
+
+// The NVFP4 tensor scale (one fp32 in the packed trailer), 1 for the other
+// formats; applied to the row totals.
+template <int FMT>
+__device__ __forceinline__ float tensor_scale(const Geom &g)
+{
+    if (FMT == QG_NVFP4) return *(const QG_GLOBAL float *)(g.w + g.tsoff);
+    return 1.0f;
+}
 
 // Slot -> staged activation row map of the dense product: slot t reads row t.
 struct IdMap {
@@ -536,6 +602,65 @@ struct Engine {
                         s = __builtin_fmaf(v[qd >> 1][4 * (qd & 1) + 3], xq.w, s);
                     }
                     acc[t] = __builtin_fmaf(d, s, acc[t]);
+                }
+            }
+        } else if (FMT == QG_NVFP4) {
+            // two 16-weight blocks: dwords 0-1 with the first E4M3 scale, 2-3
+            // with the second (the tensor scale is applied to the row totals)
+            const float s0 = e4m3_to_f32(sbits & 0xFF), s1 = e4m3_to_f32(sbits >> 8);
+            const uint32_t cw[4] = {c[0].x, c[0].y, c[0].z, c[0].w};
+            if (DOT) {
+                bf16x2_t pr[4][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pr[i][0] = fp4_pair_bf16<0>(cw[i]);
+                    pr[i][1] = fp4_pair_bf16<1>(cw[i]);
+                    pr[i][2] = fp4_pair_bf16<2>(cw[i]);
+                    pr[i][3] = fp4_pair_bf16<3>(cw[i]);
+                }
+#pragma unroll
+                for (int t = 0; t < M; ++t) {
+                    if (t >= xm.count()) break;
+                    float sh[2] = {0.0f, 0.0f};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint4 xq = xs[(xm(t) * 4 + i) * g.wblk + bl];
+                        float &s = sh[i >> 1];
+                        s = dot2(pr[i][0], u32_as_bf16x2(xq.x), s);
+                        s = dot2(pr[i][1], u32_as_bf16x2(xq.y), s);
+                        s = dot2(pr[i][2], u32_as_bf16x2(xq.z), s);
+                        s = dot2(pr[i][3], u32_as_bf16x2(xq.w), s);
+                    }
+                    acc[t] = __builtin_fmaf(s1, sh[1], __builtin_fmaf(s0, sh[0], acc[t]));
+                }
+            } else {
+                f32x2_t pr[4][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pr[i][0] = fp4_pair_f32<0>(cw[i]);
+                    pr[i][1] = fp4_pair_f32<1>(cw[i]);
+                    pr[i][2] = fp4_pair_f32<2>(cw[i]);
+                    pr[i][3] = fp4_pair_f32<3>(cw[i]);
+                }
+#pragma unroll
+                for (int t = 0; t < M; ++t) {
+                    if (t >= xm.count()) break;
+                    float sh[2] = {0.0f, 0.0f};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float4 xa = __builtin_bit_cast(float4, xs[(xm(t) * 8 + 2 * i) * g.wblk + bl]);
+                        const float4 xb = __builtin_bit_cast(float4, xs[(xm(t) * 8 + 2 * i + 1) * g.wblk + bl]);
+                        float &s = sh[i >> 1];
+                        s = __builtin_fmaf(pr[i][0].x, xa.x, s);
+                        s = __builtin_fmaf(pr[i][0].y, xa.y, s);
+                        s = __builtin_fmaf(pr[i][1].x, xa.z, s);
+                        s = __builtin_fmaf(pr[i][1].y, xa.w, s);
+                        s = __builtin_fmaf(pr[i][2].x, xb.x, s);
+                        s = __builtin_fmaf(pr[i][2].y, xb.y, s);
+                        s = __builtin_fmaf(pr[i][3].x, xb.z, s);
+                        s = __builtin_fmaf(pr[i][3].y, xb.w, s);
+                    }
+                    acc[t] = __builtin_fmaf(s1, sh[1], __builtin_fmaf(s0, sh[0], acc[t]));
                 }
             }
         } else {
@@ -735,9 +860,10 @@ __global__ __launch_bounds__(TPB) void k_dense(Geom g, const void *__restrict__ 
         reduce_partials<M>(g, red, acc);
         const int64_t row = (int64_t)tile * g.R + rsub;
         if (kpart == 0 && tile < g.tiles && row < g.n) {
+            const float ts = tensor_scale<FMT>(g);
 #pragma unroll
             for (int t = 0; t < M; ++t)
-                if ((t & (g.L - 1)) == slot) y[(int64_t)sl.yrow[t] * g.n + row] = acc[t];
+                if ((t & (g.L - 1)) == slot) y[(int64_t)sl.yrow[t] * g.n + row] = FMT == QG_NVFP4 ? acc[t] * ts : acc[t];
         }
     }
 }
@@ -842,9 +968,10 @@ __global__ __launch_bounds__(TPB, one_waves(FMT, XBF16, U)) void k_dense_one(Geo
     const int tile = blockIdx.x * g.tpi + (wave >> g.ksh);
     const int64_t row = (int64_t)tile * g.R + (lane >> g.lsh);
     if ((wave & (g.KS - 1)) == 0 && tile < g.tiles && row < g.n) {
+        const float ts = tensor_scale<FMT>(g);
 #pragma unroll
         for (int t = 0; t < M; ++t)
-            if ((t & (g.L - 1)) == (lane & (g.L - 1))) y[(int64_t)t * g.n + row] = acc[t];
+            if ((t & (g.L - 1)) == (lane & (g.L - 1))) y[(int64_t)t * g.n + row] = FMT == QG_NVFP4 ? acc[t] * ts : acc[t];
     }
 }
 
@@ -1068,9 +1195,12 @@ typedef void (*dense_fn)(Geom, const void *, float *);
 dense_fn dense_kernel_q8_0(int xt, int m);
 dense_fn dense_kernel_q4_0(int xt, int m);
 dense_fn dense_kernel_mxfp4(int xt, int m);
+dense_fn dense_kernel_nvfp4(int xt, int m);
 dense_fn dense_one_kernel_q8_0(int xt, int m, int u);
 dense_fn dense_one_kernel_q4_0(int xt, int m, int u);
 dense_fn dense_one_kernel_mxfp4(int xt, int m, int u);
+dense_fn dense_one_kernel_nvfp4(int xt, int m, int u);
+hipError_t launch_requant_nvfp4(const Layout &lo, const uint8_t *canon_q8_0, uint8_t *packed, hipStream_t s);
 hipError_t launch_moe_q8_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,
                            const void *x, float *y, hipStream_t s);
 hipError_t launch_moe_q4_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,

@@ -235,10 +235,12 @@ __global__ __launch_bounds__(TPB) void k_dense_ep(Geom g, EpiArgs e, const void 
         reduce_partials<M>(g, red, acc);
         const int64_t row = (int64_t)tile * g.R + rsub;
         if (kpart == 0 && tile < g.tiles && row < e.n_out) {
+            const float ts = tensor_scale<FMT>(g);
 #pragma unroll
             for (int t = 0; t < M; ++t) {
                 if ((t & (g.L - 1)) != slot) continue;
-                const float v = NORM ? acc[t] * rinv_of<WAVES>(s_part, t, g.k, e.eps) : acc[t];
+                float v = NORM ? acc[t] * rinv_of<WAVES>(s_part, t, g.k, e.eps) : acc[t];
+                if (FMT == QG_NVFP4) v *= ts;
                 store_out(e, (int64_t)t * e.n_out + row, v);
             }
         }
@@ -257,9 +259,11 @@ __global__ __launch_bounds__(TPB, one_waves(FMT, XBF16, U)) void k_dense_one_ep(
     const int tile = blockIdx.x * g.tpi + (wave >> g.ksh);
     const int64_t row = (int64_t)tile * g.R + (lane >> g.lsh);
     if ((wave & (g.KS - 1)) == 0 && tile < g.tiles && row < e.n_out) {
+        const float ts = tensor_scale<FMT>(g);
 #pragma unroll
         for (int t = 0; t < M; ++t)
-            if ((t & (g.L - 1)) == (lane & (g.L - 1))) store_out(e, (int64_t)t * e.n_out + row, acc[t]);
+            if ((t & (g.L - 1)) == (lane & (g.L - 1)))
+                store_out(e, (int64_t)t * e.n_out + row, FMT == QG_NVFP4 ? acc[t] * ts : acc[t]);
     }
 }
 
@@ -308,10 +312,15 @@ __global__ __launch_bounds__(TPB) void k_dense_glu_lanes(Geom g, EpiArgs e, cons
         for (int q = 0; q < M; ++q) up[q] = __shfl_xor(acc[q], 32, 64);
         const int64_t row = (int64_t)t * g.R + rl / g.L;
         if (!upl && kpart == 0 && active && row < e.n_out) {
+            const float ts = tensor_scale<FMT>(g);
 #pragma unroll
             for (int q = 0; q < M; ++q) {
                 if ((q & (g.L - 1)) != slot) continue;
                 float gv = acc[q], uv = up[q];
+                if (FMT == QG_NVFP4) {
+                    gv *= ts;
+                    uv *= ts;
+                }
                 if (NORM) {
                     const float r = rinv_of<WAVES>(s_part, q, g.k, e.eps);
                     gv *= r;
@@ -370,10 +379,15 @@ __global__ __launch_bounds__(64 * GLU_WAVES) void k_dense_glu(Geom g, EpiArgs e,
         __syncthreads();
         const int64_t row = (int64_t)pair * g.R + rsub;
         if (!up && kpart == 0 && active && row < e.n_out) {
+            const float ts = tensor_scale<FMT>(g);
 #pragma unroll
             for (int t = 0; t < M; ++t) {
                 if ((t & (g.L - 1)) != slot) continue;
                 float gv = acc[t], uv = s_up[p][t][rsub];
+                if (FMT == QG_NVFP4) {
+                    gv *= ts;
+                    uv *= ts;
+                }
                 if (NORM) {
                     const float r = rinv_of<GLU_WAVES>(s_part, t, g.k, e.eps);
                     gv *= r;
@@ -458,8 +472,10 @@ dense_ep_fn pick_dense_one_ep(int xt, int m, int u)
 dense_ep_fn dense_ep_kernel_q8_0(int xt, int m, bool norm, int glu);
 dense_ep_fn dense_ep_kernel_q4_0(int xt, int m, bool norm, int glu);
 dense_ep_fn dense_ep_kernel_mxfp4(int xt, int m, bool norm, int glu);
+dense_ep_fn dense_ep_kernel_nvfp4(int xt, int m, bool norm, int glu);
 dense_ep_fn dense_one_ep_kernel_q8_0(int xt, int m, int u);
 dense_ep_fn dense_one_ep_kernel_q4_0(int xt, int m, int u);
 dense_ep_fn dense_one_ep_kernel_mxfp4(int xt, int m, int u);
+dense_ep_fn dense_one_ep_kernel_nvfp4(int xt, int m, int u);
 
 } // namespace qg

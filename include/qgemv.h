@@ -24,8 +24,16 @@
  *   MXFP4 17 B: UE8M0 exponent byte E, then 16 bytes with the same nibble
  *               split; each nibble is an E2M1 code c (sign in bit 3);
  *                                                                 w = E2M1(c) * 2^(E-127)
+ *   NVFP4  9 B per 16 weights: FP8 E4M3 scale s, then 8 bytes; byte j holds
+ *               code j in its low nibble and code j+8 in its high nibble; the
+ *               tensor's N * (K/16) blocks are followed by its fp32 scale s_t
+ *               (4 bytes);                                        w = E2M1(c) * E4M3(s) * s_t
+ *               (the FP4 format of imp's load-time decode cache and sm_120a
+ *               GEMV: imp README, "Why this exists" and "Features"; the
+ *               definition is the public one, the byte order a reading)
  * A matrix is N rows (outputs) by K columns (inputs), stored as N * (K/32)
- * canonical blocks, row-major.  E = 255 decodes to NaN; E2M1 has no NaN.
+ * canonical blocks (N * (K/16) for NVFP4), row-major.  E = 255 decodes to
+ * NaN; E2M1 has no NaN; E4M3 S.1111.111 is NaN.
  *
  * Packed layout.  The GEMV entry points read weights in a packed layout made
  * once at load time by qg_pack (device) or qg_pack_host (CPU): per tile of
@@ -78,7 +86,7 @@ enum {
 };
 
 /* Weight formats. */
-enum { QG_Q8_0 = 0, QG_Q4_0 = 1, QG_MXFP4 = 2 };
+enum { QG_Q8_0 = 0, QG_Q4_0 = 1, QG_MXFP4 = 2, QG_NVFP4 = 3 };
 
 /* Activation element types: fp32, or bf16 bit patterns (uint16). */
 enum { QG_F32 = 0, QG_BF16 = 1 };
@@ -115,6 +123,7 @@ typedef struct {
     int64_t scale_tile_bytes;   /* S * 64 * scale_bytes */
     int64_t scale_offset;       /* byte offset of the scale stream = tiles * code_tile_bytes */
     int64_t packed_bytes;       /* total size, rounded up to a multiple of 256 */
+    int64_t tensor_scale_offset;  /* NVFP4: byte offset of the fp32 tensor scale (a 256-byte trailer); else 0 */
 } qg_layout_t;
 
 /* Human-readable name of a status code (static string). */
@@ -154,8 +163,10 @@ int qg_unpack(int fmt, const void *packed, int64_t n, int64_t k, void *canon, vo
  * 4-byte aligned) through the same unpack steps the GEMV kernels use, so the
  * block definitions above (the Q8_0 / Q4_0 rows of the imp README "Features"
  * table and the MXFP4 format of the imp release notes v0.6) can be checked
- * weight by weight.  Every decoded weight is exact in fp32 when it is finite,
- * so the result is comparable bit for bit.  w_packed: 256-byte aligned.
+ * weight by weight.  Every Q8_0, Q4_0 and MXFP4 weight is exact in fp32
+ * when it is finite, so the result is comparable bit for bit; an NVFP4
+ * weight is E2M1 * E4M3 (exact) times the fp32 tensor scale, rounded once
+ * to nearest.  w_packed: 256-byte aligned.
  */
 int qg_dequant_f32(int fmt, const void *w_packed, int64_t n, int64_t k, float *w, void *stream);
 
@@ -181,6 +192,32 @@ int qgemv_q4_0(const void *w_packed, int64_t n, int64_t k, const void *x, int xt
                float *y, void *stream);
 int qgemv_mxfp4(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
                 float *y, void *stream);
+
+/*
+ * The same product for NVFP4 weights (packed by qg_pack from a canonical
+ * NVFP4 tensor, or made by qg_requant_q8_0_nvfp4).  Runs the vector kernel
+ * family for every m (each 32-weight record carries two block scales); the
+ * tensor scale is applied to the row totals.  Limits as qgemv_*.
+ */
+int qgemv_nvfp4(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
+                float *y, void *stream);
+
+/*
+ * Load-time decode cache: re-quantizes a Q8_0 matrix into packed NVFP4 for
+ * qgemv_nvfp4, as imp converts GGUF Q8_0 weights to FP4 when a model loads
+ * (imp README, "Why this exists").  The result approximates the Q8_0 weights
+ * (4-bit values: imp release notes v0.4.1 record the accuracy cost); the
+ * Q8_0 product is unaffected.  Recipe, fp32 arithmetic in this order:
+ *   A = max |w| (w = d * q),  s_t = A / 2688 (or 1 if A = 0);  per 16 weights:
+ *   a = max |w|,  s = E4M3 rounding of (a / 6) / s_t,  S = E4M3(s) * s_t,
+ *   code = E2M1 rounding of w / S (0 if S = 0); roundings to nearest, ties to
+ *   the even code, saturating at 448 and 6.  The trailer after the tensor
+ *   scale keeps A (fp32 bits) at tensor_scale_offset + 4.
+ * canon_q8_0: device, n * (k/32) canonical Q8_0 blocks with finite scales.
+ * nvfp4_packed: device, qg_packed_bytes(QG_NVFP4, n, k) bytes, 256-byte
+ * aligned, overwritten.  Three kernels on `stream`; deterministic.
+ */
+int qg_requant_q8_0_nvfp4(const void *canon_q8_0, int64_t n, int64_t k, void *nvfp4_packed, void *stream);
 
 /*
  * Measurement aid: reads every byte of buf once (16-byte nontemporal loads,
@@ -260,7 +297,7 @@ int qgemv_fused(int fmt, const void *w_packed, int64_t n, int64_t k, const void 
  * fp32 accumulation in a fixed order (ascending expert id, then slot), so
  * the same inputs give the same bits.  Only the selected experts' weights
  * are read; each distinct selected expert is streamed once per call for all
- * tokens that chose it.
+ * tokens that chose it.  NVFP4 experts: QG_EUNSUPPORTED.
  * Limits: 1 <= m <= 8, 1 <= top_k <= n_experts, m * top_k <= 64,
  * n_experts <= 65536.  y is overwritten, except gate_up rows of invalid ids.
  */

@@ -318,3 +318,44 @@ def test_gemm_argument_validation_and_path():
             want = q.PATH_MFMA if lanes <= 16 else q.PATH_VALU
             assert q.gemm_path(fmt, n, k, q.X_BF16, 64) == want, (fmt, n, k, lanes)
             assert q.gemm_path(fmt, n, k, q.X_F32, 64) == q.PATH_VALU
+
+
+def test_nvfp4_host_pack_round_trip_and_placement():
+    """NVFP4: two 16-weight blocks per 32-weight record; codes in adjacent-pair
+    order, the two E4M3 scales as the record's 16-bit scale entry (first block
+    low), and the fp32 tensor scale in the 256-byte trailer."""
+    import workloads as wl
+    for n, k in [(1, 32), (70, 320), (129, 608)]:
+        c = wl.nvfp4_tensor(n, k, np.random.default_rng(n), np.random.default_rng(k))
+        p = q.pack_host(q.NVFP4, c, n, k)
+        assert np.array_equal(q.unpack_host(q.NVFP4, p, n, k), c)
+        lo = q.layout(q.NVFP4, n, k)
+        assert lo["packed_bytes"] == p.size and lo["packed_bytes"] % 256 == 0
+        assert lo["tensor_scale_offset"] == lo["packed_bytes"] - 256
+        assert bytes(p[lo["tensor_scale_offset"]:lo["tensor_scale_offset"] + 4]) == bytes(c[-4:])
+        L, R, S = lo["lanes_per_row"], lo["rows_per_tile"], lo["steps"]
+        body = c[:-4].reshape(n, k // 16, 9)
+        for row, blk in [(0, 0), (n - 1, k // 32 - 1), (n // 2, (k // 32) // 2)]:
+            t, r = divmod(row, R)
+            j, s = divmod(blk, L)
+            lane = r * L + s
+            so = lo["scale_offset"] + t * lo["scale_tile_bytes"] + j * 64 * 2 + lane * 2
+            assert p[so] == body[row, 2 * blk, 0] and p[so + 1] == body[row, 2 * blk + 1, 0]
+            co = t * lo["code_tile_bytes"] + j * 1024 + lane * 16
+            codes = []
+            for h in range(2):
+                b = body[row, 2 * blk + h, 1:]
+                codes += list(b & 15) + list(b >> 4)          # elements j and j+8 of each block
+            codes = np.array(codes, dtype=np.uint8)
+            assert np.array_equal(p[co:co + 16], (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8))
+
+
+def test_nvfp4_argument_validation():
+    L = q.lib()
+    a = ctypes.c_void_p(0x100000)
+    assert L.qgemv_nvfp4(a, 64, 48, a, q.X_F32, 1, a, None) == q.QG_EINVAL
+    assert L.qgemv_nvfp4(ctypes.c_void_p(0x100000 + 16), 64, 64, a, q.X_F32, 1, a, None) == q.QG_EALIGN
+    assert L.qg_requant_q8_0_nvfp4(a, 64, 64, ctypes.c_void_p(0x100000 + 64), None) == q.QG_EALIGN
+    assert L.qg_requant_q8_0_nvfp4(None, 64, 64, a, None) == q.QG_EINVAL
+    assert L.qg_requant_q8_0_nvfp4(a, 64, 40, a, None) == q.QG_EINVAL
+    assert q.dense_path(q.NVFP4, 6144, 4096, q.X_BF16, 8) == q.PATH_VALU       # no matrix-core route

@@ -69,6 +69,10 @@ def test_device_pack_matches_host_and_round_trips(dev, fmt, n, k):
     host = q.pack_host(fmt, canon, n, k)
     pd = packed_dev(fmt, canon, n, k, dev)
     assert np.array_equal(pd.cpu().numpy(), host)
+    # into a buffer full of junk: every byte of the packed form is written
+    junk = torch.full((q.packed_bytes(fmt, n, k),), 0xAB, dtype=torch.uint8, device=dev)
+    q.pack(fmt, torch.from_numpy(canon).to(dev), n, k, out=junk)
+    assert np.array_equal(junk.cpu().numpy(), host)
     back = q.unpack(fmt, pd, n, k)
     assert np.array_equal(back.cpu().numpy(), canon)
 
