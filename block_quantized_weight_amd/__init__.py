@@ -57,6 +57,7 @@ SIGNATURES = {
     "qg_chain_plan_bytes": (_i64, [_i64]),
     "qg_chain_plan": (_i, [_i, _i, _i64, _vp, _i64, _vp]),
     "qgemv_chain": (_i, [_vp, _vp, _vp]),
+    "qgemv_chain_noalloc": (_i, [_vp, _vp]),
     "qg_chain_error": (_i, []),
 }
 
@@ -213,6 +214,7 @@ def dequant_f32(fmt, packed, n, k, out=None, stream=None):
 
 
 STREAM_SINK = 16384
+CHAIN_STATIC_BYTES = 65536     # QG_CHAIN_STATIC_BYTES: largest plan of qgemv_chain_noalloc
 
 
 def read_stream(buf, sink=None, stream=None):
@@ -439,6 +441,11 @@ class Chain:
 
     def run(self, stream=None):
         _check("qgemv_chain", lib().qgemv_chain(self.plan_host, _dev_ptr(self.plan_device, "plan"), _stream(stream)))
+
+    def run_noalloc(self, stream=None):
+        """The same chain through qgemv_chain_noalloc: the plan travels in the
+        library's static device buffer, no device copy of the caller's is read."""
+        _check("qgemv_chain_noalloc", lib().qgemv_chain_noalloc(self.plan_host, _stream(stream)))
 
 
 def chain_error():

@@ -1,5 +1,7 @@
 // qg_api.hip -- C ABI of libqgemv.so: argument validation, layout, launch
 // plans, the packer kernels and the dequantization test aid.
+#include <mutex>
+
 #include "qg_chain.h"
 #include "qg_mfma.h"
 #include "qg_moe_stream.h"
@@ -475,6 +477,45 @@ const void *chain_kernel(int fmt, int xt, int m)
 {
     return fmt == QG_Q8_0 ? chain_kernel_q8_0(xt, m) : fmt == QG_Q4_0 ? chain_kernel_q4_0(xt, m)
                                                                      : chain_kernel_mxfp4(xt, m);
+}
+
+// Launches a built plan whose device copy is at plan_device.
+int chain_launch(const ChainHdr *h, const void *plan_device, hipStream_t stream)
+{
+    const ChainLink *links = (const ChainLink *)((const uint8_t *)plan_device + sizeof(ChainHdr) + 16);
+    int nlinks = h->count;
+    const void *fn = chain_kernel(h->fmt, h->xt, h->m);
+    if (allow_lds(fn, (size_t)h->lds) != hipSuccess) return QG_EHIP;
+    int part_off = (int)h->part_off, out_off = (int)h->out_off;
+    void *args[] = {(void *)&links, (void *)&nlinks, (void *)&part_off, (void *)&out_off};
+    hipError_t e = hipLaunchCooperativeKernel(fn, dim3(h->grid), dim3(CTPB), args, (unsigned)h->lds, stream);
+    return e == hipSuccess ? launch_status() : QG_EHIP;
+}
+
+// Plan buffer of qgemv_chain_noalloc: one per device, held until the process
+// ends.  Host code never uses this name as an address: the device address of
+// each device's copy is looked up once (scratch_on_device) and passed on.
+static __device__ __align__(256) uint8_t scratch[QG_CHAIN_STATIC_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[SCRATCH_MAX_DEVICES];
+
+// Device address of the current device's scratch copy, looked up on the
+// first call on that device (the device is current), or QG_* on failure.
+int scratch_on_device(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QG_EHIP;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return QG_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QG_EHIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return QG_OK;
 }
 
 } // namespace
@@ -979,15 +1020,24 @@ int qgemv_chain(const void *plan_host, const void *plan_device, void *stream)
     const ChainHdr *h = (const ChainHdr *)plan_host;
     if (h->magic != CHAIN_MAGIC || h->count < 1 || h->grid < 1) return QG_EINVAL;
     if (!aligned(plan_device, 16)) return QG_EALIGN;
-    const ChainLink *links = (const ChainLink *)((const uint8_t *)plan_device + sizeof(ChainHdr) + 16);
-    int nlinks = h->count;
-    const void *fn = chain_kernel(h->fmt, h->xt, h->m);
-    if (allow_lds(fn, (size_t)h->lds) != hipSuccess) return QG_EHIP;
-    int part_off = (int)h->part_off, out_off = (int)h->out_off;
-    void *args[] = {(void *)&links, (void *)&nlinks, (void *)&part_off, (void *)&out_off};
-    hipError_t e = hipLaunchCooperativeKernel(fn, dim3(h->grid), dim3(CTPB), args, (unsigned)h->lds,
-                                              as_stream(stream));
-    return e == hipSuccess ? launch_status() : QG_EHIP;
+    return chain_launch(h, plan_device, as_stream(stream));
+}
+
+int qgemv_chain_noalloc(const void *plan_host, void *stream)
+{
+    if (!plan_host) return QG_EINVAL;
+    const ChainHdr *h = (const ChainHdr *)plan_host;
+    if (h->magic != CHAIN_MAGIC || h->count < 1 || h->grid < 1) return QG_EINVAL;
+    const int64_t bytes = qg_chain_plan_bytes(h->count);
+    if (bytes < 0) return QG_EINVAL;
+    if (bytes > QG_CHAIN_STATIC_BYTES) return QG_EUNSUPPORTED;
+    void *p = nullptr;
+    const int st = scratch_on_device(&p);
+    if (st) return st;
+    // the whole plan is rewritten, so nothing of an earlier call's plan is read
+    if (hipMemcpyAsync(p, plan_host, (size_t)bytes, hipMemcpyHostToDevice, as_stream(stream)) != hipSuccess)
+        return QG_EHIP;
+    return chain_launch(h, p, as_stream(stream));
 }
 
 int qg_chain_error(void)

@@ -383,6 +383,23 @@ int qg_chain_plan(int fmt, int xt, int64_t m, const qg_chain_link_t *links, int6
 /* Launches the chain.  plan_host: the built plan; plan_device: a 16-byte
  * aligned device copy of the same bytes. */
 int qgemv_chain(const void *plan_host, const void *plan_device, void *stream);
+/*
+ * For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): qgemv_chain without
+ * the caller's device copy of the plan.  The plan bytes are copied from
+ * plan_host (hipMemcpyAsync on `stream`) into a static device buffer of
+ * QG_CHAIN_STATIC_BYTES bytes that the library holds on each device until
+ * the process ends, and the chain kernel reads them there.  Allocates
+ * nothing.  plan_host must stay unchanged until the stream has run the call.
+ * A plan of more than QG_CHAIN_STATIC_BYTES bytes (qg_chain_plan_bytes of
+ * more than 511 links) is refused with QG_EUNSUPPORTED before any device
+ * work.  Every call on a device shares that device's buffer, and each call
+ * rewrites the whole plan it reads: calls that overlap on one device (other
+ * streams, other threads) race, as overlapping chain launches do anyway.
+ * Results are those of qgemv_chain with the same plan, bit for bit.
+ */
+#define QG_CHAIN_STATIC_BYTES 65536
+int qgemv_chain_noalloc(const void *plan_host, void *stream);
 /* Diagnostic: synchronises the device; returns 1 if any chain barrier timed
  * out since the previous call (and clears the record), 0 if none, -1 on a
  * HIP error. */

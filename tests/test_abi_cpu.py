@@ -4,6 +4,7 @@ made with arguments the host validation rejects."""
 import ctypes
 import os
 import re
+import struct
 
 import numpy as np
 import pytest
@@ -359,3 +360,19 @@ def test_nvfp4_argument_validation():
     assert L.qg_requant_q8_0_nvfp4(None, 64, 64, a, None) == q.QG_EINVAL
     assert L.qg_requant_q8_0_nvfp4(a, 64, 40, a, None) == q.QG_EINVAL
     assert q.dense_path(q.NVFP4, 6144, 4096, q.X_BF16, 8) == q.PATH_VALU       # no matrix-core route
+
+
+def test_chain_noalloc_refuses_on_the_host():
+    """qgemv_chain_noalloc's argument and size checks come before any device
+    work: no plan, a buffer that is not a plan, and a plan one link over the
+    static buffer's capacity."""
+    L = q.lib()
+    assert L.qg_chain_plan_bytes(511) <= q.CHAIN_STATIC_BYTES < L.qg_chain_plan_bytes(512)
+    assert L.qgemv_chain_noalloc(None, None) == q.QG_EINVAL
+    junk = (ctypes.c_uint8 * 256)()
+    assert L.qgemv_chain_noalloc(junk, None) == q.QG_EINVAL
+    # a header (magic, fmt, xt, m, count, grid, lds, part_off, out_off) of 512 links
+    hdr = struct.pack("<Iiiiiiqqq", 0x51474333, q.Q8_0, q.X_BF16, 1, 512, 256, 0, 0, 0)
+    buf = (ctypes.c_uint8 * L.qg_chain_plan_bytes(512)).from_buffer_copy(
+        hdr + bytes(L.qg_chain_plan_bytes(512) - len(hdr)))
+    assert L.qgemv_chain_noalloc(buf, None) == q.QG_EUNSUPPORTED
