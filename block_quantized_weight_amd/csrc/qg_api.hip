@@ -274,7 +274,32 @@ Plan make_plan(const Layout &lo, int M, bool dot, int maxslots_lds)
     int grid = g.ngroups;
     if (grid > 65535) grid = 65535;
     p.grid = grid;
+    p.threads = TPB;
     return p;
+}
+
+// Workgroup size of an unsplit plan (one tile per wave): as many waves as
+// put about one workgroup on every compute unit, at most WAVES.  Measured on
+// MI355X, one token, bf16 x, graph replay over rotated copies, us per launch
+// at 4 / 3 / 2 / 1 waves per workgroup:
+//   768 tiles (qkv 6144x2560)   Q8_0 6.97 / 6.75 / 7.49 / 7.13   Q4_0 6.11 / 5.88 / 6.98 / 5.94
+//   640 tiles (down 2560x9728)  Q8_0 10.03 / 9.65 / 11.33 / 10.86  MXFP4 7.40 / 7.19 / 8.97 / 8.27
+//   896 tiles (3584x2048)       Q8_0 5.00 / 5.79 / 5.13 / 5.02   Q4_0 4.19 / 5.05 / 4.68 / 4.32
+//   512 tiles (2048x2048)       Q8_0 4.62 / 4.37 / 4.17 / 4.24   MXFP4 3.71 / 3.63 / 3.57 / 3.78
+//   256 tiles (2048x1792)       Q8_0 5.12 / 4.95 / 4.69 / 4.50   MXFP4 4.27 / 3.97 / 3.92 / 3.75
+// (NVFP4 alike.)  A grid of more workgroups than compute units loses where
+// some units get two (896 tiles at three waves, 640-768 at two).
+void fit_workgroups(Plan &p)
+{
+    Geom &g = p.g;
+    if (g.KS != 1) return;
+    int64_t w = (g.tiles + QG_CUS - 1) / QG_CUS;
+    if (w >= WAVES) return;
+    if (w < 1) w = 1;
+    g.tpi = (int32_t)w;
+    g.ngroups = (int32_t)((g.tiles + w - 1) / w);
+    p.grid = g.ngroups > 65535 ? 65535 : g.ngroups;
+    p.threads = (int)(64 * w);
 }
 
 inline bool uses_dot(int fmt, int xt) { return fmt != QG_Q8_0 && xt == QG_BF16; }
@@ -368,10 +393,11 @@ MPlan make_mplan(const Layout &lo, int m, int passes = 0, int TG = 1)
 int one_batch(int fmt, int xt, const Plan &p, int64_t m)
 {
     const Geom &g = p.g;
-    if (g.nwin != 1 || m * g.wblk > (int64_t)ONE_XR * TPB || g.ngroups != p.grid) return 0;
+    if (g.nwin != 1 || m * g.wblk > (int64_t)ONE_XR * p.threads || g.ngroups != p.grid) return 0;
     const int u = one_batch_u(fmt, (int)m, (g.S + g.KS - 1) / g.KS);
     if (!u) return 0;
-    int per_cu = one_waves(fmt, xt == QG_BF16, u);
+    // workgroups per compute unit: by registers (one_waves per SIMD) and by LDS
+    int per_cu = one_waves(fmt, xt == QG_BF16, u) * WAVES / (p.threads / 64);
     const int lds_cu = p.lds > 0 ? (int)((160 * 1024) / p.lds) : per_cu;
     if (lds_cu < per_cu) per_cu = lds_cu;
     return p.grid <= per_cu * QG_CUS ? u : 0;
@@ -403,6 +429,7 @@ int dense(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
     }
     const bool dot = uses_dot(fmt, xt);
     Plan p = make_plan(lo, (int)m, dot, (int)m);
+    fit_workgroups(p);
     p.g.w = (const uint8_t *)w;
     const int u = one_batch(fmt, xt, p, m);
     dense_fn f = u ? (fmt == QG_Q8_0 ? dense_one_kernel_q8_0(xt, (int)m, u)
@@ -413,7 +440,7 @@ int dense(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
                       : fmt == QG_MXFP4 ? dense_kernel_mxfp4(xt, (int)m) : dense_kernel_nvfp4(xt, (int)m));
     void *args[] = {(void *)&p.g, (void *)&x, (void *)&y};
     if (allow_lds((const void *)f, p.lds) != hipSuccess) return QG_EHIP;
-    hipError_t e = hipLaunchKernel((const void *)f, dim3(p.grid), dim3(TPB), args, p.lds, as_stream(stream));
+    hipError_t e = hipLaunchKernel((const void *)f, dim3(p.grid), dim3(p.threads), args, p.lds, as_stream(stream));
     return e == hipSuccess ? launch_status() : QG_EHIP;
 }
 
@@ -651,7 +678,9 @@ int qg_dense_path(int fmt, int64_t n, int64_t k, int xt, int64_t m)
     if (m < 1 || m > QG_MAX_M) return -QG_EINVAL;
     const Layout lo = make_layout(fmt, n, k);
     if (mfma_fits(lo, xt, m)) return QG_PATH_MFMA;
-    return one_batch(fmt, xt, make_plan(lo, (int)m, uses_dot(fmt, xt), (int)m), m) ? QG_PATH_VALU_ONE : QG_PATH_VALU;
+    Plan p = make_plan(lo, (int)m, uses_dot(fmt, xt), (int)m);
+    fit_workgroups(p);
+    return one_batch(fmt, xt, p, m) ? QG_PATH_VALU_ONE : QG_PATH_VALU;
 }
 
 int qgemv_q8_0(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)

@@ -909,12 +909,12 @@ __device__ __forceinline__ void dense_one_pass(const Geom &g, const void *__rest
     const int tile = blockIdx.x * g.tpi + tsub;
     const int total = M * g.wblk;
 
-    // activation blocks idx = thread + r * TPB: token idx / wblk, block idx % wblk
+    // activation blocks idx = thread + r * blockDim: token idx / wblk, block idx % wblk
     // (blocks past the row or past the call load block 0 of token 0 and stage zeros)
     uint4 raw[ONE_XR][8];
 #pragma unroll
     for (int r = 0; r < ONE_XR; ++r) {
-        const int idx = threadIdx.x + r * TPB;
+        const int idx = threadIdx.x + r * (int)blockDim.x;
         const int t = idx / g.wblk, bl = idx - t * g.wblk;
         const bool ok = idx < total && bl < g.nb;
         const int64_t off = ok ? (int64_t)t * g.k + (int64_t)bl * QK : 0;
@@ -936,7 +936,7 @@ __device__ __forceinline__ void dense_one_pass(const Geom &g, const void *__rest
 
 #pragma unroll
     for (int r = 0; r < ONE_XR; ++r) {
-        const int idx = threadIdx.x + r * TPB;
+        const int idx = threadIdx.x + r * (int)blockDim.x;
         if (idx < total) {
             const int t = idx / g.wblk, bl = idx - t * g.wblk;
             uint4 q[8];
@@ -1187,6 +1187,7 @@ struct Plan {
     Geom g;
     size_t lds;
     int grid;
+    int threads;                 // workgroup size: 64 * (tiles per workgroup) * KS
 };
 
 typedef void (*dense_fn)(Geom, const void *, float *);
