@@ -41,6 +41,7 @@
 #include <stdint.h>
 #include <string.h>
 #include <stdlib.h>
+#include <type_traits>
 
 #include "../../include/qgemv.h"
 
@@ -371,12 +372,14 @@ __device__ __forceinline__ uint4 ld_stream16(const uint8_t *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ uint32_t ld_stream_u16(const uint16_t *p)
+// Narrow results: a caller that keeps them narrow until their use keeps the
+// widening (and so the wait for the load) at the use.
+__device__ __forceinline__ uint16_t ld_stream_u16(const uint16_t *p)
 {
     return __builtin_nontemporal_load((const QG_GLOBAL uint16_t *)p);
 }
 
-__device__ __forceinline__ uint32_t ld_stream_u8(const uint8_t *p)
+__device__ __forceinline__ uint8_t ld_stream_u8(const uint8_t *p)
 {
     return __builtin_nontemporal_load((const QG_GLOBAL uint8_t *)p);
 }
@@ -515,9 +518,13 @@ struct Engine {
     static constexpr int U = UB;
     static constexpr int QPB = x_quads(FMT, DOT);
 
+    // Scales stay in their stored width until step() widens them: widened at
+    // the load, the compiler placed the widening (and so a wait for the whole
+    // batch) ahead of the next batch's loads.
+    using ScaleT = std::conditional_t<FMT == QG_MXFP4, uint8_t, uint16_t>;
     struct Regs {
         uint4 c[U][P];
-        uint32_t s[U];
+        ScaleT s[U];
     };
 
     // Issues the loads of `cnt` (>= 1) steps jfirst, jfirst+KS, ...  Every call
@@ -733,6 +740,22 @@ struct Engine {
                 const int bl = j * g.L + slot - b0;
                 step(g, r.c[u], r.s[u], xs, bl, acc, xm);
             }
+        }
+        consume(r);
+    }
+
+    // Marks every register of a batch as read, those of steps past cnt too.
+    // Otherwise the compiler, reusing such a register later, cannot tell
+    // which load it waits for and waits for all of them, the next batch's
+    // included, which serialises the batches.  The loads past cnt repeat a
+    // step already read, so waiting for them here costs nothing.
+    static __device__ __forceinline__ void consume(const Regs &r)
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            asm volatile("" ::"v"((uint32_t)r.s[u]));
+#pragma unroll
+            for (int h = 0; h < P; ++h) asm volatile("" ::"v"(r.c[u][h].x), "v"(r.c[u][h].y), "v"(r.c[u][h].z), "v"(r.c[u][h].w));
         }
     }
 

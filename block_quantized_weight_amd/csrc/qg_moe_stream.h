@@ -202,7 +202,8 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
     const int tl = tile < g.tiles ? tile : 0;
     const int nsteps = (tile < g.tiles && ipart < ni) ? g.S : 0;
     auto work = [&](int i) {
-        const uint8_t *w = a.experts + (int64_t)it.e[i] * a.expert_bytes;
+        // i past the list (a wave with nothing to stream): expert 0, never used
+        const uint8_t *w = a.experts + (int64_t)(i < ni ? it.e[i] : 0) * a.expert_bytes;
         ItemWork iw;
         iw.ct = w + (int64_t)tl * g.ctb;
         iw.st = w + g.soff + (int64_t)tl * g.stb;
@@ -211,10 +212,13 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
         iw.KS = 1;
         return iw;
     };
+    // The first batch is loaded by every wave (waves with nothing to stream
+    // load one step of expert 0 and ignore it): with the load unconditional,
+    // the staging below waits for the activations only, not for these weights.
     typename E::Regs ra, rb;
-    if (nsteps > 0) {
+    {
         const ItemWork w0 = work(ipart);
-        E::load(g, w0.ct, w0.st, lane, w0.jf, min(nsteps, E::U), 1, ra);
+        E::load(g, w0.ct, w0.st, lane, w0.jf, max(1, min(nsteps, E::U)), 1, ra);
     }
 
     // stage every activation row of the call (row r = token for gate_up,
