@@ -19,11 +19,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-Q8_0, Q4_0, MXFP4, NVFP4 = 0, 1, 2, 3
+Q8_0, Q4_0, MXFP4, NVFP4, Q4_K, Q6_K = 0, 1, 2, 3, 4, 5
 X_F32, X_BF16 = 0, 1
 MOE_GATE_UP, MOE_DOWN = 0, 1
 ACT_NONE, ACT_SWIGLU = 0, 1
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17, NVFP4: 9}      # NVFP4: per 16 weights
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17, NVFP4: 9,      # NVFP4: per 16 weights
+               Q4_K: 144, Q6_K: 210}                          # K-quants: per 256 weights
+BLOCK_LEN = {Q8_0: 32, Q4_0: 32, MXFP4: 32, NVFP4: 16, Q4_K: 256, Q6_K: 256}
 
 
 def build(force=False):

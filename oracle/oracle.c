@@ -44,7 +44,29 @@
  *     decoded block scale; roundings are to nearest, ties to the even code,
  *     saturating at the largest finite value.  Its arithmetic is fp32, in the
  *     order written in orc_nvfp4_quantize.
- * Parity pins for every function live in tests/test_oracle.py.
+ *   - Q4_K and Q6_K are the K-quant super-block formats of the imp engine's
+ *     GGUF models (imp README, "Features" table, Quantization row; imp
+ *     release notes v0.7.0, Gemma-4 Q4_K_M decode; a Q4_K_M file mixes Q4_K
+ *     and Q6_K tensors).  The pages name them but do not define them; their
+ *     public GGUF definitions, 256 weights per super-block:
+ *       Q4_K, 144 bytes: d (fp16), dmin (fp16), 12 bytes of 6-bit scales and
+ *         mins, 128 bytes of 4-bit codes.  Sub-block j (weights 32j..32j+31)
+ *         has scale sc_j and min m_j: for j < 4, sc_j = s[j] & 63 and
+ *         m_j = s[j+4] & 63; for j >= 4, sc_j = (s[j+4] & 15) | (s[j-4] >> 6) << 4
+ *         and m_j = (s[j+4] >> 4) | (s[j] >> 6) << 4.  The codes of the 64
+ *         weights 64c..64c+63 are the 32 bytes qs[32c..32c+31]: weight 64c+l
+ *         is the low nibble of qs[32c+l], weight 64c+32+l its high nibble.
+ *         w = d * sc_j * q - dmin * m_j.
+ *       Q6_K, 210 bytes: ql (128 bytes, low 4 bits), qh (64 bytes, high 2
+ *         bits), 16 int8 scales (one per 16 weights), d (fp16).  Weight
+ *         128h + 32r + l (h < 2, r < 4, l < 32) has low bits from
+ *         ql[64h + l + 32(r & 1)] (low nibble for r < 2, high for r >= 2),
+ *         high bits (qh[32h + l] >> 2r) & 3, scale sc[8h + 2r + l / 16], and
+ *         w = d * sc * (q - 32), q = low | high << 4.
+ *     The value is the exact real number of these products (the reading
+ *     taken: fp64 here, where it is exact).
+ * Parity pins for every function live in tests/test_oracle.py (K-quants:
+ * tests/test_oracle_kquants.py).
  */
 #include <math.h>
 #include <stdint.h>
@@ -54,7 +76,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_Q8_0 = 0, ORC_Q4_0 = 1, ORC_MXFP4 = 2, ORC_NVFP4 = 3 };
+enum { ORC_Q8_0 = 0, ORC_Q4_0 = 1, ORC_MXFP4 = 2, ORC_NVFP4 = 3, ORC_Q4_K = 4, ORC_Q6_K = 5 };
 
 /* Threads an OpenMP region of the oracle uses (1 without OpenMP). */
 int orc_threads(void)
@@ -138,18 +160,22 @@ double orc_e4m3(uint8_t b)
     return s ? -mag : mag;
 }
 
-/* Bytes of one canonical block (32 weights; 16 for NVFP4). */
+/* Bytes of one canonical block (32 weights; 16 for NVFP4, 256 for the K-quants). */
 static int block_bytes(int fmt)
 {
-    return fmt == ORC_Q8_0 ? 34 : fmt == ORC_Q4_0 ? 18 : fmt == ORC_MXFP4 ? 17 : fmt == ORC_NVFP4 ? 9 : 0;
+    return fmt == ORC_Q8_0 ? 34 : fmt == ORC_Q4_0 ? 18 : fmt == ORC_MXFP4 ? 17 : fmt == ORC_NVFP4 ? 9
+         : fmt == ORC_Q4_K ? 144 : fmt == ORC_Q6_K ? 210 : 0;
 }
 
-static int block_len(int fmt) { return fmt == ORC_NVFP4 ? 16 : 32; }
+static int block_len(int fmt) { return fmt == ORC_NVFP4 ? 16 : (fmt == ORC_Q4_K || fmt == ORC_Q6_K) ? 256 : 32; }
+
+/* k must be a multiple of 32, and of the super-block (256) for the K-quants. */
+static int bad_k(int fmt, int64_t k) { return k <= 0 || (k % 32) != 0 || (k % block_len(fmt)) != 0; }
 
 /* Bytes of one canonical n x k tensor (NVFP4: blocks, then the fp32 tensor scale). */
 int64_t orc_tensor_bytes(int fmt, int64_t n, int64_t k)
 {
-    if (block_bytes(fmt) == 0 || n <= 0 || k <= 0 || (k % 32) != 0)
+    if (block_bytes(fmt) == 0 || n <= 0 || bad_k(fmt, k))
         return -1;
     return n * (k / block_len(fmt)) * (int64_t)block_bytes(fmt) + (fmt == ORC_NVFP4 ? 4 : 0);
 }
@@ -163,9 +189,50 @@ static double nvfp4_tensor_scale(const uint8_t *blocks, int64_t n, int64_t k)
     return (double)v.f;
 }
 
-/* Weight i (0..31) of one canonical block. */
+/* Q4_K sub-block j's 6-bit scale and min. */
+static void q4k_scale_min(const uint8_t *s, int j, int *sc, int *m)
+{
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *m = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+        *m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+/* Weight i (0..255) of a Q4_K super-block. */
+static double q4k_weight(const uint8_t *blk, int i)
+{
+    const double d = orc_fp16((uint16_t)(blk[0] | (blk[1] << 8)));
+    const double dmin = orc_fp16((uint16_t)(blk[2] | (blk[3] << 8)));
+    int sc, m;
+    q4k_scale_min(blk + 4, i / 32, &sc, &m);
+    const int c = i / 64, l = i % 64;
+    const uint8_t byte = blk[16 + 32 * c + (l % 32)];
+    const int q = l < 32 ? (byte & 15) : (byte >> 4);
+    return d * sc * q - dmin * m;
+}
+
+/* Weight i (0..255) of a Q6_K super-block. */
+static double q6k_weight(const uint8_t *blk, int i)
+{
+    const int h = i / 128, r = (i % 128) / 32, l = i % 32;
+    const uint8_t lo_byte = blk[64 * h + l + 32 * (r & 1)];
+    const int lo = r < 2 ? (lo_byte & 15) : (lo_byte >> 4);
+    const int hi = (blk[128 + 32 * h + l] >> (2 * r)) & 3;
+    const int sc = (int8_t)blk[192 + 8 * h + 2 * r + l / 16];
+    const double d = orc_fp16((uint16_t)(blk[208] | (blk[209] << 8)));
+    return d * sc * ((lo | (hi << 4)) - 32);
+}
+
+/* Weight i (0..31; 0..15 for NVFP4, 0..255 for the K-quants) of one canonical block. */
 static double block_weight(int fmt, const uint8_t *blk, int i)
 {
+    if (fmt == ORC_Q4_K)
+        return q4k_weight(blk, i);
+    if (fmt == ORC_Q6_K)
+        return q6k_weight(blk, i);
     if (fmt == ORC_Q8_0) {
         double d = orc_fp16((uint16_t)(blk[0] | (blk[1] << 8)));
         return d * (double)(int8_t)blk[2 + i];
@@ -214,7 +281,7 @@ static double tensor_scale(int fmt, const uint8_t *blocks, int64_t n, int64_t k)
 
 static int check(int fmt, int64_t n, int64_t k, int xt)
 {
-    if (block_bytes(fmt) == 0 || n <= 0 || k <= 0 || (k % 32) != 0)
+    if (block_bytes(fmt) == 0 || n <= 0 || bad_k(fmt, k))
         return 1;
     if (xt != ORC_X_F32 && xt != ORC_X_BF16)
         return 1;

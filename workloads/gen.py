@@ -11,8 +11,13 @@ oracle consume; little-endian, scale first, one block = 32 weights along K):
 * NVFP4 (9 B per 16 weights): one FP8 E4M3 scale byte, then 8 bytes; byte j
   holds element j in its low nibble and element j+8 in its high nibble (E2M1
   codes).  A tensor ends with its fp32 scale (4 bytes, little-endian).
+* Q4_K (144 B per 256 weights): fp16 d, fp16 dmin, 12 bytes of packed 6-bit
+  sub-block scales and mins, 128 bytes of 4-bit codes (the GGUF super-block).
+* Q6_K (210 B per 256 weights): 128 bytes of low code bits, 64 bytes of high
+  code bits, 16 int8 scales, fp16 d (the GGUF super-block).
 
-A matrix of N rows by K columns is N*(K/32) blocks, row-major.
+A matrix of N rows by K columns is N*(K/32) blocks (N*(K/256) super-blocks
+for the K-quants), row-major.
 
 Seeds follow numpy.random.SeedSequence([2026, config, matrix, role]) so every
 input of every workload is reproducible on any host.
@@ -20,9 +25,12 @@ input of every workload is reproducible on any host.
 import numpy as np
 
 QK = 32
-FMT_Q8_0, FMT_Q4_0, FMT_MXFP4, FMT_NVFP4 = 0, 1, 2, 3
-FMT_NAMES = {FMT_Q8_0: "q8_0", FMT_Q4_0: "q4_0", FMT_MXFP4: "mxfp4", FMT_NVFP4: "nvfp4"}
-BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4_0: 18, FMT_MXFP4: 17, FMT_NVFP4: 9}   # NVFP4 per 16 weights
+FMT_Q8_0, FMT_Q4_0, FMT_MXFP4, FMT_NVFP4, FMT_Q4_K, FMT_Q6_K = 0, 1, 2, 3, 4, 5
+FMT_NAMES = {FMT_Q8_0: "q8_0", FMT_Q4_0: "q4_0", FMT_MXFP4: "mxfp4", FMT_NVFP4: "nvfp4", FMT_Q4_K: "q4_k",
+             FMT_Q6_K: "q6_k"}
+BLOCK_BYTES = {FMT_Q8_0: 34, FMT_Q4_0: 18, FMT_MXFP4: 17, FMT_NVFP4: 9,   # NVFP4 per 16 weights
+               FMT_Q4_K: 144, FMT_Q6_K: 210}                              # K-quants per 256 weights
+BLOCK_LEN = {FMT_Q8_0: 32, FMT_Q4_0: 32, FMT_MXFP4: 32, FMT_NVFP4: 16, FMT_Q4_K: 256, FMT_Q6_K: 256}
 
 
 def canon_bytes(fmt, n, k):
@@ -30,7 +38,12 @@ def canon_bytes(fmt, n, k):
     the 4-byte fp32 tensor scale)."""
     if fmt == FMT_NVFP4:
         return n * (k // 16) * 9 + 4
-    return n * (k // QK) * BLOCK_BYTES[fmt]
+    return n * (k // BLOCK_LEN[fmt]) * BLOCK_BYTES[fmt]
+
+
+def bytes_per_weight(fmt):
+    """Canonical bytes per weight (the NVFP4 tensor scale left out)."""
+    return BLOCK_BYTES[fmt] / BLOCK_LEN[fmt]
 
 ROLES = {"codes": 0, "scales": 1, "x": 2, "router": 3, "h": 4, "gamma": 5, "res": 6}
 
@@ -135,6 +148,39 @@ def nvfp4_tensor(n, k, rng_codes, rng_scales, ts=None):
     return np.concatenate([body.reshape(-1), tail])
 
 
+def _f16_bits(v):
+    return np.asarray(v, dtype=np.float16).view(np.uint16)
+
+
+def q4_k_blocks(n, k, rng_codes, rng_scales):
+    """Canonical Q4_K super-blocks [n, k/256, 144]: d and dmin fp16 drawn
+    uniform in [1e-4, 1e-3], the 12 scale/min bytes and the 128 code bytes
+    uniform over all byte values (so every 6-bit scale and min and every
+    4-bit code occurs)."""
+    ns = k // 256
+    out = np.empty((n, ns, 144), dtype=np.uint8)
+    d = _f16_bits(rng_scales.uniform(1e-4, 1e-3, size=(n, ns)))
+    dm = _f16_bits(rng_scales.uniform(1e-4, 1e-3, size=(n, ns)))
+    out[:, :, 0], out[:, :, 1] = d & 0xFF, d >> 8
+    out[:, :, 2], out[:, :, 3] = dm & 0xFF, dm >> 8
+    out[:, :, 4:16] = rng_scales.integers(0, 256, size=(n, ns, 12), dtype=np.uint8)
+    out[:, :, 16:] = rng_codes.integers(0, 256, size=(n, ns, 128), dtype=np.uint8)
+    return out
+
+
+def q6_k_blocks(n, k, rng_codes, rng_scales):
+    """Canonical Q6_K super-blocks [n, k/256, 210]: code bytes (low and high
+    bits) uniform over all byte values, int8 scales uniform in [-128, 127], d
+    fp16 drawn uniform in [1e-6, 1e-5] with a random sign."""
+    ns = k // 256
+    out = np.empty((n, ns, 210), dtype=np.uint8)
+    out[:, :, :192] = rng_codes.integers(0, 256, size=(n, ns, 192), dtype=np.uint8)
+    out[:, :, 192:208] = rng_scales.integers(0, 256, size=(n, ns, 16), dtype=np.uint8)
+    d = _f16_bits(rng_scales.uniform(1e-6, 1e-5, size=(n, ns)) * rng_scales.choice([-1.0, 1.0], size=(n, ns)))
+    out[:, :, 208], out[:, :, 209] = d & 0xFF, d >> 8
+    return out
+
+
 def blocks_for(fmt, n, k, config, matrix):
     """Canonical blocks of one matrix of a workload, drawn with the workload seeds."""
     rc, rs = rng_for(config, matrix, "codes"), rng_for(config, matrix, "scales")
@@ -146,6 +192,10 @@ def blocks_for(fmt, n, k, config, matrix):
         return mxfp4_blocks(n, k, rc, rs)
     if fmt == FMT_NVFP4:
         return nvfp4_tensor(n, k, rc, rs)
+    if fmt == FMT_Q4_K:
+        return q4_k_blocks(n, k, rc, rs)
+    if fmt == FMT_Q6_K:
+        return q6_k_blocks(n, k, rc, rs)
     raise ValueError(fmt)
 
 
