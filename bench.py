@@ -47,13 +47,15 @@ def parse():
     ap.add_argument("--no-events", action="store_true", help="skip the roofline / per-shape timing pass")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
-    ap.add_argument("--workload", choices=["c2", "c2f", "c2n", "c0", "c1", "c3", "c4", "gemm", "stream"], default="c2",
+    ap.add_argument("--workload", choices=["c2", "c2f", "c2n", "c0", "c1", "c3", "c4", "gemm", "stream", "kq"],
+                    default="c2",
                     help="c2: the full Q8_0 decode sweep (the headline line); c2f: the same sweep with the decode "
                          "step's neighbours fused in (RMSNorm, SwiGLU, residual; qgemv_fused) next to the plain "
                          "sweep; c0/c1/c3/c4: the other workloads, each timed over >= 1 GiB of distinct weight "
                          "copies so the device-side cache cannot serve repeated reads; gemm: qgemm on the c3 "
                          "matrices at 16..128 tokens; stream: the read-only streaming ceiling over a 4 GiB buffer; "
-                         "c2n: the c2 sweep through the NVFP4 decode cache (Q8_0 re-quantized at load)")
+                         "c2n: the c2 sweep through the NVFP4 decode cache (Q8_0 re-quantized at load); "
+                         "kq: the c2 decode layer's matrices in Q4_K and Q6_K")
     ap.add_argument("--tokens", default="16,32,64,128",
                     help="gemm workload: the token counts to run (comma-separated, 1..128)")
     ap.add_argument("--quiet", action="store_true")
@@ -135,9 +137,10 @@ def run_other(args):
         line.update(extra)
         print(json.dumps(line), flush=True)
 
-    def dense_case(cfg, mats, xt, ms, label):
-        """mats: [(name, n, k, matrix index)]; times each matrix and the whole set."""
-        fmt = wl.CONFIGS[cfg]["fmt"]
+    def dense_case(cfg, mats, xt, ms, label, fmt=None):
+        """mats: [(name, n, k, matrix index)]; times each matrix and the whole set
+        (fmt: the weight format, by default the config's)."""
+        fmt = wl.CONFIGS[cfg]["fmt"] if fmt is None else fmt
         wsz = sum(q.packed_bytes(fmt, n, k) for _, n, k, _ in mats)
         reps = copies_for(wsz)
         ws = {}
@@ -157,7 +160,7 @@ def run_other(args):
             set_bytes = 0
             useful_flop = issued_flop = 0
             for name, n, k, j in mats:
-                b = n * (k // 32) * wl.BLOCK_BYTES[fmt] + m * k * xb + m * n * 4
+                b = wl.canon_bytes(fmt, n, k) + m * k * xb + m * n * 4
                 set_bytes += b
                 path = q.dense_path(fmt, n, k, q.X_F32 if xt == "f32" else q.X_BF16, m)
                 if path == q.PATH_MFMA:
@@ -254,6 +257,12 @@ def run_other(args):
         gemm_case(3, [("qkv", 6144, 4096, 0), ("gate_up", 24576, 4096, 1), ("down", 4096, 12288, 2)],
                   [int(t) for t in args.tokens.split(",")],
                   "q4_0 qgemm, 8b-like: qkv 6144x4096 + gate_up 24576x4096 + down 4096x12288")
+    elif args.workload == "kq":
+        # the decode layer of the full sweep's shapes in the K-quant formats
+        layer = [(nm, n, k, j) for j, (nm, n, k) in enumerate(wl.configs.C2_LAYER_MATS)]
+        for fmt, fname in ((q.Q4_K, "q4_k"), (q.Q6_K, "q6_k")):
+            dense_case(2, layer, "bf16", [1], f"{fname} decode layer: qkv 6144x2560 + o 2560x4096 + gate_up "
+                       "19456x2560 + down 2560x9728, x bf16", fmt=fmt)
     elif args.workload == "c0":
         dense_case(0, [("w", 2048, 2048, 0)], "f32", [1], "q8_0 2048x2048, x fp32")
     elif args.workload == "c1":

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libqgemv.so")
 
 # enums of include/qgemv.h
 QG_OK, QG_EINVAL, QG_EUNSUPPORTED, QG_EALIGN, QG_EHIP = 0, 1, 2, 3, 4
-Q8_0, Q4_0, MXFP4, NVFP4 = 0, 1, 2, 3
+Q8_0, Q4_0, MXFP4, NVFP4, Q4_K, Q6_K = 0, 1, 2, 3, 4, 5
 X_F32, X_BF16 = 0, 1
 MOE_GATE_UP, MOE_DOWN_COMBINE = 0, 1
 MAX_M = 8
@@ -23,10 +23,14 @@ MAX_GEMM_M = 128
 PATH_VALU, PATH_MFMA, PATH_VALU_ONE = 0, 1, 2
 ACT_NONE, ACT_SWIGLU = 0, 1
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, MXFP4: 17, NVFP4: 18}     # canonical bytes per 32 weights
+SUPERBLOCK_BYTES = {Q4_K: 144, Q6_K: 210}                     # K-quants: canonical bytes per 256 weights
 
 
 def canon_bytes(fmt, n, k):
-    """Bytes of one canonical n x k tensor (NVFP4: its blocks, then the 4-byte tensor scale)."""
+    """Bytes of one canonical n x k tensor (NVFP4: its blocks, then the 4-byte
+    tensor scale; K-quants: super-blocks of 256 weights)."""
+    if fmt in SUPERBLOCK_BYTES:
+        return n * (k // 256) * SUPERBLOCK_BYTES[fmt]
     return n * (k // 32) * BLOCK_BYTES[fmt] + (4 if fmt == NVFP4 else 0)
 
 # exported functions: name -> (restype, argtypes)
@@ -46,6 +50,8 @@ SIGNATURES = {
     "qgemv_q4_0": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_mxfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qgemv_nvfp4": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
+    "qgemv_q4_k": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
+    "qgemv_q6_k": (_i, [_vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qg_requant_q8_0_nvfp4": (_i, [_vp, _i64, _i64, _vp, _vp]),
     "qgemm": (_i, [_i, _vp, _i64, _i64, _vp, _i, _i64, _vp, _vp]),
     "qg_gemm_path": (_i, [_i, _i64, _i64, _i, _i64]),
@@ -80,7 +86,8 @@ class Layout(ctypes.Structure):
                 ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("steps", ctypes.c_int64),
                 ("tiles", ctypes.c_int64), ("code_tile_bytes", ctypes.c_int64),
                 ("scale_tile_bytes", ctypes.c_int64), ("scale_offset", ctypes.c_int64),
-                ("packed_bytes", ctypes.c_int64), ("tensor_scale_offset", ctypes.c_int64)]
+                ("packed_bytes", ctypes.c_int64), ("tensor_scale_offset", ctypes.c_int64),
+                ("high_offset", ctypes.c_int64), ("superblock_offset", ctypes.c_int64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
@@ -141,7 +148,7 @@ def _np_ptr(a):
 def pack_host(fmt, canon, n, k):
     """Canonical blocks (numpy uint8) -> packed bytes (numpy uint8), on the CPU."""
     c = np.ascontiguousarray(canon, dtype=np.uint8).reshape(-1)
-    if fmt not in BLOCK_BYTES or c.size != canon_bytes(fmt, n, k):
+    if (fmt not in BLOCK_BYTES and fmt not in SUPERBLOCK_BYTES) or c.size != canon_bytes(fmt, n, k):
         raise ValueError("canonical array size does not match (fmt, n, k)")
     out = np.empty(packed_bytes(fmt, n, k), dtype=np.uint8)
     _check("qg_pack_host", lib().qg_pack_host(fmt, _np_ptr(c), n, k, _np_ptr(out)))
@@ -228,7 +235,8 @@ def read_stream(buf, sink=None, stream=None):
     return sink
 
 
-_GEMV = {Q8_0: "qgemv_q8_0", Q4_0: "qgemv_q4_0", MXFP4: "qgemv_mxfp4", NVFP4: "qgemv_nvfp4"}
+_GEMV = {Q8_0: "qgemv_q8_0", Q4_0: "qgemv_q4_0", MXFP4: "qgemv_mxfp4", NVFP4: "qgemv_nvfp4", Q4_K: "qgemv_q4_k",
+         Q6_K: "qgemv_q6_k"}
 
 
 def qgemv(fmt, w_packed, n, k, x, y=None, stream=None):

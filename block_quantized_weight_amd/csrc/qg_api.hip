@@ -20,7 +20,41 @@ __global__ void k_dequant(LayoutArgs a, const uint8_t *__restrict__ packed, floa
         if (row >= a.n || blk >= a.nb) continue;
         const uint4 c0 = *(const uint4 *)(packed + co);
         float *out = w + row * k + blk * QK;
-        if (a.fmt == QG_Q8_0) {
+        if (is_kq(a.fmt)) {
+            // each weight the single rounding of its exact value
+            const uint32_t sb = packed[so] | (packed[so + 1] << 8);
+            const uint32_t swd = *(const uint32_t *)(packed + a.sboff + (row * a.nsb + (blk >> 3)) * 4);
+            uint32_t c[4] = {c0.x, c0.y, c0.z, c0.w};
+            if (a.fmt == QG_Q4_K) {
+                const float D = f16_bits_to_f32(swd & 0xFFFF) * (float)(sb & 63);
+                const float Mn = -(f16_bits_to_f32(swd >> 16) * (float)((sb >> 8) & 63));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v[8];
+                    q4_unpack8(c[i], v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) out[8 * i + e] = __builtin_fmaf(D, __builtin_fmaf(16.0f, v[e], 8.0f), Mn);
+                }
+            } else {
+                const float d = f16_bits_to_f32(swd & 0xFFFF);
+                const float Da = d * (float)(int8_t)(sb & 0xFF), Db = d * (float)(int8_t)(sb >> 8);
+                const uint2 hh = *(const uint2 *)(packed + kq_high_off(a, rec));
+                const uint32_t hw[2] = {hh.x, hh.y};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int f = 2 * (q & 1) + e;
+                        const uint32_t H = hw[q >> 1];
+                        const uint32_t hp = f == 0 ? H << 4 : f == 1 ? H << 2 : f == 2 ? H : H >> 2;
+                        uint32_t Q = ((c[q] >> (4 * e)) & 0x0F0F0F0Fu) | (hp & 0x30303030u);
+                        const uint32_t sg = Q & 0x20202020u;
+                        Q |= (sg << 1) | (sg << 2);
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) out[8 * q + 4 * e + b] = (q < 2 ? Da : Db) * i8_at(Q, b);
+                    }
+            }
+        } else if (a.fmt == QG_Q8_0) {
             const uint4 c1 = *(const uint4 *)(packed + co + 1024);
             uint32_t s = packed[so] | (packed[so + 1] << 8);
             float d = f16_bits_to_f32(s);
@@ -89,6 +123,11 @@ __global__ void k_unpack(LayoutArgs a, const uint8_t *__restrict__ packed, uint8
 {
     const int64_t tid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (a.fmt == QG_NVFP4 && tid < 4) canon[a.cts + tid] = packed[a.tsoff + tid];      // the tensor scale
+    if (is_kq(a.fmt)) {             // one thread per super-block (its eight records share scale bytes)
+        for (int64_t u = tid; u < a.n * a.nsb; u += (int64_t)gridDim.x * blockDim.x)
+            unpack_superblock_kq(a, packed, canon, u / a.nsb, u % a.nsb);
+        return;
+    }
     for (int64_t r = tid; r < nrec; r += (int64_t)gridDim.x * blockDim.x)
         unpack_record(a, packed, canon, r);
 }
@@ -225,6 +264,7 @@ constexpr uintptr_t W_ALIGN = 256;
 int check_shape(int fmt, int64_t n, int64_t k)
 {
     if (!valid_fmt(fmt) || n <= 0 || k <= 0 || (k % QK) != 0) return QG_EINVAL;
+    if (is_kq(fmt) && (k % 256) != 0) return QG_EINVAL;         // whole super-blocks
     if (n > 0x7FFFFFFF || k > 0x7FFFFFFF) return QG_EUNSUPPORTED;
     return QG_OK;
 }
@@ -246,6 +286,10 @@ Plan make_plan(const Layout &lo, int M, bool dot, int maxslots_lds)
     g.stb = lo.stb;
     g.soff = lo.soff;
     g.tsoff = lo.tsoff;
+    g.hoff = lo.hoff;
+    g.htb = lo.htb;
+    g.sboff = lo.sboff;
+    g.nsb = (int32_t)lo.nsb;
     // activation window: as many steps as fit XBUDGET (at least one)
     const size_t per_block = (size_t)maxslots_lds * x_quads(lo.fmt, dot) * 16;
     int64_t sw_max = (int64_t)(XBUDGET / per_block) / lo.L;
@@ -302,7 +346,7 @@ void fit_workgroups(Plan &p)
     p.threads = (int)(64 * w);
 }
 
-inline bool uses_dot(int fmt, int xt) { return fmt != QG_Q8_0 && xt == QG_BF16; }
+inline bool uses_dot(int fmt, int xt) { return fmt != QG_Q8_0 && !is_kq(fmt) && xt == QG_BF16; }
 
 // Co-batches of at least this many bf16 tokens run on the matrix cores
 // (measured crossover on MI355X: the int8 codes' per-weight VALU cost makes
@@ -322,7 +366,8 @@ struct MPlan {
 // row, and tiles whose per-lane offsets fit in 32 bits.
 bool mfma_fits(const Layout &lo, int xt, int64_t m)
 {
-    if (lo.fmt == QG_NVFP4 || xt != QG_BF16 || m < mfma_min_m(lo.fmt) || lo.L > MFMA_MAX_L) return false;
+    if (lo.fmt == QG_NVFP4 || is_kq(lo.fmt) || xt != QG_BF16 || m < mfma_min_m(lo.fmt) || lo.L > MFMA_MAX_L)
+        return false;
     const int64_t tpw = lo.L >= 8 ? lo.L / 4 : 1;
     return lo.ctb * tpw < ((int64_t)1 << 31) && lo.stb * tpw < ((int64_t)1 << 31);
 }
@@ -434,10 +479,12 @@ int dense(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
     const int u = one_batch(fmt, xt, p, m);
     dense_fn f = u ? (fmt == QG_Q8_0 ? dense_one_kernel_q8_0(xt, (int)m, u)
                       : fmt == QG_Q4_0 ? dense_one_kernel_q4_0(xt, (int)m, u)
-                      : fmt == QG_MXFP4 ? dense_one_kernel_mxfp4(xt, (int)m, u) : dense_one_kernel_nvfp4(xt, (int)m, u))
+                      : fmt == QG_MXFP4 ? dense_one_kernel_mxfp4(xt, (int)m, u)
+                      : fmt == QG_NVFP4 ? dense_one_kernel_nvfp4(xt, (int)m, u) : dense_one_kernel_kq(fmt, xt, (int)m, u))
                    : (fmt == QG_Q8_0 ? dense_kernel_q8_0(xt, (int)m)
                       : fmt == QG_Q4_0 ? dense_kernel_q4_0(xt, (int)m)
-                      : fmt == QG_MXFP4 ? dense_kernel_mxfp4(xt, (int)m) : dense_kernel_nvfp4(xt, (int)m));
+                      : fmt == QG_MXFP4 ? dense_kernel_mxfp4(xt, (int)m)
+                      : fmt == QG_NVFP4 ? dense_kernel_nvfp4(xt, (int)m) : dense_kernel_kq(fmt, xt, (int)m));
     void *args[] = {(void *)&p.g, (void *)&x, (void *)&y};
     if (allow_lds((const void *)f, p.lds) != hipSuccess) return QG_EHIP;
     hipError_t e = hipLaunchKernel((const void *)f, dim3(p.grid), dim3(p.threads), args, p.lds, as_stream(stream));
@@ -593,6 +640,8 @@ int qg_layout(int fmt, int64_t n, int64_t k, qg_layout_t *out)
     out->scale_offset = lo.soff;
     out->packed_bytes = lo.total;
     out->tensor_scale_offset = lo.tsoff;
+    out->high_offset = lo.hoff;
+    out->superblock_offset = lo.sboff;
     return QG_OK;
 }
 
@@ -618,6 +667,12 @@ int qg_unpack_host(int fmt, const void *packed, int64_t n, int64_t k, void *cano
     const LayoutArgs a = layout_args(lo);
     const int64_t nrec = nrecords(lo);
     if (fmt == QG_NVFP4) memcpy((uint8_t *)canon + a.cts, (const uint8_t *)packed + a.tsoff, 4);
+    if (is_kq(fmt)) {
+        for (int64_t r = 0; r < n; ++r)
+            for (int64_t sbi = 0; sbi < a.nsb; ++sbi)
+                unpack_superblock_kq(a, (const uint8_t *)packed, (uint8_t *)canon, r, sbi);
+        return QG_OK;
+    }
     for (int64_t r = 0; r < nrec; ++r) unpack_record(a, (const uint8_t *)packed, (uint8_t *)canon, r);
     return QG_OK;
 }
@@ -703,6 +758,16 @@ int qgemv_nvfp4(const void *w, int64_t n, int64_t k, const void *x, int xt, int6
     return dense(QG_NVFP4, w, n, k, x, xt, m, y, stream);
 }
 
+int qgemv_q4_k(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
+{
+    return dense(QG_Q4_K, w, n, k, x, xt, m, y, stream);
+}
+
+int qgemv_q6_k(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)
+{
+    return dense(QG_Q6_K, w, n, k, x, xt, m, y, stream);
+}
+
 int qg_requant_q8_0_nvfp4(const void *canon_q8_0, int64_t n, int64_t k, void *nvfp4_packed, void *stream)
 {
     int st = check_shape(QG_NVFP4, n, k);
@@ -731,6 +796,7 @@ int qg_gemm_path(int fmt, int64_t n, int64_t k, int xt, int64_t m)
     if (st) return -st;
     if (xt != QG_F32 && xt != QG_BF16) return -QG_EINVAL;
     if (m < 1 || m > QG_MAX_GEMM_M) return -QG_EINVAL;
+    if (is_kq(fmt)) return -QG_EUNSUPPORTED;
     return gemm_fits(make_layout(fmt, n, k), xt) ? QG_PATH_MFMA : QG_PATH_VALU;
 }
 
@@ -741,6 +807,7 @@ int qgemm(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
     if (!w || !x || !y) return QG_EINVAL;
     if (xt != QG_F32 && xt != QG_BF16) return QG_EINVAL;
     if (m < 1 || m > QG_MAX_GEMM_M) return QG_EINVAL;
+    if (is_kq(fmt)) return QG_EUNSUPPORTED;
     if (!aligned(w, W_ALIGN) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
     const Layout lo = make_layout(fmt, n, k);
     if (gemm_fits(lo, xt)) {
@@ -788,6 +855,7 @@ int qgemv_fused(int fmt, const void *w, int64_t n, int64_t k, const void *x, int
     if (m < 1 || m > QG_MAX_M) return QG_EINVAL;
     if (norm_weight && !(norm_eps >= 0.0f && norm_eps <= 3.4e38f)) return QG_EINVAL;    // rejects NaN too
     if (act == QG_ACT_SWIGLU && (n % 2) != 0) return QG_EINVAL;
+    if (is_kq(fmt)) return QG_EUNSUPPORTED;
     if (!aligned(w, W_ALIGN) || !aligned(x, 16) || !aligned(y, yt == QG_F32 ? 4 : 2)) return QG_EALIGN;
     if ((norm_weight && !aligned(norm_weight, 16)) || (residual && !aligned(residual, 4))) return QG_EALIGN;
     const int64_t n_out = act == QG_ACT_SWIGLU ? n / 2 : n;
@@ -848,6 +916,7 @@ static int moe_impl(int fmt, const void *w_experts, int64_t n_experts, int64_t n
     if (st) return st;
     if (!w_experts || !topk_ids || !x || !y) return QG_EINVAL;
     if (fmt == QG_NVFP4) return QG_EUNSUPPORTED;   // per-expert tensor scales: not served by the expert kernels
+    if (is_kq(fmt)) return QG_EUNSUPPORTED;        // super-block formats: the dense product only
     if (xt != QG_F32 && xt != QG_BF16) return QG_EINVAL;
     if (yt != QG_F32 && yt != QG_BF16) return QG_EINVAL;
     if (mode != QG_MOE_GATE_UP && mode != QG_MOE_DOWN_COMBINE) return QG_EINVAL;
@@ -998,7 +1067,7 @@ int qg_chain_plan(int fmt, int xt, int64_t m, const qg_chain_link_t *links, int6
 {
     if (!valid_fmt(fmt) || (xt != QG_F32 && xt != QG_BF16) || m < 1 || m > QG_MAX_M) return QG_EINVAL;
     if (!links || !plan || count < 1) return QG_EINVAL;
-    if (fmt == QG_NVFP4) return QG_EUNSUPPORTED;
+    if (fmt == QG_NVFP4 || is_kq(fmt)) return QG_EUNSUPPORTED;
     if (count > (1 << 20)) return QG_EUNSUPPORTED;
     int dev = 0, cus = 0, occ = 0;
     if (hipGetDevice(&dev) != hipSuccess) return QG_EHIP;

@@ -61,7 +61,14 @@ struct Layout {
     int fmt, L, lsh, R, P, sb;
     int64_t n, k, nb, S, tiles;
     int64_t ctb, stb, soff, tsoff, total;   // tsoff: NVFP4 tensor scale (fp32), 0 otherwise
+    int64_t htb, hoff;           // Q6_K: high code bits, 8 B per record (S * 512 per tile), else 0
+    int64_t nsb, sboff;          // K-quants: super-blocks per row, per-row super-block words (4 B), else 0
+    int64_t used;                // end of the streams; [used, total) is padding (and the NVFP4 trailer)
 };
+
+// The K-quant super-block formats: 256 weights, eight 32-weight sub-blocks.
+__host__ __device__ constexpr bool is_kq(int fmt) { return fmt == QG_Q4_K || fmt == QG_Q6_K; }
+__host__ __device__ constexpr int kq_bytes(int fmt) { return fmt == QG_Q4_K ? 144 : 210; }
 
 // Staged form of one block of 32 activations in LDS: x_quads() 16-byte quads
 // (fp32, or bf16 pairs for the bf16 dot).
@@ -70,11 +77,16 @@ __host__ __device__ constexpr int x_quads(int fmt, bool dot) { return dot ? 4 : 
 // Canonical bytes per 32 weights (NVFP4: two 16-weight blocks of 9 bytes).
 inline int block_bytes(int fmt) { return fmt == QG_Q8_0 ? 34 : fmt == QG_MXFP4 ? 17 : 18; }
 
-inline bool valid_fmt(int fmt) { return fmt == QG_Q8_0 || fmt == QG_Q4_0 || fmt == QG_MXFP4 || fmt == QG_NVFP4; }
+inline bool valid_fmt(int fmt)
+{
+    return fmt == QG_Q8_0 || fmt == QG_Q4_0 || fmt == QG_MXFP4 || fmt == QG_NVFP4 || is_kq(fmt);
+}
 
-// Bytes of a canonical n x k tensor (NVFP4: blocks, then its fp32 tensor scale).
+// Bytes of a canonical n x k tensor (NVFP4: blocks, then its fp32 tensor
+// scale; K-quants: super-blocks of 256 weights).
 inline int64_t canon_bytes(int fmt, int64_t n, int64_t k)
 {
+    if (is_kq(fmt)) return n * (k / 256) * kq_bytes(fmt);
     return n * (k / 32) * block_bytes(fmt) + (fmt == QG_NVFP4 ? 4 : 0);
 }
 
@@ -122,7 +134,21 @@ inline Layout make_layout(int fmt, int64_t n, int64_t k)
     lo.ctb = lo.S * lo.P * 1024;
     lo.stb = lo.S * 64 * lo.sb;
     lo.soff = lo.tiles * lo.ctb;
-    lo.total = (lo.soff + lo.tiles * lo.stb + 255) / 256 * 256;   // experts stay 256-byte aligned
+    int64_t end = lo.soff + lo.tiles * lo.stb;
+    if (is_kq(fmt)) {
+        // Q6_K high code bits; then d (and dmin) per row and super-block,
+        // rows of the last tile's padding included
+        if (fmt == QG_Q6_K) {
+            lo.htb = lo.S * 512;
+            lo.hoff = end;
+            end += lo.tiles * lo.htb;
+        }
+        lo.nsb = k / 256;
+        lo.sboff = end;
+        end += lo.tiles * lo.R * lo.nsb * 4;
+    }
+    lo.used = end;
+    lo.total = (end + 255) / 256 * 256;   // experts stay 256-byte aligned
     lo.tsoff = 0;
     if (fmt == QG_NVFP4) {
         // the fp32 tensor scale in a 256-byte trailer of its own
@@ -225,6 +251,7 @@ struct LayoutArgs {
     int fmt, L, lsh, R, P, sb, bb;
     int64_t n, nb, S, tiles, ctb, stb, soff, end, total;   // [end, total) is tail padding
     int64_t tsoff, cts;          // NVFP4: tensor scale offsets, packed and canonical (else 0)
+    int64_t htb, hoff, nsb, sboff;   // K-quants (Layout)
 };
 
 inline LayoutArgs layout_args(const Layout &lo)
@@ -234,7 +261,8 @@ inline LayoutArgs layout_args(const Layout &lo)
     a.bb = block_bytes(lo.fmt);
     a.n = lo.n; a.nb = lo.nb; a.S = lo.S; a.tiles = lo.tiles;
     a.ctb = lo.ctb; a.stb = lo.stb; a.soff = lo.soff;
-    a.end = lo.soff + lo.tiles * lo.stb;
+    a.end = lo.used;
+    a.htb = lo.htb; a.hoff = lo.hoff; a.nsb = lo.nsb; a.sboff = lo.sboff;
     a.total = lo.total;
     a.tsoff = lo.tsoff;
     a.cts = lo.fmt == QG_NVFP4 ? lo.n * lo.nb * 18 : 0;
@@ -261,8 +289,162 @@ __host__ __device__ inline void record_geom(const LayoutArgs &a, int64_t rec, in
     *scale_off = a.soff + tile * a.stb + j * 64 * a.sb + lane * a.sb;
 }
 
+// ------------------------------------------------------- K-quant records
+// A K-quant record is one 32-weight sub-block (sub-block j = blk % 8 of
+// super-block blk / 8 of its row), in element order (weights 32j..32j+31 of
+// the super-block):
+//  Q4_K: codes as Q4_0 (packed byte B = t[2B] | t[2B+1] << 4, t = q ^ 8); the
+//        16-bit scale entry is sc | m << 8.
+//  Q6_K: with t = q ^ 32 (the 6-bit two's complement of q - 32): code dword a
+//        byte b = (t[8a+b] & 15) | (t[8a+4+b] & 15) << 4; high-bits dword h
+//        byte b holds t >> 4 of elements 16h+b, 16h+4+b, 16h+8+b, 16h+12+b in
+//        its bit pairs 0-1, 2-3, 4-5, 6-7; the scale entry is the two int8
+//        scales (elements 0..15 low byte, 16..31 high byte).
+//  The row's super-block word (d | dmin << 16 for Q4_K, d for Q6_K) sits in
+//  the super-block stream at sboff + (row * nsb + blk / 8) * 4.
+
+// Sub-block j's 6-bit scale and min of a Q4_K super-block's 12 scale bytes.
+__host__ __device__ inline void q4k_scale_min(const uint8_t *s, int j, int *sc, int *m)
+{
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *m = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+        *m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+// Byte offset of the Q6_K high bits of record rec.
+__host__ __device__ inline int64_t kq_high_off(const LayoutArgs &a, int64_t rec)
+{
+    const int64_t lane = rec & 63, rest = rec >> 6;
+    return a.hoff + (rest / a.S) * a.htb + (rest % a.S) * 512 + lane * 8;
+}
+
+__host__ __device__ inline void pack_record_kq(const LayoutArgs &a, const uint8_t *canon, uint8_t *packed, int64_t rec)
+{
+    int64_t row, blk, co, so;
+    record_geom(a, rec, &row, &blk, &co, &so);
+    uint8_t codes[16], hi[8];
+    for (int i = 0; i < 16; ++i) codes[i] = 0;
+    for (int i = 0; i < 8; ++i) hi[i] = 0;
+    uint32_t scale = 0, sbw = 0;
+    if (row < a.n && blk < a.nb) {
+        const int j = (int)(blk & 7);
+        const uint8_t *sb = canon + (row * a.nsb + (blk >> 3)) * kq_bytes(a.fmt);
+        uint8_t t[32];
+        if (a.fmt == QG_Q4_K) {
+            for (int l = 0; l < 32; ++l) {
+                const uint8_t byte = sb[16 + 32 * (j >> 1) + l];
+                t[l] = (uint8_t)(((j & 1) ? byte >> 4 : byte & 15) ^ 8);
+            }
+            for (int b = 0; b < 16; ++b) codes[b] = (uint8_t)(t[2 * b] | (t[2 * b + 1] << 4));
+            int sc, m;
+            q4k_scale_min(sb + 4, j, &sc, &m);
+            scale = (uint32_t)sc | ((uint32_t)m << 8);
+            sbw = (uint32_t)sb[0] | ((uint32_t)sb[1] << 8) | ((uint32_t)sb[2] << 16) | ((uint32_t)sb[3] << 24);
+        } else {
+            const int h = j >> 2, r = j & 3;
+            for (int l = 0; l < 32; ++l) {
+                const uint8_t lb = sb[64 * h + l + 32 * (r & 1)];
+                const int lo = r < 2 ? (lb & 15) : (lb >> 4);
+                const int hb = (sb[128 + 32 * h + l] >> (2 * r)) & 3;
+                t[l] = (uint8_t)((lo | (hb << 4)) ^ 32);
+            }
+            for (int q = 0; q < 4; ++q)
+                for (int b = 0; b < 4; ++b) codes[4 * q + b] = (uint8_t)((t[8 * q + b] & 15) | ((t[8 * q + 4 + b] & 15) << 4));
+            for (int q = 0; q < 2; ++q)
+                for (int b = 0; b < 4; ++b)
+                    hi[4 * q + b] = (uint8_t)((t[16 * q + b] >> 4) | ((t[16 * q + 4 + b] >> 4) << 2) |
+                                              ((t[16 * q + 8 + b] >> 4) << 4) | ((t[16 * q + 12 + b] >> 4) << 6));
+            scale = (uint32_t)sb[192 + 8 * h + 2 * r] | ((uint32_t)sb[192 + 8 * h + 2 * r + 1] << 8);
+            sbw = (uint32_t)sb[208] | ((uint32_t)sb[209] << 8);
+        }
+    }
+    for (int i = 0; i < 16; ++i) packed[co + i] = codes[i];
+    packed[so] = (uint8_t)(scale & 0xFF);
+    packed[so + 1] = (uint8_t)(scale >> 8);
+    if (a.fmt == QG_Q6_K) {
+        const int64_t ho = kq_high_off(a, rec);
+        for (int i = 0; i < 8; ++i) packed[ho + i] = hi[i];
+    }
+    if ((blk & 7) == 0 && blk < a.nb) {       // the row's super-block word (zero on padding rows)
+        const int64_t wo = a.sboff + (row * a.nsb + (blk >> 3)) * 4;
+        for (int i = 0; i < 4; ++i) packed[wo + i] = (uint8_t)(sbw >> (8 * i));
+    }
+}
+
+// Rebuilds canonical super-block s of row `row` from its eight records.
+__host__ __device__ inline void unpack_superblock_kq(const LayoutArgs &a, const uint8_t *packed, uint8_t *canon,
+                                                     int64_t row, int64_t s)
+{
+    uint8_t out[210];
+    const int nbytes = kq_bytes(a.fmt);
+    for (int i = 0; i < nbytes; ++i) out[i] = 0;
+    const int64_t wo = a.sboff + (row * a.nsb + s) * 4;
+    if (a.fmt == QG_Q4_K) {
+        for (int i = 0; i < 4; ++i) out[i] = packed[wo + i];
+    } else {
+        out[208] = packed[wo];
+        out[209] = packed[wo + 1];
+    }
+    const int64_t tile = row / a.R, rr = row % a.R;
+    for (int j = 0; j < 8; ++j) {
+        const int64_t blk = 8 * s + j;
+        const int64_t rec = ((tile * a.S) + (blk >> a.lsh)) * 64 + ((rr << a.lsh) | (blk & (a.L - 1)));
+        int64_t r2, b2, co, so;
+        record_geom(a, rec, &r2, &b2, &co, &so);
+        const uint32_t scale = (uint32_t)packed[so] | ((uint32_t)packed[so + 1] << 8);
+        uint8_t t[32];
+        if (a.fmt == QG_Q4_K) {
+            for (int b = 0; b < 16; ++b) {
+                t[2 * b] = (uint8_t)((packed[co + b] & 15) ^ 8);
+                t[2 * b + 1] = (uint8_t)((packed[co + b] >> 4) ^ 8);
+            }
+            for (int l = 0; l < 32; ++l) out[16 + 32 * (j >> 1) + l] |= (uint8_t)((j & 1) ? t[l] << 4 : t[l]);
+            const int sc = scale & 63, m = (scale >> 8) & 63;
+            uint8_t *sx = out + 4;
+            if (j < 4) {
+                sx[j] |= (uint8_t)sc;
+                sx[j + 4] |= (uint8_t)m;
+            } else {
+                sx[j + 4] |= (uint8_t)((sc & 15) | ((m & 15) << 4));
+                sx[j - 4] |= (uint8_t)((sc >> 4) << 6);
+                sx[j] |= (uint8_t)((m >> 4) << 6);
+            }
+        } else {
+            const int64_t ho = kq_high_off(a, rec);
+            for (int q = 0; q < 4; ++q)
+                for (int b = 0; b < 4; ++b) {
+                    t[8 * q + b] = packed[co + 4 * q + b] & 15;
+                    t[8 * q + 4 + b] = packed[co + 4 * q + b] >> 4;
+                }
+            for (int q = 0; q < 2; ++q)
+                for (int b = 0; b < 4; ++b) {
+                    const uint8_t hb = packed[ho + 4 * q + b];
+                    for (int f = 0; f < 4; ++f) t[16 * q + 4 * f + b] |= (uint8_t)(((hb >> (2 * f)) & 3) << 4);
+                }
+            const int h = j >> 2, r = j & 3;
+            for (int l = 0; l < 32; ++l) {
+                const int qv = t[l] ^ 32;
+                out[64 * h + l + 32 * (r & 1)] |= (uint8_t)(r < 2 ? (qv & 15) : (qv & 15) << 4);
+                out[128 + 32 * h + l] |= (uint8_t)((qv >> 4) << (2 * r));
+            }
+            out[192 + 8 * h + 2 * r] = (uint8_t)(scale & 0xFF);
+            out[192 + 8 * h + 2 * r + 1] = (uint8_t)(scale >> 8);
+        }
+    }
+    uint8_t *dst = canon + (row * a.nsb + s) * nbytes;
+    for (int i = 0; i < nbytes; ++i) dst[i] = out[i];
+}
+
 __host__ __device__ inline void pack_record(const LayoutArgs &a, const uint8_t *canon, uint8_t *packed, int64_t rec)
 {
+    if (is_kq(a.fmt)) {
+        pack_record_kq(a, canon, packed, rec);
+        return;
+    }
     int64_t row, blk, co, so;
     record_geom(a, rec, &row, &blk, &co, &so);
     uint8_t codes[32];
@@ -449,6 +631,8 @@ struct Geom {
     int32_t L, lsh, R, S, tiles;
     int64_t ctb, stb, soff;
     int64_t tsoff;               // NVFP4: byte offset of the fp32 tensor scale
+    int64_t hoff, htb, sboff;    // K-quants: high-bits stream (Q6_K), super-block words
+    int32_t nsb;                 // K-quants: super-blocks per row
     int32_t KS, ksh, tpi, ngroups;
     int32_t SW, nwin, wblk;      // steps per window, windows, blocks per window
 };
@@ -512,6 +696,34 @@ struct IdMap {
 // Steps per batch (loads in flight per lane before the first use).
 template <int FMT, bool DOT> struct Batch { static constexpr int U = (FMT == QG_Q8_0 || !DOT) ? 4 : 8; };
 
+// Per-lane extras of a K-quant batch: the row's super-block word of each
+// step, and for Q6_K the record's high code bits.
+template <int FMT, int U> struct KqRegs {};
+template <int U> struct KqRegs<QG_Q4_K, U> { uint32_t sw[U]; };
+template <int U> struct KqRegs<QG_Q6_K, U> { uint32_t sw[U]; uint2 hh[U]; };
+
+// Where a K-quant lane finds them: its tile's high-bits stream and its row's
+// super-block words.
+struct KqPtr {
+    const uint8_t *ht = nullptr;
+    const uint8_t *sbrow = nullptr;
+};
+
+__device__ __forceinline__ KqPtr kq_ptr(const Geom &g, int tl, int rl)
+{
+    KqPtr p;
+    p.ht = g.w + g.hoff + (int64_t)tl * g.htb;
+    p.sbrow = g.w + g.sboff + ((int64_t)tl * g.R + (rl >> g.lsh)) * g.nsb * 4;
+    return p;
+}
+
+__device__ __forceinline__ uint2 ld_stream8(const uint8_t *p)
+{
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_nontemporal_load((const QG_GLOBAL u32x2 *)p);
+    return make_uint2(v.x, v.y);
+}
+
 template <int FMT, bool XBF16, bool DOT, int M, int UB = Batch<FMT, DOT>::U>
 struct Engine {
     static constexpr int P = FMT == QG_Q8_0 ? 2 : 1;
@@ -522,7 +734,8 @@ struct Engine {
     // the load, the compiler placed the widening (and so a wait for the whole
     // batch) ahead of the next batch's loads.
     using ScaleT = std::conditional_t<FMT == QG_MXFP4, uint8_t, uint16_t>;
-    struct Regs {
+    static constexpr bool KQ = is_kq(FMT);
+    struct Regs : KqRegs<FMT, U> {
         uint4 c[U][P];
         ScaleT s[U];
     };
@@ -532,7 +745,7 @@ struct Engine {
     // hit, never used).  The fixed count keeps the compiler's vmcnt waits exact,
     // so a batch in flight overlaps the compute of the previous one.
     static __device__ __forceinline__ void load(const Geom &g, const uint8_t *ct, const uint8_t *st, int lane,
-                                                int jfirst, int cnt, int KS, Regs &r)
+                                                int jfirst, int cnt, int KS, Regs &r, const KqPtr &kp = KqPtr{})
     {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -544,6 +757,85 @@ struct Engine {
                 r.s[u] = ld_stream_u8(st + (int64_t)j * 64 + lane);
             else
                 r.s[u] = ld_stream_u16((const uint16_t *)st + (int64_t)j * 64 + lane);
+            if constexpr (KQ) {
+                // the word of the record's super-block (padding steps repeat the row's last)
+                const int sbi = min((j * g.L + (lane & (g.L - 1))) >> 3, g.nsb - 1);
+                r.sw[u] = *(const QG_GLOBAL uint32_t *)(kp.sbrow + sbi * 4);
+                if constexpr (FMT == QG_Q6_K) r.hh[u] = ld_stream8(kp.ht + (int64_t)j * 512 + lane * 8);
+            }
+        }
+    }
+
+    // K-quant record: its 32 weights formed exactly, then their products.
+    // Q4_K: w = d sc q - dmin m, rounded once (fma of exact fp32 factors).
+    // Q6_K: the integer q - 32 (exact), summed against x per 16 elements,
+    // each sum scaled by d sc (exact in fp32).
+    template <typename XMap = IdMap>
+    static __device__ __forceinline__ void step_kq(const Geom &g, const Regs &r, int u, const uint4 *xs, int bl,
+                                                   float acc[M], const XMap &xm = XMap())
+    {
+        const uint4 c = r.c[u][0];
+        const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+        const uint32_t sbits = r.s[u], swd = r.sw[u];
+        if constexpr (FMT == QG_Q4_K) {
+            const float D = f16_bits_to_f32(swd & 0xFFFF) * (float)(sbits & 63);
+            const float Mn = -(f16_bits_to_f32(swd >> 16) * (float)((sbits >> 8) & 63));
+            float wv[32];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                float v[8];
+                q4_unpack8(cw[a], v);           // (q - 8) / 16, exact
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wv[8 * a + e] = __builtin_fmaf(D, __builtin_fmaf(16.0f, v[e], 8.0f), Mn);
+            }
+#pragma unroll
+            for (int t = 0; t < M; ++t) {
+                if (t >= xm.count()) break;
+                float s = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float4 xq = __builtin_bit_cast(float4, xs[(xm(t) * 8 + i) * g.wblk + bl]);
+                    s = __builtin_fmaf(wv[4 * i], xq.x, s);
+                    s = __builtin_fmaf(wv[4 * i + 1], xq.y, s);
+                    s = __builtin_fmaf(wv[4 * i + 2], xq.z, s);
+                    s = __builtin_fmaf(wv[4 * i + 3], xq.w, s);
+                }
+                acc[t] += s;
+            }
+        } else {
+            const float d = f16_bits_to_f32(swd & 0xFFFF);
+            const float Da = d * (float)(int8_t)(sbits & 0xFF), Db = d * (float)(int8_t)(sbits >> 8);
+            const uint32_t hw[2] = {r.hh[u].x, r.hh[u].y};
+            float dv[32];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int f = 2 * (a & 1) + e;
+                    const uint32_t H = hw[a >> 1];
+                    const uint32_t hp = f == 0 ? H << 4 : f == 1 ? H << 2 : f == 2 ? H : H >> 2;
+                    uint32_t Q = ((cw[a] >> (4 * e)) & 0x0F0F0F0Fu) | (hp & 0x30303030u);
+                    const uint32_t sg = Q & 0x20202020u;      // bytes: 6-bit two's complement -> int8
+                    Q |= (sg << 1) | (sg << 2);
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) dv[8 * a + 4 * e + b] = i8_at(Q, b);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < M; ++t) {
+                if (t >= xm.count()) break;
+                float sh[2] = {0.0f, 0.0f};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float4 xq = __builtin_bit_cast(float4, xs[(xm(t) * 8 + i) * g.wblk + bl]);
+                    float &s = sh[i >> 2];
+                    s = __builtin_fmaf(dv[4 * i], xq.x, s);
+                    s = __builtin_fmaf(dv[4 * i + 1], xq.y, s);
+                    s = __builtin_fmaf(dv[4 * i + 2], xq.z, s);
+                    s = __builtin_fmaf(dv[4 * i + 3], xq.w, s);
+                }
+                acc[t] = __builtin_fmaf(Db, sh[1], __builtin_fmaf(Da, sh[0], acc[t]));
+            }
         }
     }
 
@@ -738,7 +1030,10 @@ struct Engine {
             if (u < cnt) {
                 const int j = jfirst + u * KS;
                 const int bl = j * g.L + slot - b0;
-                step(g, r.c[u], r.s[u], xs, bl, acc, xm);
+                if constexpr (KQ)
+                    step_kq(g, r, u, xs, bl, acc, xm);
+                else
+                    step(g, r.c[u], r.s[u], xs, bl, acc, xm);
             }
         }
         consume(r);
@@ -756,6 +1051,8 @@ struct Engine {
             asm volatile("" ::"v"((uint32_t)r.s[u]));
 #pragma unroll
             for (int h = 0; h < P; ++h) asm volatile("" ::"v"(r.c[u][h].x), "v"(r.c[u][h].y), "v"(r.c[u][h].z), "v"(r.c[u][h].w));
+            if constexpr (KQ) asm volatile("" ::"v"(r.sw[u]));
+            if constexpr (FMT == QG_Q6_K) asm volatile("" ::"v"(r.hh[u].x), "v"(r.hh[u].y));
         }
     }
 
@@ -779,8 +1076,10 @@ struct Engine {
         const bool active = tile < g.tiles;
         // inactive waves load (and ignore) tile 0, step 0, so that loads stay unconditional
         const int tl = active ? tile : 0;
+        KqPtr kp;
+        if constexpr (KQ) kp = kq_ptr(g, tl, threadIdx.x & 63);
         pass_core(g, x, sl, g.w + (int64_t)tl * g.ctb, g.w + g.soff + (int64_t)tl * g.stb, threadIdx.x & 63, active,
-                  staged, xs, acc, stg);
+                  staged, xs, acc, stg, kp);
     }
 
     // The pass with the lane's own tile bases (ct, st) and record lane rl:
@@ -790,7 +1089,7 @@ struct Engine {
     template <class ST>
     static __device__ __forceinline__ void pass_core(const Geom &g, const void *x, const Slots &sl, const uint8_t *ct,
                                                      const uint8_t *st, int rl, bool active, bool &staged, uint4 *xs,
-                                                     float acc[M], ST &stg)
+                                                     float acc[M], ST &stg, const KqPtr &kp = KqPtr{})
     {
         const int lane = rl, wave = threadIdx.x >> 6;
         const int KS = g.KS, kpart = wave & (KS - 1);
@@ -804,7 +1103,7 @@ struct Engine {
             const int nsteps = (active && jf < j1) ? (j1 - jf + KS - 1) / KS : 0;
             const int jlast = nsteps > 0 ? jf + (nsteps - 1) * KS : 0;
             Regs ra, rb;
-            load(g, ct, st, lane, nsteps > 0 ? jf : 0, max(1, min(nsteps, U)), KS, ra);
+            load(g, ct, st, lane, nsteps > 0 ? jf : 0, max(1, min(nsteps, U)), KS, ra, kp);
             if (g.nwin > 1 || !staged) {
                 __syncthreads();
                 stg.template run<M, FMT>(g, x, sl, w, xs);
@@ -816,13 +1115,13 @@ struct Engine {
             while (done < nsteps) {
                 const int cA = min(nsteps - done, U);
                 const int rB = nsteps - done - cA;
-                load(g, ct, st, lane, rB > 0 ? jf + (done + cA) * KS : jlast, rB > 0 ? min(rB, U) : 1, KS, rb);
+                load(g, ct, st, lane, rB > 0 ? jf + (done + cA) * KS : jlast, rB > 0 ? min(rB, U) : 1, KS, rb, kp);
                 compute(g, ra, cA, jf + done * KS, KS, slot, b0, xs, acc);
                 done += cA;
                 if (done >= nsteps) break;
                 const int cB = min(nsteps - done, U);
                 const int rA = nsteps - done - cB;
-                load(g, ct, st, lane, rA > 0 ? jf + (done + cB) * KS : jlast, rA > 0 ? min(rA, U) : 1, KS, ra);
+                load(g, ct, st, lane, rA > 0 ? jf + (done + cB) * KS : jlast, rA > 0 ? min(rA, U) : 1, KS, ra, kp);
                 compute(g, rb, cB, jf + done * KS, KS, slot, b0, xs, acc);
                 done += cB;
             }
@@ -911,7 +1210,7 @@ constexpr int QG_CUS = 256;             // compute units of the MI355X / MI350X
 // a workgroup has one wave per SIMD, so a compute unit holds this many.
 __host__ __device__ constexpr int one_waves(int fmt, bool xbf16, int u)
 {
-    return !xbf16 ? 2 : fmt == QG_Q8_0 ? 3 : u <= 8 ? 4 : u <= 12 ? 3 : 2;
+    return (!xbf16 || is_kq(fmt)) ? 2 : fmt == QG_Q8_0 ? 3 : u <= 8 ? 4 : u <= 12 ? 3 : 2;
 }
 
 // The workgroup's one-batch pass over its tile group (grid = ngroups): on
@@ -954,8 +1253,10 @@ __device__ __forceinline__ void dense_one_pass(const Geom &g, const void *__rest
     const uint8_t *ct = g.w + (int64_t)tl * g.ctb;
     const uint8_t *st = g.w + g.soff + (int64_t)tl * g.stb;
     const int nsteps = (active && kpart < g.S) ? (g.S - kpart + g.KS - 1) / g.KS : 0;
+    KqPtr kp;
+    if constexpr (is_kq(FMT)) kp = kq_ptr(g, tl, lane);
     typename E::Regs rw;
-    E::load(g, ct, st, lane, nsteps > 0 ? kpart : 0, max(1, nsteps), g.KS, rw);
+    E::load(g, ct, st, lane, nsteps > 0 ? kpart : 0, max(1, nsteps), g.KS, rw, kp);
 
 #pragma unroll
     for (int r = 0; r < ONE_XR; ++r) {
@@ -1224,6 +1525,8 @@ dense_fn dense_one_kernel_q8_0(int xt, int m, int u);
 dense_fn dense_one_kernel_q4_0(int xt, int m, int u);
 dense_fn dense_one_kernel_mxfp4(int xt, int m, int u);
 dense_fn dense_one_kernel_nvfp4(int xt, int m, int u);
+dense_fn dense_kernel_kq(int fmt, int xt, int m);
+dense_fn dense_one_kernel_kq(int fmt, int xt, int m, int u);
 hipError_t launch_requant_nvfp4(const Layout &lo, const uint8_t *canon_q8_0, uint8_t *packed, hipStream_t s);
 hipError_t launch_moe_q8_0(int xt, int mode, const Plan &p, const MoeArgs &a, int maxdistinct, size_t lds,
                            const void *x, float *y, hipStream_t s);
@@ -1261,7 +1564,7 @@ constexpr int ONE_MAX_M = 3;
 
 inline int one_batch_u(int fmt, int m, int need)
 {
-    if (fmt == QG_Q8_0) return m == 1 && need <= 8 ? 8 : 0;
+    if (fmt == QG_Q8_0 || is_kq(fmt)) return m == 1 && need <= 8 ? 8 : 0;
     if (m > ONE_MAX_M) return 0;
     return need <= 8 ? 8 : need <= 12 ? 12 : need <= ONE_MAX_U ? ONE_MAX_U : 0;
 }
@@ -1277,7 +1580,7 @@ dense_fn pick_dense_one_u(int u)
 template <int FMT, bool XBF16, bool DOT>
 dense_fn pick_dense_one(int m, int u)
 {
-    if constexpr (FMT == QG_Q8_0) {
+    if constexpr (FMT == QG_Q8_0 || is_kq(FMT)) {
         return k_dense_one<FMT, XBF16, DOT, 1, 8>;
     } else {
         return m == 1 ? pick_dense_one_u<FMT, XBF16, DOT, 1>(u)

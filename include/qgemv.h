@@ -31,9 +31,25 @@
  *               (the FP4 format of imp's load-time decode cache and sm_120a
  *               GEMV: imp README, "Why this exists" and "Features"; the
  *               definition is the public one, the byte order a reading)
+ *   K-quant super-blocks of 256 weights (the GGUF Q4_K / Q6_K formats of the
+ *   imp engine's models: imp README, "Features" table, Quantization row; imp
+ *   release notes v0.7.0, Q4_K_M; named on the pages, defined publicly):
+ *   Q4_K 144 B: fp16 d, fp16 dmin, 12 bytes s of 6-bit scales and mins, 128
+ *               code bytes qs.  Sub-block j (weights 32j..32j+31): for j < 4
+ *               sc = s[j] & 63, m = s[j+4] & 63; for j >= 4
+ *               sc = (s[j+4] & 15) | (s[j-4] >> 6) << 4,
+ *               m = (s[j+4] >> 4) | (s[j] >> 6) << 4.  Weight 64c+l (l < 32)
+ *               is the low nibble of qs[32c+l], weight 64c+32+l its high nibble;
+ *                                                                 w = d * sc * q - dmin * m
+ *   Q6_K 210 B: ql[128], qh[64], 16 int8 scales sc, fp16 d.  Weight
+ *               128h+32r+l (h < 2, r < 4, l < 32): low 4 bits from
+ *               ql[64h+l+32(r&1)] (low nibble if r < 2, else high), high 2
+ *               bits (qh[32h+l] >> 2r) & 3, scale sc[8h+2r+l/16];
+ *                                                                 w = d * sc * (q - 32)
  * A matrix is N rows (outputs) by K columns (inputs), stored as N * (K/32)
- * canonical blocks (N * (K/16) for NVFP4), row-major.  E = 255 decodes to
- * NaN; E2M1 has no NaN; E4M3 S.1111.111 is NaN.
+ * canonical blocks (N * (K/16) for NVFP4, N * (K/256) for the K-quants, whose
+ * K must be a multiple of 256), row-major.  E = 255 decodes to NaN; E2M1 has
+ * no NaN; E4M3 S.1111.111 is NaN.  K-quant scales (d, dmin) must be finite.
  *
  * Packed layout.  The GEMV entry points read weights in a packed layout made
  * once at load time by qg_pack (device) or qg_pack_host (CPU): per tile of
@@ -79,14 +95,15 @@ extern "C" {
 /* Status codes. */
 enum {
     QG_OK = 0,
-    QG_EINVAL = 1,        /* null pointer, non-positive size, k % 32 != 0, m outside [1, 8], bad enum */
+    QG_EINVAL = 1,        /* null pointer, non-positive size, k % 32 != 0 (K-quants: k % 256 != 0),
+                             m outside [1, 8], bad enum */
     QG_EUNSUPPORTED = 2,  /* valid but outside what the kernels serve (see the limits per call) */
     QG_EALIGN = 3,        /* device pointer misaligned */
     QG_EHIP = 4           /* a HIP runtime call failed */
 };
 
 /* Weight formats. */
-enum { QG_Q8_0 = 0, QG_Q4_0 = 1, QG_MXFP4 = 2, QG_NVFP4 = 3 };
+enum { QG_Q8_0 = 0, QG_Q4_0 = 1, QG_MXFP4 = 2, QG_NVFP4 = 3, QG_Q4_K = 4, QG_Q6_K = 5 };
 
 /* Activation element types: fp32, or bf16 bit patterns (uint16). */
 enum { QG_F32 = 0, QG_BF16 = 1 };
@@ -124,6 +141,9 @@ typedef struct {
     int64_t scale_offset;       /* byte offset of the scale stream = tiles * code_tile_bytes */
     int64_t packed_bytes;       /* total size, rounded up to a multiple of 256 */
     int64_t tensor_scale_offset;  /* NVFP4: byte offset of the fp32 tensor scale (a 256-byte trailer); else 0 */
+    int64_t high_offset;          /* Q6_K: byte offset of the stream of high code bits (8 B per record); else 0 */
+    int64_t superblock_offset;    /* K-quants: byte offset of the per-row super-block words
+                                     (d | dmin << 16, fp16 bits; 4 B each); else 0 */
 } qg_layout_t;
 
 /* Human-readable name of a status code (static string). */
@@ -201,6 +221,25 @@ int qgemv_mxfp4(const void *w_packed, int64_t n, int64_t k, const void *x, int x
  */
 int qgemv_nvfp4(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
                 float *y, void *stream);
+
+/*
+ * The same product for K-quant weights (Q4_K, Q6_K; packed by qg_pack from
+ * canonical super-blocks).  The packed form keeps a 32-weight sub-block per
+ * 16-byte record with its scale (and min) in the scale stream, the Q6_K
+ * high code bits in a stream of their own and d (and dmin) once per row and
+ * super-block.  Each weight is formed exactly before its product (Q4_K:
+ * d * sc * q - dmin * m rounded once to fp32; Q6_K: the integer q - 32,
+ * whose sum is scaled by d * sc per 16 weights), so rounding stays relative
+ * to the sum of |w * x| and zero weights contribute exactly zero.
+ * Activations are staged in fp32 for both x types.  Runs the vector kernel
+ * family for every m.  Limits as qgemv_*, with k % 256 == 0.
+ * The other entry points (expert, fused, many-token and chain products)
+ * return QG_EUNSUPPORTED for these formats.
+ */
+int qgemv_q4_k(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
+               float *y, void *stream);
+int qgemv_q6_k(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,
+               float *y, void *stream);
 
 /*
  * Load-time decode cache: re-quantizes a Q8_0 matrix into packed NVFP4 for
@@ -392,7 +431,7 @@ int qgemv_chain(const void *plan_host, const void *plan_device, void *stream);
  * the process ends, and the chain kernel reads them there.  Allocates
  * nothing.  plan_host must stay unchanged until the stream has run the call.
  * A plan of more than QG_CHAIN_STATIC_BYTES bytes (qg_chain_plan_bytes of
- * more than 511 links) is refused with QG_EUNSUPPORTED before any device
+ * more than 430 links) is refused with QG_EUNSUPPORTED before any device
  * work.  Every call on a device shares that device's buffer, and each call
  * rewrites the whole plan it reads: calls that overlap on one device (other
  * streams, other threads) race, as overlapping chain launches do anyway.

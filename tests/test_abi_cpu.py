@@ -367,12 +367,86 @@ def test_chain_noalloc_refuses_on_the_host():
     work: no plan, a buffer that is not a plan, and a plan one link over the
     static buffer's capacity."""
     L = q.lib()
-    assert L.qg_chain_plan_bytes(511) <= q.CHAIN_STATIC_BYTES < L.qg_chain_plan_bytes(512)
+    most = 430                  # the header's stated capacity
+    assert L.qg_chain_plan_bytes(most) <= q.CHAIN_STATIC_BYTES < L.qg_chain_plan_bytes(most + 1)
     assert L.qgemv_chain_noalloc(None, None) == q.QG_EINVAL
     junk = (ctypes.c_uint8 * 256)()
     assert L.qgemv_chain_noalloc(junk, None) == q.QG_EINVAL
-    # a header (magic, fmt, xt, m, count, grid, lds, part_off, out_off) of 512 links
-    hdr = struct.pack("<Iiiiiiqqq", 0x51474333, q.Q8_0, q.X_BF16, 1, 512, 256, 0, 0, 0)
-    buf = (ctypes.c_uint8 * L.qg_chain_plan_bytes(512)).from_buffer_copy(
-        hdr + bytes(L.qg_chain_plan_bytes(512) - len(hdr)))
+    # a header (magic, fmt, xt, m, count, grid, lds, part_off, out_off) of one link too many
+    hdr = struct.pack("<Iiiiiiqqq", 0x51474333, q.Q8_0, q.X_BF16, 1, most + 1, 256, 0, 0, 0)
+    buf = (ctypes.c_uint8 * L.qg_chain_plan_bytes(most + 1)).from_buffer_copy(
+        hdr + bytes(L.qg_chain_plan_bytes(most + 1) - len(hdr)))
     assert L.qgemv_chain_noalloc(buf, None) == q.QG_EUNSUPPORTED
+
+
+# ------------------------------------------------------------------ K-quants
+@pytest.mark.parametrize("fmt", [q.Q4_K, q.Q6_K])
+@pytest.mark.parametrize("n,k", [(1, 256), (3, 256), (65, 768), (300, 2560), (19, 9728)])
+def test_kquant_host_pack_round_trip(fmt, n, k):
+    canon = wl.blocks_for(fmt, n, k, config=71, matrix=n).reshape(-1)
+    packed = q.pack_host(fmt, canon, n, k)
+    assert packed.size % 256 == 0
+    assert np.array_equal(q.unpack_host(fmt, packed, n, k), canon)
+
+
+def test_kquant_shape_validation():
+    L = q.lib()
+    for fmt in (q.Q4_K, q.Q6_K):
+        assert L.qg_packed_bytes(fmt, 4, 96) == -1          # not whole super-blocks
+        assert L.qg_packed_bytes(fmt, 4, 288) == -1
+        assert L.qg_packed_bytes(fmt, 4, 512) > 0
+    lo4, lo6 = q.layout(q.Q4_K, 65, 768), q.layout(q.Q6_K, 65, 768)
+    assert lo4["high_offset"] == 0 and lo4["superblock_offset"] > lo4["scale_offset"]
+    assert lo6["high_offset"] > lo6["scale_offset"] and lo6["superblock_offset"] > lo6["high_offset"]
+
+
+def _record(lo, row, blk):
+    """(code offset, scale offset, record index) of (row, 32-weight block blk)."""
+    L, R, S = lo["lanes_per_row"], lo["rows_per_tile"], lo["steps"]
+    tile, lane = row // R, (row % R) * L + blk % L
+    step = blk // L
+    co = tile * lo["code_tile_bytes"] + step * 1024 + lane * 16
+    so = lo["scale_offset"] + tile * lo["scale_tile_bytes"] + step * 128 + lane * 2
+    return co, so, (tile * S + step) * 64 + lane
+
+
+def test_kquant_packed_record_placement():
+    """Each 32-weight sub-block's codes, scales and super-block words sit
+    where the layout says, in the stated encoding (Q4_K codes as q ^ 8
+    nibble pairs; Q6_K codes t = q ^ 32 split into low nibbles and high bit
+    pairs), read back here from the canonical bytes by position."""
+    n, k = 9, 768
+    rng = np.random.default_rng(72)
+    for fmt in (q.Q4_K, q.Q6_K):
+        canon = wl.blocks_for(fmt, n, k, config=72, matrix=fmt)
+        packed = q.pack_host(fmt, canon, n, k)
+        lo = q.layout(fmt, n, k)
+        sbb = 144 if fmt == q.Q4_K else 210
+        cb = canon.reshape(n, k // 256, sbb)
+        for row, blk in [(0, 0), (n - 1, k // 32 - 1)] + [(int(rng.integers(n)), int(rng.integers(k // 32))) for _ in range(6)]:
+            s, j = blk // 8, blk % 8
+            sb = cb[row, s]
+            co, so, rec = _record(lo, row, blk)
+            code = packed[co:co + 16]
+            word = packed[lo["superblock_offset"] + (row * (k // 256) + s) * 4:][:4]
+            if fmt == q.Q4_K:
+                qs = [(sb[16 + 32 * (j // 2) + l] >> (4 * (j % 2))) & 15 for l in range(32)]
+                got = [((code[i // 2] >> (4 * (i % 2))) & 15) ^ 8 for i in range(32)]
+                assert got == qs
+                assert bytes(word) == bytes(sb[0:4])
+            else:
+                h, r = j // 4, j % 4
+                qv = [((sb[64 * h + l + 32 * (r & 1)] >> (4 * (r // 2))) & 15) | (((sb[128 + 32 * h + l] >> (2 * r)) & 3) << 4)
+                      for l in range(32)]
+                hb = packed[lo["high_offset"] + rec * 8:][:8]
+                t = []
+                for i in range(32):
+                    a4, rem = i // 8, i % 8
+                    e, b = rem // 4, rem % 4
+                    lo4 = (code[4 * a4 + b] >> (4 * e)) & 15
+                    f = 2 * (a4 % 2) + e
+                    hi2 = (hb[4 * (a4 // 2) + b] >> (2 * f)) & 3
+                    t.append(lo4 | (hi2 << 4))
+                assert [v ^ 32 for v in t] == qv
+                assert list(packed[so:so + 2]) == [sb[192 + 8 * h + 2 * r], sb[192 + 8 * h + 2 * r + 1]]
+                assert bytes(word[:2]) == bytes(sb[208:210]) and bytes(word[2:]) == b"\0\0"
