@@ -344,6 +344,14 @@ def run_other(args):
             emit(f"mxfp4 moe 32 experts top-4: gate_up 3584x2048 + down 2048x1792 m={m}", (gbytes + dbytes) / us / 1e3,
                  us, {"per_mode": per, "distinct_experts": distinct, "bytes_per_set": gbytes + dbytes,
                       "weight_copies": reps, "us_with_device_router": round(wus, 3), "fused_ffn": fused})
+    if args.calib_copy_mib:
+        # a device copy of known size, for scaling the HBM byte counters of the same run
+        nb = args.calib_copy_mib << 20
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
 
 
 def log(args, *a):

@@ -346,7 +346,7 @@ void fit_workgroups(Plan &p)
     p.threads = (int)(64 * w);
 }
 
-inline bool uses_dot(int fmt, int xt) { return fmt != QG_Q8_0 && !is_kq(fmt) && xt == QG_BF16; }
+inline bool uses_dot(int fmt, int xt) { return fmt != QG_Q8_0 && fmt != QG_Q4_K && xt == QG_BF16; }
 
 // Co-batches of at least this many bf16 tokens run on the matrix cores
 // (measured crossover on MI355X: the int8 codes' per-weight VALU cost makes

@@ -694,7 +694,7 @@ struct IdMap {
 };
 
 // Steps per batch (loads in flight per lane before the first use).
-template <int FMT, bool DOT> struct Batch { static constexpr int U = (FMT == QG_Q8_0 || !DOT) ? 4 : 8; };
+template <int FMT, bool DOT> struct Batch { static constexpr int U = (FMT == QG_Q8_0 || is_kq(FMT) || !DOT) ? 4 : 8; };
 
 // Per-lane extras of a K-quant batch: the row's super-block word of each
 // step, and for Q6_K the record's high code bits.
@@ -821,20 +821,42 @@ struct Engine {
                     for (int b = 0; b < 4; ++b) dv[8 * a + 4 * e + b] = i8_at(Q, b);
                 }
             }
+            if constexpr (DOT) {
+                // bf16 activations: q - 32 is exact in bf16, two weights per dot2
+                bf16x2_t pr[16];
 #pragma unroll
-            for (int t = 0; t < M; ++t) {
-                if (t >= xm.count()) break;
-                float sh[2] = {0.0f, 0.0f};
+                for (int p = 0; p < 16; ++p) pr[p] = pk_bf16(dv[2 * p], dv[2 * p + 1]);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float4 xq = __builtin_bit_cast(float4, xs[(xm(t) * 8 + i) * g.wblk + bl]);
-                    float &s = sh[i >> 2];
-                    s = __builtin_fmaf(dv[4 * i], xq.x, s);
-                    s = __builtin_fmaf(dv[4 * i + 1], xq.y, s);
-                    s = __builtin_fmaf(dv[4 * i + 2], xq.z, s);
-                    s = __builtin_fmaf(dv[4 * i + 3], xq.w, s);
+                for (int t = 0; t < M; ++t) {
+                    if (t >= xm.count()) break;
+                    float sh[2] = {0.0f, 0.0f};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint4 xq = xs[(xm(t) * 4 + i) * g.wblk + bl];
+                        float &s = sh[i >> 1];
+                        s = dot2(pr[4 * i], u32_as_bf16x2(xq.x), s);
+                        s = dot2(pr[4 * i + 1], u32_as_bf16x2(xq.y), s);
+                        s = dot2(pr[4 * i + 2], u32_as_bf16x2(xq.z), s);
+                        s = dot2(pr[4 * i + 3], u32_as_bf16x2(xq.w), s);
+                    }
+                    acc[t] = __builtin_fmaf(Db, sh[1], __builtin_fmaf(Da, sh[0], acc[t]));
                 }
-                acc[t] = __builtin_fmaf(Db, sh[1], __builtin_fmaf(Da, sh[0], acc[t]));
+            } else {
+#pragma unroll
+                for (int t = 0; t < M; ++t) {
+                    if (t >= xm.count()) break;
+                    float sh[2] = {0.0f, 0.0f};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float4 xq = __builtin_bit_cast(float4, xs[(xm(t) * 8 + i) * g.wblk + bl]);
+                        float &s = sh[i >> 2];
+                        s = __builtin_fmaf(dv[4 * i], xq.x, s);
+                        s = __builtin_fmaf(dv[4 * i + 1], xq.y, s);
+                        s = __builtin_fmaf(dv[4 * i + 2], xq.z, s);
+                        s = __builtin_fmaf(dv[4 * i + 3], xq.w, s);
+                    }
+                    acc[t] = __builtin_fmaf(Db, sh[1], __builtin_fmaf(Da, sh[0], acc[t]));
+                }
             }
         }
     }

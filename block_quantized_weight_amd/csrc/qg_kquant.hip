@@ -9,16 +9,20 @@
 
 namespace qg {
 
+// Q6_K with bf16 x runs the bf16 dot path (its q - 32 is exact in bf16);
+// Q4_K forms each weight in fp32 and stages fp32 activations.
 template <int FMT>
 static dense_fn dense_for(int xt, int m)
 {
-    return xt == QG_BF16 ? pick_dense<FMT, true, false>(m) : pick_dense<FMT, false, false>(m);
+    constexpr bool DOT = FMT == QG_Q6_K;
+    return xt == QG_BF16 ? pick_dense<FMT, true, DOT>(m) : pick_dense<FMT, false, false>(m);
 }
 
 template <int FMT>
 static dense_fn dense_one_for(int xt, int m, int u)
 {
-    return xt == QG_BF16 ? pick_dense_one<FMT, true, false>(m, u) : pick_dense_one<FMT, false, false>(m, u);
+    constexpr bool DOT = FMT == QG_Q6_K;
+    return xt == QG_BF16 ? pick_dense_one<FMT, true, DOT>(m, u) : pick_dense_one<FMT, false, false>(m, u);
 }
 
 dense_fn dense_kernel_kq(int fmt, int xt, int m)

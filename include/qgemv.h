@@ -231,7 +231,8 @@ int qgemv_nvfp4(const void *w_packed, int64_t n, int64_t k, const void *x, int x
  * d * sc * q - dmin * m rounded once to fp32; Q6_K: the integer q - 32,
  * whose sum is scaled by d * sc per 16 weights), so rounding stays relative
  * to the sum of |w * x| and zero weights contribute exactly zero.
- * Activations are staged in fp32 for both x types.  Runs the vector kernel
+ * Q4_K stages activations in fp32 for both x types; Q6_K with bf16
+ * activations pairs the exact bf16 q - 32 with them through dot2.  Runs the vector kernel
  * family for every m.  Limits as qgemv_*, with k % 256 == 0.
  * The other entry points (expert, fused, many-token and chain products)
  * return QG_EUNSUPPORTED for these formats.
