@@ -353,8 +353,12 @@ inline bool uses_dot(int fmt, int xt) { return fmt != QG_Q8_0 && fmt != QG_Q4_K 
 // Q8_0 gain from two tokens, the 4-bit formats from four).
 inline int mfma_min_m(int fmt) { return fmt == QG_Q8_0 ? 2 : 4; }
 
-// LDS per co-batch workgroup is kept within 80 KiB, so two fit on a CU.
+// LDS per co-batch workgroup is kept within 80 KiB, so two fit on a CU; a
+// co-batch grid of at most one workgroup per CU may use all 160 KiB, which
+// fits longer activation windows (4 tokens, 8 lanes per row, split in 4: K up
+// to 18432 in one window instead of 8192).
 constexpr int MFMA_WG_LDS = 80 * 1024;
+constexpr int MFMA_WG_LDS_ONE = 160 * 1024;
 
 struct MPlan {
     MGeom g;
@@ -398,18 +402,21 @@ MPlan make_mplan(const Layout &lo, int m, int passes = 0, int TG = 1)
     const int64_t tpw = lo.L >= 8 ? lo.L / 4 : 1;
     g.units = (int32_t)((lo.tiles + tpw - 1) / tpw);
     const size_t per_block = (size_t)m * 64;
+    int64_t budget = MFMA_WG_LDS;
     // activation window: as many steps as fit beside the fixed areas (at least one)
     auto sw_for = [&](int ks) {
-        const int64_t xbudget = (int64_t)MFMA_WG_LDS - (int64_t)mfma_lds_bytes(lo.fmt, m, 0, lo.L, ks, TG);
+        const int64_t xbudget = budget - (int64_t)mfma_lds_bytes(lo.fmt, m, 0, lo.L, ks, TG);
         const int64_t v = (xbudget / (int64_t)per_block) / lo.L;
         return v < 1 ? (int64_t)1 : v;
     };
+    auto groups = [&](int ks) { return (g.units + WAVES / ks - 1) / (WAVES / ks); };
     int KS = 1;
     if (passes > 0) {
-        while (KS < WAVES && ((g.units + WAVES / KS - 1) / (WAVES / KS)) * passes < 300) KS <<= 1;
+        while (KS < WAVES && groups(KS) * passes < 300) KS <<= 1;
     } else {
         if (g.units < 4096) KS = 2;
         if (g.units < 2048) KS = 4;
+        if (groups(KS) <= QG_CUS) budget = MFMA_WG_LDS_ONE;   // fewer KS only means fewer groups
     }
     while (KS > 1 && (lo.S < KS || sw_for(KS) < KS)) KS >>= 1;
     const int64_t sw_max = sw_for(KS);

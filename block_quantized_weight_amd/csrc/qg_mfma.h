@@ -7,13 +7,13 @@
 // M dot products, each reading its activations from LDS) becomes the bound.
 // Here one v_mfma_f32_16x16x32_bf16 takes a 32-weight block of 16 rows:
 //   A (16 x 32)  the tokens' activations of that block (A row = token, rows
-//                past M are zero), bf16 exactly as given;
+//                past M repeat the last token), bf16 exactly as given;
 //   B (32 x 16)  the 16 rows' codes, converted to bf16 in registers (exact:
 //                Q4_0 as (q-8)/16, E2M1 values, int8 codes);
 //   C            zero;
 //   D[t][r]      the block's dot product for token t and row r before the
 //                block scale, which is applied in fp32: acc += d * D (16 d
-//                for Q4_0).
+//                for Q4_0); rows t >= M are computed and never stored.
 // The sum over k inside the instruction is order-free, so any assignment of
 // the 32 k values to operand slots works as long as A and B agree: lane l of
 // both holds 8 consecutive k (octet l/16 of the block), A for token l%16 and
@@ -174,12 +174,58 @@ struct MEngine {
         return FMT == QG_MXFP4 ? e8m0_to_f32(bits) : FMT == QG_Q4_0 ? q4_scale(bits) : f16_bits_to_f32(bits);
     }
 
-    // The MFMAs of one step (block index jL + s of every row of the unit)
-    // for the mp (<= 16) tokens of the group.  wl: this wave's transpose area.
+    // What one block of the step reads from LDS: the rows' codes (one octet
+    // per lane and 16-row group) and scales, and the token groups'
+    // activations.
+    struct Raw {
+        uint32_t cw[Sh::RG][2];
+        float sc[Sh::RG];
+        bf16x8_t a[TG];
+    };
+
+    // Reads block s of the step (block index jL + s of every row of the unit)
+    // from the transpose area and the staged activations.  A rows past mp
+    // repeat the last token: a row of D depends only on its row of A, and
+    // those rows are never stored.
+    static __device__ __forceinline__ void fetch(int s, int j, int b0, const uint4 *xs, const uint8_t *wl,
+                                                 const float *wsc, int mp, Raw &o)
+    {
+        const int lane = threadIdx.x & 63, i = lane & 15, oct = lane >> 4;
+        const int bl = j * LL + s - b0;
+#pragma unroll
+        for (int G = 0; G < Sh::RG; ++G) {
+            const int tt = LL >= 8 ? i / Sh::R : 0;
+            const int rr = LL >= 8 ? i % Sh::R : 16 * G + i;
+            const int sl = rr * LL + s;
+            if (FMT == QG_Q8_0) {
+                const uint2 v = *(const uint2 *)(wl + (tt * P + (oct >> 1)) * MPLANE + slot(sl) + 8 * (oct & 1));
+                o.cw[G][0] = v.x;
+                o.cw[G][1] = v.y;
+            } else {
+                o.cw[G][0] = *(const uint32_t *)(wl + tt * MPLANE + slot(sl) + 4 * oct);
+                o.cw[G][1] = 0;
+            }
+            o.sc[G] = wsc[tt * 64 + sl];
+        }
+#pragma unroll
+        for (int tg = 0; tg < TG; ++tg)
+            o.a[tg] = __builtin_bit_cast(bf16x8_t, xs[(bl * mp + min(16 * tg + i, mp - 1)) * 4 + oct]);
+    }
+
+    static __device__ __forceinline__ void decode(const Raw &o, bf16x8_t (&bw)[Sh::RG])
+    {
+#pragma unroll
+        for (int G = 0; G < Sh::RG; ++G) bw[G] = unpack(o.cw[G]);
+    }
+
+    // The MFMAs of one step for the mp (<= 16) tokens of the group, every
+    // token group unconditionally.  wl: this wave's transpose area.  While
+    // the matrix cores work on block s, block s + 1 is unpacked and the LDS
+    // reads of block s + 2 are issued; block s's scale is applied after.
     static __device__ __forceinline__ void step(const MGeom &g, const Regs &r, int u, int j, int b0, const uint4 *xs,
                                                 uint8_t *wl, f32x4_t (&acc)[TG][Sh::RG], int mp)
     {
-        const int lane = threadIdx.x & 63, i = lane & 15, oct = lane >> 4;
+        const int lane = threadIdx.x & 63;
         float *wsc = (float *)(wl + TPW * P * MPLANE);
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
@@ -187,44 +233,29 @@ struct MEngine {
             for (int h = 0; h < P; ++h) *(uint4 *)(wl + (tt * P + h) * MPLANE + slot(lane)) = r.c[u][tt][h];
             wsc[tt * 64 + lane] = scale(r.s[u][tt]);
         }
+        constexpr int NS = Sh::NS;
+        Raw rw[NS];
+        bf16x8_t bw[NS][Sh::RG];
+        fetch(0, j, b0, xs, wl, wsc, mp, rw[0]);
+        if (NS > 1) fetch(1, j, b0, xs, wl, wsc, mp, rw[NS > 1 ? 1 : 0]);
+        decode(rw[0], bw[0]);
 #pragma unroll
-        for (int s = 0; s < Sh::NS; ++s) {
-            const int bl = j * LL + s - b0;
-            // the rows' weight operands and scales
-            bf16x8_t bw[Sh::RG];
-            float sc[Sh::RG];
+        for (int s = 0; s < NS; ++s) {
+            const f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4_t d[TG][Sh::RG];
 #pragma unroll
-            for (int G = 0; G < Sh::RG; ++G) {
-                const int tt = LL >= 8 ? i / Sh::R : 0;
-                const int rr = LL >= 8 ? i % Sh::R : 16 * G + i;
-                const int sl = rr * LL + s;
-                uint32_t cw[2];
-                if (FMT == QG_Q8_0) {
-                    const uint2 v = *(const uint2 *)(wl + (tt * P + (oct >> 1)) * MPLANE + slot(sl) + 8 * (oct & 1));
-                    cw[0] = v.x;
-                    cw[1] = v.y;
-                } else {
-                    cw[0] = *(const uint32_t *)(wl + tt * MPLANE + slot(sl) + 4 * oct);
-                    cw[1] = 0;
-                }
-                bw[G] = unpack(cw);
-                sc[G] = wsc[tt * 64 + sl];
-            }
-            // every token group, unconditionally (tokens past mp read zeros)
+            for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-            for (int tg = 0; tg < TG; ++tg) {
-                const int tok = 16 * tg + i;
-                uint4 av = xs[(bl * mp + min(tok, mp - 1)) * 4 + oct];
-                if (tok >= mp) av = make_uint4(0, 0, 0, 0);
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
-                const f32x4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int G = 0; G < Sh::RG; ++G)
+                    d[tg][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rw[s].a[tg], bw[s][G], c, 0, 0, 0);
+            if (s + 2 < NS) fetch(s + 2, j, b0, xs, wl, wsc, mp, rw[s + 2 < NS ? s + 2 : 0]);
+            if (s + 1 < NS) decode(rw[s + 1 < NS ? s + 1 : 0], bw[s + 1 < NS ? s + 1 : 0]);
 #pragma unroll
-                for (int G = 0; G < Sh::RG; ++G) {
-                    const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[G], c, 0, 0, 0);
+            for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[tg][G][q] = __builtin_fmaf(sc[G], d[q], acc[tg][G][q]);
-                }
-            }
+                for (int G = 0; G < Sh::RG; ++G)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[tg][G][q] = __builtin_fmaf(rw[s].sc[G], d[tg][G][q], acc[tg][G][q]);
         }
     }
 
@@ -238,21 +269,33 @@ struct MEngine {
 };
 
 // Stages window w of the mp tokens' activations (x already offset to the
-// group's first token) as xs[(bl*mp + t)*4 + oct] (bf16 octets).
+// group's first token) as xs[(bl*mp + t)*4 + oct] (bf16 octets).  xs is
+// filled as 16-byte pieces p = (bl*mp + t)*4 + oct, so consecutive threads
+// write consecutive LDS addresses; each thread issues the loads of MS_CH
+// pieces before writing any, one memory round trip per MS_CH * blockDim
+// pieces.  Loads past the matrix read the token's first block and are
+// replaced by zeros.
+constexpr int MS_CH = 8;
 __device__ __forceinline__ void mfma_stage(const MGeom &g, const uint16_t *x, int w, uint4 *xs, int mp)
 {
     const int b0 = w * g.SW * g.L;
-    const int total = g.wblk * mp;
-    for (int idx = threadIdx.x; idx < total; idx += (int)blockDim.x) {
-        const int bl = idx / mp, t = idx - bl * mp, b = b0 + bl;
-        uint4 r[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-        if (b < g.nb) {
-            const uint4 *src = (const uint4 *)(x + (int64_t)t * g.k + (int64_t)b * QK);
+    const int pieces = g.wblk * mp * 4;
+    const int T = (int)blockDim.x;
+    for (int base = 0; base < pieces; base += MS_CH * T) {
+        uint4 r[MS_CH];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) r[q] = ld_global16(src + q);
+        for (int c = 0; c < MS_CH; ++c) {
+            const int p = min(base + c * T + (int)threadIdx.x, pieces - 1);
+            const int idx = p >> 2, bl = idx / mp, t = idx - bl * mp, b = b0 + bl;
+            const bool ok = b < g.nb;
+            const uint4 v = ld_global16(x + (int64_t)t * g.k + (int64_t)(ok ? b : 0) * QK + (p & 3) * 8);
+            r[c] = ok ? v : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xs[idx * 4 + q] = r[q];
+        for (int c = 0; c < MS_CH; ++c) {
+            const int p = base + c * T + (int)threadIdx.x;
+            if (p < pieces) xs[p] = r[c];
+        }
     }
 }
 

@@ -319,8 +319,12 @@ def test_mixed_range_activations(dev, fmt, xt):
 # bf16 co-batches of 4..8 tokens on layouts of 1..8 lanes per row run on the
 # matrix cores.  (n, k) pick each layout class: 33001 rows -> 1 lane per row,
 # 20000 -> 2, 9001 -> 4, 5000 and 4100 -> 8 (odd tile counts leave a half
-# unit); K = 12288 at 8 tokens needs several activation windows.
-MFMA_SHAPES = [(33001, 256, 1), (20000, 2048, 2), (9001, 2048, 4), (5000, 2048, 8), (4100, 12288, 8)]
+# unit); K = 12288 at 8 tokens needs several activation windows.  4090 and
+# 4089 rows make 256 units, one workgroup per compute unit, whose plan takes
+# the whole LDS: K = 12256 (383 blocks, a ragged last step and tile) in one
+# window at 4 and 5 tokens, two at 8; K = 18400 at 4 tokens fills one window.
+MFMA_SHAPES = [(33001, 256, 1), (20000, 2048, 2), (9001, 2048, 4), (5000, 2048, 8), (4100, 12288, 8),
+               (4090, 12256, 8), (4089, 18400, 8)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
