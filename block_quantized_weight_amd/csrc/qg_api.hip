@@ -416,6 +416,12 @@ MPlan make_mplan(const Layout &lo, int m, int passes = 0, int TG = 1)
     } else {
         if (g.units < 4096) KS = 2;
         if (g.units < 2048) KS = 4;
+        // Past 4 tokens each workgroup stages twice the activations: two
+        // units per workgroup halve that traffic once the units fill the
+        // CUs.  Measured on MI355X at 8 tokens, split 2 / 4: Q4_0 6144x4096
+        // 10.35 / 11.00 us, 24576x4096 20.28 / 21.14, Q8_0 11.10 / 15.82 and
+        // 27.80 / 31.68; 4096x12288 (256 units) 27.99 / 22.25 keeps 4.
+        if (m > 4 && g.units >= 384 && KS > 2) KS = 2;
         if (groups(KS) <= QG_CUS) budget = MFMA_WG_LDS_ONE;   // fewer KS only means fewer groups
     }
     while (KS > 1 && (lo.S < KS || sw_for(KS) < KS)) KS >>= 1;

@@ -269,34 +269,32 @@ struct MEngine {
 };
 
 // Stages window w of the mp tokens' activations (x already offset to the
-// group's first token) as xs[(bl*mp + t)*4 + oct] (bf16 octets).  xs is
-// filled as 16-byte pieces p = (bl*mp + t)*4 + oct, so consecutive threads
-// write consecutive LDS addresses; each thread issues the loads of MS_CH
-// pieces before writing any, one memory round trip per MS_CH * blockDim
-// pieces.  Loads past the matrix read the token's first block and are
-// replaced by zeros.
-constexpr int MS_CH = 8;
+// group's first token) as xs[(bl*mp + t)*4 + oct] (bf16 octets), i.e. 16-byte
+// pieces p = (bl*mp + t)*4 + oct.  Thread p of each round of blockDim pieces
+// loads piece p straight into LDS (global_load_lds_dwordx4: the wave's 64
+// pieces land at the wave-uniform base + 16 * lane), so every round is in
+// flight at once and no registers hold the data; pieces of blocks past the
+// matrix are written as zeros.  Returns once this wave's pieces are in LDS
+// (the caller's barrier then covers the workgroup).
+typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void mfma_stage(const MGeom &g, const uint16_t *x, int w, uint4 *xs, int mp)
 {
     const int b0 = w * g.SW * g.L;
     const int pieces = g.wblk * mp * 4;
     const int T = (int)blockDim.x;
-    for (int base = 0; base < pieces; base += MS_CH * T) {
-        uint4 r[MS_CH];
-#pragma unroll
-        for (int c = 0; c < MS_CH; ++c) {
-            const int p = min(base + c * T + (int)threadIdx.x, pieces - 1);
+    const int wbase = (int)threadIdx.x & ~63;
+    for (int base = 0; base < pieces; base += T) {
+        const int p = base + (int)threadIdx.x;
+        if (p < pieces) {
             const int idx = p >> 2, bl = idx / mp, t = idx - bl * mp, b = b0 + bl;
-            const bool ok = b < g.nb;
-            const uint4 v = ld_global16(x + (int64_t)t * g.k + (int64_t)(ok ? b : 0) * QK + (p & 3) * 8);
-            r[c] = ok ? v : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int c = 0; c < MS_CH; ++c) {
-            const int p = base + c * T + (int)threadIdx.x;
-            if (p < pieces) xs[p] = r[c];
+            if (b < g.nb)
+                __builtin_amdgcn_global_load_lds((const void *)(x + (int64_t)t * g.k + (int64_t)b * QK + (p & 3) * 8),
+                                                 (lds_void *)(xs + base + wbase), 16, 0, 0);
+            else
+                xs[p] = make_uint4(0, 0, 0, 0);
         }
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's LDS loads have landed
 }
 
 // blockIdx.y: a pass over TG token groups of 16 (tokens 16*TG*y .. of the
