@@ -348,10 +348,9 @@ void fit_workgroups(Plan &p)
 
 inline bool uses_dot(int fmt, int xt) { return fmt != QG_Q8_0 && fmt != QG_Q4_K && xt == QG_BF16; }
 
-// Co-batches of at least this many bf16 tokens run on the matrix cores
-// (measured crossover on MI355X: the int8 codes' per-weight VALU cost makes
-// Q8_0 gain from two tokens, the 4-bit formats from four).
-inline int mfma_min_m(int fmt) { return fmt == QG_Q8_0 ? 2 : 4; }
+// Co-batches of at least this many bf16 tokens may run on the matrix cores
+// (dense_kind: unless the one-batch vector kernel applies).
+inline int mfma_min_m(int) { return 2; }
 
 // LDS per co-batch workgroup is kept within 80 KiB, so two fit on a CU; a
 // co-batch grid of at most one workgroup per CU may use all 160 KiB, which
@@ -466,6 +465,24 @@ int one_batch(int fmt, int xt, const Plan &p, int64_t m)
     return p.grid <= per_cu * QG_CUS ? u : 0;
 }
 
+// The kernel family of a dense call.  bf16 co-batches run on the matrix
+// cores (mfma_fits) unless the one-batch vector kernel applies (4-bit formats,
+// 2 or 3 tokens, grids resident at once), which is faster there; everything
+// else on the vector kernel, one-batch where it applies.  p receives the
+// vector plan, u its steps in flight (0: the batched pass).  Measured on
+// MI355X, Q4_0 vector / matrix cores (us): 2 tokens 6144x4096 (one-batch)
+// 7.62 / 8.74, 4096x12288 (one-batch) 11.87 / 12.09, 24576x4096 (batched)
+// 19.68 / 17.44; 3 tokens 6144x4096 (one-batch) 8.59 / 9.11, 24576x4096
+// (batched) 21.63 / 16.50, 4096x12288 (batched) 17.64 / 12.88.
+int dense_kind(int fmt, const Layout &lo, int xt, int64_t m, Plan &p, int &u)
+{
+    p = make_plan(lo, (int)m, uses_dot(fmt, xt), (int)m);
+    fit_workgroups(p);
+    u = one_batch(fmt, xt, p, m);
+    if (!u && mfma_fits(lo, xt, m)) return QG_PATH_MFMA;
+    return u ? QG_PATH_VALU_ONE : QG_PATH_VALU;
+}
+
 int launch_status()
 {
     hipError_t e = hipGetLastError();
@@ -481,20 +498,18 @@ int dense(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
     if (m < 1 || m > QG_MAX_M) return QG_EINVAL;
     if (!aligned(w, W_ALIGN) || !aligned(x, 16) || !aligned(y, 4)) return QG_EALIGN;
     const Layout lo = make_layout(fmt, n, k);
-    if (mfma_fits(lo, xt, m)) {
-        MPlan p = make_mplan(lo, (int)m);
-        p.g.w = (const uint8_t *)w;
+    Plan p;
+    int u = 0;
+    if (dense_kind(fmt, lo, xt, m, p, u) == QG_PATH_MFMA) {
+        MPlan mp = make_mplan(lo, (int)m);
+        mp.g.w = (const uint8_t *)w;
         mfma_fn f = fmt == QG_Q8_0 ? mfma_kernel_q8_0(lo.L) : fmt == QG_Q4_0 ? mfma_kernel_q4_0(lo.L) : mfma_kernel_mxfp4(lo.L);
-        void *args[] = {(void *)&p.g, (void *)&x, (void *)&y};
-        if (allow_lds((const void *)f, p.lds) != hipSuccess) return QG_EHIP;
-        hipError_t e = hipLaunchKernel((const void *)f, dim3(p.grid), dim3(TPB), args, p.lds, as_stream(stream));
+        void *args[] = {(void *)&mp.g, (void *)&x, (void *)&y};
+        if (allow_lds((const void *)f, mp.lds) != hipSuccess) return QG_EHIP;
+        hipError_t e = hipLaunchKernel((const void *)f, dim3(mp.grid), dim3(TPB), args, mp.lds, as_stream(stream));
         return e == hipSuccess ? launch_status() : QG_EHIP;
     }
-    const bool dot = uses_dot(fmt, xt);
-    Plan p = make_plan(lo, (int)m, dot, (int)m);
-    fit_workgroups(p);
     p.g.w = (const uint8_t *)w;
-    const int u = one_batch(fmt, xt, p, m);
     dense_fn f = u ? (fmt == QG_Q8_0 ? dense_one_kernel_q8_0(xt, (int)m, u)
                       : fmt == QG_Q4_0 ? dense_one_kernel_q4_0(xt, (int)m, u)
                       : fmt == QG_MXFP4 ? dense_one_kernel_mxfp4(xt, (int)m, u)
@@ -749,11 +764,9 @@ int qg_dense_path(int fmt, int64_t n, int64_t k, int xt, int64_t m)
     if (st) return -st;
     if (xt != QG_F32 && xt != QG_BF16) return -QG_EINVAL;
     if (m < 1 || m > QG_MAX_M) return -QG_EINVAL;
-    const Layout lo = make_layout(fmt, n, k);
-    if (mfma_fits(lo, xt, m)) return QG_PATH_MFMA;
-    Plan p = make_plan(lo, (int)m, uses_dot(fmt, xt), (int)m);
-    fit_workgroups(p);
-    return one_batch(fmt, xt, p, m) ? QG_PATH_VALU_ONE : QG_PATH_VALU;
+    Plan p;
+    int u = 0;
+    return dense_kind(fmt, make_layout(fmt, n, k), xt, m, p, u);
 }
 
 int qgemv_q8_0(const void *w, int64_t n, int64_t k, const void *x, int xt, int64_t m, float *y, void *stream)

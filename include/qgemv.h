@@ -198,12 +198,13 @@ int qg_dequant_f32(int fmt, const void *w_packed, int64_t n, int64_t k, float *w
  * y: device, fp32 [m][n] row-major, 4-byte aligned, overwritten.
  * Accumulation is fp32; x is used exactly (bf16 -> fp32 is exact).
  * Two kernel families compute it (qg_dense_path says which one a call uses):
- * lane-per-block vector code, and for bf16 co-batches (Q8_0 from 2 tokens,
- * Q4_0 and MXFP4 from 4) on layouts of at most 8 lanes per row, the matrix
- * cores (one bf16 MFMA per 16 rows x 32-weight block, scales applied in
- * fp32).  Results of the two agree within the rounding of fp32 sums.  For
- * one token over short rows the vector code requests each wave's whole
- * weight stream at once (same arithmetic, same bits).
+ * lane-per-block vector code, and for bf16 co-batches of 2 or more tokens
+ * on layouts of at most 8 lanes per row, the matrix cores (one bf16 MFMA per
+ * 16 rows x 32-weight block, scales applied in fp32).  Results of the two
+ * agree within the rounding of fp32 sums.  For one token (4-bit formats: up
+ * to 3) over short rows the vector code requests each wave's whole weight
+ * stream at once (same arithmetic, same bits); where it does, it also takes
+ * those co-batches.
  * Limits: n, k <= 2^31 - 1 and k % 32 == 0.
  */
 int qgemv_q8_0(const void *w_packed, int64_t n, int64_t k, const void *x, int xt, int64_t m,

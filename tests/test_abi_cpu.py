@@ -186,9 +186,10 @@ def test_pack_and_dequant_validation():
 
 
 def test_dense_path_rule():
-    """bf16 co-batches on layouts of <= 8 lanes per row take the matrix cores:
-    Q8_0 from 2 tokens, the 4-bit formats from 4; everything else the vector path,
-    one token over short rows its one-batch form."""
+    """bf16 co-batches of 2..8 tokens on layouts of <= 8 lanes per row take the
+    matrix cores unless the one-batch vector kernel applies (4-bit formats, up to
+    3 tokens, short rows); everything else the vector path, one token over short
+    rows its one-batch form."""
     V, M = q.PATH_VALU, q.PATH_MFMA
     assert q.layout(q.Q4_0, 6144, 4096)["lanes_per_row"] == 8
     assert q.dense_path(q.Q8_0, 6144, 4096, q.X_BF16, 1) == V
@@ -213,8 +214,11 @@ def test_dense_path_rule():
     assert q.dense_path(q.Q8_0, 151936, 2560, q.X_BF16, 1) == V       # 40 per wave
     assert q.dense_path(q.MXFP4, 6144, 4096, q.X_F32, 1) == O
     # only when every workgroup is resident at once: 768 workgroups of 16 steps per
-    # wave need 3 per compute unit, the 20-step variant holds 2
-    assert q.dense_path(q.Q4_0, 24576, 4096, q.X_BF16, 2) == V
+    # wave need 3 per compute unit, the 20-step variant holds 2 (two tokens then
+    # go to the matrix cores)
+    assert q.dense_path(q.Q4_0, 24576, 4096, q.X_BF16, 2) == M
+    assert q.dense_path(q.Q4_0, 24576, 4096, q.X_BF16, 3) == M
+    assert q.dense_path(q.Q4_0, 24576, 4096, q.X_F32, 2) == V
     assert q.dense_path(q.Q4_0, 24576, 4096, q.X_BF16, 1) == V
     assert q.dense_path(q.Q4_0, 6144, 4096, q.X_BF16, 2) == O          # 768 of 4 steps: 4 per unit
     for bad in [(q.Q8_0, 64, 33, q.X_BF16, 1), (q.Q8_0, 64, 64, q.X_BF16, 0), (q.Q8_0, 64, 64, q.X_BF16, 9),

@@ -342,6 +342,21 @@ def test_mfma_cobatch(dev, fmt, n, k, L, m):
     assert err <= TOL, err
 
 
+# Two and three tokens run on the matrix cores wherever the one-batch vector
+# kernel does not apply (long rows, or grids too large to be resident at once).
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k,m", [(4100, 12288, 3), (4089, 18400, 2), (4090, 12256, 3), (24576, 4096, 2)])
+def test_mfma_cobatch_few_tokens(dev, fmt, n, k, m):
+    say(f"mfma few tokens fmt={fmt} n={n} k={k} m={m}")
+    assert q.dense_path(fmt, n, k, q.X_BF16, m) == q.PATH_MFMA
+    canon = wl.blocks_for(fmt, n, k, config=69, matrix=n + m)
+    x = draw_x((m, k), oracle.X_BF16, 69, n + m)
+    y = run_dense(fmt, canon, n, k, x, oracle.X_BF16, dev)
+    ref, l1 = oracle.gemv(fmt, canon, n, k, x, oracle.X_BF16)
+    err = oracle.max_rel_err(y, ref, l1)
+    assert err <= TOL, err
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_mfma_deterministic_and_token_consistent(dev, fmt):
     n, k = 9001, 2048
