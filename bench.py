@@ -360,12 +360,15 @@ def log(args, *a):
 
 
 def source_digest():
-    """sha256 over the HIP sources: ties recorded counter values to a kernel version."""
+    """sha256 over the HIP sources and the build script (its compiler flags):
+    ties recorded counter values to a kernel version."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_quantized_weight_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
+    with open(os.path.join(ROOT, "block_quantized_weight_amd", "build.py"), "rb") as fh:
+        h.update(b"build.py" + fh.read())
     return h.hexdigest()[:16]
 
 
