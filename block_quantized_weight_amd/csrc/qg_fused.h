@@ -459,6 +459,8 @@ template <int FMT>
 dense_ep_fn pick_dense_one_ep(int xt, int m, int u)
 {
     if constexpr (FMT == QG_Q8_0) {
+        if (u == 10)
+            return xt == QG_BF16 ? k_dense_one_ep<FMT, true, false, 1, 10> : k_dense_one_ep<FMT, false, false, 1, 10>;
         return xt == QG_BF16 ? k_dense_one_ep<FMT, true, false, 1, 8> : k_dense_one_ep<FMT, false, false, 1, 8>;
     } else {
         if (xt == QG_BF16)

@@ -201,10 +201,11 @@ def test_dense_path_rule():
     assert q.layout(q.Q4_0, 2560, 9728)["lanes_per_row"] == 16
     assert q.dense_path(q.Q4_0, 2560, 9728, q.X_BF16, 8) == V         # 16 lanes per row
     # one token (4-bit formats: up to 3) over short rows: the one-batch vector
-    # kernel (4-bit formats up to 20 steps per wave, Q8_0 up to 8)
+    # kernel (4-bit formats up to 20 steps per wave, Q8_0 up to 10)
     O = q.PATH_VALU_ONE
     assert q.dense_path(q.Q8_0, 2560, 4096, q.X_BF16, 1) == O         # 8 steps per lane
-    assert q.dense_path(q.Q8_0, 6144, 2560, q.X_BF16, 1) == V         # 10
+    assert q.dense_path(q.Q8_0, 6144, 2560, q.X_BF16, 1) == O         # 10
+    assert q.dense_path(q.Q8_0, 2560, 9728, q.X_BF16, 1) == V         # 38
     assert q.dense_path(q.Q8_0, 2048, 2048, q.X_F32, 1) == O
     assert q.dense_path(q.Q4_0, 2560, 9728, q.X_BF16, 1) == O         # 19
     assert q.dense_path(q.Q4_0, 19456, 2560, q.X_BF16, 1) == O        # 40 over 4 waves

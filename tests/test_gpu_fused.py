@@ -139,6 +139,19 @@ def test_fused_plain_matches_one_batch_bitwise(dev, fmt, n, k, m):
     assert torch.equal(y, yp)
 
 
+@pytest.mark.parametrize("n,k", [(4100, 2560), (2060, 4096)])
+def test_fused_plain_matches_one_batch_bitwise_q8_0(dev, n, k):
+    # Q8_0 one token: 10 and 8 steps per wave, the one-batch kernel's two Q8_0
+    # variants; nothing fused, so the same bits as qgemv
+    assert q.dense_path(q.Q8_0, n, k, q.X_BF16, 1) == q.PATH_VALU_ONE
+    c = Case(q.Q8_0, n, k, 1, oracle.X_BF16, False, NONE, False, False, matrix=61 + n % 7, xscale=1.0)
+    say(c.label(), "vs one-batch qgemv")
+    w, y = c.run(dev)
+    yp = q.qgemv(q.Q8_0, w, n, k, x_dev(c.x, c.xt, dev))
+    torch.cuda.synchronize()
+    assert torch.equal(y, yp)
+
+
 def test_fused_residual_in_place_and_deterministic(dev):
     c = Case(q.Q4_0, 2048, 2560, 4, oracle.X_BF16, True, SWIGLU, True, False, matrix=50)
     say(c.label(), "in place")
