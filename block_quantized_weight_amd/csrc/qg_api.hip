@@ -298,12 +298,18 @@ Plan make_plan(const Layout &lo, int M, bool dot, int maxslots_lds)
     // the steps of a tile or of a window.  A single token over short rows (at
     // most 20 steps per lane) runs unsplit: the cross-wave reduction then
     // costs more than it saves (MI355X: -0.7 to -1.0 us per launch on the
-    // 2560..6144-row decode matrices).  Co-batches keep the split, which also
-    // spreads their heavier per-step arithmetic.
+    // 2560..6144-row decode matrices).  The 4-bit formats with bf16
+    // activations (dot) keep the split from 16 steps per lane on (one token,
+    // us unsplit / split: Q4_0 2560x9728
+    // 8.14 / 7.63, 2048x8192 7.07 / 5.91, 4096x4096 7.05 / 5.80; NVFP4
+    // 2560x9728 8.67 / 7.63; at 12 steps mixed, 3072x6144 Q4_0 6.39 / 6.51).
+    // Co-batches keep the split, which also spreads their heavier per-step
+    // arithmetic.
     int KS = 1;
     if (lo.tiles < 4096) KS = 2;
     if (lo.tiles < 2048) KS = 4;
-    if (M == 1 && lo.S <= 20) KS = 1;
+    const bool four_bit = lo.fmt != QG_Q8_0 && !is_kq(lo.fmt);
+    if (M == 1 && lo.S <= 20 && !(four_bit && dot && lo.S >= 16)) KS = 1;
     while (KS > 1 && (lo.S < KS || sw_max < KS)) KS >>= 1;
     g.KS = KS;
     g.ksh = ilog2(KS);
