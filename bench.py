@@ -44,6 +44,8 @@ def parse():
                          "between products); graph: the 145 launches replayed from one captured HIP graph; "
                          "eager: the 145 launches issued one by one")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-others", action="store_true",
+                    help="c2: skip the other workloads (c0, c1, c3, c4) measured after the sweep")
     ap.add_argument("--no-events", action="store_true", help="skip the roofline / per-shape timing pass")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
@@ -107,8 +109,9 @@ def mfma_issued(fmt, n, k):
     return units * S * per_step
 
 
-def run_other(args):
-    """Per-launch throughput of the other workloads (one JSON line per case)."""
+def run_other(args, collect=None):
+    """Per-launch throughput of the other workloads (one JSON line per case;
+    with `collect` a list, the lines are appended to it instead of printed)."""
     import torch
     import block_quantized_weight_amd as q
 
@@ -135,7 +138,10 @@ def run_other(args):
                 "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
                 "config": {"workload": name}, "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
         line.update(extra)
-        print(json.dumps(line), flush=True)
+        if collect is not None:
+            collect.append(line)
+        else:
+            print(json.dumps(line), flush=True)
 
     def dense_case(cfg, mats, xt, ms, label, fmt=None):
         """mats: [(name, n, k, matrix index)]; times each matrix and the whole set
@@ -751,6 +757,7 @@ def main():
                                " for these kernel sources (null if the sources changed since)",
                     "trace_mean_gemv_us": trace_us,
                     "trace_source": os.path.relpath(TRACE_FILE, ROOT)}}
+        sink = torch.empty(q.STREAM_SINK, dtype=torch.int32, device=dev)
         groups = {}
         for i, (_, name, n, k) in enumerate(shapes):
             groups.setdefault(name.split(".")[-1], []).append(i)
@@ -760,11 +767,40 @@ def main():
                     _, _, n, k = shapes[i]
                     q.qgemv(fmt, wviews[i], n, k, xs[i], y=ys[i])
             us = graph_time(torch, launches, 5) / len(idx)
+
+            def reads(idx=idx):
+                for i in idx:
+                    q.read_stream(wviews[i], sink)
+            rus = graph_time(torch, reads, 5) / len(idx)
             _, _, n, k = shapes[idx[0]]
             per_shape[key] = {"n": n, "k": k, "bytes": alg[idx[0]], "us": round(us, 3),
-                              "gbs": round(alg[idx[0]] / us / 1e3, 1), "launches": len(idx)}
+                              "gbs": round(alg[idx[0]] / us / 1e3, 1), "launches": len(idx),
+                              "read_only_us": round(rus, 3)}
         roof["basis"]["per_shape_sum_us"] = round(sum(v["us"] * v["launches"] for v in per_shape.values()), 1)
         log(args, f"roofline {roof}; per shape {per_shape}")
+
+        # The same 145 launches as plain reads of the same bytes (qg_read_stream over each
+        # matrix's packed weights, one graph): what this launch structure allows a kernel that
+        # only streams; and the launch floor alone (the same call over 256 bytes).
+        tiny = wbuf[:256]
+
+        def read_launches():
+            for i in range(len(shapes)):
+                q.read_stream(wviews[i], sink)
+
+        def empty_launches():
+            for _ in range(len(shapes)):
+                q.read_stream(tiny, sink)
+        reps = max(3, args.steps // 3)
+        read_us = graph_time(torch, read_launches, reps)
+        floor_us = graph_time(torch, empty_launches, reps) / len(shapes)
+        packed_total = sum(q.packed_bytes(fmt, n, k) for (_, _, n, k) in shapes)
+        read_sweep = {"us": round(read_us, 1), "gbs": round(packed_total / read_us / 1e3, 1),
+                      "gemv_step_over_read_step": round(ms_step * 1e3 / read_us, 4),
+                      "launch_floor_us": round(floor_us, 3),
+                      "kernel": "qg_read_stream (16-byte nontemporal loads, every byte once)"}
+        roof["same_launches_read_only"] = read_sweep
+        log(args, f"read-only sweep of the same launches: {read_sweep}")
 
     if args.calib_copy_mib:
         nb = args.calib_copy_mib << 20
@@ -774,6 +810,23 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         log(args, f"calibration copy of {nb} bytes done")
+
+    # ---- the other workloads, measured in the same run (same code as --workload c0/c1/c3/c4)
+    others = None
+    if not args.no_events and not args.no_others:
+        lines = []
+        for wk in ("c0", "c1", "c3", "c4"):
+            sub = argparse.Namespace(**vars(args))
+            sub.workload, sub.calib_copy_mib = wk, 0
+            run_other(sub, collect=lines)
+        others = {}
+        for ln in lines:
+            e = {"us": round(ln["ms_per_step"] * 1e3, 3), "gbs": ln["value"], "pct_of_peak": ln["pct_of_peak"]}
+            for key in ("per_matrix", "per_mode"):
+                if key in ln:
+                    e[key] = {nm: {f: v[f] for f in ("us", "gbs", "path") if f in v} for nm, v in ln[key].items()}
+            others[ln["config"]["workload"]] = e
+        log(args, f"other workloads: {others}")
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample of the same workload
     cpu = None
@@ -833,6 +886,7 @@ def main():
         "roofline": roof,
         "eager_us_per_step": None if eager_us is None else round(eager_us, 1),
         "per_shape": per_shape or None,
+        "other_workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
