@@ -457,7 +457,10 @@ MPlan make_mplan(const Layout &lo, int m, int passes = 0, int TG = 1)
 // one_waves per compute unit, its LDS may allow fewer).  A grid that needs
 // two rounds loses to the batched pass (MI355X, Q4_0 24576x4096 at two
 // tokens, 768 workgroups of 16 steps per wave: 18.9 us batched, 21.2 one
-// batch at 2 per compute unit).
+// batch at 2 per compute unit).  One exception, measured: Q8_0 with bf16
+// activations at one token takes up to 1.25x the resident grid (19456x2560,
+// 608 workgroups of 10 steps per wave at 2 per unit: 13.56 -> 13.15 us; 36
+// decode layers 1284 -> 1269 us; bitwise the same results).
 int one_batch(int fmt, int xt, const Plan &p, int64_t m)
 {
     const Geom &g = p.g;
@@ -468,7 +471,9 @@ int one_batch(int fmt, int xt, const Plan &p, int64_t m)
     int per_cu = one_waves(fmt, xt == QG_BF16, u) * WAVES / (p.threads / 64);
     const int lds_cu = p.lds > 0 ? (int)((160 * 1024) / p.lds) : per_cu;
     if (lds_cu < per_cu) per_cu = lds_cu;
-    return p.grid <= per_cu * QG_CUS ? u : 0;
+    const int64_t resident = (int64_t)per_cu * QG_CUS;
+    if (fmt == QG_Q8_0 && xt == QG_BF16 && m == 1) return 4 * (int64_t)p.grid <= 5 * resident ? u : 0;
+    return p.grid <= resident ? u : 0;
 }
 
 // The kernel family of a dense call.  bf16 co-batches run on the matrix

@@ -221,6 +221,10 @@ def test_dense_path_rule():
     assert q.dense_path(q.Q4_0, 24576, 4096, q.X_BF16, 3) == M
     assert q.dense_path(q.Q4_0, 24576, 4096, q.X_F32, 2) == V
     assert q.dense_path(q.Q4_0, 24576, 4096, q.X_BF16, 1) == V
+    # Q8_0 with bf16 activations at one token allows a short second round: 608
+    # workgroups of 10 steps per wave against 512 resident
+    assert q.dense_path(q.Q8_0, 19456, 2560, q.X_BF16, 1) == O
+    assert q.dense_path(q.Q8_0, 19456, 2560, q.X_F32, 1) == V
     assert q.dense_path(q.Q4_0, 6144, 4096, q.X_BF16, 2) == O          # 768 of 4 steps: 4 per unit
     for bad in [(q.Q8_0, 64, 33, q.X_BF16, 1), (q.Q8_0, 64, 64, q.X_BF16, 0), (q.Q8_0, 64, 64, q.X_BF16, 9),
                 (q.Q8_0, 64, 64, 5, 1), (9, 64, 64, q.X_BF16, 1), (q.Q8_0, 0, 64, q.X_BF16, 1)]:
