@@ -39,6 +39,8 @@ struct MoeItems {
     int e[64];
     int n[64];
     int s[64][QG_MAX_M];
+    int tk[64][QG_MAX_M];       // the token of each slot (slot / top_k), divided once here
+    float g[64][QG_MAX_M];      // down-combine: each slot's router weight, read with the ids
 };
 
 // Slot -> staged activation row of one item (uniform over the wave).
@@ -56,7 +58,8 @@ struct SlotMap {
 // order.  Two passes of lane reads (v_readlane) in which every lane works out
 // its own slot's place -- one over the slots, one over the distinct experts
 // -- so no step waits on LDS.  The caller synchronises afterwards.
-__device__ __forceinline__ void route_items(int id, int nslots, int n_experts, int ms, MoeItems *it)
+__device__ __forceinline__ void route_items(int id, float gw, int nslots, int n_experts, int ms, int top_k,
+                                            MoeItems *it)
 {
     const int lane = threadIdx.x & 63;
     const bool valid = lane < nslots && id >= 0 && id < n_experts;
@@ -82,6 +85,8 @@ __device__ __forceinline__ void route_items(int id, int nslots, int n_experts, i
     if (valid) {
         const int item = base + before / ms, pos = before - (before / ms) * ms;
         it->s[item][pos] = lane;
+        it->tk[item][pos] = lane / top_k;
+        it->g[item][pos] = gw;
         if (pos == 0) {
             it->e[item] = e;
             it->n[item] = min(ms, same - before);
@@ -176,7 +181,10 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
         return (const uint8_t *)x + ((int64_t)r * g.k + (int64_t)min(bl, g.nb - 1) * QK) * (XBF16 ? 2 : 4);
     };
     const int my_id = a.ids[min(lane, nslots - 1)];    // lanes past the slots are ignored by the routing
-    // keep this load ahead of the activation loads (the memory counter is in
+    // down-combine: the slot's router weight, loaded here beside its id (read
+    // inside the weight stream, it would wait for the weight batch in flight)
+    const float my_gw = MODE == QG_MOE_DOWN_COMBINE ? a.gw[min(lane, nslots - 1)] : 0.0f;
+    // keep these loads ahead of the activation loads (the memory counter is in
     // order, so the routing would otherwise wait for all of them)
     __builtin_amdgcn_sched_barrier(0);
     // a fixed number of loads (units past the end repeat the last one), so
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
         for (int i = 0; i < NLD; ++i) pre[p][i] = ld_global16(src + 16 * i);
     }
 
-    if (wave == 0) route_items(my_id, nslots, a.n_experts, MS, &it);
+    if (wave == 0) route_items(my_id, my_gw, nslots, a.n_experts, MS, a.top_k, &it);
     __syncthreads();
     const int ni = it.count;
     // with the gate (PP = tpi / 2 pairs per workgroup): tile slots [0, PP)
@@ -297,8 +305,8 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
         sm.n = it.n[i];
 #pragma unroll
         for (int t = 0; t < MS; ++t) {
-            const int sid = it.s[i][min(t, sm.n - 1)];
-            sm.r[t] = MODE == QG_MOE_GATE_UP ? sid / a.top_k : sid;
+            const int q = min(t, sm.n - 1);
+            sm.r[t] = MODE == QG_MOE_GATE_UP ? it.tk[i][q] : it.s[i][q];
         }
         float acc[MS];
 #pragma unroll
@@ -341,9 +349,8 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
 #pragma unroll
             for (int t = 0; t < MS; ++t) {
                 if (t >= sm.n) break;
-                const int sid = it.s[i][t];
-                const float gw = a.gw[sid];
-                const int tk = sid / a.top_k;
+                const float gw = it.g[i][t];
+                const int tk = it.tk[i][t];
 #pragma unroll
                 for (int q = 0; q < QG_MAX_M; ++q)
                     if (q == tk) tok[q] = __builtin_fmaf(gw, acc[t], tok[q]);
