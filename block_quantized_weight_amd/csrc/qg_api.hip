@@ -1027,6 +1027,14 @@ static int moe_impl(int fmt, const void *w_experts, int64_t n_experts, int64_t n
         int IS = 1;
         if (lo.tiles < 4096) IS = 2;
         if (mode == QG_MOE_DOWN_COMBINE && lo.tiles < 2048) IS = 4;
+        // the plain gate_up of several tokens over short items (<= 4 steps per
+        // lane) splits them over four waves in batches of 4 steps: twice the
+        // waves, half the weight registers each (MI355X, 3584x2048 MXFP4 at four
+        // tokens: 23.3 -> 18.7 us; at one token 9.3 -> 9.7, so not there;
+        // down-combine, already four waves per tile, in batches of 4 steps:
+        // 18.2 -> 18.6, not taken)
+        const bool short_items = mode == QG_MOE_GATE_UP && !norm && !glu && m > 1 && lo.S <= 4;
+        if (short_items && lo.tiles < 2048) IS = 4;
         a.isplit = IS;
         g.KS = 1;
         g.ksh = 0;
@@ -1040,9 +1048,9 @@ static int moe_impl(int fmt, const void *w_experts, int64_t n_experts, int64_t n
         if (lds <= (glu ? MOE_STREAM_LDS_GLU : MOE_STREAM_LDS) && g.ngroups <= 65535) {
             g.w = (const uint8_t *)w_experts;
             const int ms = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
-            moe_stream_fn f = fmt == QG_Q8_0 ? moe_stream_kernel_q8_0(xt, mode, ms, norm, glu)
-                              : fmt == QG_Q4_0 ? moe_stream_kernel_q4_0(xt, mode, ms, norm, glu)
-                                               : moe_stream_kernel_mxfp4(xt, mode, ms, norm, glu);
+            moe_stream_fn f = fmt == QG_Q8_0 ? moe_stream_kernel_q8_0(xt, mode, ms, norm, glu, short_items)
+                              : fmt == QG_Q4_0 ? moe_stream_kernel_q4_0(xt, mode, ms, norm, glu, short_items)
+                                               : moe_stream_kernel_mxfp4(xt, mode, ms, norm, glu, short_items);
             void *args[] = {(void *)&g, (void *)&a, (void *)&e, (void *)&x};
             if (allow_lds((const void *)f, lds) != hipSuccess) return QG_EHIP;
             hipError_t err = hipLaunchKernel((const void *)f, dim3(g.ngroups), dim3(TPB), args, lds, s);

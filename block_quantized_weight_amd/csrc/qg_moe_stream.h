@@ -149,12 +149,12 @@ inline __host__ __device__ size_t moe_stream_lds(int fmt, bool dot, int nrows, i
 // the gate: gate tiles, e.half_tiles of them); one (tile, item subset) per
 // wave.  Geom: KS = 1, one activation window over K.  NORM (gate_up only):
 // stage x * gamma in fp32 (DOT false).  GLU (gate_up only): SwiGLU.
-template <int FMT, bool XBF16, bool DOT, int MS, int MODE, bool NORM, bool GLU>
+template <int FMT, bool XBF16, bool DOT, int MS, int MODE, bool NORM, bool GLU, int UB = Batch<FMT, DOT>::U>
 __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e, const void *__restrict__ x)
 {
     static_assert(!NORM || !DOT, "normalised rows are staged in fp32");
     static_assert(MODE == QG_MOE_GATE_UP || (!NORM && !GLU), "down-combine fuses only the residual");
-    using E = Engine<FMT, XBF16, DOT, MS>;
+    using E = Engine<FMT, XBF16, DOT, MS, UB>;
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ MoeItems it;
     __shared__ float s_part[WAVES * QG_MAX_M];
@@ -402,33 +402,35 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
 
 typedef void (*moe_stream_fn)(Geom, MoeArgs, EpiArgs, const void *);
 
-template <int FMT, bool XBF16, bool DOT, int MODE, bool NORM, bool GLU>
+template <int FMT, bool XBF16, bool DOT, int MODE, bool NORM, bool GLU, int UB = Batch<FMT, DOT>::U>
 moe_stream_fn pick_moe_stream_ms(int ms)
 {
     switch (ms) {
-    case 1: return k_moe_stream<FMT, XBF16, DOT, 1, MODE, NORM, GLU>;
-    case 2: return k_moe_stream<FMT, XBF16, DOT, 2, MODE, NORM, GLU>;
-    case 4: return k_moe_stream<FMT, XBF16, DOT, 4, MODE, NORM, GLU>;
-    default: return k_moe_stream<FMT, XBF16, DOT, 8, MODE, NORM, GLU>;
+    case 1: return k_moe_stream<FMT, XBF16, DOT, 1, MODE, NORM, GLU, UB>;
+    case 2: return k_moe_stream<FMT, XBF16, DOT, 2, MODE, NORM, GLU, UB>;
+    case 4: return k_moe_stream<FMT, XBF16, DOT, 4, MODE, NORM, GLU, UB>;
+    default: return k_moe_stream<FMT, XBF16, DOT, 8, MODE, NORM, GLU, UB>;
     }
 }
 
 // gate_up: the plain form, or normalised and/or gated (normalised rows are
 // staged in fp32, so those kernels take DOT false); down-combine: one form
-// (residual and output type are arguments).
+// (residual and output type are arguments).  short_items: the plain gate_up
+// over items of at most 4 steps per lane, in batches of 4 steps.
 template <int FMT, bool XBF16, bool DOT>
-moe_stream_fn pick_moe_stream(int mode, int ms, bool norm, bool glu)
+moe_stream_fn pick_moe_stream(int mode, int ms, bool norm, bool glu, bool short_items)
 {
     if (mode == QG_MOE_DOWN_COMBINE) return pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_DOWN_COMBINE, false, false>(ms);
     if (norm)
         return glu ? pick_moe_stream_ms<FMT, XBF16, false, QG_MOE_GATE_UP, true, true>(ms)
                    : pick_moe_stream_ms<FMT, XBF16, false, QG_MOE_GATE_UP, true, false>(ms);
-    return glu ? pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_GATE_UP, false, true>(ms)
-               : pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_GATE_UP, false, false>(ms);
+    if (glu) return pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_GATE_UP, false, true>(ms);
+    return short_items ? pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_GATE_UP, false, false, 4>(ms)
+                       : pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_GATE_UP, false, false>(ms);
 }
 
-moe_stream_fn moe_stream_kernel_q8_0(int xt, int mode, int ms, bool norm, bool glu);
-moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms, bool norm, bool glu);
-moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms, bool norm, bool glu);
+moe_stream_fn moe_stream_kernel_q8_0(int xt, int mode, int ms, bool norm, bool glu, bool short_items);
+moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms, bool norm, bool glu, bool short_items);
+moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms, bool norm, bool glu, bool short_items);
 
 } // namespace qg
