@@ -1006,8 +1006,14 @@ static int moe_impl(int fmt, const void *w_experts, int64_t n_experts, int64_t n
         // streaming kernel: every activation row of the call staged at once
         // (normalised rows in fp32)
         const int nrows = (int)(mode == QG_MOE_GATE_UP ? m : m * top_k);
+        // down-combine of several tokens over few tiles: workgroups of
+        // WIDE_WAVES waves, all splitting one tile's items (twice the waves of
+        // the four-wave form, two per SIMD where the tiles fill the CUs once)
+        const bool wide = mode == QG_MOE_DOWN_COMBINE && m > 1 && lo.tiles <= QG_CUS &&
+                          moe_stream_lds(fmt, dot, nrows, (int)(lo.S * lo.L), mode, 0, 0, WIDE_WAVES) <= MOE_STREAM_LDS;
+        const int nw = wide ? WIDE_WAVES : WAVES;
         const size_t lds = moe_stream_lds(fmt, dot && !norm, nrows, (int)(lo.S * lo.L), mode,
-                                          glu ? (int)(m * top_k) : 0, lo.R);
+                                          glu ? (int)(m * top_k) : 0, lo.R, nw);
         Geom g{};
         g.n = (int32_t)lo.n;
         g.k = (int32_t)lo.k;
@@ -1035,10 +1041,11 @@ static int moe_impl(int fmt, const void *w_experts, int64_t n_experts, int64_t n
         // 18.2 -> 18.6, not taken)
         const bool short_items = mode == QG_MOE_GATE_UP && !norm && !glu && m > 1 && lo.S <= 4;
         if (short_items && lo.tiles < 2048) IS = 4;
+        if (wide) IS = WIDE_WAVES;
         a.isplit = IS;
         g.KS = 1;
         g.ksh = 0;
-        g.tpi = WAVES / IS;
+        g.tpi = nw / IS;
         // with the gate a workgroup holds tpi / 2 gate/up tile pairs
         g.ngroups = glu ? (int32_t)((e.half_tiles + g.tpi / 2 - 1) / (g.tpi / 2))
                         : (int32_t)((lo.tiles + g.tpi - 1) / g.tpi);
@@ -1048,12 +1055,12 @@ static int moe_impl(int fmt, const void *w_experts, int64_t n_experts, int64_t n
         if (lds <= (glu ? MOE_STREAM_LDS_GLU : MOE_STREAM_LDS) && g.ngroups <= 65535) {
             g.w = (const uint8_t *)w_experts;
             const int ms = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
-            moe_stream_fn f = fmt == QG_Q8_0 ? moe_stream_kernel_q8_0(xt, mode, ms, norm, glu, short_items)
-                              : fmt == QG_Q4_0 ? moe_stream_kernel_q4_0(xt, mode, ms, norm, glu, short_items)
-                                               : moe_stream_kernel_mxfp4(xt, mode, ms, norm, glu, short_items);
+            moe_stream_fn f = fmt == QG_Q8_0 ? moe_stream_kernel_q8_0(xt, mode, ms, norm, glu, short_items, wide)
+                              : fmt == QG_Q4_0 ? moe_stream_kernel_q4_0(xt, mode, ms, norm, glu, short_items, wide)
+                                               : moe_stream_kernel_mxfp4(xt, mode, ms, norm, glu, short_items, wide);
             void *args[] = {(void *)&g, (void *)&a, (void *)&e, (void *)&x};
             if (allow_lds((const void *)f, lds) != hipSuccess) return QG_EHIP;
-            hipError_t err = hipLaunchKernel((const void *)f, dim3(g.ngroups), dim3(TPB), args, lds, s);
+            hipError_t err = hipLaunchKernel((const void *)f, dim3(g.ngroups), dim3(64 * nw), args, lds, s);
             return err == hipSuccess ? launch_status() : QG_EHIP;
         }
     }

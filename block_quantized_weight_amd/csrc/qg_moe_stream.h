@@ -137,27 +137,29 @@ __device__ __forceinline__ bool stream_item(const Geom &g, const ItemWork &w, co
 // Dynamic LDS: staged rows, then down-combine's split partials or, with the
 // gate, the per-slot row totals of the tile pairs.
 inline __host__ __device__ size_t moe_stream_lds(int fmt, bool dot, int nrows, int wblk, int mode, int glu_slots = 0,
-                                                 int rows_per_tile = 0)
+                                                 int rows_per_tile = 0, int nw = WAVES)
 {
     size_t b = (size_t)nrows * x_quads(fmt, dot) * wblk * 16;
-    if (mode == QG_MOE_DOWN_COMBINE) b += (size_t)WAVES * QG_MAX_M * 64 * 4;
+    if (mode == QG_MOE_DOWN_COMBINE) b += (size_t)nw * QG_MAX_M * 64 * 4;
     if (glu_slots) b += (size_t)WAVES * glu_slots * rows_per_tile * 4;
     return b;
 }
 
-// grid = ceil(tiles / tpi) workgroups, tpi = WAVES / IS tiles each (with
+// grid = ceil(tiles / tpi) workgroups, tpi = NW / IS tiles each (with
 // the gate: gate tiles, e.half_tiles of them); one (tile, item subset) per
 // wave.  Geom: KS = 1, one activation window over K.  NORM (gate_up only):
 // stage x * gamma in fp32 (DOT false).  GLU (gate_up only): SwiGLU.
-template <int FMT, bool XBF16, bool DOT, int MS, int MODE, bool NORM, bool GLU, int UB = Batch<FMT, DOT>::U>
-__global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e, const void *__restrict__ x)
+template <int FMT, bool XBF16, bool DOT, int MS, int MODE, bool NORM, bool GLU, int UB = Batch<FMT, DOT>::U,
+          int NW = WAVES>
+__global__ __launch_bounds__(64 * NW) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e, const void *__restrict__ x)
 {
     static_assert(!NORM || !DOT, "normalised rows are staged in fp32");
     static_assert(MODE == QG_MOE_GATE_UP || (!NORM && !GLU), "down-combine fuses only the residual");
+    static_assert(NW == WAVES || MODE == QG_MOE_DOWN_COMBINE, "wider workgroups serve down-combine only");
     using E = Engine<FMT, XBF16, DOT, MS, UB>;
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ MoeItems it;
-    __shared__ float s_part[WAVES * QG_MAX_M];
+    __shared__ float s_part[NW * QG_MAX_M];
     constexpr int QPB = x_quads(FMT, DOT);
     const int nslots = a.m * a.top_k;
     const int nrows = MODE == QG_MOE_GATE_UP ? a.m : nslots;
@@ -402,25 +404,30 @@ __global__ __launch_bounds__(TPB) void k_moe_stream(Geom g, MoeArgs a, EpiArgs e
 
 typedef void (*moe_stream_fn)(Geom, MoeArgs, EpiArgs, const void *);
 
-template <int FMT, bool XBF16, bool DOT, int MODE, bool NORM, bool GLU, int UB = Batch<FMT, DOT>::U>
+template <int FMT, bool XBF16, bool DOT, int MODE, bool NORM, bool GLU, int UB = Batch<FMT, DOT>::U, int NW = WAVES>
 moe_stream_fn pick_moe_stream_ms(int ms)
 {
     switch (ms) {
-    case 1: return k_moe_stream<FMT, XBF16, DOT, 1, MODE, NORM, GLU, UB>;
-    case 2: return k_moe_stream<FMT, XBF16, DOT, 2, MODE, NORM, GLU, UB>;
-    case 4: return k_moe_stream<FMT, XBF16, DOT, 4, MODE, NORM, GLU, UB>;
-    default: return k_moe_stream<FMT, XBF16, DOT, 8, MODE, NORM, GLU, UB>;
+    case 1: return k_moe_stream<FMT, XBF16, DOT, 1, MODE, NORM, GLU, UB, NW>;
+    case 2: return k_moe_stream<FMT, XBF16, DOT, 2, MODE, NORM, GLU, UB, NW>;
+    case 4: return k_moe_stream<FMT, XBF16, DOT, 4, MODE, NORM, GLU, UB, NW>;
+    default: return k_moe_stream<FMT, XBF16, DOT, 8, MODE, NORM, GLU, UB, NW>;
     }
 }
 
 // gate_up: the plain form, or normalised and/or gated (normalised rows are
 // staged in fp32, so those kernels take DOT false); down-combine: one form
 // (residual and output type are arguments).  short_items: the plain gate_up
-// over items of at most 4 steps per lane, in batches of 4 steps.
+// over items of at most 4 steps per lane, in batches of 4 steps; wide:
+// down-combine in workgroups of WIDE_WAVES waves.
+constexpr int WIDE_WAVES = 8;
 template <int FMT, bool XBF16, bool DOT>
-moe_stream_fn pick_moe_stream(int mode, int ms, bool norm, bool glu, bool short_items)
+moe_stream_fn pick_moe_stream(int mode, int ms, bool norm, bool glu, bool short_items, bool wide)
 {
-    if (mode == QG_MOE_DOWN_COMBINE) return pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_DOWN_COMBINE, false, false>(ms);
+    if (mode == QG_MOE_DOWN_COMBINE)
+        return wide ? pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_DOWN_COMBINE, false, false, Batch<FMT, DOT>::U,
+                                         WIDE_WAVES>(ms)
+                    : pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_DOWN_COMBINE, false, false>(ms);
     if (norm)
         return glu ? pick_moe_stream_ms<FMT, XBF16, false, QG_MOE_GATE_UP, true, true>(ms)
                    : pick_moe_stream_ms<FMT, XBF16, false, QG_MOE_GATE_UP, true, false>(ms);
@@ -429,8 +436,11 @@ moe_stream_fn pick_moe_stream(int mode, int ms, bool norm, bool glu, bool short_
                        : pick_moe_stream_ms<FMT, XBF16, DOT, QG_MOE_GATE_UP, false, false>(ms);
 }
 
-moe_stream_fn moe_stream_kernel_q8_0(int xt, int mode, int ms, bool norm, bool glu, bool short_items);
-moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms, bool norm, bool glu, bool short_items);
-moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms, bool norm, bool glu, bool short_items);
+moe_stream_fn moe_stream_kernel_q8_0(int xt, int mode, int ms, bool norm, bool glu, bool short_items,
+                                     bool wide);
+moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms, bool norm, bool glu, bool short_items,
+                                     bool wide);
+moe_stream_fn moe_stream_kernel_mxfp4(int xt, int mode, int ms, bool norm, bool glu, bool short_items,
+                                     bool wide);
 
 } // namespace qg

@@ -32,10 +32,11 @@ int chain_error_q4_0(bool clear) { return chain_error_read(clear); }
 
 mfma_fn mfma_kernel_q4_0(int L, int tg) { return pick_mfma<QG_Q4_0>(L, tg); }
 
-moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms, bool norm, bool glu, bool short_items)
+moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms, bool norm, bool glu, bool short_items,
+                                     bool wide)
 {
-    return xt == QG_BF16 ? pick_moe_stream<QG_Q4_0, true, true>(mode, ms, norm, glu, short_items)
-                         : pick_moe_stream<QG_Q4_0, false, false>(mode, ms, norm, glu, short_items);
+    return xt == QG_BF16 ? pick_moe_stream<QG_Q4_0, true, true>(mode, ms, norm, glu, short_items, wide)
+                         : pick_moe_stream<QG_Q4_0, false, false>(mode, ms, norm, glu, short_items, wide);
 }
 
 dense_ep_fn dense_one_ep_kernel_q4_0(int xt, int m, int u) { return pick_dense_one_ep<QG_Q4_0>(xt, m, u); }
