@@ -369,6 +369,7 @@ struct MPlan {
     MGeom g;
     size_t lds;
     int grid;
+    int nw;                      // waves per workgroup
 };
 
 // The matrix-core kernel serves bf16 activations, layouts of 1 to 8 lanes per
@@ -389,9 +390,10 @@ bool mfma_fits(const Layout &lo, int xt, int64_t m)
 // Measured on MI355X, Q4_0 at 64 tokens: 6144x4096 28.6 us unsplit (384
 // workgroups) against 35.6 split in two; 4096x12288 52.0 us split in two
 // against 59.0 unsplit (256 workgroups).
-MPlan make_mplan(const Layout &lo, int m, int passes = 0, int TG = 1)
+MPlan make_mplan(const Layout &lo, int m, int passes = 0, int TG = 1, int waves = WAVES)
 {
     MPlan p{};
+    p.nw = waves;
     MGeom &g = p.g;
     g.n = (int32_t)lo.n;
     g.k = (int32_t)lo.k;
@@ -410,11 +412,11 @@ MPlan make_mplan(const Layout &lo, int m, int passes = 0, int TG = 1)
     int64_t budget = MFMA_WG_LDS;
     // activation window: as many steps as fit beside the fixed areas (at least one)
     auto sw_for = [&](int ks) {
-        const int64_t xbudget = budget - (int64_t)mfma_lds_bytes(lo.fmt, m, 0, lo.L, ks, TG);
+        const int64_t xbudget = budget - (int64_t)mfma_lds_bytes(lo.fmt, m, 0, lo.L, ks, TG, waves);
         const int64_t v = (xbudget / (int64_t)per_block) / lo.L;
         return v < 1 ? (int64_t)1 : v;
     };
-    auto groups = [&](int ks) { return (g.units + WAVES / ks - 1) / (WAVES / ks); };
+    auto groups = [&](int ks) { return (g.units + waves / ks - 1) / (waves / ks); };
     int KS = 1;
     if (passes > 0) {
         while (KS < WAVES && groups(KS) * passes < 300) KS <<= 1;
@@ -427,13 +429,16 @@ MPlan make_mplan(const Layout &lo, int m, int passes = 0, int TG = 1)
         // 10.35 / 11.00 us, 24576x4096 20.28 / 21.14, Q8_0 11.10 / 15.82 and
         // 27.80 / 31.68; 4096x12288 (256 units) 27.99 / 22.25 keeps 4.
         if (m > 4 && g.units >= 384 && KS > 2) KS = 2;
+        // eight-wave workgroups: a unit's steps over all eight waves where the
+        // units fit the compute units once, else two units of four waves each
+        if (waves == MFMA_WIDE_WAVES) KS = g.units <= QG_CUS ? 8 : 4;
         if (groups(KS) <= QG_CUS) budget = MFMA_WG_LDS_ONE;   // fewer KS only means fewer groups
     }
     while (KS > 1 && (lo.S < KS || sw_for(KS) < KS)) KS >>= 1;
     const int64_t sw_max = sw_for(KS);
     g.KS = KS;
     g.ksh = ilog2(KS);
-    g.upi = WAVES / KS;
+    g.upi = waves / KS;
     g.ngroups = (int32_t)((g.units + g.upi - 1) / g.upi);
     int64_t sw = sw_max / KS * KS;
     if (sw >= lo.S) sw = ((lo.S + KS - 1) / KS) * KS;
@@ -445,7 +450,7 @@ MPlan make_mplan(const Layout &lo, int m, int passes = 0, int TG = 1)
     g.SW = (int32_t)sw;
     g.nwin = (int32_t)((lo.S + sw - 1) / sw);
     g.wblk = (int32_t)(sw * lo.L);
-    p.lds = mfma_lds_bytes(lo.fmt, m, g.wblk, lo.L, KS, TG);
+    p.lds = mfma_lds_bytes(lo.fmt, m, g.wblk, lo.L, KS, TG, waves);
     p.grid = g.ngroups > 65535 ? 65535 : g.ngroups;
     return p;
 }
@@ -512,12 +517,15 @@ int dense(int fmt, const void *w, int64_t n, int64_t k, const void *x, int xt, i
     Plan p;
     int u = 0;
     if (dense_kind(fmt, lo, xt, m, p, u) == QG_PATH_MFMA) {
-        MPlan mp = make_mplan(lo, (int)m);
+        const int nw = lo.L == 8 && m >= 4 ? MFMA_WIDE_WAVES : WAVES;
+        MPlan mp = make_mplan(lo, (int)m, 0, 1, nw);
         mp.g.w = (const uint8_t *)w;
-        mfma_fn f = fmt == QG_Q8_0 ? mfma_kernel_q8_0(lo.L) : fmt == QG_Q4_0 ? mfma_kernel_q4_0(lo.L) : mfma_kernel_mxfp4(lo.L);
+        mfma_fn f = fmt == QG_Q8_0 ? mfma_kernel_q8_0(lo.L, 1, nw)
+                    : fmt == QG_Q4_0 ? mfma_kernel_q4_0(lo.L, 1, nw) : mfma_kernel_mxfp4(lo.L, 1, nw);
         void *args[] = {(void *)&mp.g, (void *)&x, (void *)&y};
         if (allow_lds((const void *)f, mp.lds) != hipSuccess) return QG_EHIP;
-        hipError_t e = hipLaunchKernel((const void *)f, dim3(mp.grid), dim3(TPB), args, mp.lds, as_stream(stream));
+        hipError_t e = hipLaunchKernel((const void *)f, dim3(mp.grid), dim3(64 * mp.nw), args, mp.lds,
+                                       as_stream(stream));
         return e == hipSuccess ? launch_status() : QG_EHIP;
     }
     p.g.w = (const uint8_t *)w;

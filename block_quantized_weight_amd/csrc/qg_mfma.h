@@ -86,19 +86,24 @@ inline __host__ __device__ int mfma_wave_bytes(int fmt, int LL)
 inline __host__ __device__ int gemm_groups(int LL, int64_t m) { return LL <= 2 && m > 16 ? 2 : 1; }
 
 // Split-K partials (present only when KS > 1).
-inline __host__ __device__ size_t mfma_red_bytes(int LL, int TG = 1)
+inline __host__ __device__ size_t mfma_red_bytes(int LL, int TG = 1, int nw = WAVES)
 {
     const int RG = LL >= 4 ? 1 : 4 / LL;
-    return (size_t)WAVES * TG * RG * 4 * 64 * 4;
+    return (size_t)nw * TG * RG * 4 * 64 * 4;
 }
 
-inline __host__ __device__ size_t mfma_lds_bytes(int fmt, int m, int wblk, int LL, int KS, int TG = 1)
+inline __host__ __device__ size_t mfma_lds_bytes(int fmt, int m, int wblk, int LL, int KS, int TG = 1, int nw = WAVES)
 {
     size_t b = (size_t)wblk * m * 64;                        // activations: [block][token][octet]
-    if (KS > 1) b += mfma_red_bytes(LL, TG);                 // split-K partials
-    b += (size_t)WAVES * mfma_wave_bytes(fmt, LL);           // transpose areas
+    if (KS > 1) b += mfma_red_bytes(LL, TG, nw);             // split-K partials
+    b += (size_t)nw * mfma_wave_bytes(fmt, LL);              // transpose areas
     return b;
 }
+
+// Waves per workgroup of the co-batch kernel on 8 lanes per row where its
+// units would otherwise run one wave per SIMD: eight, splitting each unit's
+// steps (or two units) over twice the waves with the same activation staging.
+constexpr int MFMA_WIDE_WAVES = 8;
 
 template <int FMT, int LL, int TG = 1>
 struct MEngine {
@@ -300,8 +305,8 @@ __device__ __forceinline__ void mfma_stage(const MGeom &g, const uint16_t *x, in
 // blockIdx.y: a pass over TG token groups of 16 (tokens 16*TG*y .. of the
 // call); the co-batch calls have one pass of one group.  LDS is planned for
 // min(m, 16*TG) tokens.
-template <int FMT, int LL, int TG>
-__global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restrict__ xv, float *__restrict__ yv)
+template <int FMT, int LL, int TG, int NW = WAVES>
+__global__ __launch_bounds__(64 * NW) void k_dense_mfma(MGeom g, const void *__restrict__ xv, float *__restrict__ yv)
 {
     using E = MEngine<FMT, LL, TG>;
     using Sh = MShape<LL>;
@@ -314,7 +319,7 @@ __global__ __launch_bounds__(TPB) void k_dense_mfma(MGeom g, const void *__restr
     const uint16_t *x = (const uint16_t *)xv + (int64_t)tb * g.k;
     float *y = yv + (int64_t)tb * g.n;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint8_t *wl = (uint8_t *)red + (g.KS > 1 ? mfma_red_bytes(LL, TG) : 0) + wave * mfma_wave_bytes(FMT, LL);
+    uint8_t *wl = (uint8_t *)red + (g.KS > 1 ? mfma_red_bytes(LL, TG, NW) : 0) + wave * mfma_wave_bytes(FMT, LL);
     const int usub = wave >> g.ksh, kpart = wave & (g.KS - 1);
     const int KS = g.KS;
     bool staged = false;
@@ -408,9 +413,10 @@ typedef void (*mfma_fn)(MGeom, const void *, float *);
 // tg: token groups per pass, 1 (co-batch calls, and qgemm where L > 2) or 2
 // (qgemm, L <= 2: gemm_groups).  L = 16 serves only qgemm.
 template <int FMT>
-mfma_fn pick_mfma(int L, int tg = 1)
+mfma_fn pick_mfma(int L, int tg = 1, int nw = WAVES)
 {
     if (tg == 2) return L == 1 ? k_dense_mfma<FMT, 1, 2> : k_dense_mfma<FMT, 2, 2>;
+    if (nw == MFMA_WIDE_WAVES) return k_dense_mfma<FMT, 8, 1, MFMA_WIDE_WAVES>;
     switch (L) {
     case 1: return k_dense_mfma<FMT, 1, 1>;
     case 2: return k_dense_mfma<FMT, 2, 1>;
@@ -420,8 +426,8 @@ mfma_fn pick_mfma(int L, int tg = 1)
     }
 }
 
-mfma_fn mfma_kernel_q8_0(int L, int tg = 1);
-mfma_fn mfma_kernel_q4_0(int L, int tg = 1);
-mfma_fn mfma_kernel_mxfp4(int L, int tg = 1);
+mfma_fn mfma_kernel_q8_0(int L, int tg = 1, int nw = WAVES);
+mfma_fn mfma_kernel_q4_0(int L, int tg = 1, int nw = WAVES);
+mfma_fn mfma_kernel_mxfp4(int L, int tg = 1, int nw = WAVES);
 
 } // namespace qg

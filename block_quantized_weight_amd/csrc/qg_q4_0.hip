@@ -30,7 +30,7 @@ const void *chain_kernel_q4_0(int xt, int m)
 
 int chain_error_q4_0(bool clear) { return chain_error_read(clear); }
 
-mfma_fn mfma_kernel_q4_0(int L, int tg) { return pick_mfma<QG_Q4_0>(L, tg); }
+mfma_fn mfma_kernel_q4_0(int L, int tg, int nw) { return pick_mfma<QG_Q4_0>(L, tg, nw); }
 
 moe_stream_fn moe_stream_kernel_q4_0(int xt, int mode, int ms, bool norm, bool glu, bool short_items,
                                      bool wide)
