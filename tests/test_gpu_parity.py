@@ -343,6 +343,23 @@ def test_mfma_cobatch(dev, fmt, n, k, L, m):
     assert err <= TOL, err
 
 
+# Eight-wave workgroups on 8 lanes per row (4+ tokens): the token counts the
+# matrix-core test above does not draw, with a ragged last unit and two windows.
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", [(5000, 2048), (4090, 12256)])
+@pytest.mark.parametrize("m", [6, 7])
+def test_mfma_cobatch_wide_token_counts(dev, fmt, n, k, m):
+    say(f"mfma wide fmt={fmt} n={n} k={k} m={m}")
+    assert q.layout(fmt, n, k)["lanes_per_row"] == 8
+    assert q.dense_path(fmt, n, k, q.X_BF16, m) == q.PATH_MFMA
+    canon = wl.blocks_for(fmt, n, k, config=72, matrix=n + m)
+    x = draw_x((m, k), oracle.X_BF16, 72, n + m)
+    y = run_dense(fmt, canon, n, k, x, oracle.X_BF16, dev)
+    ref, l1 = oracle.gemv(fmt, canon, n, k, x, oracle.X_BF16)
+    err = oracle.max_rel_err(y, ref, l1)
+    assert err <= TOL, err
+
+
 # Two and three tokens run on the matrix cores wherever the one-batch vector
 # kernel does not apply (long rows, or grids too large to be resident at once).
 @pytest.mark.parametrize("fmt", FMTS)
@@ -504,6 +521,21 @@ def test_moe_formats_and_shapes(dev, fmt, xt, mode):
     say(f"moe fmt={fmt} xt={xt} mode={mode}")
     _, ids, g = wl.router_topk(m, E, top_k, wl.rng_for(69, fmt, "router"))
     y, ref, l1 = _moe_case(dev, fmt, E, n, k, ids, g, xt, mode, 69)
+    assert oracle.max_rel_err(y, ref, l1) <= TOL
+
+
+# Several tokens over few tiles: down-combine in eight-wave workgroups (all of
+# them splitting one tile's items), gate_up over short items in four-wave
+# splits with batches of 4 steps; token counts and top-k around those paths.
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", [(200, 4096), (2048, 1792), (136, 608)])
+@pytest.mark.parametrize("m,top_k", [(2, 1), (3, 8), (5, 4), (8, 8)])
+@pytest.mark.parametrize("mode", [q.MOE_GATE_UP, q.MOE_DOWN_COMBINE])
+def test_moe_several_tokens_few_tiles(dev, fmt, n, k, m, top_k, mode):
+    E = 12
+    say(f"moe few tiles fmt={fmt} n={n} k={k} m={m} top_k={top_k} mode={mode}")
+    _, ids, g = wl.router_topk(m, E, top_k, wl.rng_for(71, m * 16 + top_k, "router"))
+    y, ref, l1 = _moe_case(dev, fmt, E, n, k, ids, g, oracle.X_BF16, mode, 71)
     assert oracle.max_rel_err(y, ref, l1) <= TOL
 
 
