@@ -524,12 +524,13 @@ def test_moe_formats_and_shapes(dev, fmt, xt, mode):
     assert oracle.max_rel_err(y, ref, l1) <= TOL
 
 
-# Several tokens over few tiles: down-combine in eight-wave workgroups (all of
-# them splitting one tile's items), gate_up over short items in four-wave
-# splits with batches of 4 steps; token counts and top-k around those paths.
+# Few tiles: down-combine of several tokens in eight-wave workgroups (all of
+# them splitting one tile's items), gate_up of several tokens over short items
+# in four-wave splits with batches of 4 steps, and one token with fewer items
+# than waves (top-1 / 2 / 4); token counts and top-k around those paths.
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", [(200, 4096), (2048, 1792), (136, 608)])
-@pytest.mark.parametrize("m,top_k", [(2, 1), (3, 8), (5, 4), (8, 8)])
+@pytest.mark.parametrize("m,top_k", [(1, 1), (1, 2), (1, 4), (2, 1), (3, 8), (5, 4), (8, 8)])
 @pytest.mark.parametrize("mode", [q.MOE_GATE_UP, q.MOE_DOWN_COMBINE])
 def test_moe_several_tokens_few_tiles(dev, fmt, n, k, m, top_k, mode):
     E = 12
